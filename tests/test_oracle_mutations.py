@@ -1,0 +1,107 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each case swaps one oracle function for a plausibly wrong variant (dropped
+term, wrong index, wrong tie rule, transposed operand) and runs the pins
+that should catch it; the pins must fail.  The real oracle is restored
+afterwards.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import tr_oracle as O
+import tests.test_oracle_pins as P
+
+
+def _bonus_from_parent(t, tok, greedy):
+    v = ORIG["verify"](t, tok, greedy)
+    par = v.path[-2] if len(v.path) > 1 else 0
+    v.bonus = int(greedy[par])
+    v.emitted = np.concatenate([tok[v.path[1:]], [v.bonus]])
+    return v
+
+
+def _first_match_walk(t, tok, greedy):
+    # walks the first accepted child only (not the globally deepest node)
+    n = 0
+    while True:
+        nxt = [c for c in t.children(n) if tok[c] == greedy[n]]
+        if not nxt:
+            break
+        n = nxt[0]
+    path = np.array(t.ancestors[n])
+    return O.Verdict(len(path) - 1, path, int(greedy[n]),
+                     np.concatenate([tok[path[1:]], [greedy[n]]]))
+
+
+def _topk_ties_high_id(z, k):
+    z = np.asarray(z, dtype=np.float64)
+    ids = np.lexsort((-np.arange(len(z)), -z))[:k]
+    return ids
+
+
+def _update_first_writer(M, tok, topk):
+    for n in reversed(range(len(tok))):
+        M[tok[n], :] = topk[n, : M.shape[1]]
+
+
+def _update_accepted_only_root(M, tok, topk):
+    M[tok[0], :] = topk[0, : M.shape[1]]
+
+
+def _retrieve_rank_off(t, M, root):
+    tok = np.empty(t.n_nodes, dtype=np.int64)
+    tok[0] = root
+    for n in range(1, t.n_nodes):
+        tok[n] = M[tok[t.parent[n]], min(t.rank[n] + 1, M.shape[1] - 1)]
+    return tok
+
+
+def _mask_without_self(t):
+    m = ORIG["ancestor_mask"](t)
+    np.fill_diagonal(m, False)
+    m[0, 0] = True
+    return m
+
+
+def _attention_no_scale(t, q, kt, vt, kc, vc, P_, scale=None):
+    return ORIG["tree_attention"](t, q, kt, vt, kc, vc, P_, 1.0)
+
+
+def _attention_wrong_group(t, q, kt, vt, kc, vc, P_, scale=None):
+    # interleaved instead of contiguous head groups
+    Hq, Hkv = q.shape[1], kt.shape[1]
+    perm = [(h % Hkv) * (Hq // Hkv) + h // Hkv for h in range(Hq)]
+    return ORIG["tree_attention"](t, q[:, perm], kt, vt, kc, vc, P_, scale)[:, np.argsort(perm)]
+
+
+ORIG = {name: getattr(O, name) for name in
+        ("verify", "topk_row", "update", "retrieve", "ancestor_mask", "tree_attention")}
+
+CASES = [
+    ("verify", _bonus_from_parent, [P.test_worked_example_verify_and_update,
+                                    P.test_verify_matches_path_enumeration,
+                                    P.test_lossless_first_order_target]),
+    ("verify", _first_match_walk, [P.test_verify_matches_path_enumeration]),
+    ("topk_row", _topk_ties_high_id, [P.test_topk_matches_full_sort_with_ties]),
+    ("update", _update_first_writer, [P.test_update_last_writer_wins_brute_force]),
+    ("update", _update_accepted_only_root, [P.test_worked_example_verify_and_update]),
+    ("retrieve", _retrieve_rank_off, [P.test_worked_example_retrieval_gives_merged_sequence,
+                                      P.test_retrieve_matches_recursive_definition]),
+    ("ancestor_mask", _mask_without_self, [P.test_worked_example_mask,
+                                           P.test_mask_invariants_random,
+                                           P.test_attention_matches_per_path_brute_force]),
+    ("tree_attention", _attention_no_scale, [P.test_chain_tree_is_causal_attention,
+                                             P.test_single_node_is_decode_attention]),
+    ("tree_attention", _attention_wrong_group, [P.test_attention_gqa_grouping_uses_contiguous_heads,
+                                                P.test_attention_matches_per_path_brute_force]),
+]
+
+
+@pytest.mark.parametrize("name,bad,pins", CASES, ids=[f"{c[0]}:{c[1].__name__}" for c in CASES])
+def test_planted_mistake_is_caught(monkeypatch, name, bad, pins):
+    monkeypatch.setattr(O, name, bad)
+    for pin in pins:
+        with pytest.raises(AssertionError):
+            pin()

@@ -1,0 +1,429 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Each test pins the oracle to something other than itself: the worked example
+printed by the Token Recycling walk-through, closed forms, brute-force
+definitions written a different way, and special cases that reduce to a
+textbook or library routine.  CPU only.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import tr_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def load_example():
+    with open(os.path.join(GOLDEN, "worked_example.json")) as f:
+        ex = json.load(f)
+    ids = {name: i for i, name in enumerate(ex["vocab"])}
+    V, k = len(ex["vocab"]), ex["k"]
+    M = np.full((V, k), ids["pad"], dtype=np.int64)
+    for name, row in ex["M_pre"].items():
+        M[ids[name]] = [ids[x] for x in row]
+    logits = np.zeros((len(ex["logits"]), V), dtype=np.float32)
+    for n, row in enumerate(ex["logits"]):
+        for name, val in row.items():
+            logits[n, ids[name]] = val
+    return ex, ids, M, logits
+
+
+# ---------------------------------------------------------------- worked example
+def test_worked_example_template():
+    ex, ids, M, _ = load_example()
+    t = O.template_from_levels(ex["levels"])
+    assert t.parent.tolist() == ex["parent"]
+    assert t.rank.tolist() == ex["rank"]
+
+
+def test_worked_example_retrieval_gives_merged_sequence():
+    ex, ids, M, _ = load_example()
+    t = O.template_from_levels(ex["levels"])
+    tok = O.retrieve(t, M, ids[ex["root"]])
+    assert [ex["vocab"][x] for x in tok] == ex["merged_sequence"]
+
+
+def test_worked_example_mask():
+    ex, ids, M, _ = load_example()
+    t = O.template_from_levels(ex["levels"])
+    tok = O.retrieve(t, M, ids[ex["root"]])
+    mask = O.ancestor_mask(t)
+    names = ex["merged_sequence"]
+    for node_name, seen in ex["visible"].items():
+        n = names.index(node_name)
+        assert sorted(names[j] for j in np.flatnonzero(mask[n])) == sorted(seen)
+    # siblings never see each other (speaker/speak/event; at/for)
+    for a, b in ((1, 2), (1, 3), (2, 3), (4, 5)):
+        assert not mask[a, b] and not mask[b, a]
+
+
+def test_worked_example_verify_and_update():
+    ex, ids, M, logits = load_example()
+    t = O.template_from_levels(ex["levels"])
+    tok = O.retrieve(t, M, ids[ex["root"]])
+    res, _ = O.step_after_forward(t, M, tok, logits, ex["k"])
+    e = ex["expected"]
+    assert res.verdict.accept_len == e["accept_len"]
+    assert res.verdict.path.tolist() == e["path"]
+    assert ex["vocab"][res.verdict.bonus] == e["bonus"]
+    assert [ex["vocab"][x] for x in res.verdict.emitted] == e["emitted"]
+    for name, row in e["M_post"].items():
+        assert [ex["vocab"][x] for x in M[ids[name]]] == row, name
+    # rows of tokens outside the tree are untouched
+    for name in ex["vocab"]:
+        if name not in e["M_post"]:
+            assert (M[ids[name]] == ids["pad"]).all()
+    assert [ex["vocab"][x] for x in res.next_tok] == e["next_tree"]
+
+
+def test_storage_closed_form():
+    # V=32000, K=8, 64-bit ids: exactly 2,048,000 bytes, about 1.95 MiB, under 2 MB (MiB)
+    assert O.storage_bytes(32000, 8, 8) == 2_048_000
+    assert np.zeros((32000, 8), dtype=np.int64).nbytes == 2_048_000
+    assert abs(2_048_000 / 2 ** 20 - 1.953) < 1e-3
+
+
+# ---------------------------------------------------------------- templates
+def test_workload_trees():
+    from synth.workloads import TREE_16, TREE_81
+    t16 = O.template_from_levels(TREE_16)
+    assert t16.n_nodes == 16 and t16.max_depth == 3
+    # rank-0 chain 0 -> 1 -> 5 -> 13
+    assert [t16.parent[13], t16.parent[5], t16.parent[1]] == [5, 1, 0]
+    assert t16.rank[13] == t16.rank[5] == t16.rank[1] == 0
+    t81 = O.template_from_levels(TREE_81)
+    assert t81.n_nodes == 81 and t81.max_depth == 6
+    assert np.bincount(t81.depth).tolist() == [1, 8, 20, 22, 18, 10, 2]
+    # imbalanced: within a layer, child counts never increase
+    for d in range(6):
+        layer = np.flatnonzero(t81.depth == d)
+        counts = [len(t81.children(n)) for n in layer]
+        assert counts == sorted(counts, reverse=True)
+
+
+def random_levels(rng, k, max_depth=4, max_nodes=24):
+    levels, width = [], 1
+    for _ in range(rng.integers(1, max_depth + 1)):
+        counts = [int(rng.integers(0, k + 1)) for _ in range(width)]
+        counts = sorted(counts, reverse=True)
+        if sum(counts) == 0 or 1 + sum(sum(l) for l in levels) + sum(counts) > max_nodes:
+            break
+        levels.append(counts)
+        width = sum(counts)
+    return levels or [[1]]
+
+
+def test_mask_invariants_random():
+    rng = np.random.default_rng(1)
+    for _ in range(50):
+        t = O.template_from_levels(random_levels(rng, 4))
+        mask = O.ancestor_mask(t)
+        for n in range(t.n_nodes):
+            row = np.flatnonzero(mask[n])
+            assert len(row) == t.depth[n] + 1
+            assert row[0] == 0 and row[-1] == n and (row <= n).all()
+            # a chain: each visible node's parent is visible too
+            for j in row[1:]:
+                assert mask[n, t.parent[j]]
+            # siblings (other children of the same parent) are never visible
+            if n:
+                sib = [m for m in t.children(int(t.parent[n])) if m != n]
+                assert not mask[n, sib].any()
+
+
+def test_template_rejects_bad_input():
+    with pytest.raises(ValueError):
+        O.Template(np.array([-1, 1]), np.array([-1, 0]))        # parent after child
+    with pytest.raises(ValueError):
+        O.Template(np.array([-1, 0, 0]), np.array([-1, 0, 0]))  # duplicate rank
+    with pytest.raises(ValueError):
+        O.Template(np.array([-1, 0, 1, 0]), np.array([-1, 0, 0, 1]))  # not layer order
+
+
+# ---------------------------------------------------------------- retrieval
+def retrieve_recursive(t, M, root):
+    """Brute-force definition: expand the tree depth-first, recursively."""
+    tok = {}
+
+    def expand(n, token):
+        tok[n] = token
+        for c in t.children(n):
+            expand(c, M[token, t.rank[c]])
+    expand(0, root)
+    return np.array([tok[n] for n in range(t.n_nodes)])
+
+
+def test_retrieve_matches_recursive_definition():
+    rng = np.random.default_rng(2)
+    for _ in range(100):
+        k = int(rng.integers(1, 5))
+        V = int(rng.integers(2, 12))
+        t = O.template_from_levels(random_levels(rng, k))
+        M = rng.integers(0, V, size=(V, k))
+        root = int(rng.integers(0, V))
+        assert (O.retrieve(t, M, root) == retrieve_recursive(t, M, root)).all()
+
+
+# ---------------------------------------------------------------- top-k
+def topk_full_sort(z, k):
+    return [i for _, i in sorted(((-float(z[i]), i) for i in range(len(z))))[:k]]
+
+
+def test_topk_matches_full_sort_with_ties():
+    rng = np.random.default_rng(3)
+    for _ in range(300):
+        V = int(rng.integers(1, 60))
+        k = int(rng.integers(1, V + 1))
+        z = rng.integers(-3, 4, size=V).astype(np.float32) * 0.5     # many ties
+        if rng.random() < 0.3:
+            z[rng.integers(0, V, size=max(1, V // 4))] = -0.0
+        if rng.random() < 0.2:
+            z[rng.integers(0, V)] = np.inf
+        if rng.random() < 0.2:
+            z[rng.integers(0, V)] = -np.inf
+        assert O.topk_row(z, k).tolist() == topk_full_sort(z, k)
+
+
+def test_topk_signed_zero_and_infinities():
+    z = np.array([-0.0, 0.0, -np.inf, -0.0, np.inf, -np.inf], dtype=np.float32)
+    assert O.topk_row(z, 4).tolist() == [4, 0, 1, 3]
+    assert O.topk_row(z, 6).tolist() == [4, 0, 1, 3, 2, 5]
+
+
+def test_topk_bf16_rows_invariants():
+    g = torch.Generator().manual_seed(4)
+    Z = (torch.randn((8, 32000), generator=g) * 3).to(torch.bfloat16).float().numpy()
+    for z in Z:
+        ids = O.topk_row(z, 8)
+        assert len(set(ids.tolist())) == 8
+        rest = np.delete(z, ids)
+        assert z[ids].min() >= rest.max()
+        for a, b in zip(ids[:-1], ids[1:]):
+            assert z[a] > z[b] or (z[a] == z[b] and a < b)
+        assert ids.tolist() == topk_full_sort(z, 8)
+
+
+# ---------------------------------------------------------------- verification
+def verify_enumerate(t, tok, greedy):
+    """Brute force: enumerate every root-to-node path, keep the correct ones
+    (each token equals the target's greedy token after its predecessor), pick
+    the longest, ties to the smaller end node."""
+    best = (0, 0)
+    for n in range(t.n_nodes):
+        path = t.ancestors[n]
+        ok = all(tok[path[i + 1]] == greedy[path[i]] for i in range(len(path) - 1))
+        if ok and (len(path) - 1, -n) > (best[0], -best[1]):
+            best = (len(path) - 1, n)
+    L, n = best
+    return L, list(t.ancestors[n]), int(greedy[n])
+
+
+def test_verify_matches_path_enumeration():
+    rng = np.random.default_rng(5)
+    for _ in range(300):
+        k = int(rng.integers(1, 5))
+        V = int(rng.integers(2, 6))            # tiny vocab: many matches and duplicates
+        t = O.template_from_levels(random_levels(rng, k))
+        tok = rng.integers(0, V, size=t.n_nodes)
+        greedy = rng.integers(0, V, size=t.n_nodes)
+        v = O.verify(t, tok, greedy)
+        L, path, bonus = verify_enumerate(t, tok, greedy)
+        assert (v.accept_len, v.path.tolist(), v.bonus) == (L, path, bonus)
+        assert v.emitted.tolist() == [int(tok[x]) for x in path[1:]] + [bonus]
+
+
+def linear_greedy_loop(draft, target_next):
+    """The draft/verify loop with the bonus token, greedy form: accept drafts
+    while they equal the target's token; on the first miss emit the target's
+    token and stop; if every draft passed, emit the target's next token."""
+    out = []
+    for j, tokn in enumerate(draft):
+        if tokn == target_next[j]:
+            out.append(tokn)
+        else:
+            out.append(target_next[j])
+            break
+    else:
+        out.append(target_next[len(draft)])
+    return out
+
+
+def test_chain_tree_reduces_to_linear_loop():
+    rng = np.random.default_rng(6)
+    for gamma in range(1, 6):
+        t = O.template_from_levels([[1]] * gamma)
+        for _ in range(100):
+            tok = rng.integers(0, 3, size=gamma + 1)
+            greedy = rng.integers(0, 3, size=gamma + 1)
+            v = O.verify(t, tok, greedy)
+            assert v.emitted.tolist() == linear_greedy_loop(tok[1:].tolist(), greedy.tolist())
+
+
+def test_expected_tokens_per_pass_closed_form():
+    # (1 - a^(g+1)) / (1 - a) at a=0.8, g=4 is about 3.4 tokens per target pass
+    alpha, gamma, trials = 0.8, 4, 40000
+    expect = (1 - alpha ** (gamma + 1)) / (1 - alpha)
+    assert abs(expect - 3.3616) < 1e-9
+    rng = np.random.default_rng(7)
+    t = O.template_from_levels([[1]] * gamma)
+    total = 0
+    for _ in range(trials):
+        tok = np.arange(gamma + 1) + 10
+        hit = rng.random(gamma) < alpha
+        greedy = np.where(np.append(hit, False), np.append(tok[1:], 0), 0)
+        total += len(O.verify(t, tok, greedy).emitted)
+    assert abs(total / trials - expect) < 0.03
+
+
+# ---------------------------------------------------------------- update
+def test_update_last_writer_wins_brute_force():
+    rng = np.random.default_rng(8)
+    for _ in range(200):
+        V, k, T = 6, 3, int(rng.integers(1, 12))
+        M = rng.integers(0, V, size=(V, k))
+        M0 = M.copy()
+        tok = rng.integers(0, V, size=T)                 # many duplicated tokens
+        top = rng.integers(0, V, size=(T, k))
+        O.update(M, tok, top)
+        for v in range(V):
+            writers = [n for n in range(T) if tok[n] == v]
+            want = top[max(writers)] if writers else M0[v]
+            assert (M[v] == want).all()
+
+
+# ---------------------------------------------------------------- attention
+def attention_per_path(t, q, kt, vt, kc, vc, P, scale):
+    """Textbook attention for one node at a time: its key sequence is the
+    prefix followed by the tree nodes on its own path; plain loops."""
+    T, Hq, d = q.shape
+    G = Hq // kt.shape[1]
+    out = np.zeros((T, Hq, d))
+    for n in range(T):
+        for h in range(Hq):
+            kh = h // G
+            keys = [kc[kh, j] for j in range(P)] + [kt[j, kh] for j in t.ancestors[n]]
+            vals = [vc[kh, j] for j in range(P)] + [vt[j, kh] for j in t.ancestors[n]]
+            s = [float(np.dot(q[n, h], kk)) * scale for kk in keys]
+            m = max(s)
+            w = [math.exp(x - m) for x in s]
+            tot = sum(w)
+            out[n, h] = sum(wi * vv for wi, vv in zip(w, vals)) / tot
+    return out
+
+
+def rand_attn(rng, T, Hq, Hkv, d, P, cap=None):
+    cap = cap or P + 3
+    return (rng.standard_normal((T, Hq, d)), rng.standard_normal((T, Hkv, d)),
+            rng.standard_normal((T, Hkv, d)), rng.standard_normal((Hkv, cap, d)),
+            rng.standard_normal((Hkv, cap, d)))
+
+
+def test_attention_matches_per_path_brute_force():
+    rng = np.random.default_rng(9)
+    for levels, Hq, Hkv, P in (([[3], [2, 1]], 2, 2, 5), ([[2], [2, 1], [1]], 4, 2, 0),
+                               ([[4], [1, 1, 1, 1]], 6, 3, 3)):
+        t = O.template_from_levels(levels)
+        q, kt, vt, kc, vc = rand_attn(rng, t.n_nodes, Hq, Hkv, 8, P)
+        got = O.tree_attention(t, q, kt, vt, kc, vc, P, 0.3)
+        want = attention_per_path(t, q, kt, vt, kc, vc, P, 0.3)
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_chain_tree_is_causal_attention():
+    # a chain tree is ordinary causal attention over prefix ++ chain (library SDPA)
+    rng = np.random.default_rng(10)
+    T, H, d, P = 5, 3, 16, 7
+    t = O.template_from_levels([[1]] * (T - 1))
+    q, kt, vt, kc, vc = rand_attn(rng, T, H, H, d, P)
+    got = O.tree_attention(t, q, kt, vt, kc, vc, P)
+    Kseq = np.concatenate([kc[:, :P], kt.transpose(1, 0, 2)], axis=1)          # [H, P+T, d]
+    Vseq = np.concatenate([vc[:, :P], vt.transpose(1, 0, 2)], axis=1)
+    Qseq = np.concatenate([np.zeros((H, P, d)), q.transpose(1, 0, 2)], axis=1)  # queries at every position
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Qseq)[None], torch.from_numpy(Kseq)[None], torch.from_numpy(Vseq)[None],
+        is_causal=True)[0, :, P:].numpy().transpose(1, 0, 2)
+    np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_single_node_is_decode_attention():
+    rng = np.random.default_rng(11)
+    t = O.template_from_levels([])
+    q, kt, vt, kc, vc = rand_attn(rng, 1, 4, 4, 16, 9)
+    got = O.tree_attention(t, q, kt, vt, kc, vc, 9)
+    K = torch.from_numpy(np.concatenate([kc[:, :9], kt.transpose(1, 0, 2)], axis=1))
+    V = torch.from_numpy(np.concatenate([vc[:, :9], vt.transpose(1, 0, 2)], axis=1))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q.transpose(1, 0, 2))[None], K[None], V[None])[0].numpy().transpose(1, 0, 2)
+    np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_attention_ignores_non_ancestors():
+    rng = np.random.default_rng(12)
+    t = O.template_from_levels([[3], [2, 1], [1]])
+    q, kt, vt, kc, vc = rand_attn(rng, t.n_nodes, 2, 1, 8, 4)
+    base = O.tree_attention(t, q, kt, vt, kc, vc, 4)
+    mask = O.ancestor_mask(t)
+    for j in range(t.n_nodes):
+        kt2, vt2 = kt.copy(), vt.copy()
+        kt2[j] += 5.0
+        vt2[j] -= 3.0
+        out = O.tree_attention(t, q, kt2, vt2, kc, vc, 4)
+        for n in range(t.n_nodes):
+            if mask[n, j]:
+                assert not np.allclose(out[n], base[n])
+            else:
+                assert (out[n] == base[n]).all()
+
+
+def test_attention_gqa_grouping_uses_contiguous_heads():
+    rng = np.random.default_rng(13)
+    t = O.template_from_levels([[2]])
+    q, kt, vt, kc, vc = rand_attn(rng, 3, 4, 2, 8, 3)
+    out = O.tree_attention(t, q, kt, vt, kc, vc, 3)
+    # heads 0,1 use kv head 0; heads 2,3 use kv head 1: compare with MHA on repeated kv
+    mha = O.tree_attention(t, q, np.repeat(kt, 2, axis=1), np.repeat(vt, 2, axis=1),
+                           np.repeat(kc, 2, axis=0), np.repeat(vc, 2, axis=0), 3)
+    np.testing.assert_allclose(out, mha, rtol=1e-13)
+
+
+# ---------------------------------------------------------------- whole loop
+def test_lossless_first_order_target():
+    """With a target whose greedy next token depends only on the last token,
+    the stream the loop emits equals plain greedy decoding, token for token."""
+    rng = np.random.default_rng(14)
+    for trial in range(20):
+        V, k = int(rng.integers(5, 40)), int(rng.integers(1, 5))
+        t = O.template_from_levels(random_levels(rng, k, max_depth=4))
+        H = rng.integers(0, V, size=V)
+        M = rng.integers(0, V, size=(V, k))
+        root = int(rng.integers(0, V))
+        tok = O.retrieve(t, M, root)
+        stream = []
+        for s in range(15):
+            logits = rng.standard_normal((t.n_nodes, V))
+            logits[np.arange(t.n_nodes), H[tok]] = logits.max(axis=1) + 1.0
+            res, _ = O.step_after_forward(t, M, tok, logits, k)
+            stream += res.verdict.emitted.tolist()
+            tok = res.next_tok
+        greedy = [root]
+        for _ in range(len(stream)):
+            greedy.append(int(H[greedy[-1]]))
+        assert stream == greedy[1:]
+
+
+def test_commit_appends_path_rows():
+    rng = np.random.default_rng(15)
+    kc = np.zeros((2, 10, 4)); vc = np.zeros((2, 10, 4))
+    kt = rng.standard_normal((5, 2, 4)); vt = rng.standard_normal((5, 2, 4))
+    P = O.commit(kc, vc, kt, vt, 3, [0, 2, 4])
+    assert P == 6
+    assert (kc[:, 3] == kt[0]).all() and (kc[:, 4] == kt[2]).all() and (vc[:, 5] == vt[4]).all()
+    assert (kc[:, :3] == 0).all() and (kc[:, 6:] == 0).all()
+    with pytest.raises(ValueError):
+        O.commit(kc, vc, kt, vt, 8, [0, 1, 2])
