@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Benchmark of the Token Recycling step hot path on one MI355X.
+
+One step = tr_tree_attn (tree attention of the merged sequence against the
+prefix cache, one layer) + tr_step (top-k of every node's logits,
+verification, update of M, commit of the accepted path, retrieval of the
+next tree).  Default workload: the Vicuna-7B-shaped step loop (V=32000,
+k=8, 81-node depth-6 tree, 32 heads x d=128 bf16, 2048-token prefix, 256
+steps).
+
+Protocol: a record pass runs the whole trajectory once and keeps every
+step's synthetic inputs (queries, tree keys/values, logits with the planted
+continuation of that step's tree) in HBM.  The state is then reset to the
+start and the same trajectory is replayed: `--warmup` steps untimed, then
+`--steps` steps timed between two device synchronisations, with HIP events
+around every call on the launch stream.  The replay must end in the same
+state as the record pass (checked).  Prints one JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "TR steps/sec (retrieve+tree-attn+verify+top-k update); achieved HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default: the workload's)")
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="vicuna7b")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="budget of the CPU oracle baseline (0 disables it)")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, inputs, init_host, seconds):
+    """The CPU oracle, as it stands, on the first steps of the same trajectory."""
+    import numpy as np
+    from oracle import tr_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    t = O.template_from_levels(w.levels)
+    b = 0
+    M = init_host.M[b].numpy().astype(np.int64).copy()
+    kc = init_host.k_cache[b].float().numpy().copy()
+    vc = init_host.v_cache[b].float().numpy().copy()
+    P = int(init_host.prefix_len[b])
+    tok = O.retrieve(t, M, int(init_host.root[b]))
+    done, elapsed = 0, 0.0
+    for (q, kt, vt, z) in inputs:
+        if elapsed >= seconds:
+            break
+        qh, kth, vth, zh = (x[b].float().cpu().numpy() for x in (q, kt, vt, z))
+        t0 = time.perf_counter()
+        O.tree_attention(t, qh, kth, vth, kc, vc, P)
+        res, P = O.step_after_forward(t, M, tok, zh, w.k, kc, vc, kth, vth, P)
+        tok = res.next_tok
+        elapsed += time.perf_counter() - t0
+        done += 1
+    return {"value": done * w.B / elapsed if elapsed else None, "unit": "steps/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"first {done} steps of the same trajectory, sequence 0 of {w.B} "
+                      f"(tree attention + top-k + verify + update + commit + retrieve, float64 "
+                      f"numpy), {elapsed:.1f} s of CPU time; value scaled to all {w.B} sequences"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(sequences shard across GPUs with no exchange; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from draft_tree_retrieval_amd import tr
+    from draft_tree_retrieval_amd.loop import TRDecoder
+    from synth import workloads as W
+
+    tr.load()
+    w = W.WORKLOADS[args.workload]
+    steps = args.steps if args.steps is not None else w.steps
+    total = args.warmup + steps
+    dev = "cuda"
+    init = W.initial_state(w, dev, cap=w.cap(total))
+    init_host = init.to("cpu")
+    tree = tr.Tree.from_levels(w.levels, w.k)
+
+    # ---- record pass: the trajectory's inputs, kept in HBM
+    t0 = time.time()
+    st = init.clone()
+    dec = TRDecoder(tree, st.M, st.k_cache, st.v_cache, st.prefix_len, st.root, Hq=w.Hq)
+    out = torch.empty((w.B, w.T, w.Hq, w.d), dtype=w.kv_dtype, device=dev)
+    inputs, prefix_hist, accepted = [], [], []
+    for s in range(total):
+        q, kt, vt = W.step_qkv(w, s, dev)
+        z = W.step_logits(w, s, dec.tree_tok, dev)
+        prefix_hist.append(dec.prefix_len.clone())
+        dec.attend(q, kt, vt, out)
+        dec.step(z, kt, vt)
+        accepted.append(dec.accept_len.clone())
+        inputs.append((q, kt, vt, z))
+    torch.cuda.synchronize()
+    rec_tok, rec_M = dec.tree_tok.clone(), dec.M.clone()
+    assert dec.device_flags() == 0
+    prefix_hist = torch.stack(prefix_hist).cpu()          # [total, B]
+    accepted = torch.stack(accepted).cpu()
+    log(f"record pass: {total} steps in {time.time() - t0:.1f} s")
+
+    # ---- replay: warmup, then the timed region
+    st = init.clone()
+    dec = TRDecoder(tree, st.M, st.k_cache, st.v_cache, st.prefix_len, st.root, Hq=w.Hq)
+    stream = torch.cuda.current_stream()
+    for s in range(args.warmup):
+        q, kt, vt, z = inputs[s]
+        dec.attend(q, kt, vt, out)
+        dec.step(z, kt, vt)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(steps):
+        q, kt, vt, z = inputs[args.warmup + i]
+        ev[i][0].record(stream)
+        dec.attend(q, kt, vt, out)
+        ev[i][1].record(stream)
+        dec.step(z, kt, vt)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    same = torch.equal(dec.tree_tok, rec_tok) and torch.equal(dec.M, rec_M)
+    assert same, "replay diverged from the record pass"
+    assert dec.device_flags() == 0
+
+    attn_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    step_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    ms_per_step = wall * 1e3 / steps
+
+    # ---- algorithmic bytes per call (what the method must move)
+    esz = torch.tensor([], dtype=w.kv_dtype).element_size()
+    lsz = torch.tensor([], dtype=w.logit_dtype).element_size()
+    timed = slice(args.warmup, total)
+    P_sum = prefix_hist[timed].double().sum(dim=1)        # prefix positions per step, all sequences
+    kv_bytes = (P_sum * w.Hkv * w.d * 2 * esz).mean().item()
+    qo_bytes = 2 * w.B * w.T * w.Hq * w.d * esz
+    tkv_bytes = 2 * w.B * w.T * w.Hkv * w.d * esz
+    attn_bytes = kv_bytes + qo_bytes + tkv_bytes
+    L_mean = accepted[timed].double().mean().item()
+    commit_bytes = 2 * 2 * (L_mean + 1) * w.Hkv * w.d * esz * w.B   # K and V rows, read + write
+    logits_bytes = w.B * w.T * w.V * lsz
+    m_bytes = w.B * w.T * w.k * 4 * 2                              # rows written + read back
+    step_bytes = logits_bytes + commit_bytes + m_bytes
+    calls = {
+        "tr_tree_attn": (attn_ms, attn_bytes),
+        "tr_step": (step_ms, step_bytes),
+    }
+    dom = max(calls, key=lambda c: calls[c][0])
+    dms, dbytes = calls[dom]
+    achieved = dbytes / (dms * 1e-3) / 1e9
+    detail = {c: {"avg_us": round(ms * 1e3, 2), "bytes": int(b),
+                  "GB_s": round(b / (ms * 1e-3) / 1e9, 1)} for c, (ms, b) in calls.items()}
+    log("per call:", json.dumps(detail))
+    log(f"mean accepted drafts {L_mean:.3f}, emitted/step {L_mean + 1:.3f}")
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(w, inputs, init_host, args.cpu_seconds)
+
+    res = {
+        "metric": METRIC,
+        "value": round(steps / wall, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.kv_dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.description, "V": w.V, "k": w.k, "sequences": w.B,
+                   "tree_nodes": w.T, "tree_depth": w.depth, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "head_dim": w.d, "prefix": list(w.prefix), "M_dtype": str(w.m_dtype)[6:]},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None},
+        "per_call": detail,
+        "emitted_per_step": round(L_mean + 1, 3),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

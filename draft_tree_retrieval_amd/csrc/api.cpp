@@ -1,0 +1,358 @@
+// extern "C" entry points of libtr: argument checks on the host, then the
+// kernel launches.  No call here allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "tr_internal.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+tr_status fail(tr_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+tr_status ok() {
+  g_err[0] = 0;
+  return TR_OK;
+}
+
+tr_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(TR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define TR_CHECK(cond, status, ...) \
+  do {                              \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+tr_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  TR_CHECK(ws != nullptr, TR_ERR_INVALID_ARGUMENT, "workspace is null");
+  TR_CHECK((reinterpret_cast<uintptr_t>(ws) & 255) == 0, TR_ERR_INVALID_ARGUMENT,
+           "workspace must be 256-byte aligned");
+  TR_CHECK(ws_bytes >= need, TR_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu",
+           ws_bytes, need);
+  return TR_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Builds the template from parent/rank and checks it: root first, parents
+// before children, distinct ranks below k under one parent, layer order.
+tr_status build_tree(int32_t n, const int32_t* parent, const int32_t* rank, int32_t k,
+                     tr_tree** out) {
+  TR_CHECK(out != nullptr, TR_ERR_INVALID_ARGUMENT, "out is null");
+  *out = nullptr;
+  TR_CHECK(parent && rank, TR_ERR_INVALID_ARGUMENT, "parent/rank is null");
+  TR_CHECK(n >= 1 && n <= tr::kMaxNodes, TR_ERR_INVALID_ARGUMENT, "n_nodes %d outside 1..%d", n,
+           tr::kMaxNodes);
+  TR_CHECK(k >= 1 && k <= tr::kMaxK, TR_ERR_INVALID_ARGUMENT, "k %d outside 1..%d", k, tr::kMaxK);
+  TR_CHECK(parent[0] == -1 && rank[0] == -1, TR_ERR_INVALID_TREE,
+           "node 0 must be the root (parent -1, rank -1)");
+  tr_tree* t = new (std::nothrow) tr_tree();
+  TR_CHECK(t != nullptr, TR_ERR_INVALID_ARGUMENT, "out of host memory");
+  t->k = k;
+  t->dev.T = n;
+  t->dev.D = 0;
+  t->dev.parent[0] = 0xFF;
+  t->dev.rank[0] = 0xFF;
+  t->dev.depth[0] = 0;
+  std::memset(t->anc, 0, sizeof t->anc);
+  t->anc[0][0] = 1;
+  std::vector<uint32_t> used(size_t(n), 0);   // rank bitmask per parent
+  int prev_d = 0, prev_p = -1, prev_r = -1;
+  for (int i = 1; i < n; ++i) {
+    const int p = parent[i], r = rank[i];
+    if (p < 0 || p >= i) { delete t; return fail(TR_ERR_INVALID_TREE, "node %d: parent %d must precede it", i, p); }
+    if (r < 0 || r >= k) { delete t; return fail(TR_ERR_INVALID_TREE, "node %d: rank %d outside 0..k-1", i, r); }
+    if (used[p] & (1u << r)) { delete t; return fail(TR_ERR_INVALID_TREE, "node %d: rank %d repeated under parent %d", i, r, p); }
+    used[p] |= 1u << r;
+    const int d = t->dev.depth[p] + 1;
+    const bool in_order = d > prev_d || (d == prev_d && (p > prev_p || (p == prev_p && r > prev_r)));
+    if (!in_order) { delete t; return fail(TR_ERR_INVALID_TREE, "node %d breaks layer order (depth, parent, rank)", i); }
+    prev_d = d; prev_p = p; prev_r = r;
+    t->dev.parent[i] = uint8_t(p);
+    t->dev.rank[i] = uint8_t(r);
+    t->dev.depth[i] = uint8_t(d);
+    if (d > t->dev.D) t->dev.D = d;
+    t->anc[i][0] = t->anc[p][0];
+    t->anc[i][1] = t->anc[p][1];
+    t->anc[i][i >> 6] |= uint64_t(1) << (i & 63);
+  }
+  for (int i = n; i < tr::kMaxNodes; ++i) {
+    t->dev.parent[i] = 0xFF;
+    t->dev.rank[i] = 0xFF;
+    t->dev.depth[i] = 0xFF;
+  }
+  *out = t;
+  return ok();
+}
+
+size_t topk_need(const tr_tree* t, int32_t B, int64_t V, int32_t k) {
+  return tr::plan_topk(int64_t(B) * t->dev.T, V, k).end;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tr_status_string(tr_status s) {
+  switch (s) {
+    case TR_OK: return "TR_OK";
+    case TR_ERR_INVALID_ARGUMENT: return "TR_ERR_INVALID_ARGUMENT";
+    case TR_ERR_UNSUPPORTED: return "TR_ERR_UNSUPPORTED";
+    case TR_ERR_INVALID_TREE: return "TR_ERR_INVALID_TREE";
+    case TR_ERR_WORKSPACE_TOO_SMALL: return "TR_ERR_WORKSPACE_TOO_SMALL";
+    case TR_ERR_HIP: return "TR_ERR_HIP";
+  }
+  return "TR_UNKNOWN_STATUS";
+}
+
+const char* tr_last_error(void) { return g_err; }
+
+tr_status tr_tree_create(int32_t n_nodes, const int32_t* parent, const int32_t* rank, int32_t k,
+                         tr_tree** out) {
+  return build_tree(n_nodes, parent, rank, k, out);
+}
+
+tr_status tr_tree_create_levels(int32_t n_levels, const int32_t* level_len, const int32_t* counts,
+                                int32_t k, tr_tree** out) {
+  TR_CHECK(out != nullptr, TR_ERR_INVALID_ARGUMENT, "out is null");
+  *out = nullptr;
+  TR_CHECK(n_levels >= 0 && (n_levels == 0 || (level_len && counts)), TR_ERR_INVALID_ARGUMENT,
+           "level arrays are null");
+  std::vector<int32_t> parent{-1}, rank{-1}, layer{0};
+  size_t pos = 0;
+  for (int l = 0; l < n_levels; ++l) {
+    TR_CHECK(level_len[l] >= 0 && size_t(level_len[l]) <= layer.size(), TR_ERR_INVALID_TREE,
+             "layer %d lists %d counts for %zu nodes", l, level_len[l], layer.size());
+    std::vector<int32_t> next;
+    for (int i = 0; i < level_len[l]; ++i) {
+      const int c = counts[pos++];
+      TR_CHECK(c >= 0 && c <= k, TR_ERR_INVALID_TREE, "layer %d node %d: %d children, k = %d", l, i, c, k);
+      for (int r = 0; r < c; ++r) {
+        parent.push_back(layer[size_t(i)]);
+        rank.push_back(r);
+        next.push_back(int32_t(parent.size()) - 1);
+        TR_CHECK(parent.size() <= size_t(tr::kMaxNodes), TR_ERR_INVALID_ARGUMENT,
+                 "more than %d nodes", tr::kMaxNodes);
+      }
+    }
+    layer.swap(next);
+  }
+  return build_tree(int32_t(parent.size()), parent.data(), rank.data(), k, out);
+}
+
+void tr_tree_destroy(tr_tree* t) { delete t; }
+
+tr_status tr_tree_info(const tr_tree* t, int32_t* n_nodes, int32_t* depth, int32_t* k,
+                       int32_t* parent_out, int32_t* rank_out, int32_t* depth_out,
+                       uint64_t* anc_out) {
+  TR_CHECK(t != nullptr, TR_ERR_INVALID_ARGUMENT, "tree is null");
+  if (n_nodes) *n_nodes = t->dev.T;
+  if (depth) *depth = t->dev.D;
+  if (k) *k = t->k;
+  for (int i = 0; i < t->dev.T; ++i) {
+    if (parent_out) parent_out[i] = i ? t->dev.parent[i] : -1;
+    if (rank_out) rank_out[i] = i ? t->dev.rank[i] : -1;
+    if (depth_out) depth_out[i] = t->dev.depth[i];
+    if (anc_out) {
+      anc_out[2 * i] = t->anc[i][0];
+      anc_out[2 * i + 1] = t->anc[i][1];
+    }
+  }
+  return ok();
+}
+
+size_t tr_workspace_size(const tr_tree* t, int32_t B, int64_t V, int32_t k, int32_t Hq,
+                         int32_t Hkv, int32_t d, int64_t cap) {
+  if (!t || B < 1) return 0;
+  size_t need = tr::kDataOff;
+  if (V >= 1 && k >= 1) {
+    size_t a = topk_need(t, B, V, k);
+    if (a > need) need = a;
+  }
+  if (Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0 && d == tr::kHeadDim && cap >= 0) {
+    size_t a = tr::plan_attn(t->dev.T, B, Hq, Hkv, cap).end;
+    if (a > need) need = a;
+  }
+  return need;
+}
+
+tr_status tr_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  tr_status st = check_ws(ws, ws_bytes, tr::kDataOff);
+  if (st != TR_OK) return st;
+  TR_CHECK(ws_bytes % 16 == 0, TR_ERR_INVALID_ARGUMENT, "workspace size must be a multiple of 16");
+  return hip_status(tr::launch_fill_zero(ws, ws_bytes, hipStream_t(stream)), "tr_workspace_init");
+}
+
+tr_status tr_read_device_status(void* ws, uint32_t* flags, void* stream) {
+  TR_CHECK(ws && flags, TR_ERR_INVALID_ARGUMENT, "null argument");
+  hipStream_t s = hipStream_t(stream);
+  hipError_t e = hipMemcpyAsync(flags, ws, 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e == hipSuccess && *flags) {
+    e = tr::launch_fill_zero(ws, 16, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+  }
+  return hip_status(e, "tr_read_device_status");
+}
+
+tr_status tr_retrieve(const tr_tree* t, int32_t B, const void* M, tr_dtype m_dtype, int64_t V,
+                      int32_t k, const int32_t* root_tok, int32_t* tree_tok, void* ws,
+                      size_t ws_bytes, void* stream) {
+  TR_CHECK(t != nullptr, TR_ERR_INVALID_ARGUMENT, "tree is null");
+  TR_CHECK(B >= 1, TR_ERR_INVALID_ARGUMENT, "B must be >= 1");
+  TR_CHECK(M && root_tok && tree_tok, TR_ERR_INVALID_ARGUMENT, "null tensor");
+  TR_CHECK(m_dtype == TR_INT32 || m_dtype == TR_INT64, TR_ERR_UNSUPPORTED, "M must be int32 or int64");
+  TR_CHECK(k == t->k, TR_ERR_INVALID_ARGUMENT, "k %d differs from the tree's %d", k, t->k);
+  TR_CHECK(V >= 1 && V <= INT32_MAX, TR_ERR_INVALID_ARGUMENT, "V outside 1..2^31-1");
+  tr_status st = check_ws(ws, ws_bytes, tr::kDataOff);
+  if (st != TR_OK) return st;
+  return hip_status(tr::launch_retrieve(t->dev, B, M, m_dtype == TR_INT64, V, k, root_tok, tree_tok,
+                                        static_cast<uint8_t*>(ws), hipStream_t(stream)),
+                    "tr_retrieve");
+}
+
+tr_status tr_tree_attn(const tr_tree* t, int32_t B, int32_t Hq, int32_t Hkv, int32_t d, tr_dtype dt,
+                       const void* q, const void* k_tree, const void* v_tree, const void* k_cache,
+                       const void* v_cache, int64_t cap, const int32_t* prefix_len, float scale,
+                       void* out, void* ws, size_t ws_bytes, void* stream) {
+  TR_CHECK(t != nullptr, TR_ERR_INVALID_ARGUMENT, "tree is null");
+  TR_CHECK(B >= 1, TR_ERR_INVALID_ARGUMENT, "B must be >= 1");
+  TR_CHECK(q && k_tree && v_tree && k_cache && v_cache && prefix_len && out,
+           TR_ERR_INVALID_ARGUMENT, "null tensor");
+  TR_CHECK(dt == TR_FLOAT32 || dt == TR_BFLOAT16, TR_ERR_UNSUPPORTED, "attention dtype must be float32 or bfloat16");
+  TR_CHECK(d == tr::kHeadDim, TR_ERR_UNSUPPORTED, "head dimension must be %d", tr::kHeadDim);
+  TR_CHECK(Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0, TR_ERR_INVALID_ARGUMENT,
+           "Hq (%d) must be a positive multiple of Hkv (%d)", Hq, Hkv);
+  TR_CHECK(cap >= 0, TR_ERR_INVALID_ARGUMENT, "negative capacity");
+  TR_CHECK(int64_t(B) * Hkv <= 65535, TR_ERR_UNSUPPORTED, "B*Hkv above 65535");
+  TR_CHECK(aligned16(q) && aligned16(k_tree) && aligned16(v_tree) && aligned16(k_cache) &&
+               aligned16(v_cache) && aligned16(out), TR_ERR_INVALID_ARGUMENT,
+           "attention tensors must be 16-byte aligned");
+  const tr::AttnPlan plan = tr::plan_attn(t->dev.T, B, Hq, Hkv, cap);
+  tr_status st = check_ws(ws, ws_bytes, plan.end);
+  if (st != TR_OK) return st;
+  return hip_status(tr::launch_attn(t->dev, B, Hq, Hkv, dt == TR_BFLOAT16, q, k_tree, v_tree, k_cache,
+                                    v_cache, cap, prefix_len, scale, out, static_cast<uint8_t*>(ws),
+                                    plan, hipStream_t(stream)),
+                    "tr_tree_attn");
+}
+
+static tr_status check_topk_args(const tr_tree* t, int32_t B, const void* logits, tr_dtype l_dtype,
+                                 int64_t V, int32_t k) {
+  TR_CHECK(t != nullptr, TR_ERR_INVALID_ARGUMENT, "tree is null");
+  TR_CHECK(B >= 1, TR_ERR_INVALID_ARGUMENT, "B must be >= 1");
+  TR_CHECK(logits != nullptr, TR_ERR_INVALID_ARGUMENT, "logits is null");
+  TR_CHECK(l_dtype == TR_FLOAT32 || l_dtype == TR_BFLOAT16, TR_ERR_UNSUPPORTED,
+           "logits must be float32 or bfloat16");
+  TR_CHECK(k == t->k, TR_ERR_INVALID_ARGUMENT, "k %d differs from the tree's %d", k, t->k);
+  TR_CHECK(V >= k && V <= INT32_MAX, TR_ERR_INVALID_ARGUMENT, "V must be in k..2^31-1");
+  TR_CHECK(int64_t(B) * t->dev.T <= int64_t(tr::kMaxRowCnt), TR_ERR_UNSUPPORTED,
+           "B * nodes above %zu", tr::kMaxRowCnt);
+  TR_CHECK(size_t(B) <= tr::kMaxSeqCnt, TR_ERR_UNSUPPORTED, "B above %zu", tr::kMaxSeqCnt);
+  const uintptr_t esz = l_dtype == TR_BFLOAT16 ? 2 : 4;
+  TR_CHECK((reinterpret_cast<uintptr_t>(logits) & (esz - 1)) == 0, TR_ERR_INVALID_ARGUMENT,
+           "logits must be aligned to their element size");
+  return TR_OK;
+}
+
+tr_status tr_update_topk(const tr_tree* t, int32_t B, const void* logits, tr_dtype l_dtype,
+                         int64_t V, int32_t k, const int32_t* tree_tok, void* M, tr_dtype m_dtype,
+                         int32_t* topk_out, void* ws, size_t ws_bytes, void* stream) {
+  tr_status st = check_topk_args(t, B, logits, l_dtype, V, k);
+  if (st != TR_OK) return st;
+  TR_CHECK(M || topk_out, TR_ERR_INVALID_ARGUMENT, "nothing to write: M and topk_out are null");
+  if (M) {
+    TR_CHECK(tree_tok != nullptr, TR_ERR_INVALID_ARGUMENT, "tree_tok is null");
+    TR_CHECK(m_dtype == TR_INT32 || m_dtype == TR_INT64, TR_ERR_UNSUPPORTED, "M must be int32 or int64");
+  }
+  const tr::TopkPlan plan = tr::plan_topk(int64_t(B) * t->dev.T, V, k);
+  st = check_ws(ws, ws_bytes, plan.end);
+  if (st != TR_OK) return st;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  int32_t* ids = topk_out ? topk_out : reinterpret_cast<int32_t*>(w + plan.ids_off);
+  tr::TailArgs tail{};
+  tail.mode = M ? tr::TAIL_UPDATE : tr::TAIL_NONE;
+  tail.m_is64 = m_dtype == TR_INT64;
+  tail.M = M;
+  tail.tree_tok = const_cast<int32_t*>(tree_tok);
+  return hip_status(tr::launch_topk(t->dev, B, logits, l_dtype == TR_BFLOAT16, V, k, ids, tail, w,
+                                    plan, hipStream_t(stream)),
+                    "tr_update_topk");
+}
+
+tr_status tr_verify(const tr_tree* t, int32_t B, const int32_t* topk, int32_t k,
+                    const int32_t* tree_tok, int32_t* accept_len, int32_t* accept_path,
+                    int32_t* bonus, int32_t* emitted, void* stream) {
+  TR_CHECK(t != nullptr, TR_ERR_INVALID_ARGUMENT, "tree is null");
+  TR_CHECK(B >= 1, TR_ERR_INVALID_ARGUMENT, "B must be >= 1");
+  TR_CHECK(topk && tree_tok && accept_len && bonus, TR_ERR_INVALID_ARGUMENT, "null tensor");
+  TR_CHECK(k == t->k, TR_ERR_INVALID_ARGUMENT, "k %d differs from the tree's %d", k, t->k);
+  return hip_status(tr::launch_verify(t->dev, B, topk, k, tree_tok, accept_len, accept_path, bonus,
+                                      emitted, hipStream_t(stream)),
+                    "tr_verify");
+}
+
+tr_status tr_step(const tr_tree* t, int32_t B, int64_t V, int32_t k, const void* logits,
+                  tr_dtype l_dtype, void* M, tr_dtype m_dtype, int32_t* tree_tok, int32_t* root_tok,
+                  int32_t* accept_len, int32_t* accept_path, int32_t* emitted, int32_t Hkv,
+                  int32_t d, tr_dtype kv_dtype, const void* k_tree, const void* v_tree,
+                  void* k_cache, void* v_cache, int64_t cap, int32_t* prefix_len, int32_t* topk_out,
+                  void* ws, size_t ws_bytes, void* stream) {
+  tr_status st = check_topk_args(t, B, logits, l_dtype, V, k);
+  if (st != TR_OK) return st;
+  TR_CHECK(M && tree_tok && root_tok && accept_len, TR_ERR_INVALID_ARGUMENT, "null tensor");
+  TR_CHECK(m_dtype == TR_INT32 || m_dtype == TR_INT64, TR_ERR_UNSUPPORTED, "M must be int32 or int64");
+  int row_bytes = 0;
+  if (k_cache) {
+    TR_CHECK(v_cache && k_tree && v_tree && prefix_len, TR_ERR_INVALID_ARGUMENT,
+             "commit needs k_tree, v_tree, v_cache and prefix_len");
+    TR_CHECK(kv_dtype == TR_FLOAT32 || kv_dtype == TR_BFLOAT16, TR_ERR_UNSUPPORTED,
+             "key/value dtype must be float32 or bfloat16");
+    TR_CHECK(d == tr::kHeadDim, TR_ERR_UNSUPPORTED, "head dimension must be %d", tr::kHeadDim);
+    TR_CHECK(Hkv >= 1 && cap >= 0, TR_ERR_INVALID_ARGUMENT, "bad Hkv or cap");
+    TR_CHECK(aligned16(k_cache) && aligned16(v_cache) && aligned16(k_tree) && aligned16(v_tree),
+             TR_ERR_INVALID_ARGUMENT, "key/value tensors must be 16-byte aligned");
+    row_bytes = d * (kv_dtype == TR_BFLOAT16 ? 2 : 4);
+  }
+  const tr::TopkPlan plan = tr::plan_topk(int64_t(B) * t->dev.T, V, k);
+  st = check_ws(ws, ws_bytes, plan.end);
+  if (st != TR_OK) return st;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  int32_t* ids = topk_out ? topk_out : reinterpret_cast<int32_t*>(w + plan.ids_off);
+  tr::TailArgs tail{};
+  tail.mode = tr::TAIL_STEP;
+  tail.m_is64 = m_dtype == TR_INT64;
+  tail.M = M;
+  tail.tree_tok = tree_tok;
+  tail.root_tok = root_tok;
+  tail.accept_len = accept_len;
+  tail.accept_path = accept_path;
+  tail.emitted = emitted;
+  tail.k_tree = static_cast<const uint8_t*>(k_tree);
+  tail.v_tree = static_cast<const uint8_t*>(v_tree);
+  tail.k_cache = static_cast<uint8_t*>(k_cache);
+  tail.v_cache = static_cast<uint8_t*>(v_cache);
+  tail.prefix_len = prefix_len;
+  tail.cap = cap;
+  tail.Hkv = Hkv;
+  tail.row_bytes = row_bytes;
+  return hip_status(tr::launch_topk(t->dev, B, logits, l_dtype == TR_BFLOAT16, V, k, ids, tail, w,
+                                    plan, hipStream_t(stream)),
+                    "tr_step");
+}
+
+}  // extern "C"

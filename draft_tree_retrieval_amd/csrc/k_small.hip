@@ -1,0 +1,64 @@
+// Stand-alone retrieval and verification kernels (one workgroup per
+// sequence) and the workspace fill.  Retrieval is a chain of dependent
+// gathers, one per tree layer ("Token Recycling" summary, Method, second
+// module: a BFS-like expansion of the last token's candidates); it is
+// latency-bound, so one workgroup per sequence walks the layers with a
+// barrier between them and one lane per node.
+#include "tail.h"
+
+namespace tr {
+
+__global__ __launch_bounds__(128) void retrieve_kernel(TreeDev tree, const void* __restrict__ M,
+                                                       int m_is64, int64_t V, int32_t k,
+                                                       const int32_t* __restrict__ root_tok,
+                                                       int32_t* __restrict__ tree_tok, uint8_t* ws) {
+  __shared__ TailShared S;
+  const int b = blockIdx.x;
+  const size_t msz = m_is64 ? 8 : 4;
+  const void* M_b = reinterpret_cast<const uint8_t*>(M) + size_t(b) * size_t(V) * size_t(k) * msz;
+  tail_retrieve(S, tree, root_tok[b], M_b, m_is64, V, k, tree_tok + int64_t(b) * tree.T, ws);
+}
+
+__global__ __launch_bounds__(128) void verify_kernel(TreeDev tree, const int32_t* __restrict__ topk,
+                                                     int32_t k, const int32_t* __restrict__ tree_tok,
+                                                     int32_t* accept_len, int32_t* accept_path,
+                                                     int32_t* bonus, int32_t* emitted) {
+  __shared__ TailShared S;
+  const int b = blockIdx.x;
+  tail_load(S, tree, tree_tok + int64_t(b) * tree.T, topk + int64_t(b) * tree.T * k, k);
+  tail_verify(S, tree);
+  tail_write_verdict(S, tree, b, accept_len, accept_path, bonus, emitted);
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint4* p, size_t n16) {
+  for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < n16; i += size_t(gridDim.x) * 256)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+hipError_t launch_retrieve(const TreeDev& tree, int32_t B, const void* M, int m_is64, int64_t V,
+                           int32_t k, const int32_t* root_tok, int32_t* tree_tok, uint8_t* ws,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(retrieve_kernel, dim3(B), dim3(128), 0, s, tree, M, m_is64, V, k, root_tok,
+                     tree_tok, ws);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify(const TreeDev& tree, int32_t B, const int32_t* topk, int32_t k,
+                         const int32_t* tree_tok, int32_t* accept_len, int32_t* accept_path,
+                         int32_t* bonus, int32_t* emitted, hipStream_t s) {
+  hipLaunchKernelGGL(verify_kernel, dim3(B), dim3(128), 0, s, tree, topk, k, tree_tok, accept_len,
+                     accept_path, bonus, emitted);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
+  size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(unsigned(blocks)), dim3(256), 0, s,
+                     reinterpret_cast<uint4*>(p), n16);
+  return hipGetLastError();
+}
+
+}  // namespace tr

@@ -1,0 +1,113 @@
+// Internal declarations shared by the libtr sources (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/tr.h"
+
+namespace tr {
+
+constexpr int kMaxNodes = 128;   // tree nodes, root included
+constexpr int kMaxK = 16;        // candidates per row of M
+constexpr int kHeadDim = 128;    // attention head dimension
+
+// Tree template as kernels see it: passed by value as a kernel argument,
+// so no device allocation is tied to a tree.
+struct TreeDev {
+  int32_t T;                     // nodes, root included
+  int32_t D;                     // depth (root = 0)
+  uint8_t parent[kMaxNodes];     // 0xFF for the root
+  uint8_t rank[kMaxNodes];
+  uint8_t depth[kMaxNodes];
+};
+
+}  // namespace tr
+
+struct tr_tree {
+  tr::TreeDev dev;
+  int32_t k;
+  uint64_t anc[tr::kMaxNodes][2];
+};
+
+namespace tr {
+
+// ---------------------------------------------------------------- workspace
+// [0, 256)             status word (TR_FLAG_* bits) + padding
+// [256, kCntEnd)       counters, zero between calls (each call's last block
+//                      returns the ones it used to zero)
+// [kDataOff, ...)      per-call scratch (top-k partial keys, top-k ids,
+//                      attention partials); calls ordered on one stream may
+//                      reuse it.
+constexpr size_t kSeqCntOff = 256;                    // uint32 [<= 4096]
+constexpr size_t kMaxSeqCnt = 4096;
+constexpr size_t kRowCntOff = kSeqCntOff + 4 * kMaxSeqCnt;   // uint32 [<= 32768]
+constexpr size_t kMaxRowCnt = 32768;
+constexpr size_t kDataOff = 256 * 1024;
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Top-k launch shape: rows x segments.
+struct TopkPlan {
+  int64_t rows;
+  int32_t segs;       // segments per row (1..64)
+  int64_t seg_len;    // elements per segment (multiple of 8)
+  int32_t kmax;       // 8 or 16 (list length kept per thread)
+  size_t part_off;    // uint64 [rows][segs][kmax] partial keys (segs > 1)
+  size_t ids_off;     // int32  [rows][k] ids when the caller gives no buffer
+  size_t end;
+};
+TopkPlan plan_topk(int64_t rows, int64_t V, int32_t k);
+
+// Attention launch shape.
+struct AttnPlan {
+  int32_t G;          // query heads per key/value head
+  int32_t R;          // query rows per (sequence, kv head) = T * G
+  int32_t row_tiles;  // ceil(R / 128)
+  int32_t chunks;     // prefix chunks per (sequence, kv head)
+  size_t o_off;       // float [B*Hkv][chunks][row_tiles*128][128]
+  size_t ml_off;      // float2 [B*Hkv][chunks][row_tiles*128]
+  size_t end;
+};
+AttnPlan plan_attn(int32_t T, int32_t B, int32_t Hq, int32_t Hkv, int64_t cap);
+
+// ---------------------------------------------------------------- launchers
+enum TailMode : int32_t { TAIL_NONE = 0, TAIL_UPDATE = 1, TAIL_STEP = 2 };
+
+struct TailArgs {
+  int32_t mode;
+  int32_t m_is64;
+  void* M;                 // [B][V][k]
+  int32_t* tree_tok;       // [B][T]
+  int32_t* root_tok;       // [B]
+  int32_t* accept_len;     // [B]
+  int32_t* accept_path;    // [B][D+1] or null
+  int32_t* emitted;        // [B][D+1] or null
+  // commit
+  const uint8_t* k_tree;   // [B][T][Hkv][d] bytes
+  const uint8_t* v_tree;
+  uint8_t* k_cache;        // [B][Hkv][cap][d] or null
+  uint8_t* v_cache;
+  int32_t* prefix_len;
+  int64_t cap;
+  int32_t Hkv;
+  int32_t row_bytes;       // d * element size
+};
+
+hipError_t launch_topk(const TreeDev& tree, int32_t B, const void* logits, int l_is_bf16, int64_t V,
+                       int32_t k, int32_t* topk_ids, const TailArgs& tail, uint8_t* ws,
+                       const TopkPlan& plan, hipStream_t s);
+hipError_t launch_retrieve(const TreeDev& tree, int32_t B, const void* M, int m_is64, int64_t V,
+                           int32_t k, const int32_t* root_tok, int32_t* tree_tok, uint8_t* ws,
+                           hipStream_t s);
+hipError_t launch_verify(const TreeDev& tree, int32_t B, const int32_t* topk, int32_t k,
+                         const int32_t* tree_tok, int32_t* accept_len, int32_t* accept_path,
+                         int32_t* bonus, int32_t* emitted, hipStream_t s);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_attn(const TreeDev& tree, int32_t B, int32_t Hq, int32_t Hkv, int is_bf16,
+                       const void* q, const void* k_tree, const void* v_tree, const void* k_cache,
+                       const void* v_cache, int64_t cap, const int32_t* prefix_len, float scale,
+                       void* out, uint8_t* ws, const AttnPlan& plan, hipStream_t s);
+
+}  // namespace tr

@@ -1,0 +1,50 @@
+"""A TR decoding loop on one GPU: device state plus the two calls of a step.
+
+One step of Token Recycling ("Token Recycling" summary, Method; walk-through
+"why it is called Token Recycling"): the target model's forward pass over
+the merged tree sequence calls tree attention once per layer
+(`attend`); after the forward pass, `step` takes the logits of every tree
+node and runs top-k, verification, the update of M, the commit of the
+accepted path's key/value rows and the retrieval of the next tree, in one
+fused launch.  The state never leaves the GPU; nothing here synchronises.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import tr
+
+
+class TRDecoder:
+    def __init__(self, tree: tr.Tree, M, k_cache, v_cache, prefix_len, root_tok, Hq,
+                 V=None, stream=None):
+        self.tree = tree
+        self.M, self.k_cache, self.v_cache = M, k_cache, v_cache
+        self.prefix_len, self.root_tok = prefix_len, root_tok
+        self.stream = stream
+        B, Vm, k = M.shape
+        self.B, self.V, self.k = B, (V or Vm), k
+        T, D = tree.n_nodes, tree.depth
+        self.Hq, self.Hkv, self.cap, self.d = Hq, k_cache.shape[1], k_cache.shape[2], k_cache.shape[3]
+        dev = M.device
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.tree_tok = torch.empty((B, T), **i32)
+        self.accept_len = torch.zeros((B,), **i32)
+        self.accept_path = torch.full((B, D + 1), -1, **i32)
+        self.emitted = torch.full((B, D + 1), -1, **i32)
+        self.topk = torch.empty((B, T, k), **i32)
+        self.ws = tr.new_workspace(tree, B, self.V, k, Hq, self.Hkv, self.d, self.cap, device=dev,
+                                   stream=stream)
+        tr.tr_retrieve(tree, M, root_tok, self.tree_tok, self.ws, stream)
+
+    def attend(self, q, k_tree, v_tree, out, scale=None):
+        tr.tr_tree_attn(self.tree, q, k_tree, v_tree, self.k_cache, self.v_cache, self.prefix_len,
+                        out, self.ws, scale, self.stream)
+
+    def step(self, logits, k_tree, v_tree):
+        tr.tr_step(self.tree, logits, self.M, self.tree_tok, self.root_tok, self.accept_len,
+                   self.accept_path, self.emitted, self.ws, k_tree, v_tree, self.k_cache,
+                   self.v_cache, self.prefix_len, self.topk, self.stream)
+
+    def device_flags(self):
+        return tr.tr_read_device_status(self.ws, self.stream)

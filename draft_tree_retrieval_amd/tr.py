@@ -1,0 +1,211 @@
+"""Python binding of libtr (the C ABI in include/tr.h).
+
+Argument marshalling only: every function takes torch tensors (device
+memory), checks nothing the library does not check itself beyond deriving
+sizes from tensor shapes, and calls the entry point of the same name.  All
+work runs in the HIP kernels of libtr.so; there is no fallback.  A missing
+or unloadable library raises at import of this module's first call.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtr.so")
+
+TR_OK, TR_ERR_INVALID_ARGUMENT, TR_ERR_UNSUPPORTED, TR_ERR_INVALID_TREE, \
+    TR_ERR_WORKSPACE_TOO_SMALL, TR_ERR_HIP = range(6)
+TR_INT32, TR_INT64, TR_FLOAT32, TR_BFLOAT16 = range(4)
+TR_FLAG_BAD_TOKEN, TR_FLAG_CACHE_FULL, TR_FLAG_BAD_PREFIX = 1, 2, 4
+
+_DT = {torch.int32: TR_INT32, torch.int64: TR_INT64, torch.float32: TR_FLOAT32,
+       torch.bfloat16: TR_BFLOAT16}
+
+_P, _I32, _I64, _SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+
+# name -> argument types (restype is tr_status = int unless noted)
+_SIGS = {
+    "tr_status_string": ([C.c_int], C.c_char_p),
+    "tr_last_error": ([], C.c_char_p),
+    "tr_tree_create": ([_I32, _P, _P, _I32, C.POINTER(_P)], C.c_int),
+    "tr_tree_create_levels": ([_I32, _P, _P, _I32, C.POINTER(_P)], C.c_int),
+    "tr_tree_destroy": ([_P], None),
+    "tr_tree_info": ([_P, _P, _P, _P, _P, _P, _P, _P], C.c_int),
+    "tr_workspace_size": ([_P, _I32, _I64, _I32, _I32, _I32, _I32, _I64], _SZ),
+    "tr_workspace_init": ([_P, _SZ, _P], C.c_int),
+    "tr_read_device_status": ([_P, _P, _P], C.c_int),
+    "tr_retrieve": ([_P, _I32, _P, C.c_int, _I64, _I32, _P, _P, _P, _SZ, _P], C.c_int),
+    "tr_tree_attn": ([_P, _I32, _I32, _I32, _I32, C.c_int, _P, _P, _P, _P, _P, _I64, _P,
+                      C.c_float, _P, _P, _SZ, _P], C.c_int),
+    "tr_update_topk": ([_P, _I32, _P, C.c_int, _I64, _I32, _P, _P, C.c_int, _P, _P, _SZ, _P],
+                       C.c_int),
+    "tr_verify": ([_P, _I32, _P, _I32, _P, _P, _P, _P, _P, _P], C.c_int),
+    "tr_step": ([_P, _I32, _I64, _I32, _P, C.c_int, _P, C.c_int, _P, _P, _P, _P, _P, _I32, _I32,
+                 C.c_int, _P, _P, _P, _P, _I64, _P, _P, _P, _SZ, _P], C.c_int),
+}
+
+_lib = None
+
+
+class TRError(RuntimeError):
+    def __init__(self, status, detail):
+        self.status = status
+        super().__init__(f"{status_string(status)}: {detail}")
+
+
+def load():
+    """The loaded libtr (ctypes.CDLL); raises if the library was not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m draft_tree_retrieval_amd.build`")
+        lib = C.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(lib, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = lib
+    return _lib
+
+
+def status_string(s):
+    return load().tr_status_string(s).decode()
+
+
+def _check(status):
+    if status != TR_OK:
+        raise TRError(status, load().tr_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _dt(t):
+    return _DT[t.dtype]
+
+
+class Tree:
+    """A tr_tree template (host object)."""
+
+    def __init__(self, handle, k):
+        self._h = handle
+        self.k = k
+        n, d = C.c_int32(), C.c_int32()
+        _check(load().tr_tree_info(self._h, C.byref(n), C.byref(d), None, None, None, None, None))
+        self.n_nodes, self.depth = n.value, d.value
+
+    @classmethod
+    def from_parent_rank(cls, parent, rank, k):
+        par = (C.c_int32 * len(parent))(*parent)
+        rk = (C.c_int32 * len(rank))(*rank)
+        h = C.c_void_p()
+        _check(load().tr_tree_create(len(parent), par, rk, k, C.byref(h)))
+        return cls(h, k)
+
+    @classmethod
+    def from_levels(cls, levels, k):
+        lens = (C.c_int32 * max(1, len(levels)))(*[len(l) for l in levels])
+        flat = [c for l in levels for c in l]
+        counts = (C.c_int32 * max(1, len(flat)))(*flat)
+        h = C.c_void_p()
+        _check(load().tr_tree_create_levels(len(levels), lens, counts, k, C.byref(h)))
+        return cls(h, k)
+
+    def info(self):
+        T = self.n_nodes
+        par, rk, dp = (C.c_int32 * T)(), (C.c_int32 * T)(), (C.c_int32 * T)()
+        anc = (C.c_uint64 * (2 * T))()
+        _check(load().tr_tree_info(self._h, None, None, None, par, rk, dp, anc))
+        return list(par), list(rk), list(dp), [(anc[2 * i], anc[2 * i + 1]) for i in range(T)]
+
+    @property
+    def handle(self):
+        return self._h
+
+    def __del__(self):
+        if getattr(self, "_h", None) and _lib is not None:
+            _lib.tr_tree_destroy(self._h)
+            self._h = None
+
+
+def tr_workspace_size(tree, B, V=0, k=0, Hq=0, Hkv=0, d=0, cap=0):
+    return int(load().tr_workspace_size(tree.handle, B, V, k, Hq, Hkv, d, cap))
+
+
+def tr_workspace_init(ws, stream=None):
+    _check(load().tr_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def new_workspace(tree, B, V=0, k=0, Hq=0, Hkv=0, d=0, cap=0, device="cuda", stream=None):
+    """Allocates (through torch) and zero-initialises a workspace."""
+    n = tr_workspace_size(tree, B, V, k, Hq, Hkv, d, cap)
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    tr_workspace_init(ws, stream)
+    return ws
+
+
+def tr_read_device_status(ws, stream=None):
+    flags = C.c_uint32()
+    _check(load().tr_read_device_status(_ptr(ws), C.byref(flags), _stream(stream)))
+    return flags.value
+
+
+def tr_retrieve(tree, M, root_tok, tree_tok, ws, stream=None):
+    B, V, k = M.shape
+    _check(load().tr_retrieve(tree.handle, B, _ptr(M), _dt(M), V, k, _ptr(root_tok), _ptr(tree_tok),
+                              _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def tr_tree_attn(tree, q, k_tree, v_tree, k_cache, v_cache, prefix_len, out, ws, scale=None,
+                 stream=None):
+    B, T, Hq, d = q.shape
+    Hkv = k_tree.shape[2]
+    cap = k_cache.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check(load().tr_tree_attn(tree.handle, B, Hq, Hkv, d, _dt(q), _ptr(q), _ptr(k_tree),
+                               _ptr(v_tree), _ptr(k_cache), _ptr(v_cache), cap, _ptr(prefix_len),
+                               float(scale), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def tr_update_topk(tree, logits, tree_tok, M, topk_out, ws, stream=None):
+    B, T, V = logits.shape
+    k = tree.k
+    _check(load().tr_update_topk(tree.handle, B, _ptr(logits), _dt(logits), V, k, _ptr(tree_tok),
+                                 _ptr(M), _dt(M) if M is not None else TR_INT32, _ptr(topk_out),
+                                 _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def tr_verify(tree, topk, tree_tok, accept_len, accept_path, bonus, emitted, stream=None):
+    B = topk.shape[0]
+    _check(load().tr_verify(tree.handle, B, _ptr(topk), topk.shape[2], _ptr(tree_tok),
+                            _ptr(accept_len), _ptr(accept_path), _ptr(bonus), _ptr(emitted),
+                            _stream(stream)))
+
+
+def tr_step(tree, logits, M, tree_tok, root_tok, accept_len, accept_path, emitted, ws,
+            k_tree=None, v_tree=None, k_cache=None, v_cache=None, prefix_len=None, topk_out=None,
+            stream=None):
+    B, T, V = logits.shape
+    if k_cache is not None:
+        Hkv, cap, d = k_cache.shape[1], k_cache.shape[2], k_cache.shape[3]
+        kv_dt = _dt(k_cache)
+    else:
+        Hkv, cap, d, kv_dt = 0, 0, 0, TR_BFLOAT16
+    _check(load().tr_step(tree.handle, B, V, tree.k, _ptr(logits), _dt(logits), _ptr(M), _dt(M),
+                          _ptr(tree_tok), _ptr(root_tok), _ptr(accept_len), _ptr(accept_path),
+                          _ptr(emitted), Hkv, d, kv_dt, _ptr(k_tree), _ptr(v_tree), _ptr(k_cache),
+                          _ptr(v_cache), cap, _ptr(prefix_len), _ptr(topk_out), _ptr(ws),
+                          ws.numel(), _stream(stream)))

@@ -1,0 +1,219 @@
+/*
+ * tr.h -- C ABI of libtr: the data-parallel hot path of Token Recycling (TR)
+ * speculative decoding on AMD Instinct MI355X (gfx950).
+ *
+ * TR keeps a |V| x k matrix M of candidate successor tokens ("Token
+ * Recycling" summary, section Method, first module).  One decoding step:
+ *   1. retrieve a static draft tree from M, starting at the last committed
+ *      token (Method, second module);
+ *   2. verify the tree's merged sequence against the prefix with tree
+ *      attention: each node sees the prefix, its ancestors and itself, never
+ *      a sibling branch (Method, third module; walk-through, workflow step 3);
+ *   3. accept the longest correct path plus the target's token after it
+ *      (walk-through, workflow step 4);
+ *   4. overwrite, for every tree node x~_i, the row M[x~_i] with
+ *      argtopk(p~_{i+1}) of that node's next-token distribution (Chinese
+ *      summary, section Method, the update equation; walk-through, "why it
+ *      is called Token Recycling").
+ *
+ * Conventions shared by every call
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller; the
+ *     library never allocates, frees or keeps them.  Buffers must not alias
+ *     unless a call says so.  Layouts are dense, row-major, innermost last.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *     asynchronous: outputs are valid once the stream has been synchronised.
+ *   - Host-side checks (null pointers, sizes, dtype pairs, tree/k mismatch,
+ *     workspace size) return a non-OK status and launch nothing; the reason
+ *     is in tr_last_error().  A failed launch returns TR_ERR_HIP.
+ *   - Data errors only the device can see set sticky bits in the workspace
+ *     status word (tr_read_device_status) and skip the offending write:
+ *     a token outside [0, V) (TR_FLAG_BAD_TOKEN), a commit that would
+ *     overflow the cache capacity (TR_FLAG_CACHE_FULL) and a prefix_len
+ *     outside [0, cap] given to tr_tree_attn (TR_FLAG_BAD_PREFIX; the
+ *     length is clamped to that range).
+ *   - Tie and duplicate rules (fixed here; the pages leave them open):
+ *     top-k orders by value descending, then token id ascending, with
+ *     -0.0 == +0.0; when two tree nodes carry the same token, the node with
+ *     the highest merged-sequence index writes M; the accepted path is the
+ *     deepest accepted node, ties to the smallest index.
+ *   - Logits must not be NaN (+-inf are fine).
+ *
+ * Limits: 1 <= k <= 16, 1 <= tree nodes <= 128, head dimension d = 128,
+ * Hq a multiple of Hkv.
+ */
+#ifndef TR_H
+#define TR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TR_OK = 0,
+  TR_ERR_INVALID_ARGUMENT = 1,
+  TR_ERR_UNSUPPORTED = 2,
+  TR_ERR_INVALID_TREE = 3,
+  TR_ERR_WORKSPACE_TOO_SMALL = 4,
+  TR_ERR_HIP = 5
+} tr_status;
+
+typedef enum { TR_INT32 = 0, TR_INT64 = 1, TR_FLOAT32 = 2, TR_BFLOAT16 = 3 } tr_dtype;
+
+enum { TR_FLAG_BAD_TOKEN = 1u, TR_FLAG_CACHE_FULL = 2u, TR_FLAG_BAD_PREFIX = 4u };
+
+/* Opaque, immutable draft-tree template (host memory, library-owned).
+ * Shareable across streams and threads. */
+typedef struct tr_tree tr_tree;
+
+/* Human-readable name of a status code (static string). */
+const char* tr_status_string(tr_status s);
+
+/* Detail of the last non-OK status returned on the calling thread
+ * (thread-local, static storage; empty string if none). */
+const char* tr_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Tree template (host only; no GPU needed).
+ * The tree is static and imbalanced ("Token Recycling" summary, Method,
+ * second module): children counts are fixed across steps; a node with c
+ * children expands the c best candidates (ranks 0..c-1) of its row.
+ * Nodes are numbered in merged-sequence order: layer by layer, inside a
+ * layer by (parent index, rank) (Method, "merged sequence"; walk-through
+ * step 3 prints [guest, speaker, speak, event, at, for, ing]).
+ * ------------------------------------------------------------------------ */
+
+/* parent[0] = -1 and rank[0] = -1 (root); for n > 0: 0 <= parent[n] < n,
+ * 0 <= rank[n] < k, ranks distinct under one parent, nodes in layer order.
+ * Host arrays of n_nodes entries, copied.  *out receives the template;
+ * release it with tr_tree_destroy.  Errors: TR_ERR_INVALID_TREE,
+ * TR_ERR_INVALID_ARGUMENT (null pointer, n_nodes outside 1..128, k outside
+ * 1..16). */
+tr_status tr_tree_create(int32_t n_nodes, const int32_t* parent, const int32_t* rank, int32_t k,
+                         tr_tree** out);
+
+/* Same from per-layer child counts: layer l (0 = the root's layer) has
+ * level_len[l] counts, stored one layer after another in `counts`; entry i
+ * of layer l is the number of children of the i-th node of that layer
+ * (missing entries: no children).  Host arrays, copied. */
+tr_status tr_tree_create_levels(int32_t n_levels, const int32_t* level_len, const int32_t* counts,
+                                int32_t k, tr_tree** out);
+
+void tr_tree_destroy(tr_tree* t);
+
+/* Template facts, to host memory.  Any output pointer may be NULL.
+ * parent_out/rank_out/depth_out: [n_nodes] int32; anc_out: [n_nodes][2]
+ * uint64 ancestor bitmask (bit j of row n set iff node j is n or one of
+ * its ancestors: the tree-attention mask). */
+tr_status tr_tree_info(const tr_tree* t, int32_t* n_nodes, int32_t* depth, int32_t* k,
+                       int32_t* parent_out, int32_t* rank_out, int32_t* depth_out,
+                       uint64_t* anc_out);
+
+/* ------------------------------------------------------------------------
+ * Workspace.  One device buffer per stream holds counters, partial results
+ * and the device status word.  Size it with tr_workspace_size for the
+ * largest (B, V, heads, capacity) it will serve, zero it once with
+ * tr_workspace_init; afterwards every call leaves it ready for the next
+ * (counters return to zero), so it can be reused across calls and
+ * captured in a HIP graph.  Calls sharing one workspace must be ordered
+ * on one stream.
+ * ------------------------------------------------------------------------ */
+size_t tr_workspace_size(const tr_tree* t, int32_t B, int64_t V, int32_t k, int32_t Hq,
+                         int32_t Hkv, int32_t d, int64_t cap);
+
+/* Zero-fills ws (a kernel, not a memset).  ws must be 256-byte aligned. */
+tr_status tr_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Copies the sticky status word (TR_FLAG_* bits) to *flags and clears it.
+ * Synchronises `stream`. */
+tr_status tr_read_device_status(void* ws, uint32_t* flags, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Hot path.
+ * ------------------------------------------------------------------------ */
+
+/* Draft tree retrieval ("Token Recycling" summary, Method, second module;
+ * walk-through, workflow steps 1-2): tree_tok[b][0] = root_tok[b] and,
+ * layer by layer, tree_tok[b][n] = M[b][tree_tok[b][parent n]][rank n].
+ *   M        [B][V][k] int32 or int64 (m_dtype), read only.
+ *   root_tok [B] int32.  tree_tok [B][T] int32, written.
+ *   ws       workspace (for the status word).
+ * A token outside [0, V) sets TR_FLAG_BAD_TOKEN; its children get -1. */
+tr_status tr_retrieve(const tr_tree* t, int32_t B, const void* M, tr_dtype m_dtype, int64_t V,
+                      int32_t k, const int32_t* root_tok, int32_t* tree_tok, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/* Tree attention over the prefix cache (Method, third module; walk-through
+ * step 3): for every node n, query head h (key/value head h / (Hq/Hkv)):
+ *   out[b][n][h] = sum_j softmax_j(scale * q[b][n][h] . key_j) value_j
+ * with j over cache positions 0..prefix_len[b]-1 and the tree nodes that
+ * are n or its ancestors.
+ *   q         [B][T][Hq][d]      dt (TR_FLOAT32 or TR_BFLOAT16)
+ *   k_tree,
+ *   v_tree    [B][T][Hkv][d]     dt: the tree nodes' own keys/values
+ *   k_cache,
+ *   v_cache   [B][Hkv][cap][d]   dt: positions >= prefix_len[b] unread
+ *   prefix_len [B] int32 (device; 0 <= prefix_len <= cap)
+ *   out       [B][T][Hq][d]      dt, written
+ * Arithmetic: float32 accumulation; bf16 inputs use bf16 matrix cores for
+ * both products.  The result does not depend on how the prefix is split. */
+tr_status tr_tree_attn(const tr_tree* t, int32_t B, int32_t Hq, int32_t Hkv, int32_t d, tr_dtype dt,
+                       const void* q, const void* k_tree, const void* v_tree, const void* k_cache,
+                       const void* v_cache, int64_t cap, const int32_t* prefix_len, float scale,
+                       void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* argtopk of every node's next-token logits and the recycling update
+ * M[tree_tok[b][n]] = argtopk(logits[b][n]) for every node n, in merged
+ * order (Chinese summary, Method, update equation; walk-through "why it is
+ * called Token Recycling": rejected nodes update M too).
+ *   logits   [B][T][V]  l_dtype (TR_FLOAT32 or TR_BFLOAT16)
+ *   tree_tok [B][T] int32 (may be NULL when M is NULL)
+ *   M        [B][V][k]  m_dtype, updated in place; NULL: top-k only
+ *   topk_out [B][T][k] int32 token ids, best first; may be NULL when M
+ *            is given. */
+tr_status tr_update_topk(const tr_tree* t, int32_t B, const void* logits, tr_dtype l_dtype,
+                         int64_t V, int32_t k, const int32_t* tree_tok, void* M, tr_dtype m_dtype,
+                         int32_t* topk_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Greedy verification (Method, third module: the longest correct sequence
+ * is the step's output; walk-through step 4: the target's own token follows
+ * it).  g(n) = topk[b][n][0]; node n > 0 is accepted iff its parent is and
+ * tree_tok[b][n] == g(parent).  best = deepest accepted node (ties: lowest
+ * index).  Outputs (Dmax = tree depth):
+ *   accept_len  [B]         L = depth(best)
+ *   accept_path [B][Dmax+1] node ids root..best, then -1 (may be NULL)
+ *   bonus       [B]         g(best)
+ *   emitted     [B][Dmax+1] tree_tok of path[1..L], then bonus, then -1
+ *                           (may be NULL) */
+tr_status tr_verify(const tr_tree* t, int32_t B, const int32_t* topk, int32_t k,
+                    const int32_t* tree_tok, int32_t* accept_len, int32_t* accept_path,
+                    int32_t* bonus, int32_t* emitted, void* stream);
+
+/* One whole TR step after the target's forward pass, fused:
+ *   top-k of every node -> verify -> update M -> commit the accepted path's
+ *   key/value rows -> next root = bonus -> retrieve the next tree.
+ * The current tree was retrieved from M before this update; the next tree
+ * sees the update (walk-through step 2).
+ *   tree_tok  [B][T] in: this step's tree; out: the next step's tree
+ *   root_tok  [B]    out: the bonus token (the next root)
+ *   accept_len [B], accept_path [B][Dmax+1] (nullable),
+ *   emitted [B][Dmax+1] (nullable) as tr_verify
+ *   k_tree, v_tree [B][T][Hkv][d], k_cache, v_cache [B][Hkv][cap][d] in
+ *   kv_dtype; prefix_len [B] in/out: rows path[0..L] are copied to cache
+ *   positions prefix_len .. prefix_len+L and prefix_len grows by L+1.
+ *   If k_cache is NULL no commit is done.
+ *   topk_out  [B][T][k] (nullable). */
+tr_status tr_step(const tr_tree* t, int32_t B, int64_t V, int32_t k, const void* logits,
+                  tr_dtype l_dtype, void* M, tr_dtype m_dtype, int32_t* tree_tok, int32_t* root_tok,
+                  int32_t* accept_len, int32_t* accept_path, int32_t* emitted, int32_t Hkv,
+                  int32_t d, tr_dtype kv_dtype, const void* k_tree, const void* v_tree,
+                  void* k_cache, void* v_cache, int64_t cap, int32_t* prefix_len, int32_t* topk_out,
+                  void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TR_H */

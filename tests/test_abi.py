@@ -1,0 +1,133 @@
+"""The C ABI without a GPU: libtr loads, exports every function include/tr.h
+declares, builds and checks tree templates on the host, and rejects bad
+arguments before launching anything (no compute call needs a device here).
+"""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import tr_oracle as O
+from synth.workloads import TREE_16, TREE_81
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def tr():
+    from draft_tree_retrieval_amd import tr as _tr
+    if not os.path.exists(_tr.LIB_PATH):
+        pytest.fail("libtr.so is not built: run python -m draft_tree_retrieval_amd.build")
+    _tr.load()
+    return _tr
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "tr.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(tr_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(tr):
+    names = declared_functions()
+    assert {"tr_retrieve", "tr_tree_attn", "tr_verify", "tr_update_topk", "tr_step"} <= set(names)
+    lib = C.CDLL(tr.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    # and the binding wraps each of them
+    assert set(names) <= set(tr._SIGS)
+
+
+def test_status_strings(tr):
+    assert tr.status_string(tr.TR_OK) == "TR_OK"
+    assert tr.status_string(tr.TR_ERR_WORKSPACE_TOO_SMALL) == "TR_ERR_WORKSPACE_TOO_SMALL"
+
+
+@pytest.mark.parametrize("levels", [TREE_16, TREE_81, [[3], [2, 1]], [], [[1]] * 20])
+def test_tree_matches_oracle_template(tr, levels):
+    t = O.template_from_levels(levels)
+    tree = tr.Tree.from_levels(levels, 8)
+    parent, rank, depth, anc = tree.info()
+    assert tree.n_nodes == t.n_nodes and tree.depth == t.max_depth
+    assert parent == t.parent.tolist() and rank == t.rank.tolist() and depth == t.depth.tolist()
+    mask = O.ancestor_mask(t)
+    for n in range(t.n_nodes):
+        bits = [(anc[n][j >> 6] >> (j & 63)) & 1 for j in range(t.n_nodes)]
+        assert bits == mask[n].astype(int).tolist()
+    tree2 = tr.Tree.from_parent_rank(t.parent.tolist(), t.rank.tolist(), 8)
+    assert tree2.info() == tree.info()
+
+
+@pytest.mark.parametrize("parent,rank", [
+    ([-1, 1], [-1, 0]),              # parent does not precede
+    ([-1, 0, 0], [-1, 0, 0]),        # repeated rank
+    ([-1, 0, 1, 0], [-1, 0, 0, 1]),  # not in layer order
+    ([-1, 0], [-1, 8]),              # rank >= k
+    ([0, 0], [-1, 0]),               # root not first
+])
+def test_bad_templates_rejected(tr, parent, rank):
+    with pytest.raises(tr.TRError) as e:
+        tr.Tree.from_parent_rank(parent, rank, 8)
+    assert e.value.status == tr.TR_ERR_INVALID_TREE
+
+
+def test_bad_sizes_rejected(tr):
+    with pytest.raises(tr.TRError) as e:
+        tr.Tree.from_parent_rank([-1] + [0] * 128, [-1] + list(range(128)), 8)
+    assert e.value.status == tr.TR_ERR_INVALID_ARGUMENT
+    with pytest.raises(tr.TRError):
+        tr.Tree.from_levels([[17]], 16)          # more children than k
+    with pytest.raises(tr.TRError):
+        tr.Tree.from_levels([[2], [1, 1, 1]], 4) # more counts than nodes in the layer
+
+
+def test_host_checks_launch_nothing(tr):
+    lib = tr.load()
+    tree = tr.Tree.from_levels([[3], [2, 1]], 3)
+    h = tree.handle
+    fake = C.c_void_p(1 << 20)                  # never dereferenced: checks fail first
+    ws = C.c_void_p(1 << 24)
+    # null tensors
+    assert lib.tr_retrieve(h, 1, None, tr.TR_INT32, 16, 3, fake, fake, ws, 1 << 20, None) == \
+        tr.TR_ERR_INVALID_ARGUMENT
+    # wrong dtype of M
+    assert lib.tr_retrieve(h, 1, fake, tr.TR_FLOAT32, 16, 3, fake, fake, ws, 1 << 20, None) == \
+        tr.TR_ERR_UNSUPPORTED
+    # k differs from the tree's
+    assert lib.tr_retrieve(h, 1, fake, tr.TR_INT32, 16, 4, fake, fake, ws, 1 << 20, None) == \
+        tr.TR_ERR_INVALID_ARGUMENT
+    # workspace too small / misaligned
+    assert lib.tr_retrieve(h, 1, fake, tr.TR_INT32, 16, 3, fake, fake, ws, 100, None) == \
+        tr.TR_ERR_WORKSPACE_TOO_SMALL
+    assert lib.tr_retrieve(h, 1, fake, tr.TR_INT32, 16, 3, fake, fake, C.c_void_p((1 << 24) + 8),
+                           1 << 20, None) == tr.TR_ERR_INVALID_ARGUMENT
+    # attention: unsupported head dim, bad grouping, fp16
+    args = lambda d, Hq, Hkv, dt: (h, 1, Hq, Hkv, d, dt, fake, fake, fake, fake, fake, 64, fake,
+                                   C.c_float(0.1), fake, ws, 1 << 30, None)
+    assert lib.tr_tree_attn(*args(64, 8, 8, tr.TR_BFLOAT16)) == tr.TR_ERR_UNSUPPORTED
+    assert lib.tr_tree_attn(*args(128, 6, 4, tr.TR_BFLOAT16)) == tr.TR_ERR_INVALID_ARGUMENT
+    assert lib.tr_tree_attn(*args(128, 8, 8, tr.TR_INT32)) == tr.TR_ERR_UNSUPPORTED
+    need = tr.tr_workspace_size(tree, 1, 0, 0, 8, 8, 128, 64)
+    a = list(args(128, 8, 8, tr.TR_BFLOAT16))
+    a[-2] = need - 1
+    assert lib.tr_tree_attn(*a) == tr.TR_ERR_WORKSPACE_TOO_SMALL
+    # top-k / update / step
+    assert lib.tr_update_topk(h, 1, fake, tr.TR_BFLOAT16, 2, 3, fake, fake, tr.TR_INT32, None, ws,
+                              1 << 30, None) == tr.TR_ERR_INVALID_ARGUMENT        # V < k
+    assert lib.tr_update_topk(h, 1, fake, tr.TR_BFLOAT16, 16, 3, fake, None, tr.TR_INT32, None, ws,
+                              1 << 30, None) == tr.TR_ERR_INVALID_ARGUMENT        # nothing to write
+    assert lib.tr_step(h, 1, 16, 3, fake, tr.TR_BFLOAT16, fake, tr.TR_INT32, fake, fake, fake, None,
+                       None, 2, 128, tr.TR_BFLOAT16, fake, fake, fake, None, 64, fake, None, ws,
+                       1 << 30, None) == tr.TR_ERR_INVALID_ARGUMENT               # v_cache missing
+    assert lib.tr_verify(h, 1, None, 3, fake, fake, None, fake, None, None) == tr.TR_ERR_INVALID_ARGUMENT
+    assert "null" in tr.load().tr_last_error().decode()
+
+
+def test_workspace_size_grows_with_problem(tr):
+    tree = tr.Tree.from_levels(TREE_81, 8)
+    small = tr.tr_workspace_size(tree, 1, 32000, 8, 32, 32, 128, 3840)
+    big = tr.tr_workspace_size(tree, 32, 128256, 8, 32, 8, 128, 4992)
+    assert 256 * 1024 < small < big
+    assert small % 256 == 0 and big % 256 == 0

@@ -1,0 +1,339 @@
+"""Per-call parity of the HIP path against the CPU oracle (MI355X only).
+
+Integer results (trees, top-k ids, verification, M, committed rows) must
+match bit for bit.  Attention must match the float64 oracle within 1e-5
+relative per output row (float32 inputs; max |diff| / max |oracle| over the
+row) and within 2e-2 absolute per element (bfloat16 inputs).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import tr_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def tr():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from draft_tree_retrieval_amd import tr as _tr
+    _tr.load()
+    return _tr
+
+
+def ws_for(tr, tree, B, V=0, k=0, Hq=0, Hkv=0, cap=0):
+    return tr.new_workspace(tree, B, V, k, Hq, Hkv, 128 if Hq else 0, cap, device=DEV)
+
+
+def otree(levels):
+    return O.template_from_levels(levels)
+
+
+RAND_LEVELS = [[[3], [2, 1]], [[4], [4, 2, 1, 1], [2, 1]], [[1]] * 9, [],
+               [[8], [6, 4, 3, 2, 2, 1, 1, 1], [5, 4, 3, 2, 2, 2, 1, 1, 1, 1],
+                [4, 3, 2, 2, 2, 1, 1, 1, 1, 1], [3, 2, 2, 1, 1, 1], [2]]]
+
+
+# ------------------------------------------------------------------ worked example
+def test_worked_example_through_abi(tr):
+    with open(os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")) as f:
+        ex = json.load(f)
+    ids = {n: i for i, n in enumerate(ex["vocab"])}
+    V, k = len(ex["vocab"]), ex["k"]
+    M = torch.full((1, V, k), ids["pad"], dtype=torch.int64)
+    for name, row in ex["M_pre"].items():
+        M[0, ids[name]] = torch.tensor([ids[x] for x in row])
+    logits = torch.zeros((1, 7, V), dtype=torch.float32)
+    for n, row in enumerate(ex["logits"]):
+        for name, val in row.items():
+            logits[0, n, ids[name]] = val
+    tree = tr.Tree.from_levels(ex["levels"], k)
+    ws = ws_for(tr, tree, 1, V, k)
+    M_d, root = M.to(DEV), torch.tensor([ids[ex["root"]]], dtype=torch.int32, device=DEV)
+    tok = torch.empty((1, 7), dtype=torch.int32, device=DEV)
+    tr.tr_retrieve(tree, M_d, root, tok, ws)
+    assert [ex["vocab"][x] for x in tok[0].tolist()] == ex["merged_sequence"]
+    # verify through the stand-alone calls
+    topk = torch.empty((1, 7, k), dtype=torch.int32, device=DEV)
+    tr.tr_update_topk(tree, logits.to(DEV), None, None, topk, ws)
+    L = torch.empty((1,), dtype=torch.int32, device=DEV)
+    path = torch.empty((1, 3), dtype=torch.int32, device=DEV)
+    bonus = torch.empty((1,), dtype=torch.int32, device=DEV)
+    emitted = torch.empty((1, 3), dtype=torch.int32, device=DEV)
+    tr.tr_verify(tree, topk, tok, L, path, bonus, emitted)
+    e = ex["expected"]
+    assert int(L[0]) == e["accept_len"] and path[0].tolist() == e["path"]
+    assert ex["vocab"][int(bonus[0])] == e["bonus"]
+    assert [ex["vocab"][x] for x in emitted[0].tolist()] == e["emitted"]
+    # and through the fused step
+    tree_tok, root2 = tok.clone(), root.clone()
+    tr.tr_step(tree, logits.to(DEV), M_d, tree_tok, root2, L, path, emitted, ws)
+    Mh = M_d.cpu()[0]
+    for name, row in e["M_post"].items():
+        assert [ex["vocab"][x] for x in Mh[ids[name]].tolist()] == row
+    assert ex["vocab"][int(root2[0])] == e["next_root"]
+    assert [ex["vocab"][x] for x in tree_tok[0].tolist()] == e["next_tree"]
+    assert tr.tr_read_device_status(ws) == 0
+
+
+# ------------------------------------------------------------------ retrieval
+@pytest.mark.parametrize("m_dtype", [torch.int32, torch.int64])
+def test_retrieve_parity(tr, m_dtype):
+    g = torch.Generator().manual_seed(1)
+    for levels in RAND_LEVELS:
+        t = otree(levels)
+        for V, k, B in ((7, 8, 3), (1000, 8, 5), (32000, 8, 2)):
+            tree = tr.Tree.from_levels(levels, k)
+            M = torch.randint(0, V, (B, V, k), generator=g).to(m_dtype)
+            root = torch.randint(0, V, (B,), generator=g).to(torch.int32)
+            ws = ws_for(tr, tree, B)
+            tok = torch.empty((B, t.n_nodes), dtype=torch.int32, device=DEV)
+            tr.tr_retrieve(tree, M.to(DEV), root.to(DEV), tok, ws)
+            got = tok.cpu().numpy()
+            for b in range(B):
+                assert (got[b] == O.retrieve(t, M[b].numpy(), int(root[b]))).all()
+            assert tr.tr_read_device_status(ws) == 0
+
+
+def test_retrieve_flags_bad_root(tr):
+    tree = tr.Tree.from_levels([[2], [1]], 2)
+    ws = ws_for(tr, tree, 1)
+    M = torch.zeros((1, 10, 2), dtype=torch.int32, device=DEV)
+    tok = torch.empty((1, 4), dtype=torch.int32, device=DEV)
+    tr.tr_retrieve(tree, M, torch.tensor([12], dtype=torch.int32, device=DEV), tok, ws)
+    assert tr.tr_read_device_status(ws) & tr.TR_FLAG_BAD_TOKEN
+    assert tok[0, 1:].tolist() == [-1, -1, -1]
+    assert tr.tr_read_device_status(ws) == 0          # reading clears the word
+
+
+# ------------------------------------------------------------------ top-k
+def topk_cases():
+    g = torch.Generator().manual_seed(2)
+    cases = []
+    # heavy ties: values from a tiny set; signed zeros; infinities
+    z = (torch.randint(-3, 4, (9, 5003), generator=g).float() * 0.5)
+    z[0, ::7] = -0.0
+    z[1, 100] = math.inf
+    z[2, :] = -math.inf
+    z[2, 4000] = 0.0
+    z[3, :] = 0.0
+    z[3, 17] = -0.0
+    cases.append(("ties_f32", z))
+    cases.append(("ties_bf16", z.to(torch.bfloat16)))
+    cases.append(("normal_bf16_32000", (torch.randn((81, 32000), generator=g) * 3).to(torch.bfloat16)))
+    cases.append(("normal_f32_odd", torch.randn((17, 32003), generator=g) * 2))
+    cases.append(("normal_bf16_odd", (torch.randn((5, 1037), generator=g) * 3).to(torch.bfloat16)))
+    cases.append(("large_vocab", (torch.randn((3, 128256), generator=g) * 3).to(torch.bfloat16)))
+    cases.append(("tiny_vocab", torch.randn((6, 16), generator=g)))
+    return cases
+
+
+@pytest.mark.parametrize("k", [1, 3, 8, 16])
+def test_topk_parity(tr, k):
+    for name, z in topk_cases():
+        rows, V = z.shape
+        if V < k:
+            continue
+        tree = tr.Tree.from_levels([[1]] * (rows - 1), k)       # chain: rows nodes, B = 1
+        ws = ws_for(tr, tree, 1, V, k)
+        out = torch.empty((1, rows, k), dtype=torch.int32, device=DEV)
+        tr.tr_update_topk(tree, z[None].to(DEV), None, None, out, ws)
+        want = O.topk_rows(z.float().numpy(), k)
+        got = out[0].cpu().numpy()
+        bad = np.flatnonzero((got != want).any(axis=1))
+        assert len(bad) == 0, f"{name} k={k}: rows {bad[:5]} got {got[bad[0]]} want {want[bad[0]]}"
+
+
+def test_topk_unaligned_rows(tr):
+    # rows start at odd element offsets: a sliced view of a wider tensor
+    g = torch.Generator().manual_seed(3)
+    base = (torch.randn((4, 2 * 4001 + 3), generator=g) * 3).to(torch.bfloat16).to(DEV)
+    z = base.view(-1)[1: 1 + 8 * 4001].view(1, 8, 4001)           # odd element offset
+    tree = tr.Tree.from_levels([[1]] * 7, 8)
+    ws = ws_for(tr, tree, 1, 4001, 8)
+    out = torch.empty((1, 8, 8), dtype=torch.int32, device=DEV)
+    tr.tr_update_topk(tree, z, None, None, out, ws)
+    want = O.topk_rows(z[0].float().cpu().numpy(), 8)
+    assert (out[0].cpu().numpy() == want).all()
+
+
+# ------------------------------------------------------------------ verify + update
+def test_verify_parity_duplicates(tr):
+    rng = np.random.default_rng(4)
+    for levels in RAND_LEVELS:
+        t = otree(levels)
+        tree = tr.Tree.from_levels(levels, 8)
+        B = 16
+        tok = rng.integers(0, 4, size=(B, t.n_nodes)).astype(np.int32)   # many duplicates
+        top = rng.integers(0, 4, size=(B, t.n_nodes, 8)).astype(np.int32)
+        W = t.max_depth + 1
+        L = torch.empty((B,), dtype=torch.int32, device=DEV)
+        path = torch.empty((B, W), dtype=torch.int32, device=DEV)
+        bonus = torch.empty((B,), dtype=torch.int32, device=DEV)
+        em = torch.empty((B, W), dtype=torch.int32, device=DEV)
+        tr.tr_verify(tree, torch.from_numpy(top).to(DEV), torch.from_numpy(tok).to(DEV), L, path,
+                     bonus, em)
+        for b in range(B):
+            v = O.verify(t, tok[b].astype(np.int64), top[b, :, 0].astype(np.int64))
+            assert int(L[b]) == v.accept_len and int(bonus[b]) == v.bonus
+            assert path[b].tolist() == v.path.tolist() + [-1] * (W - len(v.path))
+            assert em[b].tolist() == v.emitted.tolist() + [-1] * (W - len(v.emitted))
+
+
+@pytest.mark.parametrize("m_dtype", [torch.int32, torch.int64])
+def test_update_parity_duplicate_rows(tr, m_dtype):
+    rng = np.random.default_rng(5)
+    levels = RAND_LEVELS[4]
+    t = otree(levels)
+    tree = tr.Tree.from_levels(levels, 8)
+    B, V = 3, 50
+    tok = rng.integers(0, 12, size=(B, t.n_nodes)).astype(np.int32)     # tokens repeat often
+    z = torch.from_numpy(rng.standard_normal((B, t.n_nodes, V)).astype(np.float32))
+    M0 = torch.from_numpy(rng.integers(0, V, size=(B, V, 8))).to(m_dtype)
+    Md = M0.to(DEV)
+    ws = ws_for(tr, tree, B, V, 8)
+    tr.tr_update_topk(tree, z.to(DEV), torch.from_numpy(tok).to(DEV), Md, None, ws)
+    for b in range(B):
+        Mo = M0[b].numpy().astype(np.int64).copy()
+        O.update(Mo, tok[b], O.topk_rows(z[b].numpy(), 8))
+        assert (Md[b].cpu().numpy() == Mo).all()
+
+
+# ------------------------------------------------------------------ attention
+def attn_inputs(g, B, T, Hq, Hkv, P, cap, dtype):
+    q = torch.randn((B, T, Hq, 128), generator=g).to(dtype)
+    kt = torch.randn((B, T, Hkv, 128), generator=g).to(dtype)
+    vt = torch.randn((B, T, Hkv, 128), generator=g).to(dtype)
+    kc = torch.randn((B, Hkv, cap, 128), generator=g).to(dtype)
+    vc = torch.randn((B, Hkv, cap, 128), generator=g).to(dtype)
+    return q, kt, vt, kc, vc
+
+
+def check_attn(t, got, q, kt, vt, kc, vc, P, dtype, rows=None):
+    B = q.shape[0]
+    for b in range(B):
+        want = O.tree_attention(t, q[b].double().numpy(), kt[b].double().numpy(), vt[b].double().numpy(),
+                                kc[b].double().numpy(), vc[b].double().numpy(), int(P[b]))
+        gb = got[b].double().numpy()
+        if dtype == torch.float32:
+            num = np.abs(gb - want).max(axis=-1)
+            den = np.maximum(np.abs(want).max(axis=-1), 1e-30)
+            assert (num / den).max() <= 1e-5, (num / den).max()
+        else:
+            assert np.abs(gb - want).max() <= 2e-2, np.abs(gb - want).max()
+
+
+ATTN_CASES = [
+    # levels, B, Hq, Hkv, P list, cap
+    (RAND_LEVELS[1], 1, 8, 8, [256], 300),
+    (RAND_LEVELS[0], 2, 4, 2, [0, 5], 70),
+    (RAND_LEVELS[4], 1, 32, 32, [1000], 1100),
+    (RAND_LEVELS[4], 3, 16, 2, [63, 700, 1], 800),
+    (RAND_LEVELS[2], 2, 8, 8, [130, 64], 200),
+    (RAND_LEVELS[3], 2, 8, 1, [77, 3000], 3100),
+    (RAND_LEVELS[4], 1, 64, 8, [1500], 1600),
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("case", range(len(ATTN_CASES)))
+def test_tree_attention_parity(tr, dtype, case):
+    levels, B, Hq, Hkv, Ps, cap = ATTN_CASES[case]
+    t = otree(levels)
+    tree = tr.Tree.from_levels(levels, 8)
+    g = torch.Generator().manual_seed(100 + case)
+    q, kt, vt, kc, vc = attn_inputs(g, B, t.n_nodes, Hq, Hkv, max(Ps), cap, dtype)
+    P = torch.tensor(Ps, dtype=torch.int32)
+    ws = ws_for(tr, tree, B, Hq=Hq, Hkv=Hkv, cap=cap)
+    out = torch.empty_like(q, device=DEV)
+    tr.tr_tree_attn(tree, q.to(DEV), kt.to(DEV), vt.to(DEV), kc.to(DEV), vc.to(DEV), P.to(DEV), out, ws)
+    check_attn(t, out.cpu(), q, kt, vt, kc, vc, P, dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_attention_siblings_and_determinism(tr, dtype):
+    levels = RAND_LEVELS[4]
+    t = otree(levels)
+    tree = tr.Tree.from_levels(levels, 8)
+    g = torch.Generator().manual_seed(7)
+    q, kt, vt, kc, vc = [x.to(DEV) for x in attn_inputs(g, 1, t.n_nodes, 16, 4, 900, 1000, dtype)]
+    P = torch.tensor([900], dtype=torch.int32, device=DEV)
+    ws = ws_for(tr, tree, 1, Hq=16, Hkv=4, cap=1000)
+    base = torch.empty_like(q)
+    tr.tr_tree_attn(tree, q, kt, vt, kc, vc, P, base, ws)
+    again = torch.empty_like(q)
+    tr.tr_tree_attn(tree, q, kt, vt, kc, vc, P, again, ws)
+    assert torch.equal(base.view(torch.int16) if dtype == torch.bfloat16 else base.view(torch.int32),
+                       again.view(torch.int16) if dtype == torch.bfloat16 else again.view(torch.int32))
+    mask = O.ancestor_mask(t)
+    for j in (1, 9, 40, 80):
+        kt2, vt2 = kt.clone(), vt.clone()
+        kt2[0, j] += 3.0
+        vt2[0, j] -= 2.0
+        out = torch.empty_like(q)
+        tr.tr_tree_attn(tree, q, kt2, vt2, kc, vc, P, out, ws)
+        changed = []
+        for n in range(t.n_nodes):
+            same = torch.equal(out[0, n], base[0, n])
+            if not mask[n, j]:
+                assert same, (j, n)             # a non-ancestor never matters, bit for bit
+            else:
+                changed.append(not same)
+        # an ancestor's key/value always moves the fp32 result; bf16 rounding may hide a few
+        assert all(changed) if dtype == torch.float32 else np.mean(changed) >= 0.9
+
+
+# ------------------------------------------------------------------ step + commit
+def test_step_commit_and_cache_full_flag(tr):
+    levels = RAND_LEVELS[1]
+    t = otree(levels)
+    tree = tr.Tree.from_levels(levels, 8)
+    V, B, Hkv = 300, 2, 2
+    g = torch.Generator().manual_seed(9)
+    M = torch.randint(0, V, (B, V, 8), generator=g, dtype=torch.int32)
+    kc = torch.zeros((B, Hkv, 40, 128), dtype=torch.bfloat16)
+    vc = torch.zeros_like(kc)
+    P = torch.tensor([5, 37], dtype=torch.int32)       # sequence 1 will overflow its cache
+    root = torch.tensor([3, 4], dtype=torch.int32)
+    kt = torch.randn((B, t.n_nodes, Hkv, 128), generator=g).to(torch.bfloat16)
+    vt = torch.randn((B, t.n_nodes, Hkv, 128), generator=g).to(torch.bfloat16)
+    ws = ws_for(tr, tree, B, V, 8)
+    dM, dkc, dvc, dP, droot = (x.to(DEV) for x in (M, kc, vc, P, root))
+    tok = torch.empty((B, t.n_nodes), dtype=torch.int32, device=DEV)
+    tr.tr_retrieve(tree, dM, droot, tok, ws)
+    tok_h = tok.cpu().numpy()
+    # logits whose greedy continuation follows the rank-0 chain: accept 3 drafts
+    z = torch.randn((B, t.n_nodes, V), generator=g)
+    for b in range(B):
+        for a, c in ((0, 1), (1, 5), (5, 13)):
+            z[b, a, tok_h[b, c]] = 50.0
+    L = torch.empty((B,), dtype=torch.int32, device=DEV)
+    path = torch.empty((B, 4), dtype=torch.int32, device=DEV)
+    em = torch.empty((B, 4), dtype=torch.int32, device=DEV)
+    tr.tr_step(tree, z.to(DEV), dM, tok, droot, L, path, em, ws, kt.to(DEV), vt.to(DEV), dkc, dvc, dP)
+    flags = tr.tr_read_device_status(ws)
+    for b in range(B):
+        Mo = M[b].numpy().astype(np.int64).copy()
+        if b == 0:      # fits: the oracle commits too
+            res, newP = O.step_after_forward(t, Mo, tok_h[b].astype(np.int64), z[b].numpy(), 8,
+                                             kc[b].float().numpy(), vc[b].float().numpy(),
+                                             kt[b].float().numpy(), vt[b].float().numpy(), int(P[b]))
+        else:           # 37 + 4 > 40: no commit, prefix unchanged, flag raised
+            res, newP = O.step_after_forward(t, Mo, tok_h[b].astype(np.int64), z[b].numpy(), 8)[0], int(P[b])
+        assert int(L[b]) == 3 == res.verdict.accept_len
+        assert (dM[b].cpu().numpy() == Mo).all()
+        assert tok[b].cpu().numpy().tolist() == res.next_tok.tolist()
+        assert int(droot[b]) == res.verdict.bonus
+        assert int(dP[b]) == newP
+    assert torch.equal(dkc[0, :, 5:9].cpu(), kt[0, [0, 1, 5, 13]].transpose(0, 1))
+    assert torch.equal(dvc[0, :, 5:9].cpu(), vt[0, [0, 1, 5, 13]].transpose(0, 1))
+    assert (dkc[0, :, 9:].cpu() == 0).all() and (dkc[1].cpu() == 0).all()
+    assert flags & tr.TR_FLAG_CACHE_FULL

@@ -1,0 +1,127 @@
+"""Whole-loop parity on the five seeded workloads, at full size (MI355X only).
+
+The HIP path runs exactly what the benchmark times: per step one
+tr_tree_attn call and one fused tr_step call, on the workload's shapes and
+step count.  The oracle runs the same trajectory on the host from the same
+seeded inputs: the logits of every step are drawn from the ORACLE's tree
+tokens, after checking that the GPU's tree equals them.
+
+Checked bit for bit on every step: tree tokens, top-k of every node,
+accepted length, path, emitted tokens, next root, prefix length; at the end:
+every row of M and every committed key/value row.  Attention is checked at
+sampled steps within 2e-2 absolute (bf16) or 1e-5 relative per row (fp32).
+The large-vocabulary batch (32 sequences) is followed by the oracle on a
+seeded sample of sequences (sequences are independent).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import tr_oracle as O
+from synth import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def tr():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from draft_tree_retrieval_amd import tr as _tr
+    _tr.load()
+    return _tr
+
+
+def attn_ok(t, out, q, kt, vt, kc, vc, P, dtype):
+    want = O.tree_attention(t, q, kt, vt, kc, vc, P)
+    if dtype == torch.float32:
+        rel = np.abs(out - want).max(-1) / np.maximum(np.abs(want).max(-1), 1e-30)
+        return float(rel.max()), rel.max() <= 1e-5
+    err = float(np.abs(out - want).max())
+    return err, err <= 2e-2
+
+
+def run_loop(tr, w, steps, track, attn_steps):
+    from draft_tree_retrieval_amd.loop import TRDecoder
+    t = O.template_from_levels(w.levels)
+    st = W.initial_state(w, DEV)
+    host = st.to("cpu")
+    tree = tr.Tree.from_levels(w.levels, w.k)
+    dec = TRDecoder(tree, st.M, st.k_cache, st.v_cache, st.prefix_len, st.root, Hq=w.Hq)
+    # oracle state of the tracked sequences
+    oM = {b: host.M[b].numpy().astype(np.int64).copy() for b in track}
+    okc = {b: host.k_cache[b].float().numpy().copy() for b in track}
+    ovc = {b: host.v_cache[b].float().numpy().copy() for b in track}
+    oP = {b: int(host.prefix_len[b]) for b in track}
+    otok = {b: O.retrieve(t, oM[b], int(host.root[b])) for b in track}
+    P0 = dict(oP)
+    worst = 0.0
+    out = torch.empty((w.B, w.T, w.Hq, w.d), dtype=w.kv_dtype, device=DEV)
+    for s in range(steps):
+        gtok = dec.tree_tok.cpu().numpy()
+        for b in track:
+            assert (gtok[b] == otok[b]).all(), f"step {s} seq {b}: tree differs"
+        q, kt, vt = W.step_qkv(w, s, DEV)
+        dec.attend(q, kt, vt, out)
+        if s in attn_steps:
+            oh = out.float().cpu().numpy()
+            for b in track:
+                err, ok = attn_ok(t, oh[b], q[b].float().cpu().numpy(), kt[b].float().cpu().numpy(),
+                                  vt[b].float().cpu().numpy(), okc[b], ovc[b], oP[b], w.kv_dtype)
+                worst = max(worst, err)
+                assert ok, f"step {s} seq {b}: attention error {err}"
+        gen_tok = dec.tree_tok.clone()
+        for b in track:
+            gen_tok[b] = torch.from_numpy(otok[b]).to(torch.int32)
+        logits = W.step_logits(w, s, gen_tok, DEV)
+        dec.step(logits, kt, vt)
+        zl = {b: logits[b].float().cpu().numpy() for b in track}
+        kth = {b: kt[b].float().cpu().numpy() for b in track}
+        vth = {b: vt[b].float().cpu().numpy() for b in track}
+        gk = dec.topk.cpu().numpy()
+        gL, gem, groot, gP = (x.cpu().numpy() for x in (dec.accept_len, dec.emitted, dec.root_tok,
+                                                        dec.prefix_len))
+        for b in track:
+            res, oP[b] = O.step_after_forward(t, oM[b], otok[b], zl[b], w.k, okc[b], ovc[b],
+                                              kth[b], vth[b], oP[b])
+            assert (gk[b] == res.topk).all(), f"step {s} seq {b}: top-k differs"
+            v = res.verdict
+            assert int(gL[b]) == v.accept_len, f"step {s} seq {b}: accept length"
+            em = v.emitted.tolist() + [-1] * (t.max_depth + 1 - len(v.emitted))
+            assert gem[b].tolist() == em, f"step {s} seq {b}: emitted"
+            assert int(groot[b]) == v.bonus and int(gP[b]) == oP[b]
+            otok[b] = res.next_tok
+    assert dec.device_flags() == 0
+    Mh = dec.M.cpu()
+    for b in track:
+        assert (Mh[b].numpy().astype(np.int64) == oM[b]).all(), f"seq {b}: M differs"
+        kc = dec.k_cache[b, :, P0[b]:oP[b]].float().cpu().numpy()
+        vc = dec.v_cache[b, :, P0[b]:oP[b]].float().cpu().numpy()
+        assert (kc == okc[b][:, P0[b]:oP[b]]).all() and (vc == ovc[b][:, P0[b]:oP[b]]).all()
+    return worst
+
+
+def test_tiny_full(tr):
+    w = W.WORKLOADS["tiny"]
+    run_loop(tr, w, w.steps, [0], {0})
+
+
+def test_vicuna7b_full(tr):
+    w = W.WORKLOADS["vicuna7b"]
+    run_loop(tr, w, w.steps, [0], {0, 1, 100, w.steps - 1})
+
+
+def test_vicuna13b_full(tr):
+    w = W.WORKLOADS["vicuna13b"]
+    run_loop(tr, w, w.steps, [0], {0, 257, w.steps - 1})
+
+
+def test_codellama34b_full(tr):
+    w = W.WORKLOADS["codellama34b"]
+    run_loop(tr, w, w.steps, [0], {0, 300, w.steps - 1})
+
+
+def test_largevocab_full_sampled_sequences(tr):
+    w = W.WORKLOADS["largevocab"]
+    run_loop(tr, w, w.steps, [0, 13, 31], {0, 64, w.steps - 1})
