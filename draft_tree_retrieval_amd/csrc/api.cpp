@@ -100,7 +100,9 @@ tr_status build_tree(int32_t n, const int32_t* parent, const int32_t* rank, int3
 }
 
 size_t topk_need(const tr_tree* t, int32_t B, int64_t V, int32_t k) {
-  return tr::plan_topk(int64_t(B) * t->dev.T, V, k).end;
+  const int64_t rows = int64_t(B) * t->dev.T;
+  const size_t a = tr::plan_topk(rows, V, k, 2).end, b = tr::plan_topk(rows, V, k, 4).end;
+  return a > b ? a : b;
 }
 
 }  // namespace
@@ -279,7 +281,7 @@ tr_status tr_update_topk(const tr_tree* t, int32_t B, const void* logits, tr_dty
     TR_CHECK(tree_tok != nullptr, TR_ERR_INVALID_ARGUMENT, "tree_tok is null");
     TR_CHECK(m_dtype == TR_INT32 || m_dtype == TR_INT64, TR_ERR_UNSUPPORTED, "M must be int32 or int64");
   }
-  const tr::TopkPlan plan = tr::plan_topk(int64_t(B) * t->dev.T, V, k);
+  const tr::TopkPlan plan = tr::plan_topk(int64_t(B) * t->dev.T, V, k, l_dtype == TR_BFLOAT16 ? 2 : 4);
   st = check_ws(ws, ws_bytes, plan.end);
   if (st != TR_OK) return st;
   uint8_t* w = static_cast<uint8_t*>(ws);
@@ -328,7 +330,7 @@ tr_status tr_step(const tr_tree* t, int32_t B, int64_t V, int32_t k, const void*
              TR_ERR_INVALID_ARGUMENT, "key/value tensors must be 16-byte aligned");
     row_bytes = d * (kv_dtype == TR_BFLOAT16 ? 2 : 4);
   }
-  const tr::TopkPlan plan = tr::plan_topk(int64_t(B) * t->dev.T, V, k);
+  const tr::TopkPlan plan = tr::plan_topk(int64_t(B) * t->dev.T, V, k, l_dtype == TR_BFLOAT16 ? 2 : 4);
   st = check_ws(ws, ws_bytes, plan.end);
   if (st != TR_OK) return st;
   uint8_t* w = static_cast<uint8_t*>(ws);

@@ -12,19 +12,34 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- numbers
-// Order-preserving map of an IEEE float bit pattern to uint32 (larger value
-// -> larger code).  The folded form maps -0.0 onto +0.0 so that equal
-// values compare equal.
-__device__ __forceinline__ uint32_t ord_nofold(uint32_t bits) {
-  return (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
+// Order code of an IEEE float bit pattern: a larger value gets a larger
+// code, -0.0 and +0.0 get the same code (0x80000000), and every non-NaN
+// value gets a code above 0 (so 0 can mark "empty").  Negative values map
+// to the two's complement negation of their bits, the others to the bits
+// plus 2^31.
+__device__ __forceinline__ uint32_t ord32(uint32_t bits) {
+  return (bits & 0x80000000u) ? (0u - bits) : (bits + 0x80000000u);
 }
-__device__ __forceinline__ uint32_t ord_fold(uint32_t bits) {
-  return ord_nofold(bits == 0x80000000u ? 0u : bits);
+// The same code for each bfloat16 half of a word (16-bit arithmetic per
+// half): ord16(h) << 16 == ord32(h << 16).
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef int16_t i16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t ord16x2(uint32_t w) {
+  const u16x2 x = __builtin_bit_cast(u16x2, w);
+  const uint32_t neg_mask = __builtin_bit_cast(uint32_t, __builtin_bit_cast(i16x2, w) >> (int16_t)15);
+  const uint32_t neg = __builtin_bit_cast(uint32_t, (u16x2)(0) - x);
+  const uint32_t pos = __builtin_bit_cast(uint32_t, x + (u16x2)(0x8000));
+  return (neg & neg_mask) | (pos & ~neg_mask);
+}
+__device__ __forceinline__ uint32_t max16x2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
 }
 // Selection key: value first, then the lower token id wins ties.
-__device__ __forceinline__ uint64_t make_key(uint32_t bits, uint32_t id) {
-  return (uint64_t(ord_fold(bits)) << 32) | uint32_t(~id);
+__device__ __forceinline__ uint64_t key_of(uint32_t code, uint32_t id) {
+  return (uint64_t(code) << 32) | uint32_t(~id);
 }
+__device__ __forceinline__ uint64_t make_key(uint32_t bits, uint32_t id) { return key_of(ord32(bits), id); }
 __device__ __forceinline__ uint32_t key_id(uint64_t key) { return ~uint32_t(key); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {  // round to nearest even
@@ -38,6 +53,11 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_floa
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   uint32_t lo = __shfl_xor(uint32_t(v), m, 64);
   uint32_t hi = __shfl_xor(uint32_t(v >> 32), m, 64);
+  return (uint64_t(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
+  uint32_t lo = __shfl(uint32_t(v), src, 64);
+  uint32_t hi = __shfl(uint32_t(v >> 32), src, 64);
   return (uint64_t(hi) << 32) | lo;
 }
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
@@ -96,25 +116,59 @@ __device__ __forceinline__ void wave_merge(TopList<KM>& L, uint64_t* out) {
   }
 }
 
+// In-wave bitonic sort of one 64-bit key per lane, largest at lane 0.
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint64_t o = shfl_xor_u64(v, j);
+      const bool keep_max = ((lane & j) == 0) == ((lane & k) == 0);
+      v = keep_max ? (o > v ? o : v) : (o < v ? o : v);
+    }
+  }
+  return v;
+}
+
 // ---------------------------------------------------------------- handshake
-// Called by every thread of a block after it wrote its results.  Returns
-// true in every thread of the block that arrives last among `total`
-// blocks sharing `counter`; that block sees the others' writes, and the
-// counter is back to zero for the next call.
+// Blocks of one launch hand results to the block that arrives last.  The
+// L2 caches of the XCDs are not coherent with each other, and a device-scope
+// fence would write back and invalidate a whole L2, so nothing here uses
+// one.  Instead every value handed over is written with a device-scope
+// atomic exchange (performed at the device's coherence point) by thread 0
+// of the writing block, which waits for those atomics to complete before it
+// counts the block in; the last block reads the values with device-scope
+// atomic loads, which do not hit stale L2 lines.
+__device__ __forceinline__ void put_dev(uint64_t* p, uint64_t v) {
+  __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void put_dev(int32_t* p, int32_t v) {
+  __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t get_dev(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t get_dev(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Called by every thread of a block after thread 0 wrote its hand-over
+// values with put_dev.  Returns true in every thread of the block that
+// arrives last among `total` blocks sharing `counter`; the counter is back
+// to zero afterwards.
 __device__ __forceinline__ bool last_block_arrives(uint32_t* counter, uint32_t total) {
   __shared__ uint32_t s_last;
-  __threadfence();
   __syncthreads();
   if (threadIdx.x == 0) {
-    uint32_t prev = atomicAdd(counter, 1u);
-    bool last = (prev == total - 1);
-    if (last) atomicExch(counter, 0u);
+    __builtin_amdgcn_s_waitcnt(0);     // this thread's put_dev atomics have completed
+    const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = (prev == total - 1);
+    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = last ? 1u : 0u;
   }
   __syncthreads();
-  bool last = s_last != 0;
-  if (last) __threadfence();
-  return last;
+  return s_last != 0;
 }
 
 __device__ __forceinline__ void set_flag(uint8_t* ws, uint32_t bit) {

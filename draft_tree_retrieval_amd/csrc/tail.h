@@ -27,12 +27,13 @@ __device__ __forceinline__ void m_store(void* M, int m_is64, int64_t idx, int32_
   else reinterpret_cast<int32_t*>(M)[idx] = v;
 }
 
-// tok <- tree_tok_b, g <- column 0 of topk_b.
+// tok <- tree_tok_b, g <- column 0 of topk_b.  The top-k rows may have been
+// handed over by other blocks of the same launch: read them with get_dev.
 __device__ __forceinline__ void tail_load(TailShared& S, const TreeDev& tree, const int32_t* tok_b,
                                           const int32_t* topk_b, int32_t k) {
   for (int n = threadIdx.x; n < tree.T; n += blockDim.x) {
     S.tok[n] = tok_b[n];
-    S.g[n] = topk_b[int64_t(n) * k];
+    S.g[n] = get_dev(topk_b + int64_t(n) * k);
   }
   __syncthreads();
 }
@@ -106,7 +107,7 @@ __device__ __forceinline__ void tail_update(const TailShared& S, const TreeDev& 
       set_flag(ws, TR_FLAG_BAD_TOKEN);
       continue;
     }
-    for (int j = 0; j < k; ++j) m_store(M_b, m_is64, int64_t(t) * k + j, topk_b[int64_t(n) * k + j]);
+    for (int j = 0; j < k; ++j) m_store(M_b, m_is64, int64_t(t) * k + j, get_dev(topk_b + int64_t(n) * k + j));
   }
 }
 
@@ -124,30 +125,32 @@ __device__ __forceinline__ void tail_commit(TailShared& S, const TreeDev& tree, 
   }
   const int upr = a.row_bytes >> 4;               // 16-byte units per row
   const int per_node = a.Hkv * upr;
-  const int total = nrows * per_node;
-  for (int u0 = threadIdx.x; u0 < 2 * total; u0 += 4 * blockDim.x) {
-    uint4 buf[4];
-    uint8_t* dst[4];
+  const int total = 2 * nrows * per_node;          // keys then values
+  constexpr int R = 4;                             // units in flight per thread
+  for (int u0 = threadIdx.x; u0 < total; u0 += R * blockDim.x) {
+    u32x4 buf[R];
+    int64_t dst_off[R];
+    bool dst_v[R];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      int u = u0 + r * blockDim.x;
-      dst[r] = nullptr;
-      if (u < 2 * total) {
-        const bool isv = u >= total;
-        const int uu = isv ? u - total : u;
-        const int i = uu / per_node, rem = uu - i * per_node;
-        const int h = rem / upr, c = rem - h * upr;
-        const int node = S.path[i];
-        const uint8_t* src = (isv ? a.v_tree : a.k_tree) +
-                             ((int64_t(b) * tree.T + node) * a.Hkv + h) * a.row_bytes + c * 16;
-        dst[r] = (isv ? a.v_cache : a.k_cache) +
-                 ((int64_t(b) * a.Hkv + h) * a.cap + P + i) * a.row_bytes + c * 16;
-        buf[r] = *reinterpret_cast<const uint4*>(src);
-      }
+    for (int r = 0; r < R; ++r) {
+      const int u = min(u0 + r * int(blockDim.x), total - 1);   // clamped: loads stay in bounds
+      const bool isv = u >= total / 2;
+      const int uu = isv ? u - total / 2 : u;
+      const int i = uu / per_node, rem = uu - i * per_node;
+      const int h = rem / upr, c = rem - h * upr;
+      const int node = S.path[i];
+      const uint8_t* src = (isv ? a.v_tree : a.k_tree) +
+                           ((int64_t(b) * tree.T + node) * a.Hkv + h) * a.row_bytes + c * 16;
+      dst_off[r] = ((int64_t(b) * a.Hkv + h) * a.cap + P + i) * a.row_bytes + c * 16;
+      dst_v[r] = isv;
+      buf[r] = *reinterpret_cast<const u32x4*>(src);
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (dst[r]) *reinterpret_cast<uint4*>(dst[r]) = buf[r];
+    for (int r = 0; r < R; ++r) {
+      if (u0 + r * int(blockDim.x) >= total) break;
+      uint8_t* dst = (dst_v[r] ? a.v_cache : a.k_cache) + dst_off[r];
+      *reinterpret_cast<u32x4*>(dst) = buf[r];
+    }
   }
   __syncthreads();
   if (threadIdx.x == 0) a.prefix_len[b] = int32_t(P + nrows);

@@ -58,7 +58,7 @@ struct TopkPlan {
   size_t ids_off;     // int32  [rows][k] ids when the caller gives no buffer
   size_t end;
 };
-TopkPlan plan_topk(int64_t rows, int64_t V, int32_t k);
+TopkPlan plan_topk(int64_t rows, int64_t V, int32_t k, int32_t esz);
 
 // Attention launch shape.
 struct AttnPlan {
