@@ -42,7 +42,47 @@ def parse():
     ap.add_argument("--workload", default="vicuna7b")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the CPU oracle baseline (0 disables it)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (reference for "
+                         "the FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
+
+
+def kernel_sources_sha256():
+    """Hash of the HIP sources: traffic counters taken on other sources are stale."""
+    import hashlib
+    d = os.path.join(ROOT, "draft_tree_retrieval_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, call):
+    """HBM bytes per launch of `call` from the committed counter record of this
+    workload (FETCH_SIZE and WRITE_SIZE runs, scaled by a plain copy), or None
+    when there is no record or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("sources_sha256") != kernel_sources_sha256():
+        return None
+    return rec.get("per_call_bytes", {}).get(call)
+
+
+def copy_calibration(mib):
+    """A plain copy kernel of known size: each launch reads and writes
+    exactly mib MiB, so HBM counters read on it give their scale."""
+    import torch
+    src = torch.ones(mib << 18, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": mib << 20, "launches": 5}), flush=True)
 
 
 def cpu_baseline(w, inputs, init_host, seconds):
@@ -81,6 +121,9 @@ def cpu_baseline(w, inputs, init_host, seconds):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -199,7 +242,7 @@ def main():
                    "head_dim": w.d, "prefix": list(w.prefix), "M_dtype": str(w.m_dtype)[6:]},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(args.workload, dom)},
         "per_call": detail,
         "emitted_per_step": round(L_mean + 1, 3),
         "cpu_baseline": cpu,

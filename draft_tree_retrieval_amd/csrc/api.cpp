@@ -186,8 +186,10 @@ size_t tr_workspace_size(const tr_tree* t, int32_t B, int64_t V, int32_t k, int3
     if (a > need) need = a;
   }
   if (Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0 && d == tr::kHeadDim && cap >= 0) {
-    size_t a = tr::plan_attn(t->dev.T, B, Hq, Hkv, cap).end;
-    if (a > need) need = a;
+    for (int bf = 0; bf < 2; ++bf) {
+      size_t a = tr::plan_attn(t->dev.T, B, Hq, Hkv, cap, bf).end;
+      if (a > need) need = a;
+    }
   }
   return need;
 }
@@ -240,11 +242,12 @@ tr_status tr_tree_attn(const tr_tree* t, int32_t B, int32_t Hq, int32_t Hkv, int
   TR_CHECK(Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0, TR_ERR_INVALID_ARGUMENT,
            "Hq (%d) must be a positive multiple of Hkv (%d)", Hq, Hkv);
   TR_CHECK(cap >= 0, TR_ERR_INVALID_ARGUMENT, "negative capacity");
+  TR_CHECK(scale > 0.f && scale < 1e30f, TR_ERR_INVALID_ARGUMENT, "scale must be positive and finite");
   TR_CHECK(int64_t(B) * Hkv <= 65535, TR_ERR_UNSUPPORTED, "B*Hkv above 65535");
   TR_CHECK(aligned16(q) && aligned16(k_tree) && aligned16(v_tree) && aligned16(k_cache) &&
                aligned16(v_cache) && aligned16(out), TR_ERR_INVALID_ARGUMENT,
            "attention tensors must be 16-byte aligned");
-  const tr::AttnPlan plan = tr::plan_attn(t->dev.T, B, Hq, Hkv, cap);
+  const tr::AttnPlan plan = tr::plan_attn(t->dev.T, B, Hq, Hkv, cap, dt == TR_BFLOAT16);
   tr_status st = check_ws(ws, ws_bytes, plan.end);
   if (st != TR_OK) return st;
   return hip_status(tr::launch_attn(t->dev, B, Hq, Hkv, dt == TR_BFLOAT16, q, k_tree, v_tree, k_cache,

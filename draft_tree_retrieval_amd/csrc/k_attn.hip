@@ -24,25 +24,37 @@ namespace tr {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kSub = 64;          // keys per staged sub-block (bf16)
+constexpr int kSub = 64;          // chunk boundaries are multiples of this many keys
+constexpr int kSubB = 128;        // keys per staged sub-block (bf16 kernel)
+constexpr int kWaves = 8;         // waves per bf16 prefix block
 constexpr int kKsStride = 136;    // bf16 per staged K row: 272 bytes, conflict-free b128 reads
-constexpr int kSpw = 2;           // 16-row strips per wave
-constexpr int kRowsPerTile = 4 * kSpw * 16;
+constexpr int kVtStride = 132;    // bf16 per staged V^T row (128 keys + 4): 264 bytes
+constexpr int kSpw = 2;           // 16-row strips per wave (fp32 kernel)
+constexpr int kRowsPerTile = 4 * kSpw * 16;   // fp32 kernel: 4 waves
 constexpr float kLog2e = 1.4426950408889634f;
 
-AttnPlan plan_attn(int32_t T, int32_t B, int32_t Hq, int32_t Hkv, int64_t cap) {
+AttnPlan plan_attn(int32_t T, int32_t B, int32_t Hq, int32_t Hkv, int64_t cap, int is_bf16) {
   AttnPlan p{};
   p.G = Hq / Hkv;
   p.R = T * p.G;
-  p.row_tiles = (p.R + kRowsPerTile - 1) / kRowsPerTile;
+  if (is_bf16) {
+    // one strip per wave unless two halve the tiles at no extra padding
+    const int t1 = (p.R + 127) / 128, t2 = (p.R + 255) / 256;
+    p.spw = (t2 * 256 <= t1 * 128) ? 2 : 1;
+    p.tile_rows = kWaves * p.spw * 16;
+  } else {
+    p.spw = kSpw;
+    p.tile_rows = kRowsPerTile;
+  }
+  p.row_tiles = (p.R + p.tile_rows - 1) / p.tile_rows;
   int64_t base = int64_t(B) * Hkv * p.row_tiles;
-  int64_t chunks = (256 + base - 1) / base;
+  int64_t chunks = (256 + base - 1) / base;        // about one block per CU
   int64_t by_cap = (cap + kSub - 1) / kSub;
   if (chunks > by_cap) chunks = by_cap;
   if (chunks > 64) chunks = 64;
   if (chunks < 1) chunks = 1;
   p.chunks = int32_t(chunks);
-  const size_t rpad = size_t(p.row_tiles) * kRowsPerTile;
+  const size_t rpad = size_t(p.row_tiles) * p.tile_rows;
   const size_t units = size_t(B) * Hkv * p.chunks * rpad;
   size_t off = kDataOff;
   p.o_off = off;
@@ -68,17 +80,28 @@ __device__ __forceinline__ int clamp_prefix(int P, int64_t cap, uint8_t* ws, boo
   return P;
 }
 
-__device__ __forceinline__ int vt_swz(int row) { return (row + (row >> 4)) & 15; }
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------- bf16 prefix
-__global__ __launch_bounds__(256) void attn_prefix_bf16(
+// 8 waves; SPW 16-row strips per wave; 128-key sub-blocks staged in LDS
+// while the next sub-block is already loading into registers (64 KB in
+// flight per block).
+template <int SPW>
+__global__ __launch_bounds__(512) void attn_prefix_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, int64_t cap, const int32_t* __restrict__ prefix_len, int T,
     int Hq, int Hkv, int G, int R, int chunks, float sl2, float* __restrict__ part_o,
-    float2* __restrict__ part_ml, uint8_t* ws) {
-  const int c = blockIdx.x, rt = blockIdx.y, z = blockIdx.z;
+    float2* __restrict__ part_ml, uint8_t* ws, int B, int row_tiles) {
+  constexpr int kRows = kWaves * SPW * 16;        // query rows per tile
+  // Blocks are dealt to the 8 XCDs round-robin by block index.  The row
+  // tiles of one (sequence, kv head, chunk) group read the same keys and
+  // values, so they are given consecutive slots on the same XCD and share
+  // its L2: block i runs on XCD i % 8, slot i / 8 of that XCD.
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int rt = slot % row_tiles;
+  const int grp = (slot / row_tiles) * 8 + xcd;    // (sequence, kv head, chunk) group
+  if (grp >= B * Hkv * chunks) return;
+  const int z = grp / chunks, c = grp - z * chunks;
   const int b = z / Hkv, kvh = z - b * Hkv;
   const int P = clamp_prefix(prefix_len[b], cap, ws, c == 0 && rt == 0 && kvh == 0 && threadIdx.x == 0);
   const int cs = chunk_len(P, chunks, kSub);
@@ -86,15 +109,17 @@ __global__ __launch_bounds__(256) void attn_prefix_bf16(
   const int k1 = min(P, k0 + cs);
   if (k0 >= k1) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, g = lane >> 4;
-  const int Rpad = gridDim.y * kRowsPerTile;
+  const int Rpad = row_tiles * kRows;
+  const int row0 = rt * kRows + w * SPW * 16;      // first query row of this wave
+  const bool active = row0 < R;                    // waves past the last row only load
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kSub * kKsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[kHeadDim * kSub];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kSubB * kKsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[kHeadDim * kVtStride];
 
-  bf16x8 qb[kSpw][4];
+  bf16x8 qb[SPW][4];
 #pragma unroll
-  for (int s = 0; s < kSpw; ++s) {
-    const int r = rt * kRowsPerTile + (w * kSpw + s) * 16 + li;
+  for (int s = 0; s < SPW; ++s) {
+    const int r = row0 + s * 16 + li;
     if (r < R) {
       const int n = r / G, gq = r - n * G;
       const uint16_t* qp = q + ((int64_t(b) * T + n) * Hq + kvh * G + gq) * kHeadDim;
@@ -107,10 +132,10 @@ __global__ __launch_bounds__(256) void attn_prefix_bf16(
     }
   }
 
-  floatx4 acc[kSpw][8];
-  float mrow[kSpw], lrow[kSpw];
+  floatx4 acc[SPW][8];
+  float mrow[SPW], lrow[SPW];
 #pragma unroll
-  for (int s = 0; s < kSpw; ++s) {
+  for (int s = 0; s < SPW; ++s) {
     mrow[s] = -INFINITY;
     lrow[s] = 0.f;
 #pragma unroll
@@ -120,34 +145,35 @@ __global__ __launch_bounds__(256) void attn_prefix_bf16(
   const int64_t head_off = (int64_t(b) * Hkv + kvh) * cap * kHeadDim;
   const uint16_t* kbase = kc + head_off;
   const uint16_t* vbase = vc + head_off;
-  const int cch = tid & 15;     // 16-byte column chunk of a 256-byte row
-  const int rq = tid >> 4;      // 0..15
+  const int cch = tid & 15;     // K: 16-byte column chunk of a 256-byte row
+  const int rq = tid >> 4;      // K: rows rq + 32 j
+  const int vq = tid & 31;      // V: keys 4 vq .. 4 vq + 3
+  const int vd = tid >> 5;      // V: d = 8 vd .. 8 vd + 7 (transposed when staged)
 
   u32x4 kreg[4], vreg[4];
   auto load_sub = [&](int kb) {
-    const int nk = min(kSub, k1 - kb);
+    const int nk = min(kSubB, k1 - kb);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int rk = rq + 16 * j;
+      const int rk = rq + 32 * j;
       kreg[j] = rk < nk ? *reinterpret_cast<const u32x4*>(kbase + int64_t(kb + rk) * kHeadDim + cch * 8)
                         : u32x4{0, 0, 0, 0};
-      const int rv = 4 * rq + j;
-      vreg[j] = rv < nk ? *reinterpret_cast<const u32x4*>(vbase + int64_t(kb + rv) * kHeadDim + cch * 8)
+      const int rv = 4 * vq + j;
+      vreg[j] = rv < nk ? *reinterpret_cast<const u32x4*>(vbase + int64_t(kb + rv) * kHeadDim + vd * 8)
                         : u32x4{0, 0, 0, 0};
     }
   };
   load_sub(k0);
 
-  for (int kb = k0; kb < k1; kb += kSub) {
-    const int nk = min(kSub, k1 - kb);
+  for (int kb = k0; kb < k1; kb += kSubB) {
+    const int nk = min(kSubB, k1 - kb);
     __syncthreads();
-    // stage K rows and V transposed (4 keys x 8 d per thread)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<u32x4*>(&Ks[(rq + 16 * j) * kKsStride + cch * 8]) = kreg[j];
+      *reinterpret_cast<u32x4*>(&Ks[(rq + 32 * j) * kKsStride + cch * 8]) = kreg[j];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int d = cch * 8 + e;
+      const int d = vd * 8 + e;
       const int hw = e >> 1;
       uint32_t x0, x1;
       if (e & 1) {
@@ -157,93 +183,124 @@ __global__ __launch_bounds__(256) void attn_prefix_bf16(
         x0 = (vreg[0][hw] & 0xFFFFu) | (vreg[1][hw] << 16);
         x1 = (vreg[2][hw] & 0xFFFFu) | (vreg[3][hw] << 16);
       }
-      *reinterpret_cast<u32x2*>(&Vt[d * kSub + ((rq ^ vt_swz(d)) * 4)]) = u32x2{x0, x1};
+      *reinterpret_cast<u32x2*>(&Vt[d * kVtStride + vq * 4]) = u32x2{x0, x1};
     }
     __syncthreads();
-    if (kb + kSub < k1) load_sub(kb + kSub);
+    if (kb + kSubB < k1) load_sub(kb + kSubB);
+    if (!active) continue;
+    const bool ragged = nk < kSubB;               // mask keys past the chunk end
 
-    // S^T = K Q^T for 4 tiles of 16 keys
-    floatx4 sacc[kSpw][4];
+#pragma unroll 1
+    for (int hh = 0; hh < kSubB / 64; ++hh) {
+      if (hh * 64 >= nk) break;
+      // S^T = K Q^T for 4 tiles of 16 keys; operands read a group of tiles
+      // at a time, ahead of their products
+      constexpr int TG = SPW == 1 ? 4 : 2;           // tiles per read group
+      constexpr int VG = SPW == 1 ? 8 : 4;           // V^T tiles per read group
+      floatx4 sacc[SPW][4];
 #pragma unroll
-    for (int s = 0; s < kSpw; ++s)
+      for (int s = 0; s < SPW; ++s)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) sacc[s][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < 4; ++t) sacc[s][t] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+      for (int t0 = 0; t0 < 4; t0 += TG) {
+        bf16x8 ka[TG][4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[(t * 16 + li) * kKsStride + ks * 32 + g * 8]);
+        for (int t = 0; t < TG; ++t)
 #pragma unroll
-        for (int s = 0; s < kSpw; ++s)
-          sacc[s][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[s][ks], sacc[s][t], 0, 0, 0);
+          for (int ks = 0; ks < 4; ++ks)
+            ka[t][ks] = *reinterpret_cast<const bf16x8*>(
+                &Ks[(hh * 64 + (t0 + t) * 16 + li) * kKsStride + ks * 32 + g * 8]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int t = 0; t < TG; ++t)
+#pragma unroll
+            for (int s = 0; s < SPW; ++s)
+              sacc[s][t0 + t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[t][ks], qb[s][ks], sacc[s][t0 + t], 0, 0, 0);
       }
-    }
-
-    // online softmax per query row (the lane's column)
-    bf16x8 pb[kSpw][2];
+      // V^T operands of this half, read while the softmax runs
+      bf16x8 va[VG][2];
+      auto read_v = [&](int dt0) {
 #pragma unroll
-    for (int s = 0; s < kSpw; ++s) {
-      float x[4][4];
-      float mloc = -INFINITY;
+        for (int i = 0; i < VG; ++i) {
+          const int row = (dt0 + i) * 16 + li;
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = t * 16 + 4 * g + i;
-          x[t][i] = key < nk ? sacc[s][t][i] * sl2 : -INFINITY;
-          mloc = fmaxf(mloc, x[t][i]);
+          for (int pp = 0; pp < 2; ++pp) {
+            const int qb32 = 2 * hh + pp;          // 32-key block in the sub-block
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(&Vt[row * kVtStride + 32 * qb32 + 4 * g]);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(&Vt[row * kVtStride + 32 * qb32 + 16 + 4 * g]);
+            va[i][pp] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+          }
         }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-      const float mnew = fmaxf(mrow[s], mloc);
-      const float alpha = fast_exp2(mrow[s] - mnew);
-      float psum = 0.f;
-      uint16_t ph[4][4];
+      };
+      read_v(0);
+      __builtin_amdgcn_sched_barrier(0);
+      // online softmax per query row (the lane's column), on raw scores:
+      // scale > 0, so max(scale s) = scale max(s) and p = 2^(s sl2 - m)
+      bf16x8 pb[SPW][2];
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int s = 0; s < SPW; ++s) {
+        float x[4][4];
+        float mraw = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pr = fast_exp2(x[t][i] - mnew);
-          psum += pr;
-          ph[t][i] = f32_to_bf16(pr);
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = hh * 64 + t * 16 + 4 * g + i;
+            x[t][i] = (!ragged || key < nk) ? sacc[s][t][i] : -INFINITY;
+            mraw = fmaxf(mraw, x[t][i]);
+          }
+        mraw = fmaxf(mraw, __shfl_xor(mraw, 16, 64));
+        mraw = fmaxf(mraw, __shfl_xor(mraw, 32, 64));
+        const float mnew = fmaxf(mrow[s], mraw * sl2);
+        const float alpha = fast_exp2(mrow[s] - mnew);
+        float psum = 0.f;
+        __bf16 ph[4][4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float pr = fast_exp2(__builtin_fmaf(x[t][i], sl2, -mnew));
+            psum += pr;
+            ph[t][i] = (__bf16)pr;
+          }
+        psum += __shfl_xor(psum, 16, 64);
+        psum += __shfl_xor(psum, 32, 64);
+        lrow[s] = lrow[s] * alpha + psum;
+        mrow[s] = mnew;
+        if (__any(alpha != 1.f)) {                 // no lane's maximum moved: nothing to rescale
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) acc[s][dt] *= alpha;
         }
-      psum += __shfl_xor(psum, 16, 64);
-      psum += __shfl_xor(psum, 32, 64);
-      lrow[s] = lrow[s] * alpha + psum;
-      mrow[s] = mnew;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) acc[s][dt] *= alpha;
-#pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        u32x4 u;
-        u[0] = uint32_t(ph[2 * pp][0]) | (uint32_t(ph[2 * pp][1]) << 16);
-        u[1] = uint32_t(ph[2 * pp][2]) | (uint32_t(ph[2 * pp][3]) << 16);
-        u[2] = uint32_t(ph[2 * pp + 1][0]) | (uint32_t(ph[2 * pp + 1][1]) << 16);
-        u[3] = uint32_t(ph[2 * pp + 1][2]) | (uint32_t(ph[2 * pp + 1][3]) << 16);
-        pb[s][pp] = __builtin_bit_cast(bf16x8, u);
+        for (int pp = 0; pp < 2; ++pp)
+          pb[s][pp] = bf16x8{ph[2 * pp][0], ph[2 * pp][1], ph[2 * pp][2], ph[2 * pp][3],
+                             ph[2 * pp + 1][0], ph[2 * pp + 1][1], ph[2 * pp + 1][2], ph[2 * pp + 1][3]};
       }
-    }
-
-    // O^T += V^T P^T
+      // O^T += V^T P^T over the two 32-key blocks of this half
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const int row = dt * 16 + li;
-      const int sw = vt_swz(row);
+      for (int dt0 = 0; dt0 < 8; dt0 += VG) {
+        if (dt0 > 0) {
+          read_v(dt0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(&Vt[row * kSub + (((8 * pp + g) ^ sw) * 4)]);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(&Vt[row * kSub + (((8 * pp + 4 + g) ^ sw) * 4)]);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+        for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-        for (int s = 0; s < kSpw; ++s)
-          acc[s][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[s][pp], acc[s][dt], 0, 0, 0);
+          for (int i = 0; i < VG; ++i)
+#pragma unroll
+            for (int s = 0; s < SPW; ++s)
+              acc[s][dt0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[i][pp], pb[s][pp], acc[s][dt0 + i], 0, 0, 0);
       }
     }
   }
 
+  if (!active) return;
 #pragma unroll
-  for (int s = 0; s < kSpw; ++s) {
-    const int r = rt * kRowsPerTile + (w * kSpw + s) * 16 + li;
+  for (int s = 0; s < SPW; ++s) {
+    const int r = row0 + s * 16 + li;
     if (r < R) {
       const int64_t unit = (int64_t(z) * chunks + c) * Rpad + r;
       float* po = part_o + unit * kHeadDim;
@@ -390,73 +447,156 @@ __global__ __launch_bounds__(256) void attn_prefix_f32(
 }
 
 // ---------------------------------------------------------------- combine
-// One wave per output row (b, n, h); lane l owns d = 2l, 2l+1.  Merges the
-// prefix chunk partials (chunks in order) and then the tree keys of n's
-// path (n, its parent, ..., the root), all with an online softmax.
+// 16 lanes per output row (b, n, h), 8 head-dimension values per lane.
+// Merges the prefix chunk partials (chunks in order) and then the tree keys
+// of n's path (n, its parent, ..., the root) with an online softmax.  All
+// loads of a batch are issued before any of them is used.
+__device__ __forceinline__ float row16_sum(float v) {
+  // quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+  return v;
+}
+
 template <bool BF16>
-__global__ __launch_bounds__(256) void attn_combine(
+__device__ __forceinline__ void load8(const void* base, int64_t elem, float* f) {
+  if (BF16) {
+    const u32x4 u = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + elem);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f[2 * j] = __uint_as_float(u[j] << 16);
+      f[2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u);
+    }
+  } else {
+    const floatx4 a = *reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(base) + elem);
+    const floatx4 c = *reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(base) + elem + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f[j] = a[j];
+      f[4 + j] = c[j];
+    }
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(128) void attn_combine(
     TreeDev tree, const void* __restrict__ q, const void* __restrict__ kt,
     const void* __restrict__ vt, const int32_t* __restrict__ prefix_len, int B, int Hq, int Hkv,
     int G, int chunks, int Rpad, float sl2, const float* __restrict__ part_o,
     const float2* __restrict__ part_ml, void* __restrict__ out, int64_t cap) {
+  constexpr int kBatch = 8;
   const int T = tree.T;
-  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (row >= int64_t(B) * T * Hq) return;
-  const int lane = threadIdx.x & 63;
+  const int64_t row = int64_t(blockIdx.x) * 8 + (threadIdx.x >> 4);
+  if (row >= int64_t(B) * T * Hq) return;          // whole 16-lane groups leave together
+  const int li = threadIdx.x & 15;                 // d = 8 li .. 8 li + 7
   const int h = int(row % Hq);
   const int n = int((row / Hq) % T);
   const int b = int(row / (int64_t(Hq) * T));
   const int kvh = h / G, gq = h - kvh * G;
   const int r = n * G + gq;
   const int z = b * Hkv + kvh;
-
-  auto ld2 = [&](const void* base, int64_t elem) -> float2 {
-    if (BF16) {
-      const uint32_t u = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(base) + elem);
-      return make_float2(bf16_to_f32(uint16_t(u & 0xFFFFu)), bf16_to_f32(uint16_t(u >> 16)));
-    } else {
-      return *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(base) + elem);
-    }
-  };
-
-  float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
   const int P = clamp_prefix(prefix_len[b], cap, nullptr, false);
   const int cs = chunk_len(P, chunks, kSub);
-  for (int c = 0; c < chunks; ++c) {
-    if (int64_t(c) * cs >= P) break;
-    const int64_t unit = (int64_t(z) * chunks + c) * Rpad + r;
-    const float2 ml = part_ml[unit];
-    const float2 ov = *reinterpret_cast<const float2*>(part_o + unit * kHeadDim + 2 * lane);
-    const float mn = fmaxf(m, ml.x);
-    const float a = fast_exp2(m - mn), e = fast_exp2(ml.x - mn);
-    l = l * a + ml.y * e;
-    o0 = o0 * a + ov.x * e;
-    o1 = o1 * a + ov.y * e;
+  const int nc = cs ? min(chunks, (P + cs - 1) / cs) : 0;
+
+  float m = -INFINITY, l = 0.f, o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = 0.f;
+  auto merge = [&](float ms, float ls, const float* os) {
+    const float mn = fmaxf(m, ms);
+    const float a = fast_exp2(m - mn), e = fast_exp2(ms - mn);
+    l = l * a + ls * e;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = o[j] * a + os[j] * e;
     m = mn;
+  };
+  float2 ml[kBatch];
+  float po[kBatch][8];
+  auto load_parts = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int c = max(0, min(c0 + i, nc - 1));
+      const int64_t unit = (int64_t(z) * chunks + c) * Rpad + r;
+      ml[i] = part_ml[unit];
+      const floatx4 a = *reinterpret_cast<const floatx4*>(part_o + unit * kHeadDim + 8 * li);
+      const floatx4 bq = *reinterpret_cast<const floatx4*>(part_o + unit * kHeadDim + 8 * li + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        po[i][j] = a[j];
+        po[i][4 + j] = bq[j];
+      }
+    }
+  };
+  int j = n;                                       // next path node to visit
+  bool more = true;
+  int idx[kBatch];
+  int cnt = 0;
+  float kx[kBatch][8], vx[kBatch][8];
+  auto load_tree = [&]() {
+    cnt = 0;
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      idx[i] = j;
+      if (more) {
+        ++cnt;
+        if (j == 0) more = false;
+        else j = tree.parent[j];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int64_t kv_elem = ((int64_t(b) * T + idx[i]) * Hkv + kvh) * kHeadDim + 8 * li;
+      load8<BF16>(kt, kv_elem, kx[i]);
+      load8<BF16>(vt, kv_elem, vx[i]);
+    }
+  };
+  auto merge_tree = [&](const float* qv) {
+    float sc[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d += qv[e] * kx[i][e];
+      sc[i] = row16_sum(d) * sl2;
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i)
+      if (i < cnt) merge(sc[i], 1.f, vx[i]);
+  };
+
+  // first batch of everything in flight at once
+  float qv[8];
+  load8<BF16>(q, ((int64_t(b) * T + n) * Hq + h) * kHeadDim + 8 * li, qv);
+  load_tree();
+  if (nc > 0) load_parts(0);
+  // prefix chunk partials, chunks in order
+  for (int c0 = 0; c0 < nc; c0 += kBatch) {
+    if (c0 > 0) load_parts(c0);
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i)
+      if (c0 + i < nc) merge(ml[i].x, ml[i].y, po[i]);
   }
-  const float2 qv = ld2(q, ((int64_t(b) * T + n) * Hq + h) * kHeadDim + 2 * lane);
-  int j = n;
-  while (true) {
-    const int64_t kv_elem = ((int64_t(b) * T + j) * Hkv + kvh) * kHeadDim + 2 * lane;
-    const float2 kx = ld2(kt, kv_elem);
-    const float s = wave_sum_f32(qv.x * kx.x + qv.y * kx.y) * sl2;
-    const float2 vx = ld2(vt, kv_elem);
-    const float mn = fmaxf(m, s);
-    const float a = fast_exp2(m - mn), e = fast_exp2(s - mn);
-    l = l * a + e;
-    o0 = o0 * a + e * vx.x;
-    o1 = o1 * a + e * vx.y;
-    m = mn;
-    if (j == 0) break;
-    j = tree.parent[j];
+  // tree keys on n's path: n, its parent, ..., the root
+  merge_tree(qv);
+  while (more) {
+    load_tree();
+    merge_tree(qv);
   }
+
   const float inv = 1.f / l;
-  const int64_t oe = ((int64_t(b) * T + n) * Hq + h) * kHeadDim + 2 * lane;
+  const int64_t oe = ((int64_t(b) * T + n) * Hq + h) * kHeadDim + 8 * li;
   if (BF16) {
-    const uint32_t u = uint32_t(f32_to_bf16(o0 * inv)) | (uint32_t(f32_to_bf16(o1 * inv)) << 16);
-    *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(out) + oe) = u;
+    u32x4 u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      u[e] = uint32_t(f32_to_bf16(o[2 * e] * inv)) | (uint32_t(f32_to_bf16(o[2 * e + 1] * inv)) << 16);
+    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + oe) = u;
   } else {
-    *reinterpret_cast<float2*>(reinterpret_cast<float*>(out) + oe) = make_float2(o0 * inv, o1 * inv);
+    float* op = reinterpret_cast<float*>(out) + oe;
+    *reinterpret_cast<floatx4*>(op) = floatx4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+    *reinterpret_cast<floatx4*>(op + 4) = floatx4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
   }
 }
 
@@ -468,26 +608,36 @@ hipError_t launch_attn(const TreeDev& tree, int32_t B, int32_t Hq, int32_t Hkv, 
   float2* part_ml = reinterpret_cast<float2*>(ws + plan.ml_off);
   const float sl2 = scale * kLog2e;
   dim3 grid(plan.chunks, plan.row_tiles, B * Hkv);
-  if (is_bf16)
-    hipLaunchKernelGGL(attn_prefix_bf16, grid, dim3(256), 0, s,
-                       reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(k_cache),
-                       reinterpret_cast<const uint16_t*>(v_cache), cap, prefix_len, tree.T, Hq, Hkv,
-                       plan.G, plan.R, plan.chunks, sl2, part_o, part_ml, ws);
-  else
+  const int64_t groups = int64_t(B) * Hkv * plan.chunks;
+  dim3 grid1(unsigned((groups + 7) / 8 * 8 * plan.row_tiles));
+  if (is_bf16) {
+    const auto* qq = reinterpret_cast<const uint16_t*>(q);
+    const auto* kk = reinterpret_cast<const uint16_t*>(k_cache);
+    const auto* vv = reinterpret_cast<const uint16_t*>(v_cache);
+    if (plan.spw == 2)
+      hipLaunchKernelGGL(attn_prefix_bf16<2>, grid1, dim3(64 * kWaves), 0, s, qq, kk, vv, cap,
+                         prefix_len, tree.T, Hq, Hkv, plan.G, plan.R, plan.chunks, sl2, part_o,
+                         part_ml, ws, B, plan.row_tiles);
+    else
+      hipLaunchKernelGGL(attn_prefix_bf16<1>, grid1, dim3(64 * kWaves), 0, s, qq, kk, vv, cap,
+                         prefix_len, tree.T, Hq, Hkv, plan.G, plan.R, plan.chunks, sl2, part_o,
+                         part_ml, ws, B, plan.row_tiles);
+  } else {
     hipLaunchKernelGGL(attn_prefix_f32, grid, dim3(256), 0, s, reinterpret_cast<const float*>(q),
                        reinterpret_cast<const float*>(k_cache), reinterpret_cast<const float*>(v_cache),
                        cap, prefix_len, tree.T, Hq, Hkv, plan.G, plan.R, plan.chunks, sl2, part_o,
                        part_ml, ws);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = int64_t(B) * tree.T * Hq;
-  dim3 cgrid(unsigned((rows + 3) / 4));
-  const int Rpad = plan.row_tiles * kRowsPerTile;
+  dim3 cgrid(unsigned((rows + 7) / 8));
+  const int Rpad = plan.row_tiles * plan.tile_rows;
   if (is_bf16)
-    hipLaunchKernelGGL(attn_combine<true>, cgrid, dim3(256), 0, s, tree, q, k_tree, v_tree,
+    hipLaunchKernelGGL(attn_combine<true>, cgrid, dim3(128), 0, s, tree, q, k_tree, v_tree,
                        prefix_len, B, Hq, Hkv, plan.G, plan.chunks, Rpad, sl2, part_o, part_ml, out, cap);
   else
-    hipLaunchKernelGGL(attn_combine<false>, cgrid, dim3(256), 0, s, tree, q, k_tree, v_tree,
+    hipLaunchKernelGGL(attn_combine<false>, cgrid, dim3(128), 0, s, tree, q, k_tree, v_tree,
                        prefix_len, B, Hq, Hkv, plan.G, plan.chunks, Rpad, sl2, part_o, part_ml, out, cap);
   return hipGetLastError();
 }

@@ -64,13 +64,15 @@ TopkPlan plan_topk(int64_t rows, int64_t V, int32_t k, int32_t esz);
 struct AttnPlan {
   int32_t G;          // query heads per key/value head
   int32_t R;          // query rows per (sequence, kv head) = T * G
-  int32_t row_tiles;  // ceil(R / 128)
+  int32_t spw;        // 16-row strips per wave
+  int32_t tile_rows;  // query rows per block
+  int32_t row_tiles;  // ceil(R / tile_rows)
   int32_t chunks;     // prefix chunks per (sequence, kv head)
-  size_t o_off;       // float [B*Hkv][chunks][row_tiles*128][128]
-  size_t ml_off;      // float2 [B*Hkv][chunks][row_tiles*128]
+  size_t o_off;       // float [B*Hkv][chunks][row_tiles*tile_rows][128]
+  size_t ml_off;      // float2 [B*Hkv][chunks][row_tiles*tile_rows]
   size_t end;
 };
-AttnPlan plan_attn(int32_t T, int32_t B, int32_t Hq, int32_t Hkv, int64_t cap);
+AttnPlan plan_attn(int32_t T, int32_t B, int32_t Hq, int32_t Hkv, int64_t cap, int is_bf16);
 
 // ---------------------------------------------------------------- launchers
 enum TailMode : int32_t { TAIL_NONE = 0, TAIL_UPDATE = 1, TAIL_STEP = 2 };

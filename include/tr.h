@@ -156,6 +156,7 @@ tr_status tr_retrieve(const tr_tree* t, int32_t B, const void* M, tr_dtype m_dty
  *   k_cache,
  *   v_cache   [B][Hkv][cap][d]   dt: positions >= prefix_len[b] unread
  *   prefix_len [B] int32 (device; 0 <= prefix_len <= cap)
+ *   scale     > 0 and finite (1/sqrt(d) in the usual reading)
  *   out       [B][T][Hq][d]      dt, written
  * Arithmetic: float32 accumulation; bf16 inputs use bf16 matrix cores for
  * both products.  The result does not depend on how the prefix is split. */
