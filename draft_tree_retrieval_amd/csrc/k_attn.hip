@@ -83,9 +83,13 @@ __device__ __forceinline__ int clamp_prefix(int P, int64_t cap, uint8_t* ws, boo
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------- bf16 prefix
-// 8 waves; SPW 16-row strips per wave; 128-key sub-blocks staged in LDS
-// while the next sub-block is already loading into registers (64 KB in
-// flight per block).
+// 8 waves; SPW 16-row strips per wave.  The kernel is bound by memory
+// latency, not arithmetic, so it keeps two or three 64-key sub-blocks
+// (32 KB each) of keys and values loading into a register ring while it
+// computes on another staged in LDS (two LDS buffers, one barrier per
+// sub-block).
+constexpr int kSB = 64;                   // keys per sub-block
+constexpr int kVtS = kSB + 4;             // bf16 per staged V^T row: 136 bytes
 template <int SPW>
 __global__ __launch_bounds__(512) void attn_prefix_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
@@ -108,13 +112,14 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
   const int k0 = c * cs;
   const int k1 = min(P, k0 + cs);
   if (k0 >= k1) return;
+  const int nsub = (k1 - k0 + kSB - 1) / kSB;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, g = lane >> 4;
   const int Rpad = row_tiles * kRows;
   const int row0 = rt * kRows + w * SPW * 16;      // first query row of this wave
   const bool active = row0 < R;                    // waves past the last row only load
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kSubB * kKsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[kHeadDim * kVtStride];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks2[2][kSB * kKsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt2[2][kHeadDim * kVtS];
 
   bf16x8 qb[SPW][4];
 #pragma unroll
@@ -145,155 +150,164 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
   const int64_t head_off = (int64_t(b) * Hkv + kvh) * cap * kHeadDim;
   const uint16_t* kbase = kc + head_off;
   const uint16_t* vbase = vc + head_off;
-  const int cch = tid & 15;     // K: 16-byte column chunk of a 256-byte row
-  const int rq = tid >> 4;      // K: rows rq + 32 j
-  const int vq = tid & 31;      // V: keys 4 vq .. 4 vq + 3
+  const int cch = tid & 15;     // K: 16-byte column chunk; rows (tid >> 4) + 32 j
+  const int rk0 = tid >> 4;
+  const int vq = tid & 31;      // V: keys 2 vq, 2 vq + 1
   const int vd = tid >> 5;      // V: d = 8 vd .. 8 vd + 7 (transposed when staged)
 
-  u32x4 kreg[4], vreg[4];
-  auto load_sub = [&](int kb) {
-    const int nk = min(kSubB, k1 - kb);
+  // one ring slot: 2 K units and 2 V units of 16 bytes per thread.  No
+  // branch guards a load, so the compiler can wait for just the slot being
+  // staged and keep the others in flight: rows past the chunk end reload the
+  // chunk's last row (finite data that the key mask gives probability 0) and
+  // sub-blocks past the end reload the last sub-block.
+  auto load = [&](u32x4 (&kr)[2], u32x4 (&vr)[2], int j) {
+    const int kb = k0 + min(j, nsub - 1) * kSB;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int rk = rq + 32 * j;
-      kreg[j] = rk < nk ? *reinterpret_cast<const u32x4*>(kbase + int64_t(kb + rk) * kHeadDim + cch * 8)
-                        : u32x4{0, 0, 0, 0};
-      const int rv = 4 * vq + j;
-      vreg[j] = rv < nk ? *reinterpret_cast<const u32x4*>(vbase + int64_t(kb + rv) * kHeadDim + vd * 8)
-                        : u32x4{0, 0, 0, 0};
+    for (int i = 0; i < 2; ++i) {
+      const int rk = min(kb + rk0 + 32 * i, k1 - 1);
+      kr[i] = *reinterpret_cast<const u32x4*>(kbase + int64_t(rk) * kHeadDim + cch * 8);
+      const int rv = min(kb + 2 * vq + i, k1 - 1);
+      vr[i] = *reinterpret_cast<const u32x4*>(vbase + int64_t(rv) * kHeadDim + vd * 8);
     }
   };
-  load_sub(k0);
-
-  for (int kb = k0; kb < k1; kb += kSubB) {
-    const int nk = min(kSubB, k1 - kb);
-    __syncthreads();
+  auto stage = [&](const u32x4 (&kr)[2], const u32x4 (&vr)[2], int buf) {
+    uint16_t* Ks = Ks2[buf];
+    uint16_t* Vt = Vt2[buf];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<u32x4*>(&Ks[(rq + 32 * j) * kKsStride + cch * 8]) = kreg[j];
+    for (int i = 0; i < 2; ++i)
+      *reinterpret_cast<u32x4*>(&Ks[(rk0 + 32 * i) * kKsStride + cch * 8]) = kr[i];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int d = vd * 8 + e;
-      const int hw = e >> 1;
-      uint32_t x0, x1;
-      if (e & 1) {
-        x0 = (vreg[0][hw] >> 16) | (vreg[1][hw] & 0xFFFF0000u);
-        x1 = (vreg[2][hw] >> 16) | (vreg[3][hw] & 0xFFFF0000u);
-      } else {
-        x0 = (vreg[0][hw] & 0xFFFFu) | (vreg[1][hw] << 16);
-        x1 = (vreg[2][hw] & 0xFFFFu) | (vreg[3][hw] << 16);
-      }
-      *reinterpret_cast<u32x2*>(&Vt[d * kVtStride + vq * 4]) = u32x2{x0, x1};
+      const uint32_t lo = (e & 1) ? (vr[0][e >> 1] >> 16) : (vr[0][e >> 1] & 0xFFFFu);
+      const uint32_t hi = (e & 1) ? (vr[1][e >> 1] >> 16) : (vr[1][e >> 1] & 0xFFFFu);
+      *reinterpret_cast<uint32_t*>(&Vt[(vd * 8 + e) * kVtS + 2 * vq]) = lo | (hi << 16);
     }
-    __syncthreads();
-    if (kb + kSubB < k1) load_sub(kb + kSubB);
-    if (!active) continue;
-    const bool ragged = nk < kSubB;               // mask keys past the chunk end
-
-#pragma unroll 1
-    for (int hh = 0; hh < kSubB / 64; ++hh) {
-      if (hh * 64 >= nk) break;
-      // S^T = K Q^T for 4 tiles of 16 keys; operands read a group of tiles
-      // at a time, ahead of their products
-      constexpr int TG = SPW == 1 ? 4 : 2;           // tiles per read group
-      constexpr int VG = SPW == 1 ? 8 : 4;           // V^T tiles per read group
-      floatx4 sacc[SPW][4];
+  };
+  auto compute = [&](int buf, int nk) {
+    const uint16_t* Ks = Ks2[buf];
+    const uint16_t* Vt = Vt2[buf];
+    const bool ragged = nk < kSB;                  // mask keys past the chunk end
+    // S^T = K Q^T for 4 tiles of 16 keys; operands read ahead of the products
+    constexpr int TG = SPW == 1 ? 4 : 2;           // tiles per read group
+    constexpr int VG = SPW == 1 ? 8 : 4;           // V^T tiles per read group
+    floatx4 sacc[SPW][4];
 #pragma unroll
-      for (int s = 0; s < SPW; ++s)
+    for (int s = 0; s < SPW; ++s)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) sacc[s][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < 4; ++t) sacc[s][t] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t0 = 0; t0 < 4; t0 += TG) {
-        bf16x8 ka[TG][4];
+    for (int t0 = 0; t0 < 4; t0 += TG) {
+      bf16x8 ka[TG][4];
+#pragma unroll
+      for (int t = 0; t < TG; ++t)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          ka[t][ks] = *reinterpret_cast<const bf16x8*>(&Ks[((t0 + t) * 16 + li) * kKsStride + ks * 32 + g * 8]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int t = 0; t < TG; ++t)
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks)
-            ka[t][ks] = *reinterpret_cast<const bf16x8*>(
-                &Ks[(hh * 64 + (t0 + t) * 16 + li) * kKsStride + ks * 32 + g * 8]);
+          for (int s = 0; s < SPW; ++s)
+            sacc[s][t0 + t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[t][ks], qb[s][ks], sacc[s][t0 + t], 0, 0, 0);
+    }
+    // V^T operands, read while the softmax runs
+    bf16x8 va[VG][2];
+    auto read_v = [&](int dt0) {
+#pragma unroll
+      for (int i = 0; i < VG; ++i) {
+        const int row = (dt0 + i) * 16 + li;
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(&Vt[row * kVtS + 32 * pp + 4 * g]);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(&Vt[row * kVtS + 32 * pp + 16 + 4 * g]);
+          va[i][pp] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+        }
+      }
+    };
+    read_v(0);
+    __builtin_amdgcn_sched_barrier(0);
+    // online softmax per query row (the lane's column), on raw scores:
+    // scale > 0, so max(scale s) = scale max(s) and p = 2^(s sl2 - m)
+    bf16x8 pb[SPW][2];
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
+      float x[4][4];
+      float mraw = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = t * 16 + 4 * g + i;
+          x[t][i] = (!ragged || key < nk) ? sacc[s][t][i] : -INFINITY;
+          mraw = fmaxf(mraw, x[t][i]);
+        }
+      mraw = fmaxf(mraw, __shfl_xor(mraw, 16, 64));
+      mraw = fmaxf(mraw, __shfl_xor(mraw, 32, 64));
+      const float mnew = fmaxf(mrow[s], mraw * sl2);
+      const float alpha = fast_exp2(mrow[s] - mnew);
+      float psum = 0.f;
+      __bf16 ph[4][4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pr = fast_exp2(__builtin_fmaf(x[t][i], sl2, -mnew));
+          psum += pr;
+          ph[t][i] = (__bf16)pr;
+        }
+      psum += __shfl_xor(psum, 16, 64);
+      psum += __shfl_xor(psum, 32, 64);
+      lrow[s] = lrow[s] * alpha + psum;
+      mrow[s] = mnew;
+      if (__any(alpha != 1.f)) {                   // no lane's maximum moved: nothing to rescale
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) acc[s][dt] *= alpha;
+      }
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp)
+        pb[s][pp] = bf16x8{ph[2 * pp][0], ph[2 * pp][1], ph[2 * pp][2], ph[2 * pp][3],
+                           ph[2 * pp + 1][0], ph[2 * pp + 1][1], ph[2 * pp + 1][2], ph[2 * pp + 1][3]};
+    }
+    // O^T += V^T P^T over the two 32-key blocks
+#pragma unroll
+    for (int dt0 = 0; dt0 < 8; dt0 += VG) {
+      if (dt0 > 0) {
+        read_v(dt0);
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-          for (int t = 0; t < TG; ++t)
-#pragma unroll
-            for (int s = 0; s < SPW; ++s)
-              sacc[s][t0 + t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[t][ks], qb[s][ks], sacc[s][t0 + t], 0, 0, 0);
       }
-      // V^T operands of this half, read while the softmax runs
-      bf16x8 va[VG][2];
-      auto read_v = [&](int dt0) {
 #pragma unroll
-        for (int i = 0; i < VG; ++i) {
-          const int row = (dt0 + i) * 16 + li;
+      for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-          for (int pp = 0; pp < 2; ++pp) {
-            const int qb32 = 2 * hh + pp;          // 32-key block in the sub-block
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(&Vt[row * kVtStride + 32 * qb32 + 4 * g]);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(&Vt[row * kVtStride + 32 * qb32 + 16 + 4 * g]);
-            va[i][pp] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-          }
-        }
-      };
-      read_v(0);
-      __builtin_amdgcn_sched_barrier(0);
-      // online softmax per query row (the lane's column), on raw scores:
-      // scale > 0, so max(scale s) = scale max(s) and p = 2^(s sl2 - m)
-      bf16x8 pb[SPW][2];
+        for (int i = 0; i < VG; ++i)
 #pragma unroll
-      for (int s = 0; s < SPW; ++s) {
-        float x[4][4];
-        float mraw = -INFINITY;
+          for (int s = 0; s < SPW; ++s)
+            acc[s][dt0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[i][pp], pb[s][pp], acc[s][dt0 + i], 0, 0, 0);
+    }
+  };
+
+  // Ring slot j % kRing holds sub-block j; sub-block j is computed from
+  // LDS buffer j & 1.  The loop runs in whole rounds of kRing sub-blocks with
+  // no branch around a load or a stage; only the compute of sub-blocks past
+  // the end is skipped.  Two 16-row strips per wave leave registers for two
+  // slots only.
+  constexpr int kRing = SPW == 1 ? 3 : 2;
+  u32x4 kr[kRing][2], vr[kRing][2];
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+  for (int j = 0; j < kRing; ++j) load(kr[j], vr[j], j);
+  stage(kr[0], vr[0], 0);
+  load(kr[0], vr[0], kRing);
+  __syncthreads();
+  for (int it = 0; it < nsub; it += kRing) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = hh * 64 + t * 16 + 4 * g + i;
-            x[t][i] = (!ragged || key < nk) ? sacc[s][t][i] : -INFINITY;
-            mraw = fmaxf(mraw, x[t][i]);
-          }
-        mraw = fmaxf(mraw, __shfl_xor(mraw, 16, 64));
-        mraw = fmaxf(mraw, __shfl_xor(mraw, 32, 64));
-        const float mnew = fmaxf(mrow[s], mraw * sl2);
-        const float alpha = fast_exp2(mrow[s] - mnew);
-        float psum = 0.f;
-        __bf16 ph[4][4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float pr = fast_exp2(__builtin_fmaf(x[t][i], sl2, -mnew));
-            psum += pr;
-            ph[t][i] = (__bf16)pr;
-          }
-        psum += __shfl_xor(psum, 16, 64);
-        psum += __shfl_xor(psum, 32, 64);
-        lrow[s] = lrow[s] * alpha + psum;
-        mrow[s] = mnew;
-        if (__any(alpha != 1.f)) {                 // no lane's maximum moved: nothing to rescale
-#pragma unroll
-          for (int dt = 0; dt < 8; ++dt) acc[s][dt] *= alpha;
-        }
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp)
-          pb[s][pp] = bf16x8{ph[2 * pp][0], ph[2 * pp][1], ph[2 * pp][2], ph[2 * pp][3],
-                             ph[2 * pp + 1][0], ph[2 * pp + 1][1], ph[2 * pp + 1][2], ph[2 * pp + 1][3]};
-      }
-      // O^T += V^T P^T over the two 32-key blocks of this half
-#pragma unroll
-      for (int dt0 = 0; dt0 < 8; dt0 += VG) {
-        if (dt0 > 0) {
-          read_v(dt0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp)
-#pragma unroll
-          for (int i = 0; i < VG; ++i)
-#pragma unroll
-            for (int s = 0; s < SPW; ++s)
-              acc[s][dt0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[i][pp], pb[s][pp], acc[s][dt0 + i], 0, 0, 0);
-      }
+    for (int r = 0; r < kRing; ++r) {
+      const int cur = it + r;
+      if (active && cur < nsub) compute(cur & 1, min(kSB, k1 - (k0 + cur * kSB)));
+      const int nxt = (r + 1) % kRing;             // slot of sub-block cur + 1
+      stage(kr[nxt], vr[nxt], (cur + 1) & 1);
+      load(kr[nxt], vr[nxt], cur + 1 + kRing);     // refill it with sub-block cur + 1 + kRing
+      __syncthreads();
     }
   }
 
@@ -488,6 +502,10 @@ __global__ __launch_bounds__(128) void attn_combine(
     const float2* __restrict__ part_ml, void* __restrict__ out, int64_t cap) {
   constexpr int kBatch = 8;
   const int T = tree.T;
+  // parents in LDS: indexed reads of the kernel argument are memory round trips
+  __shared__ uint8_t s_par[kMaxNodes];
+  if (int(threadIdx.x) < T) s_par[threadIdx.x] = tree.parent[threadIdx.x];
+  __syncthreads();
   const int64_t row = int64_t(blockIdx.x) * 8 + (threadIdx.x >> 4);
   if (row >= int64_t(B) * T * Hq) return;          // whole 16-lane groups leave together
   const int li = threadIdx.x & 15;                 // d = 8 li .. 8 li + 7
@@ -542,7 +560,7 @@ __global__ __launch_bounds__(128) void attn_combine(
       if (more) {
         ++cnt;
         if (j == 0) more = false;
-        else j = tree.parent[j];
+        else j = s_par[j];
       }
     }
 #pragma unroll

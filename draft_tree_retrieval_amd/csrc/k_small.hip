@@ -14,19 +14,26 @@ __global__ __launch_bounds__(128) void retrieve_kernel(TreeDev tree, const void*
                                                        int32_t* __restrict__ tree_tok, uint8_t* ws) {
   __shared__ TailShared S;
   const int b = blockIdx.x;
-  const size_t msz = m_is64 ? 8 : 4;
-  const void* M_b = reinterpret_cast<const uint8_t*>(M) + size_t(b) * size_t(V) * size_t(k) * msz;
-  tail_retrieve(S, tree, root_tok[b], M_b, m_is64, V, k, tree_tok + int64_t(b) * tree.T, ws);
+  tail_tree(S, tree);
+  __syncthreads();
+  if (threadIdx.x >= 64) return;      // one wave walks the tree
+  int32_t* out_b = tree_tok + int64_t(b) * tree.T;
+  if (m_is64)
+    tail_retrieve<int64_t>(S, tree, root_tok[b], reinterpret_cast<const int64_t*>(M) + int64_t(b) * V * k,
+                           V, k, out_b, ws, false);
+  else
+    tail_retrieve<int32_t>(S, tree, root_tok[b], reinterpret_cast<const int32_t*>(M) + int64_t(b) * V * k,
+                           V, k, out_b, ws, false);
 }
 
-__global__ __launch_bounds__(128) void verify_kernel(TreeDev tree, const int32_t* __restrict__ topk,
+__global__ __launch_bounds__(256) void verify_kernel(TreeDev tree, const int32_t* __restrict__ topk,
                                                      int32_t k, const int32_t* __restrict__ tree_tok,
                                                      int32_t* accept_len, int32_t* accept_path,
                                                      int32_t* bonus, int32_t* emitted) {
   __shared__ TailShared S;
   const int b = blockIdx.x;
   tail_load(S, tree, tree_tok + int64_t(b) * tree.T, topk + int64_t(b) * tree.T * k, k);
-  tail_verify(S, tree);
+  tail_verify(S, tree, k);
   tail_write_verdict(S, tree, b, accept_len, accept_path, bonus, emitted);
 }
 
@@ -46,7 +53,7 @@ hipError_t launch_retrieve(const TreeDev& tree, int32_t B, const void* M, int m_
 hipError_t launch_verify(const TreeDev& tree, int32_t B, const int32_t* topk, int32_t k,
                          const int32_t* tree_tok, int32_t* accept_len, int32_t* accept_path,
                          int32_t* bonus, int32_t* emitted, hipStream_t s) {
-  hipLaunchKernelGGL(verify_kernel, dim3(B), dim3(128), 0, s, tree, topk, k, tree_tok, accept_len,
+  hipLaunchKernelGGL(verify_kernel, dim3(B), dim3(256), 0, s, tree, topk, k, tree_tok, accept_len,
                      accept_path, bonus, emitted);
   return hipGetLastError();
 }

@@ -11,38 +11,44 @@
 // per lane) and selects in three steps:
 //   1. every lane turns its values into order codes in place and takes
 //      their maximum;
-//   2. the lanes of a wave form KM groups; each group's maximum is reached
-//      by one of its elements, so the smallest of the KM group maxima is
-//      reached by KM distinct elements and nothing below it can be among
-//      the KM best.  The block threshold is the largest of the four waves'
-//      values;
-//   3. only elements at or above the threshold -- usually a few dozen --
-//      go to a candidate list in LDS, where each is ranked against the
-//      others.
-// Rows full of ties can overflow the candidate list; the block then falls
+//   2. every wave finds, by bisection on the code bits with ballot counts
+//      over all the block's lane maxima (shared through LDS), the largest
+//      code t that at least k lane maxima reach: k distinct elements are
+//      >= t, so nothing below t is among the k best;
+//   3. only elements at or above t -- usually k or a few more -- are
+//      written, by ballot, to per-wave candidate lists in LDS; one wave
+//      ranks them in registers (all threads rank them when there are many).
+// Rows full of ties can overflow a candidate list; the block then falls
 // back to exact per-lane insertion of every element above the threshold.
 //
-// Launch: grid (segments, rows), 256 threads.  Segments spread short
-// vocabularies over the CUs; the last segment block of a row merges the
+// Launch: grid (segments, rows).  Many rows: 256 threads holding 16
+// vectors per lane, segments spreading short vocabularies over the CUs.
+// Few rows (latency-bound): 512 threads holding 8 vectors per lane, so two
+// waves per SIMD share the selection work.  The last segment block of
+// a row merges the
 // segment lists, and the last row block of a sequence runs that sequence's
 // tail (hand-over through device-scope atomics, see dev_common.h).
 #include "tail.h"
 
 namespace tr {
 
-constexpr int kNV = 16;       // 16-byte vectors per lane per segment
-constexpr int kCand = 512;    // candidate slots per block
+constexpr int kCandW = 64;   // candidate slots per wave
 
 TopkPlan plan_topk(int64_t rows, int64_t V, int32_t k, int32_t esz) {
   TopkPlan p{};
   p.rows = rows;
   p.kmax = k <= 8 ? 8 : 16;
-  const int64_t cap = int64_t(256) * kNV * (16 / esz);   // largest segment a block holds
+  p.threads = rows < 256 ? 512 : 256;
+  const int64_t nv = p.threads == 512 ? 8 : 16;           // vectors per lane
+  const int64_t cap = int64_t(p.threads) * nv * (16 / esz);  // largest segment a block holds
   const int64_t max_segs = 256 / p.kmax;                 // the final merge ranks <= 256 keys
   int64_t need = (V + cap - 1) / cap;
-  int64_t want = (256 + rows - 1) / rows;         // about one block per CU
-  int64_t by_len = V / 4096;                      // but segments of >= 4096 logits
-  int64_t segs = want < by_len ? want : by_len;
+  // Few rows: one block per row when a row fits, so no segment hand-over
+  // (a round trip through device memory) stands between the scan and the
+  // step's tail.  Many rows: about one block per CU, segments of >= 4096.
+  int64_t want = (256 + rows - 1) / rows;
+  int64_t by_len = V / 4096;
+  int64_t segs = rows < 256 ? 1 : (want < by_len ? want : by_len);
   if (segs < need) segs = need;
   if (segs < 1) segs = 1;
   if (segs > max_segs) segs = max_segs;
@@ -60,8 +66,9 @@ TopkPlan plan_topk(int64_t rows, int64_t V, int32_t k, int32_t esz) {
   return p;
 }
 
-// The KM largest of n <= blockDim.x distinct keys held in LDS, best first,
-// into out[KM] (LDS; zero where n < KM): key t is ranked by thread t.
+// The KM largest of n <= blockDim.x distinct keys held contiguously in LDS,
+// best first, into out[KM] (LDS; zero where n < KM): key t is ranked by
+// thread t.
 template <int KM>
 __device__ __forceinline__ void rank_select(const uint64_t* keys, int n, uint64_t* out) {
   const int tid = threadIdx.x;
@@ -76,9 +83,32 @@ __device__ __forceinline__ void rank_select(const uint64_t* keys, int n, uint64_
   __syncthreads();
 }
 
+// The same over NW per-wave lists: list w holds cnt[w] keys from
+// keys + w * kCandW; n = cnt[0] + ... + cnt[NW-1] <= blockDim.x.
+template <int KM, int NW>
+__device__ __forceinline__ void rank_select_lists(const uint64_t* keys, const uint32_t* cnt, int n,
+                                                  uint64_t* out) {
+  const int tid = threadIdx.x;
+  if (tid < KM) out[tid] = 0;
+  __syncthreads();
+  if (tid < n) {
+    int w = 0, idx = tid;
+    while (idx >= int(cnt[w])) { idx -= int(cnt[w]); ++w; }
+    const uint64_t mine = keys[w * kCandW + idx];
+    int rank = 0;
+    for (int v = 0; v < NW; ++v) {
+      const uint64_t* kv = keys + v * kCandW;
+      const int c = int(cnt[v]);
+      for (int j = 0; j < c; ++j) rank += kv[j] > mine ? 1 : 0;
+    }
+    if (rank < KM) out[rank] = mine;
+  }
+  __syncthreads();
+}
+
 // Block merge of per-lane lists: each wave's KM best, then the block's,
 // into out[KM] (LDS).
-template <int KM>
+template <int KM, int NW>
 __device__ __forceinline__ void block_merge(TopList<KM>& L, uint64_t (*s_keys)[KM], uint64_t* out) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint64_t best[KM];
@@ -90,7 +120,7 @@ __device__ __forceinline__ void block_merge(TopList<KM>& L, uint64_t (*s_keys)[K
   __syncthreads();
   if (wave == 0) {
     L.clear();
-    if (lane < 4) {
+    if (lane < NW) {
 #pragma unroll
       for (int r = 0; r < KM; ++r) L.v[r] = s_keys[lane][r];
     }
@@ -103,15 +133,54 @@ __device__ __forceinline__ void block_merge(TopList<KM>& L, uint64_t (*s_keys)[K
   __syncthreads();
 }
 
-template <bool BF16, int KM>
-__global__ __launch_bounds__(256) void topk_kernel(const void* __restrict__ logits, int64_t V,
+// The per-sequence tail: update only (TAIL_UPDATE) or the whole step
+// (TAIL_STEP: verification, update, commit, next retrieval).  Needs at
+// least 256 threads.  After verification, wave 0 retrieves the next tree
+// while wave 1 writes the updated rows of M and waves 1.. copy the accepted
+// key/value rows, so retrieval's loads never wait behind their stores.
+template <typename MT>
+__device__ __forceinline__ void seq_tail(TailShared& S, const TreeDev& tree, int b, int32_t k,
+                                         int64_t V, const int32_t* topk_b, int32_t* tok_b,
+                                         const TailArgs& tail, uint8_t* ws) {
+  void* M_b = reinterpret_cast<MT*>(tail.M) + int64_t(b) * V * k;
+  const int wave = threadIdx.x >> 6;
+  if (tail.mode != TAIL_STEP) {
+    tail_load(S, tree, tok_b, topk_b, k);
+    if (wave == 0) {
+      tail_update_claim(S, tree, V, ws);
+      wave_lds_sync();
+      tail_update_store<MT>(S, tree, k, M_b, V);
+    }
+    return;
+  }
+  tail_load(S, tree, tok_b, topk_b, k, tail.k_cache ? tail.prefix_len + b : nullptr);
+  PreRows<MT> pre;
+  if (wave == 0) tail_prefetch<MT>(S, tree, k, M_b, V, pre);   // in flight during verification
+  tail_verify(S, tree, k);
+  tail_write_verdict(S, tree, b, tail.accept_len, tail.accept_path, nullptr, tail.emitted);
+  if (wave == 0) tail_update_claim(S, tree, V, ws);
+  __syncthreads();                                   // the LDS map is complete
+  const bool fits = tail_commit(S, tree, b, tail, ws, wave == 0 ? 1 << 30 : 64);
+  if (wave == 1) tail_update_store<MT>(S, tree, k, M_b, V);
+  if (wave != 0) return;
+  tail_prefetch_store(S, tree, k, V, pre);
+  wave_lds_sync();
+  tail_retrieve<MT>(S, tree, S.bonus, M_b, V, k, tok_b, ws, true, true);
+  if (threadIdx.x == 0) {
+    tail.root_tok[b] = S.bonus;
+    if (fits) tail.prefix_len[b] = int32_t(S.P + S.L + 1);
+  }
+}
+
+template <bool BF16, int KM, int NT, int NV>
+__global__ __launch_bounds__(NT) void topk_kernel(const void* __restrict__ logits, int64_t V,
                                                    int32_t k, int32_t segs, int64_t seg_len,
                                                    int32_t* __restrict__ ids_out,
                                                    uint64_t* __restrict__ part, uint8_t* ws,
                                                    TreeDev tree, TailArgs tail) {
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int VE = 16 / ESZ;             // elements per 16-byte vector
-  constexpr int GL = 64 / KM;              // lanes per threshold group
+  constexpr int NW = NT / 64;              // waves
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t row = blockIdx.y;
   const int seg = blockIdx.x;
@@ -119,12 +188,12 @@ __global__ __launch_bounds__(256) void topk_kernel(const void* __restrict__ logi
   const int64_t s1 = min(V, s0 + seg_len);
   const uint8_t* rowp = reinterpret_cast<const uint8_t*>(logits) + row * V * ESZ;
 
+  constexpr int kCand = NW * kCandW;
   __shared__ uint64_t s_cand[kCand];
-  __shared__ uint64_t s_keys[4][KM];
+  __shared__ uint64_t s_keys[NW][KM];
   __shared__ uint64_t s_best[KM];
-  __shared__ uint32_t s_cnt;
-  __shared__ uint32_t s_lo[4];
-  if (tid == 0) s_cnt = 0;
+  __shared__ uint32_t s_wcnt[NW];
+  __shared__ uint32_t s_lm[NT];
 
   // aligned vector range [a0, a1) inside [s0, s1); at most VE-1 loose
   // elements on each side
@@ -140,10 +209,10 @@ __global__ __launch_bounds__(256) void topk_kernel(const void* __restrict__ logi
 
   // ---- 1. load, order codes in place (0 marks "no element"), lane maximum
   const u32x4* vp = reinterpret_cast<const u32x4*>(rowp + a0 * ESZ);
-  u32x4 x[kNV];
+  u32x4 x[NV];
 #pragma unroll
-  for (int i = 0; i < kNV; ++i) {
-    const int idx = i * 256 + tid;
+  for (int i = 0; i < NV; ++i) {
+    const int idx = i * NT + tid;
     x[i] = idx < nv ? __builtin_nontemporal_load(vp + idx) : u32x4{0, 0, 0, 0};
   }
   uint32_t loose_code[2] = {0, 0};       // head and tail elements
@@ -153,8 +222,8 @@ __global__ __launch_bounds__(256) void topk_kernel(const void* __restrict__ logi
   uint32_t mt = max(loose_code[0], loose_code[1]);
   uint32_t m2 = 0;
 #pragma unroll
-  for (int i = 0; i < kNV; ++i) {
-    const uint32_t keep = (i * 256 + tid < nv) ? ~0u : 0u;
+  for (int i = 0; i < NV; ++i) {
+    const uint32_t keep = (i * NT + tid < nv) ? ~0u : 0u;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (BF16) {
@@ -168,103 +237,141 @@ __global__ __launch_bounds__(256) void topk_kernel(const void* __restrict__ logi
   }
   if (BF16) mt = max(mt, max(m2 & 0xFFFFu, m2 >> 16) << 16);
 
-  // ---- 2. threshold
-  uint32_t gm = mt;
-#pragma unroll
-  for (int sh = 1; sh < GL; sh <<= 1) gm = max(gm, (uint32_t)__shfl_xor(gm, sh, 64));
-#pragma unroll
-  for (int sh = GL; sh < 64; sh <<= 1) gm = min(gm, (uint32_t)__shfl_xor(gm, sh, 64));
-  if (lane == 0) s_lo[wave] = gm;
+  // ---- 2. threshold: the largest code reached by at least k lane maxima
+  // of the block (every wave computes the same value)
+  s_lm[tid] = mt;
   __syncthreads();
-  const uint32_t lo = max(max(s_lo[0], s_lo[1]), max(s_lo[2], s_lo[3]));
+  uint32_t lm[NW];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) lm[w] = s_lm[w * 64 + lane];
+  uint32_t lo = 0;
+#pragma unroll
+  for (int bit = 31; bit >= (BF16 ? 16 : 0); --bit) {
+    const uint32_t c = lo | (1u << bit);
+    int reach = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) reach += __popcll(__ballot(lm[w] >= c));
+    if (reach >= k) lo = c;
+  }
 
-  // ---- 3. candidates
-  auto push = [&](uint32_t code, int64_t id) {
-    const uint32_t slot = atomicAdd(&s_cnt, 1u);
-    if (slot < uint32_t(kCand)) s_cand[slot] = key_of(code, uint32_t(id));
-  };
-  if (BF16) {
-    const uint32_t lo16 = lo >> 16;
-    const uint32_t below2 = lo16 ? (lo16 - 1) * 0x10001u : 0u;   // lo16-1 in both halves
-#pragma unroll
-    for (int i = 0; i < kNV; ++i) {
-      const uint32_t vmx = max16x2(max16x2(x[i][0], x[i][1]), max16x2(x[i][2], x[i][3]));
-      const bool hit = lo16 ? max16x2(vmx, below2) != below2 : vmx != 0u;
-      if (hit) {
-        const int64_t id = a0 + int64_t(i * 256 + tid) * VE;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t c0 = x[i][j] & 0xFFFFu, c1 = x[i][j] >> 16;
-          if (c0 && c0 >= lo16) push(c0 << 16, id + 2 * j);
-          if (c1 && c1 >= lo16) push(c1 << 16, id + 2 * j + 1);
-        }
-      }
+  // ---- 3. candidates: each element at or above lo gets the next slot of
+  // its wave's list, in lane order (ballot + lane-masked bit count)
+  uint64_t* wc = s_cand + wave * kCandW;
+  uint32_t wpos = 0;                        // wave-uniform
+  auto put = [&](bool pred, uint32_t code, int64_t id) {
+    const uint64_t m = __ballot(pred);
+    if (m) {
+      const uint32_t off =
+          wpos + __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
+      if (pred && off < uint32_t(kCandW)) wc[off] = key_of(code, uint32_t(id));
+      wpos += uint32_t(__popcll(m));
     }
-  } else {
+  };
+  const uint32_t lo16 = lo >> 16;
+  const uint32_t below2 = lo16 ? (lo16 - 1) * 0x10001u : 0u;     // bf16: lo16-1 in both halves
 #pragma unroll
-    for (int i = 0; i < kNV; ++i) {
-      const uint32_t vmx = max(max(x[i][0], x[i][1]), max(x[i][2], x[i][3]));
-      if (vmx && vmx >= lo) {
-        const int64_t id = a0 + int64_t(i * 256 + tid) * VE;
+  for (int i = 0; i < NV; ++i) {
+    uint32_t hv[4];                          // nonzero where an element reaches lo
+    bool hit = false;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (x[i][j] && x[i][j] >= lo) push(x[i][j], id + j);
+    for (int j = 0; j < 4; ++j) {
+      hv[j] = BF16 ? (max16x2(x[i][j], below2) ^ below2) : ((x[i][j] && x[i][j] >= lo) ? 1u : 0u);
+      hit = hit || hv[j] != 0u;
+    }
+    if (__ballot(hit) == 0) continue;
+    const int64_t id = a0 + int64_t(i * NT + tid) * VE;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (BF16) {
+        put((hv[j] & 0xFFFFu) != 0u, (x[i][j] & 0xFFFFu) << 16, id + 2 * j);
+        put(hv[j] > 0xFFFFu, x[i][j] & 0xFFFF0000u, id + 2 * j + 1);
+      } else {
+        put(hv[j] != 0u, x[i][j], id + j);
       }
     }
   }
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
-    if (loose_code[h] && loose_code[h] >= lo) push(loose_code[h], loose_id[h]);
+  for (int h = 0; h < 2; ++h) put(loose_code[h] && loose_code[h] >= lo, loose_code[h], loose_id[h]);
+  if (lane == 0) s_wcnt[wave] = wpos;
   __syncthreads();
-  const uint32_t n = s_cnt;
+  uint32_t n = 0, most = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    n += s_wcnt[w];
+    most = max(most, s_wcnt[w]);
+  }
+  const bool overflow = most > uint32_t(kCandW);
 
-  // ---- the block's KM best into s_best
-  if (n <= 256u) {
-    rank_select<KM>(s_cand, int(n), s_best);
-  } else {
-    TopList<KM> L;
-    L.clear();
-    if (n <= uint32_t(kCand)) {
-      for (uint32_t c = tid; c < n; c += 256) L.insert(s_cand[c]);
-    } else {
-      // too many ties at the threshold: exact insertion from the registers
-#pragma unroll
-      for (int i = 0; i < kNV; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t id = a0 + int64_t(i * 256 + tid) * VE + (BF16 ? 2 * j : j);
-          if (BF16) {
-            const uint32_t c0 = (x[i][j] & 0xFFFFu) << 16, c1 = x[i][j] & 0xFFFF0000u;
-            if (c0 && c0 >= lo) L.insert(key_of(c0, uint32_t(id)));
-            if (c1 && c1 >= lo) L.insert(key_of(c1, uint32_t(id + 1)));
-          } else if (x[i][j] && x[i][j] >= lo) {
-            L.insert(key_of(x[i][j], uint32_t(id)));
-          }
-        }
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        if (loose_code[h] && loose_code[h] >= lo) L.insert(key_of(loose_code[h], uint32_t(loose_id[h])));
+  // ---- the block's KM best
+  if (!overflow && n <= 64u) {
+    // one wave: lane i ranks candidate i against the others in registers
+    if (wave == 0) {
+      uint64_t key = 0;
+      if (lane < int(n)) {
+        int w = 0, idx = lane;
+        while (idx >= int(s_wcnt[w])) { idx -= int(s_wcnt[w]); ++w; }
+        key = s_cand[w * kCandW + idx];
+      }
+      int rank = 0;
+      for (int j = 0; j < int(n); ++j) rank += readlane_u64(key, j) > key ? 1 : 0;
+      if (lane >= int(n)) rank = lane;           // empty places n.. hold key 0
+      if (rank < KM) {
+        if (segs > 1) put_dev(&part[(row * segs + seg) * KM + rank], key);
+        else if (rank < k) put_dev(&ids_out[row * k + rank], int32_t(key_id(key)));
+      }
     }
-    block_merge<KM>(L, s_keys, s_best);
+  } else {
+    if (!overflow && n <= uint32_t(NT)) {
+      rank_select_lists<KM, NW>(s_cand, s_wcnt, int(n), s_best);
+    } else {
+      TopList<KM> L;
+      L.clear();
+      if (!overflow) {
+        for (int c = tid; c < kCand; c += NT)
+          if (uint32_t(c % kCandW) < s_wcnt[c / kCandW]) L.insert(s_cand[c]);
+      } else {
+        // too many ties at the threshold: exact insertion from the registers
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int64_t id = a0 + int64_t(i * NT + tid) * VE + (BF16 ? 2 * j : j);
+            if (BF16) {
+              const uint32_t c0 = (x[i][j] & 0xFFFFu) << 16, c1 = x[i][j] & 0xFFFF0000u;
+              if (c0 && c0 >= lo) L.insert(key_of(c0, uint32_t(id)));
+              if (c1 && c1 >= lo) L.insert(key_of(c1, uint32_t(id + 1)));
+            } else if (x[i][j] && x[i][j] >= lo) {
+              L.insert(key_of(x[i][j], uint32_t(id)));
+            }
+          }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          if (loose_code[h] && loose_code[h] >= lo) L.insert(key_of(loose_code[h], uint32_t(loose_id[h])));
+      }
+      block_merge<KM, NW>(L, s_keys, s_best);
+    }
+    if (tid == 0) {
+#pragma unroll
+      for (int r = 0; r < KM; ++r) {
+        if (segs > 1) put_dev(&part[(row * segs + seg) * KM + r], s_best[r]);
+        else if (r < k) put_dev(&ids_out[row * k + r], int32_t(key_id(s_best[r])));
+      }
+    }
   }
 
   // ---- segments of a row meet in the last one
   if (segs > 1) {
-    if (tid == 0) {
-#pragma unroll
-      for (int r = 0; r < KM; ++r) put_dev(&part[(row * segs + seg) * KM + r], s_best[r]);
-    }
     uint32_t* row_cnt = reinterpret_cast<uint32_t*>(ws + kRowCntOff);
     if (!last_block_arrives(row_cnt + row, uint32_t(segs))) return;
     const int nk = segs * KM;                   // <= 256 by the plan
-    for (int c = tid; c < nk; c += 256) s_cand[c] = get_dev(&part[row * segs * KM + c]);
+    for (int c = tid; c < nk; c += NT) s_cand[c] = get_dev(&part[row * segs * KM + c]);
     __syncthreads();
     rank_select<KM>(s_cand, nk, s_best);
-  }
-  if (tid == 0) {
+    if (tid == 0) {
 #pragma unroll
-    for (int r = 0; r < KM; ++r)
-      if (r < k) put_dev(&ids_out[row * k + r], int32_t(key_id(s_best[r])));
+      for (int r = 0; r < KM; ++r)
+        if (r < k) put_dev(&ids_out[row * k + r], int32_t(key_id(s_best[r])));
+    }
   }
   if (tail.mode == TAIL_NONE) return;
 
@@ -276,19 +383,8 @@ __global__ __launch_bounds__(256) void topk_kernel(const void* __restrict__ logi
   __shared__ TailShared S;
   const int32_t* topk_b = ids_out + int64_t(b) * tree.T * k;
   int32_t* tok_b = tail.tree_tok + int64_t(b) * tree.T;
-  const size_t msz = tail.m_is64 ? 8 : 4;
-  void* M_b = reinterpret_cast<uint8_t*>(tail.M) + size_t(b) * size_t(V) * size_t(k) * msz;
-  tail_load(S, tree, tok_b, topk_b, k);
-  if (tail.mode == TAIL_STEP) {
-    tail_verify(S, tree);
-    tail_write_verdict(S, tree, b, tail.accept_len, tail.accept_path, nullptr, tail.emitted);
-  }
-  tail_update(S, tree, topk_b, k, M_b, tail.m_is64, V, ws);
-  if (tail.mode != TAIL_STEP) return;
-  tail_commit(S, tree, b, tail, ws);
-  __syncthreads();          // the M rows written above are read below by this block
-  tail_retrieve(S, tree, S.bonus, M_b, tail.m_is64, V, k, tok_b, ws);
-  if (threadIdx.x == 0) tail.root_tok[b] = S.bonus;
+  if (tail.m_is64) seq_tail<int64_t>(S, tree, b, k, V, topk_b, tok_b, tail, ws);
+  else seq_tail<int32_t>(S, tree, b, k, V, topk_b, tok_b, tail, ws);
 }
 
 hipError_t launch_topk(const TreeDev& tree, int32_t B, const void* logits, int l_is_bf16, int64_t V,
@@ -296,14 +392,20 @@ hipError_t launch_topk(const TreeDev& tree, int32_t B, const void* logits, int l
                        const TopkPlan& plan, hipStream_t s) {
   dim3 grid(plan.segs, unsigned(plan.rows));
   uint64_t* part = reinterpret_cast<uint64_t*>(ws + plan.part_off);
-#define TR_TOPK(BF, KMV)                                                                       \
-  hipLaunchKernelGGL((topk_kernel<BF, KMV>), grid, dim3(256), 0, s, logits, V, k, plan.segs, \
-                     plan.seg_len, topk_ids, part, ws, tree, tail)
+#define TR_TOPK(BF, KMV, NTV, NVV)                                                             \
+  hipLaunchKernelGGL((topk_kernel<BF, KMV, NTV, NVV>), grid, dim3(NTV), 0, s, logits, V, k,     \
+                     plan.segs, plan.seg_len, topk_ids, part, ws, tree, tail)
+#define TR_TOPK_NT(BF, KMV)                                 \
+  do {                                                      \
+    if (plan.threads == 512) TR_TOPK(BF, KMV, 512, 8);      \
+    else TR_TOPK(BF, KMV, 256, 16);                         \
+  } while (0)
   if (l_is_bf16) {
-    if (plan.kmax == 8) TR_TOPK(true, 8); else TR_TOPK(true, 16);
+    if (plan.kmax == 8) TR_TOPK_NT(true, 8); else TR_TOPK_NT(true, 16);
   } else {
-    if (plan.kmax == 8) TR_TOPK(false, 8); else TR_TOPK(false, 16);
+    if (plan.kmax == 8) TR_TOPK_NT(false, 8); else TR_TOPK_NT(false, 16);
   }
+#undef TR_TOPK_NT
 #undef TR_TOPK
   return hipGetLastError();
 }

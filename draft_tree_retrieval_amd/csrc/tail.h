@@ -1,61 +1,180 @@
-// Per-sequence integer work of a TR step, run by one workgroup
-// (blockDim.x >= number of tree nodes): verification, the recycling update
-// of M, the commit of the accepted path's key/value rows and the retrieval
-// of the next draft tree.
+// Per-sequence integer work of a TR step, run by one workgroup of at least
+// 256 threads: verification, the recycling update of M, the commit of the
+// accepted path's key/value rows and the retrieval of the next draft tree.
+//
+// The work is a chain of dependent steps, each waiting on memory, so the
+// code keeps independent memory traffic off that chain: the M rows the next
+// tree's first layer may need are fetched while verification runs, and
+// after verification wave 0 alone does the tree work (update, retrieval;
+// two nodes per lane, at most 128 nodes, synchronised through LDS inside
+// the wave) while the other waves copy the accepted rows into the cache.
+// A wave's memory counter covers its stores as well as its loads, so the
+// copy on other waves never delays retrieval's waits.
 #pragma once
 
 #include "dev_common.h"
 
 namespace tr {
 
+// LDS writes of a wave are visible to its later LDS reads (the LDS unit
+// runs one wave's operations in order); this keeps the compiler from moving
+// LDS accesses across the point.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 struct TailShared {
-  int32_t tok[kMaxNodes];    // this step's tree tokens
-  int32_t g[kMaxNodes];      // target's top-1 after each node
-  int32_t acc[kMaxNodes];    // accepted?
-  int32_t nxt[kMaxNodes];    // next tree tokens
-  int32_t path[kMaxNodes];   // accepted path, root first
+  uint8_t par[kMaxNodes];               // the template (LDS copy: indexed reads of the
+  uint8_t dep[kMaxNodes];               // kernel argument would each be a memory
+  uint8_t rnk[kMaxNodes];               // round trip)
+  int32_t tok[kMaxNodes];               // this step's tree tokens
+  int32_t topk[kMaxNodes * kMaxK];      // this step's top-k rows, [T][k]
+  int32_t pre[kMaxNodes * kMaxK];       // M row of each node's greedy token, as before the update
+  int32_t nxt[kMaxNodes];               // next tree tokens
+  int32_t path[kMaxNodes];              // accepted path, root first
+  int32_t hkey[256];                    // token -> node whose row M now holds
+  int32_t hval[256];
   uint32_t red[16];
   int32_t best, L, bonus, P;
 };
 
-__device__ __forceinline__ int64_t m_load(const void* M, int m_is64, int64_t idx) {
-  return m_is64 ? reinterpret_cast<const int64_t*>(M)[idx]
-                : int64_t(reinterpret_cast<const int32_t*>(M)[idx]);
+// M holds int32 or int64 ids (MT); the element type is a template
+// parameter so that no load sits behind a branch on it (the compiler waits
+// for a load before such a branch joins).
+template <typename MT>
+__device__ __forceinline__ int64_t m_load(const void* M, int64_t idx) {
+  return int64_t(reinterpret_cast<const MT*>(M)[idx]);
 }
-__device__ __forceinline__ void m_store(void* M, int m_is64, int64_t idx, int32_t v) {
-  if (m_is64) reinterpret_cast<int64_t*>(M)[idx] = int64_t(v);
-  else reinterpret_cast<int32_t*>(M)[idx] = v;
+template <typename MT>
+__device__ __forceinline__ void m_store(void* M, int64_t idx, int32_t v) {
+  reinterpret_cast<MT*>(M)[idx] = MT(v);
 }
 
-// tok <- tree_tok_b, g <- column 0 of topk_b.  The top-k rows may have been
-// handed over by other blocks of the same launch: read them with get_dev.
-__device__ __forceinline__ void tail_load(TailShared& S, const TreeDev& tree, const int32_t* tok_b,
-                                          const int32_t* topk_b, int32_t k) {
+// Small open-addressing map in LDS from a token to the highest tree node
+// carrying it (the node whose top-k row M holds for that token after this
+// step's update).  At most 128 keys in 256 slots.
+__device__ __forceinline__ uint32_t tok_hash(int32_t t) { return (uint32_t(t) * 2654435761u) >> 24; }
+__device__ __forceinline__ void map_clear(TailShared& S) {
+  for (int i = threadIdx.x; i < 256; i += blockDim.x) {
+    S.hkey[i] = -1;
+    S.hval[i] = -1;
+  }
+}
+// Slot of token t, claimed if t is not in the map yet.
+__device__ __forceinline__ uint32_t map_claim(TailShared& S, int32_t t) {
+  uint32_t slot = tok_hash(t);
+  while (true) {
+    const int32_t prev = atomicCAS(&S.hkey[slot], -1, t);
+    if (prev == -1 || prev == t) return slot;
+    slot = (slot + 1) & 255u;
+  }
+}
+__device__ __forceinline__ int32_t map_get(const TailShared& S, int32_t t) {
+  uint32_t slot = tok_hash(t);
+  while (true) {
+    const int32_t key = S.hkey[slot];
+    if (key == t) return S.hval[slot];
+    if (key == -1) return -1;
+    slot = (slot + 1) & 255u;
+  }
+}
+
+// The template into LDS; the caller synchronises before use.
+__device__ __forceinline__ void tail_tree(TailShared& S, const TreeDev& tree) {
   for (int n = threadIdx.x; n < tree.T; n += blockDim.x) {
-    S.tok[n] = tok_b[n];
-    S.g[n] = get_dev(topk_b + int64_t(n) * k);
+    S.par[n] = tree.parent[n];
+    S.dep[n] = tree.depth[n];
+    S.rnk[n] = tree.rank[n];
   }
+}
+
+// tok <- tree_tok_b, the template, the sequence's top-k rows and (when
+// given) its prefix length into LDS.  The rows were handed over by other
+// blocks of the same launch: read them with get_dev, all in flight at once.
+// Needs blockDim.x >= 256 (T * k <= 2048 ids, at most 8 per thread).
+__device__ __forceinline__ void tail_load(TailShared& S, const TreeDev& tree, const int32_t* tok_b,
+                                          const int32_t* topk_b, int32_t k,
+                                          const int32_t* prefix_len_b = nullptr) {
+  constexpr int kPer = kMaxNodes * kMaxK / 256;
+  const int nk = tree.T * k;
+  const int n = threadIdx.x;
+  int32_t v[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r)                 // clamped: every load in bounds, none branched
+    v[r] = get_dev(topk_b + min(n + r * int(blockDim.x), nk - 1));
+  const int32_t t = tok_b[min(n, tree.T - 1)];
+  const int32_t P = prefix_len_b ? *prefix_len_b : 0;
+  tail_tree(S, tree);
+  map_clear(S);
+#pragma unroll
+  for (int r = 0; r < kPer; ++r)
+    if (n + r * int(blockDim.x) < nk) S.topk[n + r * int(blockDim.x)] = v[r];
+  if (n < tree.T) S.tok[n] = t;
+  if (n == 0) S.P = P;
   __syncthreads();
 }
 
-// Greedy verification: acc(0); acc(n) = acc(parent) && tok(n) == g(parent);
-// best = deepest accepted node, ties to the lowest index; path root..best.
-__device__ __forceinline__ void tail_verify(TailShared& S, const TreeDev& tree) {
-  const int tid = threadIdx.x;
-  if (tid == 0) S.acc[0] = 1;
-  __syncthreads();
-  for (int d = 1; d <= tree.D; ++d) {
-    for (int n = tid; n < tree.T; n += blockDim.x) {
-      if (tree.depth[n] == d) {
-        int p = tree.parent[n];
-        S.acc[n] = S.acc[p] && (S.tok[n] == S.g[p]);
-      }
-    }
-    __syncthreads();
+// Loads of M[g(n)] (g = the node's greedy token), by wave 0 for nodes
+// lane and lane + 64: the next tree's root is g(best) for the accepted
+// node best, so its first layer is one of these rows.  The values stay in
+// registers until tail_prefetch_store, so the loads overlap verification.
+template <typename MT>
+struct PreRows {
+  MT v[2][kMaxK];
+  bool ok[2];                               // the node's greedy token is a valid id
+};
+template <typename MT>
+__device__ __forceinline__ void tail_prefetch(const TailShared& S, const TreeDev& tree, int32_t k,
+                                              const void* M_b, int64_t V, PreRows<MT>& r) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int n = lane + 64 * h;
+    const int32_t g = n < tree.T ? S.topk[n * k] : -1;
+    r.ok[h] = g >= 0 && int64_t(g) < V;
+    const int64_t base = r.ok[h] ? int64_t(g) * k : 0;   // row 0 stands in: no branch
+    // (no later write to r.v before tail_prefetch_store, or the compiler
+    // would wait for the loads there)
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      r.v[h][j] = reinterpret_cast<const MT*>(M_b)[base + min(j, k - 1)];
   }
+}
+// Out-of-range ids become -2 (flagged where used).
+template <typename MT>
+__device__ __forceinline__ void tail_prefetch_store(TailShared& S, const TreeDev& tree, int32_t k,
+                                                    int64_t V, const PreRows<MT>& r) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int n = lane + 64 * h;
+    if (n >= tree.T) continue;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      const int64_t v = int64_t(r.v[h][j]);
+      if (j < k) S.pre[n * k + j] = !r.ok[h] ? -1 : (v >= 0 && v < V) ? int32_t(v) : -2;
+    }
+  }
+}
+
+// Greedy verification: node n is accepted when every node m on its path
+// below the root carries the greedy token of its parent, tok(m) == g(par m);
+// best = deepest accepted node, ties to the lowest index; path root..best.
+// Each thread walks its own node's path in LDS (no barrier per level).
+__device__ __forceinline__ void tail_verify(TailShared& S, const TreeDev& tree, int32_t k) {
+  const int tid = threadIdx.x;
   uint32_t key = 0;
-  for (int n = tid; n < tree.T; n += blockDim.x)
-    if (S.acc[n]) key = max(key, (uint32_t(tree.depth[n]) << 8) | uint32_t(255 - n));
+  for (int n = tid; n < tree.T; n += blockDim.x) {
+    bool ok = true;
+    for (int m = n; m != 0;) {
+      const int p = S.par[m];
+      ok = ok && (S.tok[m] == S.topk[p * k]);
+      m = p;
+    }
+    if (ok) key = max(key, (uint32_t(S.dep[n]) << 8) | uint32_t(255 - n));
+  }
   key = wave_max_u32(key);
   const int nw = blockDim.x >> 6;
   if ((tid & 63) == 0) S.red[tid >> 6] = key;
@@ -63,16 +182,16 @@ __device__ __forceinline__ void tail_verify(TailShared& S, const TreeDev& tree) 
   if (tid == 0) {
     uint32_t m = S.red[0];
     for (int w = 1; w < nw; ++w) m = max(m, S.red[w]);
-    int best = 255 - int(m & 255u);
-    int L = tree.depth[best];
+    const int best = 255 - int(m & 255u);
+    const int L = S.dep[best];
     int n = best;
     for (int i = L; i >= 0; --i) {
       S.path[i] = n;
-      n = (n == 0) ? 0 : tree.parent[n];
+      n = S.par[n];
     }
     S.best = best;
     S.L = L;
-    S.bonus = S.g[best];
+    S.bonus = S.topk[best * k];
   }
   __syncthreads();
 }
@@ -93,47 +212,67 @@ __device__ __forceinline__ void tail_write_verdict(const TailShared& S, const Tr
   }
 }
 
-// M[tok n] = topk[n] for every node n whose token no later node repeats
-// (the node with the highest index wins on duplicated tokens).
-__device__ __forceinline__ void tail_update(const TailShared& S, const TreeDev& tree,
-                                            const int32_t* topk_b, int32_t k, void* M_b,
-                                            int m_is64, int64_t V, uint8_t* ws) {
-  for (int n = threadIdx.x; n < tree.T; n += blockDim.x) {
-    const int32_t t = S.tok[n];
-    bool winner = true;
-    for (int m = n + 1; m < tree.T; ++m) winner = winner && (S.tok[m] != t);
-    if (!winner) continue;
+// M[tok n] = topk[n], where among nodes carrying the same token the one
+// with the highest index wins: every node enters its token into the LDS
+// map with an atomic maximum of its index (tail_update_claim), and after
+// the map is complete the winners write their rows (tail_update_store).
+// Invalid tokens raise the flag and write nothing.  Each part is run by one
+// wave (nodes lane and lane + 64).
+__device__ __forceinline__ void tail_update_claim(TailShared& S, const TreeDev& tree, int64_t V,
+                                                  uint8_t* ws) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int n = lane + 64 * h;
+    const int32_t t = n < tree.T ? S.tok[n] : -1;
+    if (n >= tree.T) continue;
     if (t < 0 || int64_t(t) >= V) {
       set_flag(ws, TR_FLAG_BAD_TOKEN);
       continue;
     }
-    for (int j = 0; j < k; ++j) m_store(M_b, m_is64, int64_t(t) * k + j, get_dev(topk_b + int64_t(n) * k + j));
+    atomicMax(&S.hval[map_claim(S, t)], n);
+  }
+}
+template <typename MT>
+__device__ __forceinline__ void tail_update_store(const TailShared& S, const TreeDev& tree,
+                                                  int32_t k, void* M_b, int64_t V) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int n = lane + 64 * h;
+    const int32_t t = n < tree.T ? S.tok[n] : -1;
+    if (t < 0 || int64_t(t) >= V || map_get(S, t) != n) continue;
+    for (int j = 0; j < k; ++j) m_store<MT>(M_b, int64_t(t) * k + j, S.topk[n * k + j]);
   }
 }
 
-// Copy the key/value rows of path[0..L] to cache positions P..P+L.
-__device__ __forceinline__ void tail_commit(TailShared& S, const TreeDev& tree, int b,
-                                            const TailArgs& a, uint8_t* ws) {
-  if (!a.k_cache) return;
-  if (threadIdx.x == 0) S.P = a.prefix_len[b];
-  __syncthreads();
+// Copy of the key/value rows of path[0..L] to cache positions P..P+L by
+// the threads [first, blockDim.x), R 16-byte units per thread in flight.
+// Returns whether the rows fit (the caller advances the prefix length);
+// they are copied only then.  S.L (verification) and S.P (tail_load) must
+// be visible.
+__device__ __forceinline__ bool tail_commit(const TailShared& S, const TreeDev& tree, int b,
+                                            const TailArgs& a, uint8_t* ws, int first) {
+  if (!a.k_cache) return false;
   const int64_t P = S.P;
   const int nrows = S.L + 1;
   if (P < 0 || P + nrows > a.cap) {
     if (threadIdx.x == 0) set_flag(ws, TR_FLAG_CACHE_FULL);
-    return;
+    return false;
   }
+  const int me = int(threadIdx.x) - first, count = int(blockDim.x) - first;
+  if (me < 0) return true;
   const int upr = a.row_bytes >> 4;               // 16-byte units per row
   const int per_node = a.Hkv * upr;
   const int total = 2 * nrows * per_node;          // keys then values
-  constexpr int R = 4;                             // units in flight per thread
-  for (int u0 = threadIdx.x; u0 < total; u0 += R * blockDim.x) {
+  constexpr int R = 4;
+  for (int u0 = me; u0 < total; u0 += R * count) {
     u32x4 buf[R];
     int64_t dst_off[R];
     bool dst_v[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int u = min(u0 + r * int(blockDim.x), total - 1);   // clamped: loads stay in bounds
+      const int u = min(u0 + r * count, total - 1);   // clamped: loads stay in bounds
       const bool isv = u >= total / 2;
       const int uu = isv ? u - total / 2 : u;
       const int i = uu / per_node, rem = uu - i * per_node;
@@ -147,41 +286,65 @@ __device__ __forceinline__ void tail_commit(TailShared& S, const TreeDev& tree, 
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      if (u0 + r * int(blockDim.x) >= total) break;
+      if (u0 + r * count >= total) break;
       uint8_t* dst = (dst_v[r] ? a.v_cache : a.k_cache) + dst_off[r];
       *reinterpret_cast<u32x4*>(dst) = buf[r];
     }
   }
-  __syncthreads();
-  if (threadIdx.x == 0) a.prefix_len[b] = int32_t(P + nrows);
+  return true;
 }
 
 // Draft tree retrieval: nxt[0] = root; layer by layer
-// nxt[n] = M[nxt[parent n]][rank n].  Invalid tokens propagate as -1.
+// nxt[n] = M[nxt[parent n]][rank n].  Run by one wave (nodes lane and
+// lane + 64).  With use_map, rows written by this block's update come from
+// LDS (every other row of M is unchanged by it); with use_pre, the first
+// layer's row M[root] comes from S.pre[S.best] (root = g(best)).  Invalid
+// tokens propagate as -1.  S holds the template (tail_tree).
+template <typename MT>
 __device__ __forceinline__ void tail_retrieve(TailShared& S, const TreeDev& tree, int32_t root,
-                                              const void* M_b, int m_is64, int64_t V, int32_t k,
-                                              int32_t* out_b, uint8_t* ws) {
-  if (threadIdx.x == 0) S.nxt[0] = root;
-  __syncthreads();
+                                              const void* M_b, int64_t V, int32_t k,
+                                              int32_t* out_b, uint8_t* ws, bool use_map,
+                                              bool use_pre = false) {
+  const int lane = threadIdx.x & 63;
+  if (lane == 0) S.nxt[0] = root;
+  wave_lds_sync();
   for (int d = 1; d <= tree.D; ++d) {
-    for (int n = threadIdx.x; n < tree.T; n += blockDim.x) {
-      if (tree.depth[n] == d) {
-        const int32_t p = S.nxt[tree.parent[n]];
-        int32_t t = -1;
-        if (p >= 0 && int64_t(p) < V) {
-          int64_t v = m_load(M_b, m_is64, int64_t(p) * k + tree.rank[n]);
-          if (v >= 0 && v < V) t = int32_t(v);
-          else set_flag(ws, TR_FLAG_BAD_TOKEN);
-        } else if (p >= 0) {
-          set_flag(ws, TR_FLAG_BAD_TOKEN);
-        }
-        S.nxt[n] = t;
-      }
+    int32_t p[2], w[2], src[2];                   // src: 0 none, 1 map, 2 prefetched, 3 M
+    int64_t idx[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int n = lane + 64 * h;
+      const bool on = n < tree.T && S.dep[n] == d;
+      p[h] = on ? S.nxt[S.par[n]] : -1;
+      const bool pv = p[h] >= 0 && int64_t(p[h]) < V;
+      if (on && p[h] >= 0 && !pv) set_flag(ws, TR_FLAG_BAD_TOKEN);
+      w[h] = (pv && use_map) ? map_get(S, p[h]) : -1;
+      src[h] = !pv ? 0 : w[h] >= 0 ? 1 : (use_pre && d == 1) ? 2 : 3;
+      idx[h] = src[h] == 3 ? int64_t(p[h]) * k + S.rnk[n] : 0;   // row 0 stands in: no branch
     }
-    __syncthreads();
+    MT mv[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) mv[h] = reinterpret_cast<const MT*>(M_b)[idx[h]];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int n = lane + 64 * h;
+      if (src[h] == 0) {
+        if (n < tree.T && S.dep[n] == d) S.nxt[n] = -1;
+        continue;
+      }
+      const int64_t v = src[h] == 1 ? int64_t(S.topk[w[h] * k + S.rnk[n]])
+                      : src[h] == 2 ? int64_t(S.pre[S.best * k + S.rnk[n]])
+                                    : int64_t(mv[h]);
+      const bool ok = v >= 0 && v < V;
+      if (!ok) set_flag(ws, TR_FLAG_BAD_TOKEN);
+      S.nxt[n] = ok ? int32_t(v) : -1;
+    }
+    wave_lds_sync();
   }
-  if (threadIdx.x == 0 && (root < 0 || int64_t(root) >= V)) set_flag(ws, TR_FLAG_BAD_TOKEN);
-  for (int n = threadIdx.x; n < tree.T; n += blockDim.x) out_b[n] = S.nxt[n];
+  if (lane == 0 && (root < 0 || int64_t(root) >= V)) set_flag(ws, TR_FLAG_BAD_TOKEN);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    if (lane + 64 * h < tree.T) out_b[lane + 64 * h] = S.nxt[lane + 64 * h];
 }
 
 }  // namespace tr
