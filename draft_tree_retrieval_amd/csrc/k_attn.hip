@@ -38,9 +38,10 @@ AttnPlan plan_attn(int32_t T, int32_t B, int32_t Hq, int32_t Hkv, int64_t cap, i
   p.G = Hq / Hkv;
   p.R = T * p.G;
   if (is_bf16) {
-    // one strip per wave unless two halve the tiles at no extra padding
-    const int t1 = (p.R + 127) / 128, t2 = (p.R + 255) / 256;
-    p.spw = (t2 * 256 <= t1 * 128) ? 2 : 1;
+    // two strips per wave once a head has more than one 128-row tile: each
+    // key/value operand read from LDS then feeds twice the products and
+    // fewer tiles re-read the same keys
+    p.spw = p.R > 128 ? 2 : 1;
     p.tile_rows = kWaves * p.spw * 16;
   } else {
     p.spw = kSpw;
@@ -82,6 +83,13 @@ __device__ __forceinline__ int clamp_prefix(int P, int64_t cap, uint8_t* ws, boo
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A chunk with no keys for its sequence still marks its rows' partials as
+// empty (weight 0), so the merge can read every chunk without knowing the
+// prefix length.
+__device__ __forceinline__ void mark_empty(float2* part_ml, int64_t unit0, int rows) {
+  for (int r = threadIdx.x; r < rows; r += blockDim.x) part_ml[unit0 + r] = make_float2(-INFINITY, 0.f);
+}
+
 // ---------------------------------------------------------------- bf16 prefix
 // 8 waves; SPW 16-row strips per wave.  The kernel is bound by memory
 // latency, not arithmetic, so it keeps two or three 64-key sub-blocks
@@ -92,8 +100,8 @@ constexpr int kSB = 64;                   // keys per sub-block
 constexpr int kVtS = kSB + 4;             // bf16 per staged V^T row: 136 bytes
 template <int SPW>
 __global__ __launch_bounds__(512) void attn_prefix_bf16(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
-    const uint16_t* __restrict__ vc, int64_t cap, const int32_t* __restrict__ prefix_len, int T,
+    const uint16_t* __restrict__ q, const uint16_t* kc,
+    const uint16_t* vc, int64_t cap, const int32_t* __restrict__ prefix_len, int T,
     int Hq, int Hkv, int G, int R, int chunks, float sl2, float* __restrict__ part_o,
     float2* __restrict__ part_ml, uint8_t* ws, int B, int row_tiles) {
   constexpr int kRows = kWaves * SPW * 16;        // query rows per tile
@@ -111,10 +119,13 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
   const int cs = chunk_len(P, chunks, kSub);
   const int k0 = c * cs;
   const int k1 = min(P, k0 + cs);
-  if (k0 >= k1) return;
+  const int Rpad = row_tiles * kRows;
+  if (k0 >= k1) {
+    mark_empty(part_ml, (int64_t(z) * chunks + c) * Rpad + rt * kRows, min(kRows, R - rt * kRows));
+    return;
+  }
   const int nsub = (k1 - k0 + kSB - 1) / kSB;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, g = lane >> 4;
-  const int Rpad = row_tiles * kRows;
   const int row0 = rt * kRows + w * SPW * 16;      // first query row of this wave
   const bool active = row0 < R;                    // waves past the last row only load
 
@@ -243,8 +254,7 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
           x[t][i] = (!ragged || key < nk) ? sacc[s][t][i] : -INFINITY;
           mraw = fmaxf(mraw, x[t][i]);
         }
-      mraw = fmaxf(mraw, __shfl_xor(mraw, 16, 64));
-      mraw = fmaxf(mraw, __shfl_xor(mraw, 32, 64));
+      mraw = xmax32(xmax16(mraw));
       const float mnew = fmaxf(mrow[s], mraw * sl2);
       const float alpha = fast_exp2(mrow[s] - mnew);
       float psum = 0.f;
@@ -257,8 +267,7 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
           psum += pr;
           ph[t][i] = (__bf16)pr;
         }
-      psum += __shfl_xor(psum, 16, 64);
-      psum += __shfl_xor(psum, 32, 64);
+      psum = xsum32(xsum16(psum));
       lrow[s] = lrow[s] * alpha + psum;
       mrow[s] = mnew;
       if (__any(alpha != 1.f)) {                   // no lane's maximum moved: nothing to rescale
@@ -292,12 +301,21 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
   // no branch around a load or a stage; only the compute of sub-blocks past
   // the end is skipped.  Two 16-row strips per wave leave registers for two
   // slots only.
+  // (compiler memory barriers keep the loads in ring order: the compiler
+  // would otherwise sink them past the first staging and wait for them all;
+  // kc and vc are not __restrict__ for the same reason, loads through such
+  // pointers may move across barriers)
   constexpr int kRing = SPW == 1 ? 3 : 2;
   u32x4 kr[kRing][2], vr[kRing][2];
 #pragma unroll
-  for (int j = 0; j < kRing; ++j) load(kr[j], vr[j], j);
+  for (int j = 0; j < kRing; ++j) {
+    load(kr[j], vr[j], j);
+    asm volatile("" ::: "memory");
+  }
   stage(kr[0], vr[0], 0);
+  asm volatile("" ::: "memory");
   load(kr[0], vr[0], kRing);
+  asm volatile("" ::: "memory");
   __syncthreads();
   for (int it = 0; it < nsub; it += kRing) {
 #pragma unroll
@@ -306,7 +324,9 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
       if (active && cur < nsub) compute(cur & 1, min(kSB, k1 - (k0 + cur * kSB)));
       const int nxt = (r + 1) % kRing;             // slot of sub-block cur + 1
       stage(kr[nxt], vr[nxt], (cur + 1) & 1);
+      asm volatile("" ::: "memory");
       load(kr[nxt], vr[nxt], cur + 1 + kRing);     // refill it with sub-block cur + 1 + kRing
+      asm volatile("" ::: "memory");
       __syncthreads();
     }
   }
@@ -343,9 +363,13 @@ __global__ __launch_bounds__(256) void attn_prefix_f32(
   const int cs = chunk_len(P, chunks, kSub);
   const int k0 = c * cs;
   const int k1 = min(P, k0 + cs);
-  if (k0 >= k1) return;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, g = lane >> 4;
   const int Rpad = gridDim.y * kRowsPerTile;
+  if (k0 >= k1) {
+    mark_empty(part_ml, (int64_t(z) * chunks + c) * Rpad + rt * kRowsPerTile,
+               min(kRowsPerTile, R - rt * kRowsPerTile));
+    return;
+  }
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, g = lane >> 4;
 
   __shared__ __attribute__((aligned(16))) float Ks[kSub32 * kStride32];
   __shared__ __attribute__((aligned(16))) float Vs[kSub32 * kStride32];
@@ -421,8 +445,7 @@ __global__ __launch_bounds__(256) void attn_prefix_f32(
           x[i] = key < nk ? sacc[s][i] * sl2 : -INFINITY;
           mloc = fmaxf(mloc, x[i]);
         }
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+        mloc = xmax32(xmax16(mloc));
         const float mnew = fmaxf(mrow[s], mloc);
         const float alpha = fast_exp2(mrow[s] - mnew);
         float psum = 0.f;
@@ -431,8 +454,7 @@ __global__ __launch_bounds__(256) void attn_prefix_f32(
           x[i] = fast_exp2(x[i] - mnew);
           psum += x[i];
         }
-        psum += __shfl_xor(psum, 16, 64);
-        psum += __shfl_xor(psum, 32, 64);
+        psum = xsum32(xsum16(psum));
         lrow[s] = lrow[s] * alpha + psum;
         mrow[s] = mnew;
 #pragma unroll
@@ -462,7 +484,9 @@ __global__ __launch_bounds__(256) void attn_prefix_f32(
 
 // ---------------------------------------------------------------- combine
 // 16 lanes per output row (b, n, h), 8 head-dimension values per lane.
-// Merges the prefix chunk partials (chunks in order) and then the tree keys
+// Merges the prefix chunk partials (all chunks in order; a chunk holding
+// no keys of the sequence carries weight 0, so the prefix length is not
+// needed and every load can be issued at once) and then the tree keys
 // of n's path (n, its parent, ..., the root) with an online softmax.  All
 // loads of a batch are issued before any of them is used.
 __device__ __forceinline__ float row16_sum(float v) {
@@ -497,9 +521,8 @@ __device__ __forceinline__ void load8(const void* base, int64_t elem, float* f) 
 template <bool BF16>
 __global__ __launch_bounds__(128) void attn_combine(
     TreeDev tree, const void* __restrict__ q, const void* __restrict__ kt,
-    const void* __restrict__ vt, const int32_t* __restrict__ prefix_len, int B, int Hq, int Hkv,
-    int G, int chunks, int Rpad, float sl2, const float* __restrict__ part_o,
-    const float2* __restrict__ part_ml, void* __restrict__ out, int64_t cap) {
+    const void* __restrict__ vt, int B, int Hq, int Hkv, int G, int chunks, int Rpad, float sl2,
+    const float* __restrict__ part_o, const float2* __restrict__ part_ml, void* __restrict__ out) {
   constexpr int kBatch = 8;
   const int T = tree.T;
   // parents in LDS: indexed reads of the kernel argument are memory round trips
@@ -515,14 +538,13 @@ __global__ __launch_bounds__(128) void attn_combine(
   const int kvh = h / G, gq = h - kvh * G;
   const int r = n * G + gq;
   const int z = b * Hkv + kvh;
-  const int P = clamp_prefix(prefix_len[b], cap, nullptr, false);
-  const int cs = chunk_len(P, chunks, kSub);
-  const int nc = cs ? min(chunks, (P + cs - 1) / cs) : 0;
+  const int nc = chunks;                           // empty chunks carry weight 0
 
   float m = -INFINITY, l = 0.f, o[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = 0.f;
   auto merge = [&](float ms, float ls, const float* os) {
+    if (!(ls > 0.f)) return;                       // an empty chunk
     const float mn = fmaxf(m, ms);
     const float a = fast_exp2(m - mn), e = fast_exp2(ms - mn);
     l = l * a + ls * e;
@@ -652,11 +674,11 @@ hipError_t launch_attn(const TreeDev& tree, int32_t B, int32_t Hq, int32_t Hkv, 
   dim3 cgrid(unsigned((rows + 7) / 8));
   const int Rpad = plan.row_tiles * plan.tile_rows;
   if (is_bf16)
-    hipLaunchKernelGGL(attn_combine<true>, cgrid, dim3(128), 0, s, tree, q, k_tree, v_tree,
-                       prefix_len, B, Hq, Hkv, plan.G, plan.chunks, Rpad, sl2, part_o, part_ml, out, cap);
+    hipLaunchKernelGGL(attn_combine<true>, cgrid, dim3(128), 0, s, tree, q, k_tree, v_tree, B, Hq,
+                       Hkv, plan.G, plan.chunks, Rpad, sl2, part_o, part_ml, out);
   else
-    hipLaunchKernelGGL(attn_combine<false>, cgrid, dim3(128), 0, s, tree, q, k_tree, v_tree,
-                       prefix_len, B, Hq, Hkv, plan.G, plan.chunks, Rpad, sl2, part_o, part_ml, out, cap);
+    hipLaunchKernelGGL(attn_combine<false>, cgrid, dim3(128), 0, s, tree, q, k_tree, v_tree, B, Hq,
+                       Hkv, plan.G, plan.chunks, Rpad, sl2, part_o, part_ml, out);
   return hipGetLastError();
 }
 
