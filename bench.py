@@ -14,7 +14,11 @@ continuation of that step's tree) in HBM.  The state is then reset to the
 start and the same trajectory is replayed: `--warmup` steps untimed, then
 `--steps` steps timed between two device synchronisations, with HIP events
 around every call on the launch stream.  The replay must end in the same
-state as the record pass (checked).  Prints one JSON line.
+state as the record pass (checked).  A second replay of the same steps runs
+with the library's launch profiling on (two HIP events around every kernel,
+on the stream it runs on) and gives each kernel's average duration for the
+roofline; the headline rate comes from the first, unprofiled replay.
+Prints one JSON line.
 """
 import argparse
 import json
@@ -59,10 +63,16 @@ def kernel_sources_sha256():
     return h.hexdigest()
 
 
-def measured_traffic(workload, call):
-    """HBM bytes per launch of `call` from the committed counter record of this
-    workload (FETCH_SIZE and WRITE_SIZE runs, scaled by a plain copy), or None
-    when there is no record or the kernels changed since it was taken."""
+# profiling names of the library's kernels -> kernel name prefixes in the
+# counter record
+TRAFFIC_KERNEL = {"attn_prefix": "attn_prefix", "attn_combine": "attn_combine", "topk": "topk_kernel"}
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter record of
+    this workload (FETCH_SIZE and WRITE_SIZE runs, each scaled by what it
+    reads for a plain copy), or None when there is no record or the kernels
+    changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -70,7 +80,11 @@ def measured_traffic(workload, call):
         rec = json.load(f)
     if rec.get("sources_sha256") != kernel_sources_sha256():
         return None
-    return rec.get("per_call_bytes", {}).get(call)
+    k = rec.get("per_kernel_kib", {}).get(TRAFFIC_KERNEL.get(kernel, kernel))
+    cal = rec.get("copy_calibration", {})
+    if not k or not cal:
+        return None
+    return int(round((k["FETCH_SIZE"] * cal["fetch_scale"] + k["WRITE_SIZE"] * cal["write_scale"]) * 1024))
 
 
 def copy_calibration(mib):
@@ -194,6 +208,28 @@ def main():
     step_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
     ms_per_step = wall * 1e3 / steps
 
+    # ---- kernel timing: the same steps again, every launch between two HIP
+    # events on its stream
+    st = init.clone()
+    dec = TRDecoder(tree, st.M, st.k_cache, st.v_cache, st.prefix_len, st.root, Hq=w.Hq)
+    for s in range(args.warmup):
+        q, kt, vt, z = inputs[s]
+        dec.attend(q, kt, vt, out)
+        dec.step(z, kt, vt)
+    torch.cuda.synchronize()
+    tr.tr_profile_enable(True)
+    for i in range(steps):
+        q, kt, vt, z = inputs[args.warmup + i]
+        dec.attend(q, kt, vt, out)
+        dec.step(z, kt, vt)
+    launches = tr.tr_profile_read()
+    tr.tr_profile_enable(False)
+    assert torch.equal(dec.tree_tok, rec_tok), "profiled replay diverged from the record pass"
+    kernel_ms = {}
+    for name, ms in launches:
+        kernel_ms.setdefault(name, []).append(ms)
+    kernel_ms = {k: sum(v) / len(v) for k, v in kernel_ms.items() if len(v) == steps}
+
     # ---- algorithmic bytes per call (what the method must move)
     esz = torch.tensor([], dtype=w.kv_dtype).element_size()
     lsz = torch.tensor([], dtype=w.logit_dtype).element_size()
@@ -212,12 +248,20 @@ def main():
         "tr_tree_attn": (attn_ms, attn_bytes),
         "tr_step": (step_ms, step_bytes),
     }
-    dom = max(calls, key=lambda c: calls[c][0])
-    dms, dbytes = calls[dom]
-    achieved = dbytes / (dms * 1e-3) / 1e9
     detail = {c: {"avg_us": round(ms * 1e3, 2), "bytes": int(b),
                   "GB_s": round(b / (ms * 1e-3) / 1e9, 1)} for c, (ms, b) in calls.items()}
     log("per call:", json.dumps(detail))
+    # per kernel: the prefix pass reads the cache and the queries, the combine
+    # reads the tree keys/values and writes the output, the step kernel does
+    # the rest of the call
+    kbytes = {"attn_prefix": kv_bytes + qo_bytes / 2, "attn_combine": tkv_bytes + qo_bytes / 2,
+              "topk": step_bytes}
+    kdetail = {k: {"avg_us": round(ms * 1e3, 2), "bytes": int(kbytes[k]),
+                   "GB_s": round(kbytes[k] / (ms * 1e-3) / 1e9, 1)} for k, ms in kernel_ms.items()}
+    log("per kernel:", json.dumps(kdetail))
+    dom = max(kernel_ms, key=kernel_ms.get)
+    dms, dbytes = kernel_ms[dom], kbytes[dom]
+    achieved = dbytes / (dms * 1e-3) / 1e9
     log(f"mean accepted drafts {L_mean:.3f}, emitted/step {L_mean + 1:.3f}")
 
     cpu = None
@@ -244,6 +288,7 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(args.workload, dom)},
         "per_call": detail,
+        "per_kernel": kdetail,
         "emitted_per_step": round(L_mean + 1, 3),
         "cpu_baseline": cpu,
     }

@@ -10,6 +10,38 @@
 
 #include "tr_internal.h"
 
+namespace tr {
+
+// Launch timing for tr_profile_*: a pool of event pairs, one per launch.
+namespace {
+constexpr int kProfMax = 16384;
+struct ProfState {
+  bool on = false;
+  std::vector<hipEvent_t> ev;        // 2 per record, created when enabled
+  std::vector<int32_t> id;
+  int n = 0;                         // records since the last read
+  int open = -1;                     // record begun, not ended
+};
+ProfState g_prof;
+}  // namespace
+
+void prof_begin(hipStream_t s, int32_t kernel_id) {
+  g_prof.open = -1;
+  if (!g_prof.on || g_prof.n >= kProfMax || size_t(2 * g_prof.n + 1) >= g_prof.ev.size()) return;
+  const int i = g_prof.n;
+  if (hipEventRecord(g_prof.ev[2 * i], s) != hipSuccess) return;
+  g_prof.id[i] = kernel_id;
+  g_prof.open = i;
+}
+
+void prof_end(hipStream_t s) {
+  if (g_prof.open < 0) return;
+  if (hipEventRecord(g_prof.ev[2 * g_prof.open + 1], s) == hipSuccess) ++g_prof.n;
+  g_prof.open = -1;
+}
+
+}  // namespace tr
+
 namespace {
 
 thread_local char g_err[512];
@@ -358,6 +390,44 @@ tr_status tr_step(const tr_tree* t, int32_t B, int64_t V, int32_t k, const void*
   return hip_status(tr::launch_topk(t->dev, B, logits, l_dtype == TR_BFLOAT16, V, k, ids, tail, w,
                                     plan, hipStream_t(stream)),
                     "tr_step");
+}
+
+}  // extern "C"
+
+extern "C" {
+
+tr_status tr_profile_enable(int32_t on) {
+  auto& P = tr::g_prof;
+  if (on && P.ev.empty()) {
+    P.ev.resize(2 * tr::kProfMax, nullptr);
+    P.id.resize(tr::kProfMax, 0);
+    for (auto& e : P.ev) {
+      const hipError_t err = hipEventCreate(&e);
+      if (err != hipSuccess) {
+        for (auto& f : P.ev)
+          if (f) hipEventDestroy(f);
+        P.ev.clear();
+        P.id.clear();
+        return hip_status(err, "tr_profile_enable");
+      }
+    }
+  }
+  P.on = on != 0;
+  P.n = 0;
+  return ok();
+}
+
+int32_t tr_profile_read(tr_launch_time* out, int32_t max) {
+  auto& P = tr::g_prof;
+  int32_t w = 0;
+  for (int i = 0; i < P.n; ++i) {
+    if (hipEventSynchronize(P.ev[2 * i + 1]) != hipSuccess) continue;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, P.ev[2 * i], P.ev[2 * i + 1]) != hipSuccess) continue;
+    if (out && w < max) out[w++] = tr_launch_time{P.id[i], ms};
+  }
+  P.n = 0;
+  return w;
 }
 
 }  // extern "C"

@@ -650,6 +650,7 @@ hipError_t launch_attn(const TreeDev& tree, int32_t B, int32_t Hq, int32_t Hkv, 
   dim3 grid(plan.chunks, plan.row_tiles, B * Hkv);
   const int64_t groups = int64_t(B) * Hkv * plan.chunks;
   dim3 grid1(unsigned((groups + 7) / 8 * 8 * plan.row_tiles));
+  prof_begin(s, TR_KERNEL_ATTN_PREFIX);
   if (is_bf16) {
     const auto* qq = reinterpret_cast<const uint16_t*>(q);
     const auto* kk = reinterpret_cast<const uint16_t*>(k_cache);
@@ -668,17 +669,20 @@ hipError_t launch_attn(const TreeDev& tree, int32_t B, int32_t Hq, int32_t Hkv, 
                        cap, prefix_len, tree.T, Hq, Hkv, plan.G, plan.R, plan.chunks, sl2, part_o,
                        part_ml, ws);
   }
+  prof_end(s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = int64_t(B) * tree.T * Hq;
   dim3 cgrid(unsigned((rows + 7) / 8));
   const int Rpad = plan.row_tiles * plan.tile_rows;
+  prof_begin(s, TR_KERNEL_ATTN_COMBINE);
   if (is_bf16)
     hipLaunchKernelGGL(attn_combine<true>, cgrid, dim3(128), 0, s, tree, q, k_tree, v_tree, B, Hq,
                        Hkv, plan.G, plan.chunks, Rpad, sl2, part_o, part_ml, out);
   else
     hipLaunchKernelGGL(attn_combine<false>, cgrid, dim3(128), 0, s, tree, q, k_tree, v_tree, B, Hq,
                        Hkv, plan.G, plan.chunks, Rpad, sl2, part_o, part_ml, out);
+  prof_end(s);
   return hipGetLastError();
 }
 

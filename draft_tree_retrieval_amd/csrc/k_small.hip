@@ -45,16 +45,20 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint4* p, size_t n16) {
 hipError_t launch_retrieve(const TreeDev& tree, int32_t B, const void* M, int m_is64, int64_t V,
                            int32_t k, const int32_t* root_tok, int32_t* tree_tok, uint8_t* ws,
                            hipStream_t s) {
+  prof_begin(s, TR_KERNEL_RETRIEVE);
   hipLaunchKernelGGL(retrieve_kernel, dim3(B), dim3(128), 0, s, tree, M, m_is64, V, k, root_tok,
                      tree_tok, ws);
+  prof_end(s);
   return hipGetLastError();
 }
 
 hipError_t launch_verify(const TreeDev& tree, int32_t B, const int32_t* topk, int32_t k,
                          const int32_t* tree_tok, int32_t* accept_len, int32_t* accept_path,
                          int32_t* bonus, int32_t* emitted, hipStream_t s) {
+  prof_begin(s, TR_KERNEL_VERIFY);
   hipLaunchKernelGGL(verify_kernel, dim3(B), dim3(256), 0, s, tree, topk, k, tree_tok, accept_len,
                      accept_path, bonus, emitted);
+  prof_end(s);
   return hipGetLastError();
 }
 
@@ -63,8 +67,10 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
   if (n16 == 0) return hipSuccess;
   size_t blocks = (n16 + 255) / 256;
   if (blocks > 4096) blocks = 4096;
+  prof_begin(s, TR_KERNEL_FILL);
   hipLaunchKernelGGL(fill_zero_kernel, dim3(unsigned(blocks)), dim3(256), 0, s,
                      reinterpret_cast<uint4*>(p), n16);
+  prof_end(s);
   return hipGetLastError();
 }
 

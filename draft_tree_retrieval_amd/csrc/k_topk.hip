@@ -400,11 +400,13 @@ hipError_t launch_topk(const TreeDev& tree, int32_t B, const void* logits, int l
     if (plan.threads == 512) TR_TOPK(BF, KMV, 512, 8);      \
     else TR_TOPK(BF, KMV, 256, 16);                         \
   } while (0)
+  prof_begin(s, TR_KERNEL_TOPK);
   if (l_is_bf16) {
     if (plan.kmax == 8) TR_TOPK_NT(true, 8); else TR_TOPK_NT(true, 16);
   } else {
     if (plan.kmax == 8) TR_TOPK_NT(false, 8); else TR_TOPK_NT(false, 16);
   }
+  prof_end(s);
 #undef TR_TOPK_NT
 #undef TR_TOPK
   return hipGetLastError();

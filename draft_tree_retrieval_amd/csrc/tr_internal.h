@@ -98,6 +98,10 @@ struct TailArgs {
   int32_t row_bytes;       // d * element size
 };
 
+// Profiling hooks around each launch (no-ops unless tr_profile_enable).
+void prof_begin(hipStream_t s, int32_t kernel_id);
+void prof_end(hipStream_t s);
+
 hipError_t launch_topk(const TreeDev& tree, int32_t B, const void* logits, int l_is_bf16, int64_t V,
                        int32_t k, int32_t* topk_ids, const TailArgs& tail, uint8_t* ws,
                        const TopkPlan& plan, hipStream_t s);

@@ -46,7 +46,16 @@ _SIGS = {
     "tr_verify": ([_P, _I32, _P, _I32, _P, _P, _P, _P, _P, _P], C.c_int),
     "tr_step": ([_P, _I32, _I64, _I32, _P, C.c_int, _P, C.c_int, _P, _P, _P, _P, _P, _I32, _I32,
                  C.c_int, _P, _P, _P, _P, _I64, _P, _P, _P, _SZ, _P], C.c_int),
+    "tr_profile_enable": ([_I32], C.c_int),
+    "tr_profile_read": ([_P, _I32], _I32),
 }
+
+# tr_kernel_id
+KERNEL_NAMES = {1: "attn_prefix", 2: "attn_combine", 3: "topk", 4: "retrieve", 5: "verify", 6: "fill"}
+
+
+class _LaunchTime(C.Structure):
+    _fields_ = [("kernel", C.c_int32), ("ms", C.c_float)]
 
 _lib = None
 
@@ -209,3 +218,16 @@ def tr_step(tree, logits, M, tree_tok, root_tok, accept_len, accept_path, emitte
                           _ptr(emitted), Hkv, d, kv_dt, _ptr(k_tree), _ptr(v_tree), _ptr(k_cache),
                           _ptr(v_cache), cap, _ptr(prefix_len), _ptr(topk_out), _ptr(ws),
                           ws.numel(), _stream(stream)))
+
+
+def tr_profile_enable(on=True):
+    """Profiling aid: bracket every library launch with HIP events."""
+    _check(load().tr_profile_enable(1 if on else 0))
+
+
+def tr_profile_read(max_records=16384):
+    """[(kernel name, ms)] of the launches recorded since the last read, in
+    launch order (synchronises on their events)."""
+    buf = (_LaunchTime * max_records)()
+    n = load().tr_profile_read(buf, max_records)
+    return [(KERNEL_NAMES.get(buf[i].kernel, str(buf[i].kernel)), float(buf[i].ms)) for i in range(n)]

@@ -213,6 +213,34 @@ tr_status tr_step(const tr_tree* t, int32_t B, int64_t V, int32_t k, const void*
                   void* k_cache, void* v_cache, int64_t cap, int32_t* prefix_len, int32_t* topk_out,
                   void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Profiling aid (outside the TR step).  While enabled, each kernel the
+ * library launches is bracketed by two HIP events recorded on the stream it
+ * is launched on, so the elapsed time between them is that launch's time on
+ * the device.  tr_profile_read synchronises on the recorded events, writes
+ * up to max (kernel, milliseconds) records in launch order, forgets all
+ * records and returns how many it wrote.  At most 16384 launches are kept
+ * between reads (later ones are not recorded).  tr_profile_enable creates
+ * the events (hipEventCreate) the first time it is turned on.  Not
+ * thread-safe: one host thread drives the library while profiling.
+ * ------------------------------------------------------------------------ */
+typedef enum {
+  TR_KERNEL_ATTN_PREFIX = 1,   /* tr_tree_attn, prefix chunks */
+  TR_KERNEL_ATTN_COMBINE = 2,  /* tr_tree_attn, merge of chunks and tree keys */
+  TR_KERNEL_TOPK = 3,          /* tr_step / tr_update_topk (top-k and tail) */
+  TR_KERNEL_RETRIEVE = 4,      /* tr_retrieve */
+  TR_KERNEL_VERIFY = 5,        /* tr_verify */
+  TR_KERNEL_FILL = 6           /* tr_workspace_init */
+} tr_kernel_id;
+
+typedef struct {
+  int32_t kernel;              /* tr_kernel_id */
+  float ms;
+} tr_launch_time;
+
+tr_status tr_profile_enable(int32_t on);
+int32_t tr_profile_read(tr_launch_time* out, int32_t max);
+
 #ifdef __cplusplus
 }
 #endif
