@@ -136,8 +136,9 @@ __device__ __forceinline__ void block_merge(TopList<KM>& L, uint64_t (*s_keys)[K
 // The per-sequence tail: update only (TAIL_UPDATE) or the whole step
 // (TAIL_STEP: verification, update, commit, next retrieval).  Needs at
 // least 256 threads.  After verification, wave 0 retrieves the next tree
-// while wave 1 writes the updated rows of M and waves 1.. copy the accepted
-// key/value rows, so retrieval's loads never wait behind their stores.
+// while waves 1.. write the verdict, wave 1 the updated rows of M and
+// waves 1.. copy the accepted key/value rows, so retrieval's loads never
+// wait behind their stores.
 template <typename MT>
 __device__ __forceinline__ void seq_tail(TailShared& S, const TreeDev& tree, int b, int32_t k,
                                          int64_t V, const int32_t* topk_b, int32_t* tok_b,
@@ -157,7 +158,7 @@ __device__ __forceinline__ void seq_tail(TailShared& S, const TreeDev& tree, int
   PreRows<MT> pre;
   if (wave == 0) tail_prefetch<MT>(S, tree, k, M_b, V, pre);   // in flight during verification
   tail_verify(S, tree, k);
-  tail_write_verdict(S, tree, b, tail.accept_len, tail.accept_path, nullptr, tail.emitted);
+  tail_write_verdict(S, tree, b, tail.accept_len, tail.accept_path, nullptr, tail.emitted, 64);
   if (wave == 0) tail_update_claim(S, tree, V, ws);
   __syncthreads();                                   // the LDS map is complete
   const bool fits = tail_commit(S, tree, b, tail, ws, wave == 0 ? 1 << 30 : 64);

@@ -7,9 +7,10 @@
 // tree's first layer may need are fetched while verification runs, and
 // after verification wave 0 alone does the tree work (update, retrieval;
 // two nodes per lane, at most 128 nodes, synchronised through LDS inside
-// the wave) while the other waves copy the accepted rows into the cache.
-// A wave's memory counter covers its stores as well as its loads, so the
-// copy on other waves never delays retrieval's waits.
+// the wave) while the other waves write every output and copy the accepted
+// rows into the cache.  A wave's memory counter covers its stores as well
+// as its loads, and a store completes far later than a load returns, so
+// wave 0 stores nothing until the retrieval is done.
 #pragma once
 
 #include "dev_common.h"
@@ -196,17 +197,20 @@ __device__ __forceinline__ void tail_verify(TailShared& S, const TreeDev& tree, 
   __syncthreads();
 }
 
-// Verification outputs of sequence b.
+// Verification outputs of sequence b, written by the threads [first,
+// blockDim.x).
 __device__ __forceinline__ void tail_write_verdict(const TailShared& S, const TreeDev& tree, int b,
                                                    int32_t* accept_len, int32_t* accept_path,
-                                                   int32_t* bonus, int32_t* emitted) {
+                                                   int32_t* bonus, int32_t* emitted, int first = 0) {
   const int W = tree.D + 1;
-  for (int i = threadIdx.x; i < W; i += blockDim.x) {
+  const int me = int(threadIdx.x) - first, count = int(blockDim.x) - first;
+  if (me < 0) return;
+  for (int i = me; i < W; i += count) {
     if (accept_path) accept_path[int64_t(b) * W + i] = (i <= S.L) ? S.path[i] : -1;
     if (emitted)
       emitted[int64_t(b) * W + i] = (i < S.L) ? S.tok[S.path[i + 1]] : (i == S.L ? S.bonus : -1);
   }
-  if (threadIdx.x == 0) {
+  if (me == 0) {
     if (accept_len) accept_len[b] = S.L;
     if (bonus) bonus[b] = S.bonus;
   }
@@ -300,51 +304,68 @@ __device__ __forceinline__ bool tail_commit(const TailShared& S, const TreeDev& 
 // LDS (every other row of M is unchanged by it); with use_pre, the first
 // layer's row M[root] comes from S.pre[S.best] (root = g(best)).  Invalid
 // tokens propagate as -1.  S holds the template (tail_tree).
+//
+// The layers form a chain of dependent reads, so each layer keeps its
+// chain short: the nodes' template data sit in registers, both nodes of a
+// lane are resolved side by side, and M is read only when some lane needs
+// a row that is neither in the map nor prefetched.
 template <typename MT>
 __device__ __forceinline__ void tail_retrieve(TailShared& S, const TreeDev& tree, int32_t root,
                                               const void* M_b, int64_t V, int32_t k,
                                               int32_t* out_b, uint8_t* ws, bool use_map,
                                               bool use_pre = false) {
   const int lane = threadIdx.x & 63;
+  int n[2], dep[2], par[2], rnk[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    n[h] = lane + 64 * h;
+    const bool in = n[h] < tree.T;
+    dep[h] = in ? S.dep[n[h]] : 0;               // 0: the root or no node
+    par[h] = in ? S.par[n[h]] : 0;
+    rnk[h] = in ? S.rnk[n[h]] : 0;
+  }
+  const int pre_row = use_pre ? S.best * k : 0;
   if (lane == 0) S.nxt[0] = root;
   wave_lds_sync();
   for (int d = 1; d <= tree.D; ++d) {
     int32_t p[2], w[2], src[2];                   // src: 0 none, 1 map, 2 prefetched, 3 M
-    int64_t idx[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) p[h] = dep[h] == d ? S.nxt[par[h]] : -1;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int n = lane + 64 * h;
-      const bool on = n < tree.T && S.dep[n] == d;
-      p[h] = on ? S.nxt[S.par[n]] : -1;
       const bool pv = p[h] >= 0 && int64_t(p[h]) < V;
-      if (on && p[h] >= 0 && !pv) set_flag(ws, TR_FLAG_BAD_TOKEN);
-      w[h] = (pv && use_map) ? map_get(S, p[h]) : -1;
+      if (p[h] >= 0 && !pv) set_flag(ws, TR_FLAG_BAD_TOKEN);
+      w[h] = -1;
+      if (pv && use_map) {                         // first probe inline, collisions in map_get
+        const uint32_t slot = tok_hash(p[h]);
+        const int32_t key = S.hkey[slot];
+        w[h] = key == p[h] ? S.hval[slot] : key == -1 ? -1 : map_get(S, p[h]);
+      }
       src[h] = !pv ? 0 : w[h] >= 0 ? 1 : (use_pre && d == 1) ? 2 : 3;
-      idx[h] = src[h] == 3 ? int64_t(p[h]) * k + S.rnk[n] : 0;   // row 0 stands in: no branch
     }
-    MT mv[2];
+    MT mv[2] = {MT(0), MT(0)};
+    if (__ballot(src[0] == 3 || src[1] == 3)) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) mv[h] = reinterpret_cast<const MT*>(M_b)[idx[h]];
+      for (int h = 0; h < 2; ++h)                  // row 0 stands in for lanes that need none
+        mv[h] = reinterpret_cast<const MT*>(M_b)[src[h] == 3 ? int64_t(p[h]) * k + rnk[h] : 0];
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int n = lane + 64 * h;
-      if (src[h] == 0) {
-        if (n < tree.T && S.dep[n] == d) S.nxt[n] = -1;
-        continue;
-      }
-      const int64_t v = src[h] == 1 ? int64_t(S.topk[w[h] * k + S.rnk[n]])
-                      : src[h] == 2 ? int64_t(S.pre[S.best * k + S.rnk[n]])
-                                    : int64_t(mv[h]);
+      if (dep[h] != d) continue;
+      int64_t v = -1;
+      if (src[h] == 1) v = S.topk[w[h] * k + rnk[h]];
+      else if (src[h] == 2) v = S.pre[pre_row + rnk[h]];
+      else if (src[h] == 3) v = int64_t(mv[h]);
       const bool ok = v >= 0 && v < V;
-      if (!ok) set_flag(ws, TR_FLAG_BAD_TOKEN);
-      S.nxt[n] = ok ? int32_t(v) : -1;
+      if (src[h] != 0 && !ok) set_flag(ws, TR_FLAG_BAD_TOKEN);
+      S.nxt[n[h]] = ok ? int32_t(v) : -1;
     }
     wave_lds_sync();
   }
   if (lane == 0 && (root < 0 || int64_t(root) >= V)) set_flag(ws, TR_FLAG_BAD_TOKEN);
 #pragma unroll
   for (int h = 0; h < 2; ++h)
-    if (lane + 64 * h < tree.T) out_b[lane + 64 * h] = S.nxt[lane + 64 * h];
+    if (n[h] < tree.T) out_b[n[h]] = S.nxt[n[h]];
 }
 
 }  // namespace tr
