@@ -307,12 +307,18 @@ __global__ __launch_bounds__(NT) void topk_kernel(const void* __restrict__ logit
   if (!overflow && n <= 64u) {
     // one wave: lane i ranks candidate i against the others in registers
     if (wave == 0) {
-      uint64_t key = 0;
-      if (lane < int(n)) {
-        int w = 0, idx = lane;
-        while (idx >= int(s_wcnt[w])) { idx -= int(s_wcnt[w]); ++w; }
-        key = s_cand[w * kCandW + idx];
+      // lane i takes candidate i: its list and place from the list sizes,
+      // read at once (not one dependent LDS read per list)
+      uint32_t c[NW];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) c[w] = s_wcnt[w];
+      int src = -1, before = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        if (src < 0 && lane < before + int(c[w])) src = w * kCandW + (lane - before);
+        before += int(c[w]);
       }
+      const uint64_t key = src >= 0 ? s_cand[src] : 0ull;
       int rank = 0;
       for (int j = 0; j < int(n); ++j) rank += readlane_u64(key, j) > key ? 1 : 0;
       if (lane >= int(n)) rank = lane;           // empty places n.. hold key 0
