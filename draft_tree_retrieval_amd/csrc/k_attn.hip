@@ -58,8 +58,8 @@ AttnPlan plan_attn(int32_t T, int32_t B, int32_t Hq, int32_t Hkv, int64_t cap, i
   const size_t rpad = size_t(p.row_tiles) * p.tile_rows;
   const size_t units = size_t(B) * Hkv * p.chunks * rpad;
   size_t off = kDataOff;
-  p.o_off = off;
-  off = align256(off + units * kHeadDim * 4);
+  p.o_off = off;                                    // bf16 path: bf16 partials
+  off = align256(off + units * kHeadDim * (is_bf16 ? 2 : 4));
   p.ml_off = off;
   off = align256(off + units * 8);
   p.end = off;
@@ -102,7 +102,7 @@ template <int SPW>
 __global__ __launch_bounds__(512) void attn_prefix_bf16(
     const uint16_t* __restrict__ q, const uint16_t* kc,
     const uint16_t* vc, int64_t cap, const int32_t* __restrict__ prefix_len, int T,
-    int Hq, int Hkv, int G, int R, int chunks, float sl2, float* __restrict__ part_o,
+    int Hq, int Hkv, int G, int R, int chunks, float sl2, uint16_t* __restrict__ part_o,
     float2* __restrict__ part_ml, uint8_t* ws, int B, int row_tiles) {
   constexpr int kRows = kWaves * SPW * 16;        // query rows per tile
   // Blocks are dealt to the 8 XCDs round-robin by block index.  The row
@@ -337,9 +337,15 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
     const int r = row0 + s * 16 + li;
     if (r < R) {
       const int64_t unit = (int64_t(z) * chunks + c) * Rpad + r;
-      float* po = part_o + unit * kHeadDim;
+      uint16_t* po = part_o + unit * kHeadDim;     // bf16: the partial sums round once
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<floatx4*>(po + dt * 16 + 4 * g) = acc[s][dt];
+      for (int dt = 0; dt < 8; ++dt) {
+        const u32x2 v = {uint32_t(__builtin_bit_cast(uint16_t, (__bf16)acc[s][dt][0])) |
+                             (uint32_t(__builtin_bit_cast(uint16_t, (__bf16)acc[s][dt][1])) << 16),
+                         uint32_t(__builtin_bit_cast(uint16_t, (__bf16)acc[s][dt][2])) |
+                             (uint32_t(__builtin_bit_cast(uint16_t, (__bf16)acc[s][dt][3])) << 16)};
+        *reinterpret_cast<u32x2*>(po + dt * 16 + 4 * g) = v;
+      }
       if (g == 0) part_ml[unit] = make_float2(mrow[s], lrow[s]);
     }
   }
@@ -522,7 +528,7 @@ template <bool BF16>
 __global__ __launch_bounds__(128) void attn_combine(
     TreeDev tree, const void* __restrict__ q, const void* __restrict__ kt,
     const void* __restrict__ vt, int B, int Hq, int Hkv, int G, int chunks, int Rpad, float sl2,
-    const float* __restrict__ part_o, const float2* __restrict__ part_ml, void* __restrict__ out) {
+    const void* __restrict__ part_o, const float2* __restrict__ part_ml, void* __restrict__ out) {
   constexpr int kBatch = 8;
   const int T = tree.T;
   // parents in LDS: indexed reads of the kernel argument are memory round trips
@@ -560,13 +566,7 @@ __global__ __launch_bounds__(128) void attn_combine(
       const int c = max(0, min(c0 + i, nc - 1));
       const int64_t unit = (int64_t(z) * chunks + c) * Rpad + r;
       ml[i] = part_ml[unit];
-      const floatx4 a = *reinterpret_cast<const floatx4*>(part_o + unit * kHeadDim + 8 * li);
-      const floatx4 bq = *reinterpret_cast<const floatx4*>(part_o + unit * kHeadDim + 8 * li + 4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        po[i][j] = a[j];
-        po[i][4 + j] = bq[j];
-      }
+      load8<BF16>(part_o, unit * kHeadDim + 8 * li, po[i]);   // bf16 partials in the bf16 path
     }
   };
   int j = n;                                       // next path node to visit
@@ -644,7 +644,7 @@ hipError_t launch_attn(const TreeDev& tree, int32_t B, int32_t Hq, int32_t Hkv, 
                        const void* q, const void* k_tree, const void* v_tree, const void* k_cache,
                        const void* v_cache, int64_t cap, const int32_t* prefix_len, float scale,
                        void* out, uint8_t* ws, const AttnPlan& plan, hipStream_t s) {
-  float* part_o = reinterpret_cast<float*>(ws + plan.o_off);
+  void* part_o = ws + plan.o_off;
   float2* part_ml = reinterpret_cast<float2*>(ws + plan.ml_off);
   const float sl2 = scale * kLog2e;
   dim3 grid(plan.chunks, plan.row_tiles, B * Hkv);
@@ -657,17 +657,17 @@ hipError_t launch_attn(const TreeDev& tree, int32_t B, int32_t Hq, int32_t Hkv, 
     const auto* vv = reinterpret_cast<const uint16_t*>(v_cache);
     if (plan.spw == 2)
       hipLaunchKernelGGL(attn_prefix_bf16<2>, grid1, dim3(64 * kWaves), 0, s, qq, kk, vv, cap,
-                         prefix_len, tree.T, Hq, Hkv, plan.G, plan.R, plan.chunks, sl2, part_o,
-                         part_ml, ws, B, plan.row_tiles);
+                         prefix_len, tree.T, Hq, Hkv, plan.G, plan.R, plan.chunks, sl2,
+                         reinterpret_cast<uint16_t*>(part_o), part_ml, ws, B, plan.row_tiles);
     else
       hipLaunchKernelGGL(attn_prefix_bf16<1>, grid1, dim3(64 * kWaves), 0, s, qq, kk, vv, cap,
-                         prefix_len, tree.T, Hq, Hkv, plan.G, plan.R, plan.chunks, sl2, part_o,
-                         part_ml, ws, B, plan.row_tiles);
+                         prefix_len, tree.T, Hq, Hkv, plan.G, plan.R, plan.chunks, sl2,
+                         reinterpret_cast<uint16_t*>(part_o), part_ml, ws, B, plan.row_tiles);
   } else {
     hipLaunchKernelGGL(attn_prefix_f32, grid, dim3(256), 0, s, reinterpret_cast<const float*>(q),
                        reinterpret_cast<const float*>(k_cache), reinterpret_cast<const float*>(v_cache),
-                       cap, prefix_len, tree.T, Hq, Hkv, plan.G, plan.R, plan.chunks, sl2, part_o,
-                       part_ml, ws);
+                       cap, prefix_len, tree.T, Hq, Hkv, plan.G, plan.R, plan.chunks, sl2,
+                       reinterpret_cast<float*>(part_o), part_ml, ws);
   }
   prof_end(s);
   hipError_t e = hipGetLastError();

@@ -84,6 +84,12 @@ def test_bad_sizes_rejected(tr):
 
 
 def test_host_checks_launch_nothing(tr):
+    # Every call below must be refused by a host-side check; the device
+    # pointers are fake.  Where a GPU is present a regression would launch on
+    # them, so this runs only on machines without one.
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("host-check test with fake device pointers: runs where no GPU is present")
     lib = tr.load()
     tree = tr.Tree.from_levels([[3], [2, 1]], 3)
     h = tree.handle
@@ -109,9 +115,14 @@ def test_host_checks_launch_nothing(tr):
     assert lib.tr_tree_attn(*args(64, 8, 8, tr.TR_BFLOAT16)) == tr.TR_ERR_UNSUPPORTED
     assert lib.tr_tree_attn(*args(128, 6, 4, tr.TR_BFLOAT16)) == tr.TR_ERR_INVALID_ARGUMENT
     assert lib.tr_tree_attn(*args(128, 8, 8, tr.TR_INT32)) == tr.TR_ERR_UNSUPPORTED
+    # tr_workspace_size covers both dtypes (fp32 partials are the larger):
+    # one byte short fails the fp32 call, a bare header fails the bf16 one
     need = tr.tr_workspace_size(tree, 1, 0, 0, 8, 8, 128, 64)
-    a = list(args(128, 8, 8, tr.TR_BFLOAT16))
+    a = list(args(128, 8, 8, tr.TR_FLOAT32))
     a[-2] = need - 1
+    assert lib.tr_tree_attn(*a) == tr.TR_ERR_WORKSPACE_TOO_SMALL
+    a = list(args(128, 8, 8, tr.TR_BFLOAT16))
+    a[-2] = 256 * 1024
     assert lib.tr_tree_attn(*a) == tr.TR_ERR_WORKSPACE_TOO_SMALL
     # top-k / update / step
     assert lib.tr_update_topk(h, 1, fake, tr.TR_BFLOAT16, 2, 3, fake, fake, tr.TR_INT32, None, ws,
