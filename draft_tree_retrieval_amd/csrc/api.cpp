@@ -343,12 +343,15 @@ tr_status tr_verify(const tr_tree* t, int32_t B, const int32_t* topk, int32_t k,
                     "tr_verify");
 }
 
-tr_status tr_step(const tr_tree* t, int32_t B, int64_t V, int32_t k, const void* logits,
-                  tr_dtype l_dtype, void* M, tr_dtype m_dtype, int32_t* tree_tok, int32_t* root_tok,
-                  int32_t* accept_len, int32_t* accept_path, int32_t* emitted, int32_t Hkv,
-                  int32_t d, tr_dtype kv_dtype, const void* k_tree, const void* v_tree,
-                  void* k_cache, void* v_cache, int64_t cap, int32_t* prefix_len, int32_t* topk_out,
-                  void* ws, size_t ws_bytes, void* stream) {
+tr_status tr_step_ex(const tr_tree* t, int32_t B, int64_t V, int32_t k, const void* logits,
+                     tr_dtype l_dtype, void* M, tr_dtype m_dtype, int32_t* tree_tok,
+                     int32_t* root_tok, int32_t* accept_len, int32_t* accept_path,
+                     int32_t* emitted, int32_t Hkv, int32_t d, tr_dtype kv_dtype,
+                     const void* k_tree, const void* v_tree, void* k_cache, void* v_cache,
+                     int64_t cap, int32_t* prefix_len, int32_t* topk_out, tr_update_mode mode,
+                     void* ws, size_t ws_bytes, void* stream) {
+  TR_CHECK(mode == TR_UPDATE_ALL || mode == TR_UPDATE_ACCEPTED, TR_ERR_INVALID_ARGUMENT,
+           "unknown update mode %d", int(mode));
   tr_status st = check_topk_args(t, B, logits, l_dtype, V, k);
   if (st != TR_OK) return st;
   TR_CHECK(M && tree_tok && root_tok && accept_len, TR_ERR_INVALID_ARGUMENT, "null tensor");
@@ -373,6 +376,7 @@ tr_status tr_step(const tr_tree* t, int32_t B, int64_t V, int32_t k, const void*
   tr::TailArgs tail{};
   tail.mode = tr::TAIL_STEP;
   tail.m_is64 = m_dtype == TR_INT64;
+  tail.update_mode = mode == TR_UPDATE_ACCEPTED ? tr::UPDATE_ACCEPTED : tr::UPDATE_ALL;
   tail.M = M;
   tail.tree_tok = tree_tok;
   tail.root_tok = root_tok;
@@ -390,6 +394,44 @@ tr_status tr_step(const tr_tree* t, int32_t B, int64_t V, int32_t k, const void*
   return hip_status(tr::launch_topk(t->dev, B, logits, l_dtype == TR_BFLOAT16, V, k, ids, tail, w,
                                     plan, hipStream_t(stream)),
                     "tr_step");
+}
+
+tr_status tr_step(const tr_tree* t, int32_t B, int64_t V, int32_t k, const void* logits,
+                  tr_dtype l_dtype, void* M, tr_dtype m_dtype, int32_t* tree_tok, int32_t* root_tok,
+                  int32_t* accept_len, int32_t* accept_path, int32_t* emitted, int32_t Hkv,
+                  int32_t d, tr_dtype kv_dtype, const void* k_tree, const void* v_tree,
+                  void* k_cache, void* v_cache, int64_t cap, int32_t* prefix_len, int32_t* topk_out,
+                  void* ws, size_t ws_bytes, void* stream) {
+  return tr_step_ex(t, B, V, k, logits, l_dtype, M, m_dtype, tree_tok, root_tok, accept_len,
+                    accept_path, emitted, Hkv, d, kv_dtype, k_tree, v_tree, k_cache, v_cache, cap,
+                    prefix_len, topk_out, TR_UPDATE_ALL, ws, ws_bytes, stream);
+}
+
+tr_status tr_init_matrix(int32_t B, int64_t V, int32_t k, void* M, tr_dtype m_dtype,
+                         tr_init_mode mode, const void* prior, tr_dtype prior_dtype,
+                         int32_t prior_batches, uint64_t seed, void* stream) {
+  TR_CHECK(B >= 1 && V >= 1 && k >= 1, TR_ERR_INVALID_ARGUMENT, "B, V and k must be at least 1");
+  TR_CHECK(V <= INT32_MAX, TR_ERR_INVALID_ARGUMENT, "V above 2^31-1");
+  TR_CHECK(M && aligned16(M), TR_ERR_INVALID_ARGUMENT, "M is null or not 16-byte aligned");
+  TR_CHECK(m_dtype == TR_INT32 || m_dtype == TR_INT64, TR_ERR_UNSUPPORTED, "M must be int32 or int64");
+  TR_CHECK(mode == TR_INIT_ZERO || mode == TR_INIT_RANDOM || mode == TR_INIT_PRIOR,
+           TR_ERR_INVALID_ARGUMENT, "unknown init mode %d", int(mode));
+  int prior_is64 = 0;
+  if (mode == TR_INIT_PRIOR) {
+    TR_CHECK(prior && aligned16(prior), TR_ERR_INVALID_ARGUMENT,
+             "prior is null or not 16-byte aligned");
+    TR_CHECK(prior_dtype == TR_INT32 || prior_dtype == TR_INT64, TR_ERR_UNSUPPORTED,
+             "prior must be int32 or int64");
+    TR_CHECK(prior_batches == 1 || prior_batches == B, TR_ERR_INVALID_ARGUMENT,
+             "prior_batches %d must be 1 or B = %d", prior_batches, B);
+    prior_is64 = prior_dtype == TR_INT64;
+  }
+  const int mode_i = mode == TR_INIT_ZERO ? tr::INIT_ZERO
+                     : mode == TR_INIT_RANDOM ? tr::INIT_RANDOM : tr::INIT_PRIOR;
+  return hip_status(tr::launch_init_m(mode_i, M, m_dtype == TR_INT64, B, V, k, prior, prior_is64,
+                                      prior_batches == 1 && B > 1 ? 1 : 0, seed,
+                                      hipStream_t(stream)),
+                    "tr_init_matrix");
 }
 
 }  // extern "C"

@@ -159,7 +159,7 @@ __device__ __forceinline__ void seq_tail(TailShared& S, const TreeDev& tree, int
   if (wave == 0) tail_prefetch<MT>(S, tree, k, M_b, V, pre);   // in flight during verification
   tail_verify(S, tree, k);
   tail_write_verdict(S, tree, b, tail.accept_len, tail.accept_path, nullptr, tail.emitted, 64);
-  if (wave == 0) tail_update_claim(S, tree, V, ws);
+  if (wave == 0) tail_update_claim(S, tree, V, ws, tail.update_mode == UPDATE_ACCEPTED);
   __syncthreads();                                   // the LDS map is complete
   const bool fits = tail_commit(S, tree, b, tail, ws, wave == 0 ? 1 << 30 : 64);
   if (wave == 1) tail_update_store<MT>(S, tree, k, M_b, V);

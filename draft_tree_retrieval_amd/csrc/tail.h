@@ -221,9 +221,12 @@ __device__ __forceinline__ void tail_write_verdict(const TailShared& S, const Tr
 // map with an atomic maximum of its index (tail_update_claim), and after
 // the map is complete the winners write their rows (tail_update_store).
 // Invalid tokens raise the flag and write nothing.  Each part is run by one
-// wave (nodes lane and lane + 64).
+// wave (nodes lane and lane + 64).  With path_only (the ablation that
+// recycles the accepted tokens only) just the nodes of the accepted path
+// enter the map; a node is on it when the path holds it at its depth.  A
+// child's index exceeds its parent's, so the highest index is the deepest.
 __device__ __forceinline__ void tail_update_claim(TailShared& S, const TreeDev& tree, int64_t V,
-                                                  uint8_t* ws) {
+                                                  uint8_t* ws, bool path_only = false) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -233,6 +236,10 @@ __device__ __forceinline__ void tail_update_claim(TailShared& S, const TreeDev& 
     if (t < 0 || int64_t(t) >= V) {
       set_flag(ws, TR_FLAG_BAD_TOKEN);
       continue;
+    }
+    if (path_only) {
+      const int dn = S.dep[n];
+      if (dn > S.L || S.path[dn] != n) continue;
     }
     atomicMax(&S.hval[map_claim(S, t)], n);
   }

@@ -78,9 +78,12 @@ AttnPlan plan_attn(int32_t T, int32_t B, int32_t Hq, int32_t Hkv, int64_t cap, i
 // ---------------------------------------------------------------- launchers
 enum TailMode : int32_t { TAIL_NONE = 0, TAIL_UPDATE = 1, TAIL_STEP = 2 };
 
+enum UpdateMode : int32_t { UPDATE_ALL = 0, UPDATE_ACCEPTED = 1 };
+
 struct TailArgs {
   int32_t mode;
   int32_t m_is64;
+  int32_t update_mode;     // UpdateMode (TAIL_STEP only)
   void* M;                 // [B][V][k]
   int32_t* tree_tok;       // [B][T]
   int32_t* root_tok;       // [B]
@@ -112,6 +115,10 @@ hipError_t launch_verify(const TreeDev& tree, int32_t B, const int32_t* topk, in
                          const int32_t* tree_tok, int32_t* accept_len, int32_t* accept_path,
                          int32_t* bonus, int32_t* emitted, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+enum InitMode : int32_t { INIT_ZERO = 0, INIT_RANDOM = 1, INIT_PRIOR = 2 };
+hipError_t launch_init_m(int mode, void* M, int m_is64, int32_t B, int64_t V, int32_t k,
+                         const void* prior, int prior_is64, int prior_bcast, uint64_t seed,
+                         hipStream_t s);
 hipError_t launch_attn(const TreeDev& tree, int32_t B, int32_t Hq, int32_t Hkv, int is_bf16,
                        const void* q, const void* k_tree, const void* v_tree, const void* k_cache,
                        const void* v_cache, int64_t cap, const int32_t* prefix_len, float scale,

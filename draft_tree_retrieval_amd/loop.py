@@ -17,8 +17,9 @@ from . import tr
 
 class TRDecoder:
     def __init__(self, tree: tr.Tree, M, k_cache, v_cache, prefix_len, root_tok, Hq,
-                 V=None, stream=None):
+                 V=None, stream=None, update="all"):
         self.tree = tree
+        self.update = update          # "all" (the method) or "accepted" (its ablation)
         self.M, self.k_cache, self.v_cache = M, k_cache, v_cache
         self.prefix_len, self.root_tok = prefix_len, root_tok
         self.stream = stream
@@ -42,9 +43,15 @@ class TRDecoder:
                         out, self.ws, scale, self.stream)
 
     def step(self, logits, k_tree, v_tree):
-        tr.tr_step(self.tree, logits, self.M, self.tree_tok, self.root_tok, self.accept_len,
-                   self.accept_path, self.emitted, self.ws, k_tree, v_tree, self.k_cache,
-                   self.v_cache, self.prefix_len, self.topk, self.stream)
+        if self.update == "all":
+            tr.tr_step(self.tree, logits, self.M, self.tree_tok, self.root_tok, self.accept_len,
+                       self.accept_path, self.emitted, self.ws, k_tree, v_tree, self.k_cache,
+                       self.v_cache, self.prefix_len, self.topk, self.stream)
+        else:
+            tr.tr_step_ex(self.tree, logits, self.M, self.tree_tok, self.root_tok,
+                          self.accept_len, self.accept_path, self.emitted, self.ws, k_tree,
+                          v_tree, self.k_cache, self.v_cache, self.prefix_len, self.topk,
+                          self.update, self.stream)
 
     def device_flags(self):
         return tr.tr_read_device_status(self.ws, self.stream)

@@ -46,12 +46,17 @@ _SIGS = {
     "tr_verify": ([_P, _I32, _P, _I32, _P, _P, _P, _P, _P, _P], C.c_int),
     "tr_step": ([_P, _I32, _I64, _I32, _P, C.c_int, _P, C.c_int, _P, _P, _P, _P, _P, _I32, _I32,
                  C.c_int, _P, _P, _P, _P, _I64, _P, _P, _P, _SZ, _P], C.c_int),
+    "tr_step_ex": ([_P, _I32, _I64, _I32, _P, C.c_int, _P, C.c_int, _P, _P, _P, _P, _P, _I32,
+                    _I32, C.c_int, _P, _P, _P, _P, _I64, _P, _P, C.c_int, _P, _SZ, _P], C.c_int),
+    "tr_init_matrix": ([_I32, _I64, _I32, _P, C.c_int, C.c_int, _P, C.c_int, _I32, C.c_uint64,
+                        _P], C.c_int),
     "tr_profile_enable": ([_I32], C.c_int),
     "tr_profile_read": ([_P, _I32], _I32),
 }
 
 # tr_kernel_id
-KERNEL_NAMES = {1: "attn_prefix", 2: "attn_combine", 3: "topk", 4: "retrieve", 5: "verify", 6: "fill"}
+KERNEL_NAMES = {1: "attn_prefix", 2: "attn_combine", 3: "topk", 4: "retrieve", 5: "verify", 6: "fill",
+                7: "init"}
 
 
 class _LaunchTime(C.Structure):
@@ -204,20 +209,57 @@ def tr_verify(tree, topk, tree_tok, accept_len, accept_path, bonus, emitted, str
                             _stream(stream)))
 
 
+def _kv_shape(k_cache):
+    if k_cache is not None:
+        return k_cache.shape[1], k_cache.shape[2], k_cache.shape[3], _dt(k_cache)
+    return 0, 0, 0, TR_BFLOAT16
+
+
 def tr_step(tree, logits, M, tree_tok, root_tok, accept_len, accept_path, emitted, ws,
             k_tree=None, v_tree=None, k_cache=None, v_cache=None, prefix_len=None, topk_out=None,
             stream=None):
     B, T, V = logits.shape
-    if k_cache is not None:
-        Hkv, cap, d = k_cache.shape[1], k_cache.shape[2], k_cache.shape[3]
-        kv_dt = _dt(k_cache)
-    else:
-        Hkv, cap, d, kv_dt = 0, 0, 0, TR_BFLOAT16
+    Hkv, cap, d, kv_dt = _kv_shape(k_cache)
     _check(load().tr_step(tree.handle, B, V, tree.k, _ptr(logits), _dt(logits), _ptr(M), _dt(M),
                           _ptr(tree_tok), _ptr(root_tok), _ptr(accept_len), _ptr(accept_path),
                           _ptr(emitted), Hkv, d, kv_dt, _ptr(k_tree), _ptr(v_tree), _ptr(k_cache),
                           _ptr(v_cache), cap, _ptr(prefix_len), _ptr(topk_out), _ptr(ws),
                           ws.numel(), _stream(stream)))
+
+
+# tr_update_mode
+TR_UPDATE_ALL, TR_UPDATE_ACCEPTED = 0, 1
+_UPDATE_MODES = {"all": TR_UPDATE_ALL, "accepted": TR_UPDATE_ACCEPTED}
+
+
+def tr_step_ex(tree, logits, M, tree_tok, root_tok, accept_len, accept_path, emitted, ws,
+               k_tree=None, v_tree=None, k_cache=None, v_cache=None, prefix_len=None,
+               topk_out=None, update="all", stream=None):
+    """tr_step with the update chosen by name: "all" or "accepted"."""
+    mode = _UPDATE_MODES[update] if isinstance(update, str) else int(update)
+    B, T, V = logits.shape
+    Hkv, cap, d, kv_dt = _kv_shape(k_cache)
+    _check(load().tr_step_ex(tree.handle, B, V, tree.k, _ptr(logits), _dt(logits), _ptr(M),
+                             _dt(M), _ptr(tree_tok), _ptr(root_tok), _ptr(accept_len),
+                             _ptr(accept_path), _ptr(emitted), Hkv, d, kv_dt, _ptr(k_tree),
+                             _ptr(v_tree), _ptr(k_cache), _ptr(v_cache), cap, _ptr(prefix_len),
+                             _ptr(topk_out), mode, _ptr(ws), ws.numel(), _stream(stream)))
+
+
+# tr_init_mode
+TR_INIT_ZERO, TR_INIT_RANDOM, TR_INIT_PRIOR = 0, 1, 2
+_INIT_MODES = {"zero": TR_INIT_ZERO, "random": TR_INIT_RANDOM, "prior": TR_INIT_PRIOR}
+
+
+def tr_init_matrix(M, mode="zero", prior=None, seed=0, stream=None):
+    """Fills M [B][V][k] on the device: "zero", "random" (SplitMix64 ids,
+    seeded) or "prior" (prior [1 or B][V][k] copied into every slot)."""
+    B, V, k = M.shape
+    m = _INIT_MODES[mode] if isinstance(mode, str) else int(mode)
+    pb = prior.shape[0] if prior is not None else 0
+    _check(load().tr_init_matrix(B, V, k, _ptr(M), _dt(M), m, _ptr(prior),
+                                 _dt(prior) if prior is not None else TR_INT32, pb,
+                                 int(seed) & ((1 << 64) - 1), _stream(stream)))
 
 
 def tr_profile_enable(on=True):

@@ -213,6 +213,60 @@ tr_status tr_step(const tr_tree* t, int32_t B, int64_t V, int32_t k, const void*
                   void* k_cache, void* v_cache, int64_t cap, int32_t* prefix_len, int32_t* topk_out,
                   void* ws, size_t ws_bytes, void* stream);
 
+/* Which nodes recycle their top-k into M (Token Recycling, Experiment,
+ * ablation of the update: every draft token against the accepted ones
+ * only; every draft token gives the longer mean accepted length and is the
+ * method's default). */
+typedef enum {
+  TR_UPDATE_ALL = 0,        /* every node of the tree (tr_step) */
+  TR_UPDATE_ACCEPTED = 1    /* the accepted path only, root included:
+                               M[tok path[i]] = topk[path[i]], i = 0..L; on a
+                               repeated token the deeper node wins */
+} tr_update_mode;
+
+/* tr_step with a choice of update (tr_update_mode); everything else,
+ * including arguments, errors and the retrieval of the next tree from the
+ * updated M, as tr_step.  An unknown mode is TR_ERR_INVALID_ARGUMENT. */
+tr_status tr_step_ex(const tr_tree* t, int32_t B, int64_t V, int32_t k, const void* logits,
+                     tr_dtype l_dtype, void* M, tr_dtype m_dtype, int32_t* tree_tok,
+                     int32_t* root_tok, int32_t* accept_len, int32_t* accept_path,
+                     int32_t* emitted, int32_t Hkv, int32_t d, tr_dtype kv_dtype,
+                     const void* k_tree, const void* v_tree, void* k_cache, void* v_cache,
+                     int64_t cap, int32_t* prefix_len, int32_t* topk_out, tr_update_mode mode,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Initial contents of M (Token Recycling, Method, first module: a hot start
+ * inherits the matrix left by earlier inference instead of an empty one;
+ * Experiment, initialisation ablation: all-zero, random ids, and prior
+ * matrices, fixed, shuffled or inherited).  Not part of a step: called once
+ * before decoding starts.
+ *   M [B][V][k] in m_dtype (int32 or int64), device memory, 16-byte aligned.
+ *   TR_INIT_ZERO    every id 0.
+ *   TR_INIT_RANDOM  id e (flat index over [B][V][k]) = floor(u_e * V), u_e =
+ *                   (z_e >> 32) / 2^32, z_e = output e of SplitMix64 seeded
+ *                   with seed: the mix of seed + (e+1) * 0x9E3779B97F4A7C15
+ *                   (Steele, Lea and Flood, OOPSLA 2014).
+ *   TR_INIT_PRIOR   M[b] = prior[prior_batches == 1 ? 0 : b]; prior is
+ *                   [prior_batches][V][k] in prior_dtype (int32 or int64),
+ *                   device memory, 16-byte aligned, prior_batches 1 (one
+ *                   prior for every sequence: fixed or shuffled priors) or B
+ *                   (each sequence its own: inherited).  Ids are converted to
+ *                   m_dtype as they are; ids outside [0, V) are flagged by
+ *                   the retrieval that reads them.  prior must not overlap M.
+ * prior and prior_dtype are ignored by the other modes, seed by all but
+ * RANDOM.  Errors: TR_ERR_INVALID_ARGUMENT for a null or misaligned tensor,
+ * B, V or k below 1, V above 2^31-1, an unknown mode or prior_batches not 1
+ * or B; TR_ERR_UNSUPPORTED for other dtypes.  Launches one kernel on stream. */
+typedef enum {
+  TR_INIT_ZERO = 0,
+  TR_INIT_RANDOM = 1,
+  TR_INIT_PRIOR = 2
+} tr_init_mode;
+
+tr_status tr_init_matrix(int32_t B, int64_t V, int32_t k, void* M, tr_dtype m_dtype,
+                         tr_init_mode mode, const void* prior, tr_dtype prior_dtype,
+                         int32_t prior_batches, uint64_t seed, void* stream);
+
 /* ------------------------------------------------------------------------
  * Profiling aid (outside the TR step).  While enabled, each kernel the
  * library launches is bracketed by two HIP events recorded on the stream it
@@ -230,7 +284,8 @@ typedef enum {
   TR_KERNEL_TOPK = 3,          /* tr_step / tr_update_topk (top-k and tail) */
   TR_KERNEL_RETRIEVE = 4,      /* tr_retrieve */
   TR_KERNEL_VERIFY = 5,        /* tr_verify */
-  TR_KERNEL_FILL = 6           /* tr_workspace_init */
+  TR_KERNEL_FILL = 6,          /* tr_workspace_init */
+  TR_KERNEL_INIT = 7           /* tr_init_matrix */
 } tr_kernel_id;
 
 typedef struct {

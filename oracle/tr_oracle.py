@@ -302,6 +302,67 @@ def update(M: np.ndarray, tok: np.ndarray, topk: np.ndarray) -> None:
         M[tok[n], :] = topk[n, : M.shape[1]]
 
 
+def update_accepted(M: np.ndarray, tok: np.ndarray, topk: np.ndarray, path) -> None:
+    """The ablation that updates with accepted tokens only: M[x~_i] =
+    argtopk(p~_{i+1}) for the nodes of the accepted path (root included),
+    in path order ([TR-en] Experiment, ablations: all draft tokens give a
+    higher mean accepted length than only the accepted ones; [TR-zh] same
+    section).  READING: "accepted tokens" are the root and the accepted
+    drafts, the nodes whose top-k the verification pass used for the
+    emitted tokens; on a repeated token the later (deeper) node wins, as
+    in update().
+    """
+    for n in path:
+        M[tok[n], :] = topk[n, : M.shape[1]]
+
+
+# --------------------------------------------------------------------------
+# initial contents of M
+# --------------------------------------------------------------------------
+_GAMMA = 0x9E3779B97F4A7C15
+_MASK64 = (1 << 64) - 1
+
+
+def splitmix64(seed: int, e) -> np.ndarray:
+    """Output e of SplitMix64 seeded with seed (Steele, Lea and Flood,
+    "Fast splittable pseudorandom number generators", OOPSLA 2014, with the
+    finaliser of Vigna's published splitmix64): the state after e+1 steps,
+    seed + (e+1)*gamma mod 2^64, through the xor-shift-multiply mixer.
+    Vectorised over e in uint64, whose products wrap mod 2^64."""
+    e = np.asarray(e, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        z = np.uint64(seed & _MASK64) + (e + np.uint64(1)) * np.uint64(_GAMMA)
+        z = (z ^ (z >> np.uint64(30))) * np.uint64(0xBF58476D1CE4E5B9)
+        z = (z ^ (z >> np.uint64(27))) * np.uint64(0x94D049BB133111EB)
+        return z ^ (z >> np.uint64(31))
+
+
+def init_matrix(B: int, V: int, k: int, mode: str, prior=None, seed: int = 0) -> np.ndarray:
+    """Initial M [B][V][k] ([TR-en] Method, first module: a hot start
+    inherits the matrix of earlier inference rather than an empty one;
+    [TR-en] Experiment, initialisation ablation: all-zero, random, and
+    fixed / shuffled / inherited priors).
+
+    READING: "zero" is every id 0; "random" draws every id uniformly from
+    the vocabulary, id e (flat over [B][V][k]) = floor(u*V) with u the high
+    32 bits of SplitMix64 output e over 2^32; "prior" copies a prior matrix
+    into every sequence's slot (one prior for all sequences, or one each),
+    which covers the fixed, shuffled and inherited settings: they differ
+    only in where the prior comes from.
+    """
+    if mode == "zero":
+        return np.zeros((B, V, k), dtype=np.int64)
+    if mode == "random":
+        z = splitmix64(seed, np.arange(B * V * k, dtype=np.uint64))
+        u = z >> np.uint64(32)
+        return ((u * np.uint64(V)) >> np.uint64(32)).astype(np.int64).reshape(B, V, k)
+    if mode == "prior":
+        prior = np.asarray(prior, dtype=np.int64).reshape(-1, V, k)
+        assert prior.shape[0] in (1, B)
+        return np.array([prior[0 if prior.shape[0] == 1 else b] for b in range(B)])
+    raise ValueError(mode)
+
+
 # --------------------------------------------------------------------------
 # a7: commit of the accepted path
 # --------------------------------------------------------------------------
@@ -338,7 +399,7 @@ class StepResult:
 
 def step_after_forward(t: Template, M: np.ndarray, tok: np.ndarray, logits: np.ndarray, k: int,
                        k_cache=None, v_cache=None, k_tree=None, v_tree=None,
-                       prefix_len: int = 0):
+                       prefix_len: int = 0, update_mode: str = "all"):
     """The part of one TR step after the target's forward pass, in the order
     the pages give ([Blog] "why recycling" loop: query M, build the tree,
     verify, accept the longest path, recycle every node's top-k):
@@ -349,11 +410,15 @@ def step_after_forward(t: Template, M: np.ndarray, tok: np.ndarray, logits: np.n
     The tree of this step was retrieved from M before the update ([Blog]
     workflow step 2: the old matrix builds the tree, the update serves the
     next round).  Mutates M (and the caches when given).  Returns the result
-    and the new prefix length.
+    and the new prefix length.  update_mode "accepted" takes the ablation
+    that recycles only the accepted path's top-k (update_accepted).
     """
     top = topk_rows(logits, k)
     v = verify(t, tok, top[:, 0])
-    update(M, tok, top)
+    if update_mode == "accepted":
+        update_accepted(M, tok, top, v.path)
+    else:
+        update(M, tok, top)
     if k_cache is not None:
         prefix_len = commit(k_cache, v_cache, k_tree, v_tree, prefix_len, v.path)
     nxt = retrieve(t, M, v.bonus)

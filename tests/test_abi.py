@@ -132,6 +132,21 @@ def test_host_checks_launch_nothing(tr):
     assert lib.tr_step(h, 1, 16, 3, fake, tr.TR_BFLOAT16, fake, tr.TR_INT32, fake, fake, fake, None,
                        None, 2, 128, tr.TR_BFLOAT16, fake, fake, fake, None, 64, fake, None, ws,
                        1 << 30, None) == tr.TR_ERR_INVALID_ARGUMENT               # v_cache missing
+    assert lib.tr_step_ex(h, 1, 16, 3, fake, tr.TR_BFLOAT16, fake, tr.TR_INT32, fake, fake, fake,
+                          None, None, 0, 0, tr.TR_BFLOAT16, None, None, None, None, 0, None, None,
+                          7, ws, 1 << 30, None) == tr.TR_ERR_INVALID_ARGUMENT    # unknown mode
+    # initial M: bad mode, prior count, misaligned prior, dtype, sizes
+    init = lambda B, V, k, M, mdt, mode, prior, pdt, pb: lib.tr_init_matrix(
+        B, V, k, M, mdt, mode, prior, pdt, pb, 0, None)
+    assert init(2, 16, 8, fake, tr.TR_INT32, 3, None, 0, 0) == tr.TR_ERR_INVALID_ARGUMENT
+    assert init(2, 16, 8, fake, tr.TR_INT32, tr.TR_INIT_PRIOR, fake, tr.TR_INT32, 3) == tr.TR_ERR_INVALID_ARGUMENT
+    assert init(2, 16, 8, fake, tr.TR_INT32, tr.TR_INIT_PRIOR, None, tr.TR_INT32, 1) == tr.TR_ERR_INVALID_ARGUMENT
+    assert init(2, 16, 8, fake, tr.TR_INT32, tr.TR_INIT_PRIOR, C.c_void_p((1 << 24) + 4),
+                tr.TR_INT32, 1) == tr.TR_ERR_INVALID_ARGUMENT
+    assert init(2, 16, 8, fake, tr.TR_INT32, tr.TR_INIT_PRIOR, fake, tr.TR_FLOAT32, 1) == tr.TR_ERR_UNSUPPORTED
+    assert init(2, 16, 8, fake, tr.TR_FLOAT32, tr.TR_INIT_ZERO, None, 0, 0) == tr.TR_ERR_UNSUPPORTED
+    assert init(0, 16, 8, fake, tr.TR_INT32, tr.TR_INIT_ZERO, None, 0, 0) == tr.TR_ERR_INVALID_ARGUMENT
+    assert init(1, 1 << 31, 8, fake, tr.TR_INT32, tr.TR_INIT_ZERO, None, 0, 0) == tr.TR_ERR_INVALID_ARGUMENT
     assert lib.tr_verify(h, 1, None, 3, fake, fake, None, fake, None, None) == tr.TR_ERR_INVALID_ARGUMENT
     assert "null" in tr.load().tr_last_error().decode()
 

@@ -291,6 +291,80 @@ def test_attention_siblings_and_determinism(tr, dtype):
         assert all(changed) if dtype == torch.float32 else np.mean(changed) >= 0.9
 
 
+# ------------------------------------------------------------------ accepted-only update
+@pytest.mark.parametrize("m_dtype", [torch.int32, torch.int64])
+def test_step_ex_accepted_only_duplicates(tr, m_dtype):
+    # Tiny vocabularies: tokens repeat along the accepted path and off it, so
+    # a node off the path often carries a path token with a higher index
+    # (the all-nodes update would let it win; this one must not).
+    g = torch.Generator().manual_seed(21)
+    rng = np.random.default_rng(21)
+    for levels in RAND_LEVELS:
+        t = otree(levels)
+        T, D = t.n_nodes, t.max_depth
+        widest = max((max(l) for l in levels), default=0)
+        for V, k, B in ((5, 3, 4), (9, 8, 3), (300, 8, 2)):
+            if k < widest:
+                continue
+            tree = tr.Tree.from_levels(levels, k)
+            M = torch.randint(0, V, (B, V, k), generator=g).to(m_dtype)
+            root = torch.randint(0, V, (B,), generator=g).to(torch.int32)
+            ws = ws_for(tr, tree, B, V, k)
+            dM, droot = M.to(DEV), root.to(DEV)
+            tok = torch.empty((B, T), dtype=torch.int32, device=DEV)
+            tr.tr_retrieve(tree, dM, droot, tok, ws)
+            tok_h = tok.cpu().numpy().astype(np.int64)
+            z = torch.randn((B, T, V), generator=g)
+            for b in range(B):                      # plant acceptance on most edges
+                for n in range(1, T):
+                    if rng.random() < 0.8:
+                        z[b, t.parent[n], tok_h[b, n]] = 20.0 + float(rng.random())
+            L = torch.empty((B,), dtype=torch.int32, device=DEV)
+            path = torch.empty((B, D + 1), dtype=torch.int32, device=DEV)
+            em = torch.empty((B, D + 1), dtype=torch.int32, device=DEV)
+            tr.tr_step_ex(tree, z.to(DEV), dM, tok, droot, L, path, em, ws, update="accepted")
+            for b in range(B):
+                Mo = M[b].numpy().astype(np.int64).copy()
+                res, _ = O.step_after_forward(t, Mo, tok_h[b], z[b].numpy(), k,
+                                              update_mode="accepted")
+                assert (dM[b].cpu().numpy().astype(np.int64) == Mo).all(), (levels, V, b)
+                assert int(L[b]) == res.verdict.accept_len
+                assert path[b, :res.verdict.accept_len + 1].cpu().tolist() == res.verdict.path.tolist()
+                assert tok[b].cpu().numpy().tolist() == res.next_tok.tolist()
+                assert int(droot[b]) == res.verdict.bonus
+            assert tr.tr_read_device_status(ws) == 0
+
+
+# ------------------------------------------------------------------ initial M
+@pytest.mark.parametrize("m_dtype", [torch.int32, torch.int64])
+def test_init_matrix_parity(tr, m_dtype):
+    # odd V*k (one id per store) and V*k % 4 == 0 (16-byte groups), one
+    # sequence and several, one prior for all and one per sequence
+    g = torch.Generator().manual_seed(31)
+    for B, V, k in ((1, 7, 3), (3, 1001, 5), (5, 13, 1), (2, 32000, 8), (4, 6, 2)):
+        M = torch.full((B, V, k), -7, dtype=m_dtype, device=DEV)
+        tr.tr_init_matrix(M, "zero")
+        assert (M == 0).all()
+        for seed in (0, 12345, 2 ** 64 - 1):
+            tr.tr_init_matrix(M, "random", seed=seed)
+            want = O.init_matrix(B, V, k, "random", seed=seed)
+            assert np.array_equal(M.cpu().numpy().astype(np.int64), want), (B, V, k, seed)
+        for p_dtype in (torch.int32, torch.int64):
+            for pb in sorted({1, B}):
+                prior = torch.randint(0, V, (pb, V, k), generator=g).to(p_dtype)
+                tr.tr_init_matrix(M, "prior", prior.to(DEV))
+                want = O.init_matrix(B, V, k, "prior", prior.numpy())
+                assert np.array_equal(M.cpu().numpy().astype(np.int64), want), (B, V, k, pb)
+
+
+def test_init_matrix_random_full_size(tr):
+    # the large-vocabulary batch: 32 sequences of 128256 x 8 int32 ids
+    B, V, k = 32, 128256, 8
+    M = torch.empty((B, V, k), dtype=torch.int32, device=DEV)
+    tr.tr_init_matrix(M, "random", seed=2024)
+    assert np.array_equal(M.cpu().numpy().astype(np.int64), O.init_matrix(B, V, k, "random", seed=2024))
+
+
 # ------------------------------------------------------------------ step + commit
 def test_step_commit_and_cache_full_flag(tr):
     levels = RAND_LEVELS[1]

@@ -42,13 +42,14 @@ def attn_ok(t, out, q, kt, vt, kc, vc, P, dtype):
     return err, err <= 2e-2
 
 
-def run_loop(tr, w, steps, track, attn_steps):
+def run_loop(tr, w, steps, track, attn_steps, update="all"):
     from draft_tree_retrieval_amd.loop import TRDecoder
     t = O.template_from_levels(w.levels)
     st = W.initial_state(w, DEV)
     host = st.to("cpu")
     tree = tr.Tree.from_levels(w.levels, w.k)
-    dec = TRDecoder(tree, st.M, st.k_cache, st.v_cache, st.prefix_len, st.root, Hq=w.Hq)
+    dec = TRDecoder(tree, st.M, st.k_cache, st.v_cache, st.prefix_len, st.root, Hq=w.Hq,
+                    update=update)
     # oracle state of the tracked sequences
     oM = {b: host.M[b].numpy().astype(np.int64).copy() for b in track}
     okc = {b: host.k_cache[b].float().numpy().copy() for b in track}
@@ -84,7 +85,7 @@ def run_loop(tr, w, steps, track, attn_steps):
                                                         dec.prefix_len))
         for b in track:
             res, oP[b] = O.step_after_forward(t, oM[b], otok[b], zl[b], w.k, okc[b], ovc[b],
-                                              kth[b], vth[b], oP[b])
+                                              kth[b], vth[b], oP[b], update_mode=update)
             assert (gk[b] == res.topk).all(), f"step {s} seq {b}: top-k differs"
             v = res.verdict
             assert int(gL[b]) == v.accept_len, f"step {s} seq {b}: accept length"
@@ -120,6 +121,17 @@ def test_vicuna13b_full(tr):
 def test_codellama34b_full(tr):
     w = W.WORKLOADS["codellama34b"]
     run_loop(tr, w, w.steps, [0], {0, 300, w.steps - 1})
+
+
+def test_tiny_accepted_only_update(tr):
+    # the ablation that recycles the accepted path only (tr_step_ex)
+    w = W.WORKLOADS["tiny"]
+    run_loop(tr, w, w.steps, [0], {0}, update="accepted")
+
+
+def test_vicuna7b_accepted_only_update(tr):
+    w = W.WORKLOADS["vicuna7b"]
+    run_loop(tr, w, 64, [0], {0, 63}, update="accepted")
 
 
 def test_largevocab_full_sampled_sequences(tr):

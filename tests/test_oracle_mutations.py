@@ -50,6 +50,41 @@ def _update_accepted_only_root(M, tok, topk):
     M[tok[0], :] = topk[0, : M.shape[1]]
 
 
+def _accepted_shallow_wins(M, tok, topk, path):
+    for n in reversed(list(path)):
+        M[tok[n], :] = topk[n, : M.shape[1]]
+
+
+def _accepted_without_root(M, tok, topk, path):
+    for n in list(path)[1:]:
+        M[tok[n], :] = topk[n, : M.shape[1]]
+
+
+def _accepted_is_all(M, tok, topk, path):
+    ORIG["update"](M, tok, topk)
+
+
+def _splitmix_counter_from_zero(seed, e):
+    # state seed + e*gamma instead of seed + (e+1)*gamma
+    return ORIG["splitmix64"](seed - 0x9E3779B97F4A7C15, e)
+
+
+def _splitmix_wrong_shift(seed, e):
+    e = np.asarray(e, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        z = np.uint64(seed) + (e + np.uint64(1)) * np.uint64(0x9E3779B97F4A7C15)
+        z = (z ^ (z >> np.uint64(31))) * np.uint64(0xBF58476D1CE4E5B9)
+        z = (z ^ (z >> np.uint64(27))) * np.uint64(0x94D049BB133111EB)
+        return z ^ (z >> np.uint64(31))
+
+
+def _init_low_word(B, V, k, mode, prior=None, seed=0):
+    if mode != "random":
+        return ORIG["init_matrix"](B, V, k, mode, prior, seed)
+    z = O.splitmix64(seed, np.arange(B * V * k, dtype=np.uint64)) & np.uint64(0xFFFFFFFF)
+    return ((z * np.uint64(V)) >> np.uint64(32)).astype(np.int64).reshape(B, V, k)
+
+
 def _retrieve_rank_off(t, M, root):
     tok = np.empty(t.n_nodes, dtype=np.int64)
     tok[0] = root
@@ -77,7 +112,8 @@ def _attention_wrong_group(t, q, kt, vt, kc, vc, P_, scale=None):
 
 
 ORIG = {name: getattr(O, name) for name in
-        ("verify", "topk_row", "update", "retrieve", "ancestor_mask", "tree_attention")}
+        ("verify", "topk_row", "update", "update_accepted", "retrieve", "ancestor_mask",
+         "tree_attention", "splitmix64", "init_matrix")}
 
 CASES = [
     ("verify", _bonus_from_parent, [P.test_worked_example_verify_and_update,
@@ -87,6 +123,14 @@ CASES = [
     ("topk_row", _topk_ties_high_id, [P.test_topk_matches_full_sort_with_ties]),
     ("update", _update_first_writer, [P.test_update_last_writer_wins_brute_force]),
     ("update", _update_accepted_only_root, [P.test_worked_example_verify_and_update]),
+    ("update_accepted", _accepted_shallow_wins, [P.test_update_accepted_brute_force]),
+    ("update_accepted", _accepted_without_root, [P.test_worked_example_accepted_only_update,
+                                                 P.test_update_accepted_brute_force]),
+    ("update_accepted", _accepted_is_all, [P.test_worked_example_accepted_only_update,
+                                           P.test_update_accepted_brute_force]),
+    ("splitmix64", _splitmix_counter_from_zero, [P.test_splitmix64_published_outputs]),
+    ("splitmix64", _splitmix_wrong_shift, [P.test_splitmix64_published_outputs]),
+    ("init_matrix", _init_low_word, [P.test_init_random_power_of_two_vocab_takes_top_bits]),
     ("retrieve", _retrieve_rank_off, [P.test_worked_example_retrieval_gives_merged_sequence,
                                       P.test_retrieve_matches_recursive_definition]),
     ("ancestor_mask", _mask_without_self, [P.test_worked_example_mask,

@@ -297,6 +297,116 @@ def test_update_last_writer_wins_brute_force():
             assert (M[v] == want).all()
 
 
+def test_worked_example_accepted_only_update():
+    # The ablation that recycles only the accepted tokens: of the page's
+    # post-step rows, those of the accepted path guest -> speaker -> at are
+    # written; speak (rejected) keeps its old row, event/for/ing stay empty.
+    ex, ids, M, logits = load_example()
+    t = O.template_from_levels(ex["levels"])
+    tok = O.retrieve(t, M, ids[ex["root"]])
+    res, _ = O.step_after_forward(t, M, tok, logits, ex["k"], update_mode="accepted")
+    e = ex["expected"]
+    assert res.verdict.path.tolist() == e["path"]
+    for name in ("guest", "speaker", "at"):
+        assert [ex["vocab"][x] for x in M[ids[name]]] == e["M_post"][name], name
+    assert [ex["vocab"][x] for x in M[ids["speak"]]] == ex["M_pre"]["speak"]
+    for name in ex["vocab"]:
+        if name not in ex["M_pre"]:
+            assert (M[ids[name]] == ids["pad"]).all(), name
+    assert [ex["vocab"][x] for x in res.next_tok] == e["next_tree"]
+
+
+def test_update_accepted_brute_force():
+    # Expected rows from the definitions written another way: a node is
+    # accepted when every edge above it carries its parent's argmax; best is
+    # the deepest accepted node (lowest index on ties); the writers of token
+    # v are the ancestors of best (itself included) carrying v, and the
+    # deepest of them wins.
+    rng = np.random.default_rng(18)
+    for trial in range(300):
+        levels = random_levels(rng, 3)
+        t = O.template_from_levels(levels)
+        T, V, k = t.n_nodes, 5, 3
+        z = rng.standard_normal((T, V))
+        arg = np.argmax(z, axis=1)
+        tok = rng.integers(0, V, size=T)
+        for n in range(1, T):                       # accept most edges
+            if rng.random() < 0.7:
+                tok[n] = arg[t.parent[n]]
+        M = rng.integers(0, V, size=(V, k))
+        M0 = M.copy()
+        O.step_after_forward(t, M, tok.copy(), z, k, update_mode="accepted")
+
+        def chain(n):
+            out = [n]
+            while out[-1] != 0:
+                out.append(int(t.parent[out[-1]]))
+            return out[::-1]
+
+        acc = [n for n in range(T) if all(tok[c] == arg[t.parent[c]] for c in chain(n)[1:])]
+        best = min(acc, key=lambda n: (-len(chain(n)), n))
+        on_path = chain(best)
+        top = np.argsort(-z, axis=1, kind="stable")[:, :k]
+        for v in range(V):
+            writers = [n for n in on_path if tok[n] == v]
+            want = top[writers[-1]] if writers else M0[v]
+            assert (M[v] == want).all(), (trial, v)
+
+
+def test_update_accepted_equals_update_on_a_fully_accepted_chain():
+    # a chain tree whose every draft is accepted: the path is the whole tree
+    rng = np.random.default_rng(19)
+    for _ in range(50):
+        n, V, k = int(rng.integers(1, 8)), 6, 3
+        t = O.template_from_levels([[1]] * (n - 1))
+        z = rng.standard_normal((n, V))
+        tok = np.empty(n, dtype=np.int64)
+        tok[0] = rng.integers(0, V)
+        tok[1:] = np.argmax(z, axis=1)[:-1]
+        Ma = rng.integers(0, V, size=(V, k))
+        Mb = Ma.copy()
+        ra, _ = O.step_after_forward(t, Ma, tok.copy(), z, k)
+        rb, _ = O.step_after_forward(t, Mb, tok.copy(), z, k, update_mode="accepted")
+        assert ra.verdict.accept_len == n - 1
+        assert (Ma == Mb).all() and (ra.next_tok == rb.next_tok).all()
+
+
+# ---------------------------------------------------------------- initial M
+def test_splitmix64_published_outputs():
+    # the first three outputs of SplitMix64 from state 0, as printed with
+    # the generator's published reference code
+    assert [int(x) for x in O.splitmix64(0, [0, 1, 2])] == [
+        0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+
+
+def test_init_random_power_of_two_vocab_takes_top_bits():
+    # floor(u * 2^m / 2^32) with u the high word is the top m bits of the draw
+    for m in (1, 8, 13):
+        M = O.init_matrix(2, 2 ** m, 3, "random", seed=77)
+        z = O.splitmix64(77, np.arange(2 * 2 ** m * 3, dtype=np.uint64))
+        assert (M.reshape(-1) == (z >> np.uint64(64 - m)).astype(np.int64)).all()
+
+
+def test_init_random_is_uniform_over_the_vocabulary():
+    V, n = 7, 7 * 3 * 4000
+    M = O.init_matrix(4, V, 3 * 1000, "random", seed=3)
+    counts = np.bincount(M.reshape(-1), minlength=V)
+    assert M.min() >= 0 and M.max() < V and counts.sum() == n
+    chi2 = float(((counts - n / V) ** 2 / (n / V)).sum())
+    assert chi2 < 22.5                  # 6 degrees of freedom, p = 0.001
+    assert not (O.init_matrix(4, V, 3000, "random", seed=4) == M).all()
+
+
+def test_init_zero_and_prior():
+    assert (O.init_matrix(3, 5, 2, "zero") == 0).all()
+    rng = np.random.default_rng(5)
+    one = rng.integers(0, 50, size=(1, 50, 4))
+    M = O.init_matrix(3, 50, 4, "prior", one)
+    assert all((M[b] == one[0]).all() for b in range(3))
+    each = rng.integers(0, 50, size=(3, 50, 4))
+    assert (O.init_matrix(3, 50, 4, "prior", each) == each).all()
+
+
 # ---------------------------------------------------------------- attention
 def attention_per_path(t, q, kt, vt, kc, vc, P, scale):
     """Textbook attention for one node at a time: its key sequence is the
