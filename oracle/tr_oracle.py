@@ -252,6 +252,7 @@ class Verdict:
     path: np.ndarray         # node ids root -> best, length L+1
     bonus: int               # target's token after the last accepted node
     emitted: np.ndarray      # tokens committed this step: accepted drafts then bonus
+    margin: float = math.inf  # sampling only: closest distance of a uniform to its threshold
 
 
 def verify(t: Template, tok: np.ndarray, greedy: np.ndarray) -> Verdict:
@@ -283,6 +284,81 @@ def verify(t: Template, tok: np.ndarray, greedy: np.ndarray) -> Verdict:
     bonus = int(greedy[best])
     emitted = np.concatenate([tok[path[1:]], [bonus]]).astype(np.int64)
     return Verdict(L, path, bonus, emitted)
+
+
+def softmax_rows(logits, temperature: float) -> np.ndarray:
+    """p = softmax(z / temperature) per row, float64."""
+    z = np.asarray(logits, dtype=np.float64) / float(temperature)
+    z = z - z.max(axis=-1, keepdims=True)
+    e = np.exp(z)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def draw(dist: np.ndarray, r: float):
+    """Inverse-CDF draw: the smallest id whose cumulative probability (ids
+    in increasing order) exceeds r in [0, 1).  Returns (id, margin), margin
+    = distance of r to the nearer end of that id's interval.  READING: the
+    pages sample without naming a method; this one lets a caller's uniform
+    decide the draw."""
+    c = np.cumsum(dist)
+    x = int(np.searchsorted(c, r, side="right"))
+    nz = np.flatnonzero(dist > 0)
+    x = min(x, int(nz[-1]))           # r within rounding of the total mass
+    lo = c[x - 1] if x > 0 else 0.0
+    return x, min(r - lo, c[x] - r)
+
+
+def verify_sample(t: Template, tok: np.ndarray, logits: np.ndarray, temperature: float,
+                  uniforms: np.ndarray) -> Verdict:
+    """Stochastic tree verification ([SD] acceptance rule, residual
+    resampling and the bonus token after a fully accepted draft; [TR-en]
+    Experiment: TR is also run with sampling).
+
+    p_n = softmax(z_n / temperature) is the target's distribution after node
+    n.  READING (the pages give the rule for one chain of drafts): TR's
+    drafts are read from M, not sampled, so each draft's q is a point mass
+    on its token.  The walk starts at the root; at node n the children are
+    tried in rank order as the drafts of the next position.  With the
+    current residual r (initially p_n), child c with token x is accepted
+    when u_c < min(1, r(x) / q(x)) = r(x); then the walk moves to c.  Else
+    r becomes norm(max(0, r - q)) (r with x removed, renormalised) and the
+    next child is tried.  When no child is accepted (a leaf has none) the
+    bonus is drawn from r with the node's second uniform, and the walk ends.
+
+    uniforms[n][0] decides node n's own acceptance as a child; uniforms[n][1]
+    the draw at n if the walk ends there.  Returns the path root -> stop
+    node, L = its depth, the bonus and the emitted tokens, as verify().
+    """
+    p = softmax_rows(logits, temperature)
+    V = p.shape[1]
+    margin = math.inf
+    n, path = 0, [0]
+    while True:
+        r = p[n].copy()
+        nxt = None
+        for c in t.children(n):
+            x = int(tok[c])
+            if not (0 <= x < V):
+                continue                      # READING: a token outside the vocabulary is rejected
+            a = min(1.0, r[x])                # q(x) = 1
+            u = float(uniforms[c][0])
+            margin = min(margin, abs(u - a))
+            if u < a:
+                nxt = c
+                break
+            q = np.zeros(V)
+            q[x] = 1.0
+            r = np.maximum(0.0, r - q)
+            r = r / r.sum()
+        if nxt is None:
+            bonus, m = draw(r, float(uniforms[n][1]))
+            margin = min(margin, m)
+            break
+        n = nxt
+        path.append(n)
+    path = np.array(path, dtype=np.int64)
+    emitted = np.concatenate([tok[path[1:]], [bonus]]).astype(np.int64)
+    return Verdict(len(path) - 1, path, bonus, emitted, margin)
 
 
 # --------------------------------------------------------------------------
@@ -399,7 +475,8 @@ class StepResult:
 
 def step_after_forward(t: Template, M: np.ndarray, tok: np.ndarray, logits: np.ndarray, k: int,
                        k_cache=None, v_cache=None, k_tree=None, v_tree=None,
-                       prefix_len: int = 0, update_mode: str = "all"):
+                       prefix_len: int = 0, update_mode: str = "all",
+                       temperature: float = 0.0, uniforms=None):
     """The part of one TR step after the target's forward pass, in the order
     the pages give ([Blog] "why recycling" loop: query M, build the tree,
     verify, accept the longest path, recycle every node's top-k):
@@ -411,10 +488,15 @@ def step_after_forward(t: Template, M: np.ndarray, tok: np.ndarray, logits: np.n
     workflow step 2: the old matrix builds the tree, the update serves the
     next round).  Mutates M (and the caches when given).  Returns the result
     and the new prefix length.  update_mode "accepted" takes the ablation
-    that recycles only the accepted path's top-k (update_accepted).
+    that recycles only the accepted path's top-k (update_accepted).  A
+    temperature above 0 verifies by sampling (verify_sample, with the given
+    uniforms [T][2]); the update still recycles each node's top-k.
     """
     top = topk_rows(logits, k)
-    v = verify(t, tok, top[:, 0])
+    if temperature > 0:
+        v = verify_sample(t, tok, logits, temperature, uniforms)
+    else:
+        v = verify(t, tok, top[:, 0])
     if update_mode == "accepted":
         update_accepted(M, tok, top, v.path)
     else:

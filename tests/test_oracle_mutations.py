@@ -85,6 +85,38 @@ def _init_low_word(B, V, k, mode, prior=None, seed=0):
     return ((z * np.uint64(V)) >> np.uint64(32)).astype(np.int64).reshape(B, V, k)
 
 
+def _sampler(renormalise=True, residual_draw=True, swap_uniforms=False):
+    # a compact walk with one of its parts done wrong
+    def run(t, tok, logits, temperature, uniforms):
+        p = O.softmax_rows(logits, temperature)
+        V = p.shape[1]
+        ua, ud = (1, 0) if swap_uniforms else (0, 1)
+        n, path = 0, [0]
+        while True:
+            r, nxt = p[n].copy(), None
+            for c in t.children(n):
+                x = int(tok[c])
+                if uniforms[c][ua] < min(1.0, r[x]):
+                    nxt = c
+                    break
+                if renormalise:
+                    r[x] = 0.0
+                    r = r / r.sum()
+            if nxt is None:
+                dist = r if residual_draw else p[n]
+                bonus = int(np.searchsorted(np.cumsum(dist), uniforms[n][ud], side="right"))
+                bonus = min(bonus, V - 1)
+                break
+            n = nxt
+            path.append(n)
+        path = np.array(path)
+        return O.Verdict(len(path) - 1, path, bonus,
+                         np.concatenate([tok[path[1:]], [bonus]]).astype(np.int64))
+    run.__name__ = ("_sample_no_residual_update" if not renormalise else
+                    "_sample_draw_from_p" if not residual_draw else "_sample_swapped_uniforms")
+    return run
+
+
 def _retrieve_rank_off(t, M, root):
     tok = np.empty(t.n_nodes, dtype=np.int64)
     tok[0] = root
@@ -113,7 +145,7 @@ def _attention_wrong_group(t, q, kt, vt, kc, vc, P_, scale=None):
 
 ORIG = {name: getattr(O, name) for name in
         ("verify", "topk_row", "update", "update_accepted", "retrieve", "ancestor_mask",
-         "tree_attention", "splitmix64", "init_matrix")}
+         "tree_attention", "splitmix64", "init_matrix", "verify_sample")}
 
 CASES = [
     ("verify", _bonus_from_parent, [P.test_worked_example_verify_and_update,
@@ -131,6 +163,11 @@ CASES = [
     ("splitmix64", _splitmix_counter_from_zero, [P.test_splitmix64_published_outputs]),
     ("splitmix64", _splitmix_wrong_shift, [P.test_splitmix64_published_outputs]),
     ("init_matrix", _init_low_word, [P.test_init_random_power_of_two_vocab_takes_top_bits]),
+    ("verify_sample", _sampler(renormalise=False), [P.test_sample_chain_is_the_speculative_loop,
+                                                     P.test_sample_is_lossless]),
+    ("verify_sample", _sampler(residual_draw=False), [P.test_sample_chain_is_the_speculative_loop,
+                                                      P.test_sample_is_lossless]),
+    ("verify_sample", _sampler(swap_uniforms=True), [P.test_sample_chain_is_the_speculative_loop]),
     ("retrieve", _retrieve_rank_off, [P.test_worked_example_retrieval_gives_merged_sequence,
                                       P.test_retrieve_matches_recursive_definition]),
     ("ancestor_mask", _mask_without_self, [P.test_worked_example_mask,

@@ -281,6 +281,121 @@ def test_expected_tokens_per_pass_closed_form():
     assert abs(total / trials - expect) < 0.03
 
 
+# ---------------------------------------------------------------- sampling verification
+def _inverse_cdf(dist, r):
+    return int(np.searchsorted(np.cumsum(dist), r, side="right"))
+
+
+def _speculative_loop(p, draft, u_acc, u_res):
+    """The draft/verify loop of the speculative-decoding lesson ([SD]) for
+    one chain of drafts, with the draft distribution q a point mass on each
+    drafted token: accept with min(1, p/q), else resample from the
+    normalised positive part of p - q and stop, else the bonus from the
+    last position."""
+    V = p.shape[1]
+    out = []
+    for j, x in enumerate(draft):
+        q = np.zeros(V)
+        q[x] = 1.0
+        if u_acc[j] < min(1.0, p[j][x] / q[x]):
+            out.append(int(x))
+        else:
+            res = np.maximum(0.0, p[j] - q)
+            out.append(_inverse_cdf(res / res.sum(), u_res[j]))
+            return out
+    out.append(_inverse_cdf(p[len(draft)], u_res[len(draft)]))
+    return out
+
+
+def test_sample_chain_is_the_speculative_loop():
+    rng = np.random.default_rng(41)
+    for trial in range(400):
+        g = int(rng.integers(0, 6))
+        t = O.template_from_levels([[1]] * g)
+        V = int(rng.integers(2, 9))
+        temp = float(rng.choice([0.5, 1.0, 2.0]))
+        z = rng.standard_normal((g + 1, V)) * 2
+        tok = rng.integers(0, V, size=g + 1)
+        for j in range(g):                    # make acceptance likely on most positions
+            if rng.random() < 0.7:
+                z[j, tok[j + 1]] += 4.0
+        u = rng.random((g + 1, 2))
+        v = O.verify_sample(t, tok, z, temp, u)
+        p = O.softmax_rows(z, temp)
+        want = _speculative_loop(p, tok[1:], u[1:, 0], u[:, 1])
+        assert v.emitted.tolist() == want, trial
+        assert v.accept_len == len(want) - 1 and v.path.tolist() == list(range(len(want)))
+        assert v.bonus == want[-1]
+
+
+def _lossless_tree():
+    # root with children carrying tokens 2, 0, 2 (a duplicate); child 0
+    # has one child; V = 5
+    t = O.template_from_levels([[3], [1, 0, 0]])
+    tok = np.array([4, 2, 0, 2, 1])
+    z = np.array([[0.3, 0.9, 1.1, -0.4, 0.2],
+                  [0.5, -0.2, 0.1, 0.8, 0.0],
+                  [1.0, 0.0, -1.0, 0.5, 0.2],
+                  [0.0, 0.4, 0.3, -0.6, 0.9],
+                  [0.2, 0.2, 0.7, -0.1, 0.0]])
+    return t, tok, z
+
+
+def _chi2(counts, probs):
+    n = counts.sum()
+    return float(((counts - n * probs) ** 2 / (n * probs)).sum())
+
+
+def test_sample_is_lossless():
+    # Emitted tokens follow the target: the first ~ p_root whatever the
+    # drafts, and after an accepted draft the next ~ p of that node
+    # (Stern, Leviathan and Chen, as the speculative-decoding lesson states).
+    t, tok, z = _lossless_tree()
+    temp, N = 1.0, 40000
+    rng = np.random.default_rng(42)
+    p = O.softmax_rows(z, temp)
+    first = np.zeros(5)
+    second = {2: np.zeros(5), 0: np.zeros(5)}      # after token 2 (node 1), token 0 (node 2)
+    for _ in range(N):
+        v = O.verify_sample(t, tok, z, temp, rng.random((5, 2)))
+        first[v.emitted[0]] += 1
+        if v.emitted[0] in second:
+            assert len(v.emitted) >= 2               # a drafted token is only ever accepted
+            second[v.emitted[0]][v.emitted[1]] += 1
+    assert _chi2(first, p[0]) < 18.47                # 4 degrees of freedom, p = 0.001
+    assert _chi2(second[2], p[1]) < 18.47
+    assert _chi2(second[0], p[2]) < 18.47
+
+
+def test_sample_low_temperature_is_greedy():
+    # As the temperature falls, p becomes the point mass on the argmax, and
+    # the walk accepts exactly the children carrying their parent's argmax.
+    # Siblings carry distinct tokens here: with a duplicate the walk
+    # descends into the first accepted sibling, greedy verification into
+    # the one with the deepest accepted node.
+    rng = np.random.default_rng(43)
+    for trial in range(200):
+        levels = random_levels(rng, 3)
+        t = O.template_from_levels(levels)
+        T, V = t.n_nodes, 7
+        z = np.stack([rng.permutation(V) * 0.1 for _ in range(T)])   # distinct, 0.1 apart
+        arg = np.argmax(z, axis=1)
+        tok = rng.integers(0, V, size=T)
+        for n in range(T):
+            ch = t.children(n)
+            if not ch:
+                continue
+            pick = rng.permutation(V)[:len(ch)]
+            if rng.random() < 0.7 and arg[n] not in pick:
+                pick[rng.integers(len(ch))] = arg[n]
+            tok[ch] = pick
+        u = rng.uniform(1e-9, 1 - 1e-9, size=(T, 2))
+        v = O.verify_sample(t, tok, z, 1e-3, u)
+        g = O.verify(t, tok, arg)
+        assert v.path.tolist() == g.path.tolist() and v.bonus == g.bonus, trial
+        assert v.emitted.tolist() == g.emitted.tolist()
+
+
 # ---------------------------------------------------------------- update
 def test_update_last_writer_wins_brute_force():
     rng = np.random.default_rng(8)
