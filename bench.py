@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default: the workload's)")
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="vicuna7b")
+    ap.add_argument("--temperature", type=float, default=0.0,
+                    help="0: greedy verification (tr_step); above 0: verification by sampling "
+                         "at this temperature (tr_step_sample, seeded uniforms)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the CPU oracle baseline (0 disables it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -100,7 +103,7 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes_per_launch": mib << 20, "launches": 5}), flush=True)
 
 
-def cpu_baseline(w, inputs, init_host, seconds):
+def cpu_baseline(w, inputs, init_host, seconds, temperature=0.0):
     """The CPU oracle, as it stands, on the first steps of the same trajectory."""
     import numpy as np
     from oracle import tr_oracle as O
@@ -117,13 +120,15 @@ def cpu_baseline(w, inputs, init_host, seconds):
     P = int(init_host.prefix_len[b])
     tok = O.retrieve(t, M, int(init_host.root[b]))
     done, elapsed = 0, 0.0
-    for (q, kt, vt, z) in inputs:
+    for (q, kt, vt, z, U) in inputs:
         if elapsed >= seconds:
             break
         qh, kth, vth, zh = (x[b].float().cpu().numpy() for x in (q, kt, vt, z))
+        uh = U[b].double().cpu().numpy() if U is not None else None
         t0 = time.perf_counter()
         O.tree_attention(t, qh, kth, vth, kc, vc, P)
-        res, P = O.step_after_forward(t, M, tok, zh, w.k, kc, vc, kth, vth, P)
+        res, P = O.step_after_forward(t, M, tok, zh, w.k, kc, vc, kth, vth, P,
+                                      temperature=temperature, uniforms=uh)
         tok = res.next_tok
         elapsed += time.perf_counter() - t0
         done += 1
@@ -163,20 +168,30 @@ def main():
     init_host = init.to("cpu")
     tree = tr.Tree.from_levels(w.levels, w.k)
 
+    temp = args.temperature
+
+    def step(dec, z, kt, vt, U):
+        if temp > 0:
+            dec.step_sample(z, kt, vt, temp, U)
+        else:
+            dec.step(z, kt, vt)
+
     # ---- record pass: the trajectory's inputs, kept in HBM
     t0 = time.time()
     st = init.clone()
     dec = TRDecoder(tree, st.M, st.k_cache, st.v_cache, st.prefix_len, st.root, Hq=w.Hq)
     out = torch.empty((w.B, w.T, w.Hq, w.d), dtype=w.kv_dtype, device=dev)
+    ug = torch.Generator(device=dev).manual_seed(w.seed + 77)
     inputs, prefix_hist, accepted = [], [], []
     for s in range(total):
         q, kt, vt = W.step_qkv(w, s, dev)
         z = W.step_logits(w, s, dec.tree_tok, dev)
+        U = torch.rand((w.B, w.T, 2), generator=ug, device=dev) if temp > 0 else None
         prefix_hist.append(dec.prefix_len.clone())
         dec.attend(q, kt, vt, out)
-        dec.step(z, kt, vt)
+        step(dec, z, kt, vt, U)
         accepted.append(dec.accept_len.clone())
-        inputs.append((q, kt, vt, z))
+        inputs.append((q, kt, vt, z, U))
     torch.cuda.synchronize()
     rec_tok, rec_M = dec.tree_tok.clone(), dec.M.clone()
     assert dec.device_flags() == 0
@@ -189,18 +204,18 @@ def main():
     dec = TRDecoder(tree, st.M, st.k_cache, st.v_cache, st.prefix_len, st.root, Hq=w.Hq)
     stream = torch.cuda.current_stream()
     for s in range(args.warmup):
-        q, kt, vt, z = inputs[s]
+        q, kt, vt, z, U = inputs[s]
         dec.attend(q, kt, vt, out)
-        dec.step(z, kt, vt)
+        step(dec, z, kt, vt, U)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(steps):
-        q, kt, vt, z = inputs[args.warmup + i]
+        q, kt, vt, z, U = inputs[args.warmup + i]
         ev[i][0].record(stream)
         dec.attend(q, kt, vt, out)
         ev[i][1].record(stream)
-        dec.step(z, kt, vt)
+        step(dec, z, kt, vt, U)
         ev[i][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
@@ -217,15 +232,15 @@ def main():
     st = init.clone()
     dec = TRDecoder(tree, st.M, st.k_cache, st.v_cache, st.prefix_len, st.root, Hq=w.Hq)
     for s in range(args.warmup):
-        q, kt, vt, z = inputs[s]
+        q, kt, vt, z, U = inputs[s]
         dec.attend(q, kt, vt, out)
-        dec.step(z, kt, vt)
+        step(dec, z, kt, vt, U)
     torch.cuda.synchronize()
     tr.tr_profile_enable(True)
     for i in range(steps):
-        q, kt, vt, z = inputs[args.warmup + i]
+        q, kt, vt, z, U = inputs[args.warmup + i]
         dec.attend(q, kt, vt, out)
-        dec.step(z, kt, vt)
+        step(dec, z, kt, vt, U)
     launches = tr.tr_profile_read()
     tr.tr_profile_enable(False)
     assert torch.equal(dec.tree_tok, rec_tok), "profiled replay diverged from the record pass"
@@ -286,7 +301,7 @@ def main():
 
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(w, inputs, init_host, args.cpu_seconds)
+        cpu = cpu_baseline(w, inputs, init_host, args.cpu_seconds, temp)
 
     res = {
         "metric": METRIC,
@@ -303,7 +318,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.description, "V": w.V, "k": w.k, "sequences": w.B,
                    "tree_nodes": w.T, "tree_depth": w.depth, "Hq": w.Hq, "Hkv": w.Hkv,
-                   "head_dim": w.d, "prefix": list(w.prefix), "M_dtype": str(w.m_dtype)[6:]},
+                   "head_dim": w.d, "prefix": list(w.prefix), "M_dtype": str(w.m_dtype)[6:],
+                   "verification": f"sampling, temperature {temp}" if temp > 0 else "greedy"},
         "roofline": roof,
         "per_call": detail,
         "per_kernel": kdetail,

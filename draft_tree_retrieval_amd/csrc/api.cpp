@@ -1,5 +1,6 @@
 // extern "C" entry points of libtr: argument checks on the host, then the
 // kernel launches.  No call here allocates device memory.
+#include <cmath>
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -343,15 +344,26 @@ tr_status tr_verify(const tr_tree* t, int32_t B, const int32_t* topk, int32_t k,
                     "tr_verify");
 }
 
-tr_status tr_step_ex(const tr_tree* t, int32_t B, int64_t V, int32_t k, const void* logits,
-                     tr_dtype l_dtype, void* M, tr_dtype m_dtype, int32_t* tree_tok,
-                     int32_t* root_tok, int32_t* accept_len, int32_t* accept_path,
-                     int32_t* emitted, int32_t Hkv, int32_t d, tr_dtype kv_dtype,
-                     const void* k_tree, const void* v_tree, void* k_cache, void* v_cache,
-                     int64_t cap, int32_t* prefix_len, int32_t* topk_out, tr_update_mode mode,
-                     void* ws, size_t ws_bytes, void* stream) {
+namespace {
+
+// The fused step; temperature 0 verifies greedily, above 0 by sampling.
+tr_status step_impl(const tr_tree* t, int32_t B, int64_t V, int32_t k, const void* logits,
+                    tr_dtype l_dtype, float temperature, const float* uniforms, void* M,
+                    tr_dtype m_dtype, int32_t* tree_tok, int32_t* root_tok, int32_t* accept_len,
+                    int32_t* accept_path, int32_t* emitted, int32_t Hkv, int32_t d,
+                    tr_dtype kv_dtype, const void* k_tree, const void* v_tree, void* k_cache,
+                    void* v_cache, int64_t cap, int32_t* prefix_len, int32_t* topk_out,
+                    tr_update_mode mode, void* ws, size_t ws_bytes, void* stream) {
   TR_CHECK(mode == TR_UPDATE_ALL || mode == TR_UPDATE_ACCEPTED, TR_ERR_INVALID_ARGUMENT,
            "unknown update mode %d", int(mode));
+  const bool sample = temperature != 0.f;
+  if (sample) {
+    TR_CHECK(temperature > 0.f && std::isfinite(temperature), TR_ERR_INVALID_ARGUMENT,
+             "temperature must be positive and finite");
+    TR_CHECK(uniforms != nullptr, TR_ERR_INVALID_ARGUMENT, "uniforms is null");
+    TR_CHECK(V <= int64_t(tr::kMaxBuckets) * tr::kDrawBucket, TR_ERR_UNSUPPORTED,
+             "sampling takes V <= %d", tr::kMaxBuckets * tr::kDrawBucket);
+  }
   tr_status st = check_topk_args(t, B, logits, l_dtype, V, k);
   if (st != TR_OK) return st;
   TR_CHECK(M && tree_tok && root_tok && accept_len, TR_ERR_INVALID_ARGUMENT, "null tensor");
@@ -377,6 +389,9 @@ tr_status tr_step_ex(const tr_tree* t, int32_t B, int64_t V, int32_t k, const vo
   tail.mode = tr::TAIL_STEP;
   tail.m_is64 = m_dtype == TR_INT64;
   tail.update_mode = mode == TR_UPDATE_ACCEPTED ? tr::UPDATE_ACCEPTED : tr::UPDATE_ALL;
+  tail.sample = sample ? 1 : 0;
+  tail.temp_scale = sample ? float(1.4426950408889634 / double(temperature)) : 0.f;
+  tail.uniforms = uniforms;
   tail.M = M;
   tail.tree_tok = tree_tok;
   tail.root_tok = root_tok;
@@ -394,6 +409,35 @@ tr_status tr_step_ex(const tr_tree* t, int32_t B, int64_t V, int32_t k, const vo
   return hip_status(tr::launch_topk(t->dev, B, logits, l_dtype == TR_BFLOAT16, V, k, ids, tail, w,
                                     plan, hipStream_t(stream)),
                     "tr_step");
+}
+
+}  // namespace
+
+tr_status tr_step_ex(const tr_tree* t, int32_t B, int64_t V, int32_t k, const void* logits,
+                     tr_dtype l_dtype, void* M, tr_dtype m_dtype, int32_t* tree_tok,
+                     int32_t* root_tok, int32_t* accept_len, int32_t* accept_path,
+                     int32_t* emitted, int32_t Hkv, int32_t d, tr_dtype kv_dtype,
+                     const void* k_tree, const void* v_tree, void* k_cache, void* v_cache,
+                     int64_t cap, int32_t* prefix_len, int32_t* topk_out, tr_update_mode mode,
+                     void* ws, size_t ws_bytes, void* stream) {
+  return step_impl(t, B, V, k, logits, l_dtype, 0.f, nullptr, M, m_dtype, tree_tok, root_tok,
+                   accept_len, accept_path, emitted, Hkv, d, kv_dtype, k_tree, v_tree, k_cache,
+                   v_cache, cap, prefix_len, topk_out, mode, ws, ws_bytes, stream);
+}
+
+tr_status tr_step_sample(const tr_tree* t, int32_t B, int64_t V, int32_t k, const void* logits,
+                         tr_dtype l_dtype, float temperature, const float* uniforms, void* M,
+                         tr_dtype m_dtype, int32_t* tree_tok, int32_t* root_tok,
+                         int32_t* accept_len, int32_t* accept_path, int32_t* emitted, int32_t Hkv,
+                         int32_t d, tr_dtype kv_dtype, const void* k_tree, const void* v_tree,
+                         void* k_cache, void* v_cache, int64_t cap, int32_t* prefix_len,
+                         int32_t* topk_out, tr_update_mode mode, void* ws, size_t ws_bytes,
+                         void* stream) {
+  TR_CHECK(temperature > 0.f && std::isfinite(temperature), TR_ERR_INVALID_ARGUMENT,
+           "temperature must be positive and finite");
+  return step_impl(t, B, V, k, logits, l_dtype, temperature, uniforms, M, m_dtype, tree_tok,
+                   root_tok, accept_len, accept_path, emitted, Hkv, d, kv_dtype, k_tree, v_tree,
+                   k_cache, v_cache, cap, prefix_len, topk_out, mode, ws, ws_bytes, stream);
 }
 
 tr_status tr_step(const tr_tree* t, int32_t B, int64_t V, int32_t k, const void* logits,

@@ -28,7 +28,7 @@
 // a row merges the
 // segment lists, and the last row block of a sequence runs that sequence's
 // tail (hand-over through device-scope atomics, see dev_common.h).
-#include "tail.h"
+#include "sample.h"
 
 namespace tr {
 
@@ -62,6 +62,8 @@ TopkPlan plan_topk(int64_t rows, int64_t V, int32_t k, int32_t esz) {
   off = align256(off + size_t(rows) * segs * p.kmax * 8);
   p.ids_off = off;
   off = align256(off + size_t(rows) * k * 4);
+  p.stat_off = off;
+  off = align256(off + size_t(rows) * segs * 8);
   p.end = off;
   return p;
 }
@@ -139,12 +141,36 @@ __device__ __forceinline__ void block_merge(TopList<KM>& L, uint64_t (*s_keys)[K
 // while waves 1.. write the verdict, wave 1 the updated rows of M and
 // waves 1.. copy the accepted key/value rows, so retrieval's loads never
 // wait behind their stores.
-template <typename MT>
+template <typename MT, bool BF16, bool SAMPLE>
 __device__ __forceinline__ void seq_tail(TailShared& S, const TreeDev& tree, int b, int32_t k,
                                          int64_t V, const int32_t* topk_b, int32_t* tok_b,
-                                         const TailArgs& tail, uint8_t* ws) {
+                                         const TailArgs& tail, uint8_t* ws, const void* logits,
+                                         const uint64_t* stat, int32_t segs) {
   void* M_b = reinterpret_cast<MT*>(tail.M) + int64_t(b) * V * k;
   const int wave = threadIdx.x >> 6;
+  if constexpr (SAMPLE) {
+    // verification by sampling: no greedy token to prefetch M rows for
+    __shared__ SampleShared SS;
+    tail_load(S, tree, tok_b, topk_b, k, tail.k_cache ? tail.prefix_len + b : nullptr);
+    sample_prepare<BF16>(S, SS, tree, b, V, logits, stat, segs, tail);
+    if (wave == 0) sample_walk(S, SS, tree, V);
+    __syncthreads();
+    sample_draw<BF16>(S, SS, tree, b, k, V, logits, tail.temp_scale);
+    __syncthreads();
+    tail_write_verdict(S, tree, b, tail.accept_len, tail.accept_path, nullptr, tail.emitted, 64);
+    if (wave == 0) tail_update_claim(S, tree, V, ws, tail.update_mode == UPDATE_ACCEPTED);
+    __syncthreads();
+    const bool fits = tail_commit(S, tree, b, tail, ws, wave == 0 ? 1 << 30 : 64);
+    if (wave == 1) tail_update_store<MT>(S, tree, k, M_b, V);
+    if (wave != 0) return;
+    wave_lds_sync();
+    tail_retrieve<MT>(S, tree, S.bonus, M_b, V, k, tok_b, ws, true, false);
+    if (threadIdx.x == 0) {
+      tail.root_tok[b] = S.bonus;
+      if (fits) tail.prefix_len[b] = int32_t(S.P + S.L + 1);
+    }
+    return;
+  }
   if (tail.mode != TAIL_STEP) {
     tail_load(S, tree, tok_b, topk_b, k);
     if (wave == 0) {
@@ -173,12 +199,15 @@ __device__ __forceinline__ void seq_tail(TailShared& S, const TreeDev& tree, int
   }
 }
 
-template <bool BF16, int KM, int NT, int NV>
-__global__ __launch_bounds__(NT) void topk_kernel(const void* __restrict__ logits, int64_t V,
+// The sampling instantiations are held to three waves per SIMD (at most
+// 168 VGPRs), as many as the greedy ones reach by themselves: with many
+// rows the blocks of a launch run in rounds, so occupancy is throughput.
+template <bool BF16, int KM, int NT, int NV, bool SAMPLE>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SAMPLE ? 3 : 1))) void topk_kernel(const void* __restrict__ logits, int64_t V,
                                                    int32_t k, int32_t segs, int64_t seg_len,
                                                    int32_t* __restrict__ ids_out,
-                                                   uint64_t* __restrict__ part, uint8_t* ws,
-                                                   TreeDev tree, TailArgs tail) {
+                                                   uint64_t* __restrict__ part, uint64_t* stat,
+                                                   uint8_t* ws, TreeDev tree, TailArgs tail) {
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int VE = 16 / ESZ;             // elements per 16-byte vector
   constexpr int NW = NT / 64;              // waves
@@ -195,6 +224,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const void* __restrict__ logit
   __shared__ uint64_t s_best[KM];
   __shared__ uint32_t s_wcnt[NW];
   __shared__ uint32_t s_lm[NT];
+  __shared__ float s_wsum[NW];
 
   // aligned vector range [a0, a1) inside [s0, s1); at most VE-1 loose
   // elements on each side
@@ -245,6 +275,41 @@ __global__ __launch_bounds__(NT) void topk_kernel(const void* __restrict__ logit
   uint32_t lm[NW];
 #pragma unroll
   for (int w = 0; w < NW; ++w) lm[w] = s_lm[w * 64 + lane];
+
+  // sampling: softmax statistics of the segment, (max, sum of
+  // exp2((z - max) * scale)), handed over with the ids
+  float seg_max = 0.f;
+  if constexpr (SAMPLE) {
+    uint32_t bm = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) bm = max(bm, lm[w]);
+    bm = wave_max_u32(bm);
+    seg_max = ord_to_f32(bm);
+    const float s2 = tail.temp_scale, off = -seg_max * s2;
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // an opaque copy: were the halves extracted here shared with the
+        // candidate scan below, all of them would stay live across the
+        // threshold search (twice the registers of x)
+        uint32_t word = x[i][j];
+        asm volatile("" : "+v"(word));
+        if (BF16) {
+          const uint32_t c0 = (word & 0xFFFFu) << 16, c1 = word & 0xFFFF0000u;
+          acc += c0 ? soft_weight(ord_to_f32(c0), s2, off) : 0.f;
+          acc += c1 ? soft_weight(ord_to_f32(c1), s2, off) : 0.f;
+        } else {
+          acc += word ? soft_weight(ord_to_f32(word), s2, off) : 0.f;
+        }
+      }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      acc += loose_code[h] ? soft_weight(ord_to_f32(loose_code[h]), s2, off) : 0.f;
+    acc = wave_sum_f32(acc);
+    if (lane == 0) s_wsum[wave] = acc;
+  }
   uint32_t lo = 0;
 #pragma unroll
   for (int bit = 31; bit >= (BF16 ? 16 : 0); --bit) {
@@ -302,6 +367,14 @@ __global__ __launch_bounds__(NT) void topk_kernel(const void* __restrict__ logit
     most = max(most, s_wcnt[w]);
   }
   const bool overflow = most > uint32_t(kCandW);
+  if constexpr (SAMPLE) {
+    if (tid == 0) {
+      float tot = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) tot += s_wsum[w];
+      put_dev(&stat[row * segs + seg], (uint64_t(__float_as_uint(tot)) << 32) | __float_as_uint(seg_max));
+    }
+  }
 
   // ---- the block's KM best
   if (!overflow && n <= 64u) {
@@ -390,8 +463,10 @@ __global__ __launch_bounds__(NT) void topk_kernel(const void* __restrict__ logit
   __shared__ TailShared S;
   const int32_t* topk_b = ids_out + int64_t(b) * tree.T * k;
   int32_t* tok_b = tail.tree_tok + int64_t(b) * tree.T;
-  if (tail.m_is64) seq_tail<int64_t>(S, tree, b, k, V, topk_b, tok_b, tail, ws);
-  else seq_tail<int32_t>(S, tree, b, k, V, topk_b, tok_b, tail, ws);
+  if (tail.m_is64)
+    seq_tail<int64_t, BF16, SAMPLE>(S, tree, b, k, V, topk_b, tok_b, tail, ws, logits, stat, segs);
+  else
+    seq_tail<int32_t, BF16, SAMPLE>(S, tree, b, k, V, topk_b, tok_b, tail, ws, logits, stat, segs);
 }
 
 hipError_t launch_topk(const TreeDev& tree, int32_t B, const void* logits, int l_is_bf16, int64_t V,
@@ -399,13 +474,19 @@ hipError_t launch_topk(const TreeDev& tree, int32_t B, const void* logits, int l
                        const TopkPlan& plan, hipStream_t s) {
   dim3 grid(plan.segs, unsigned(plan.rows));
   uint64_t* part = reinterpret_cast<uint64_t*>(ws + plan.part_off);
-#define TR_TOPK(BF, KMV, NTV, NVV)                                                             \
-  hipLaunchKernelGGL((topk_kernel<BF, KMV, NTV, NVV>), grid, dim3(NTV), 0, s, logits, V, k,     \
-                     plan.segs, plan.seg_len, topk_ids, part, ws, tree, tail)
-#define TR_TOPK_NT(BF, KMV)                                 \
-  do {                                                      \
-    if (plan.threads == 512) TR_TOPK(BF, KMV, 512, 8);      \
-    else TR_TOPK(BF, KMV, 256, 16);                         \
+  uint64_t* stat = reinterpret_cast<uint64_t*>(ws + plan.stat_off);
+#define TR_TOPK(BF, KMV, NTV, NVV, SMP)                                                         \
+  hipLaunchKernelGGL((topk_kernel<BF, KMV, NTV, NVV, SMP>), grid, dim3(NTV), 0, s, logits, V,   \
+                     k, plan.segs, plan.seg_len, topk_ids, part, stat, ws, tree, tail)
+#define TR_TOPK_NT(BF, KMV)                                                 \
+  do {                                                                      \
+    if (tail.sample) {                                                      \
+      if (plan.threads == 512) TR_TOPK(BF, KMV, 512, 8, true);              \
+      else TR_TOPK(BF, KMV, 256, 16, true);                                 \
+    } else {                                                                \
+      if (plan.threads == 512) TR_TOPK(BF, KMV, 512, 8, false);             \
+      else TR_TOPK(BF, KMV, 256, 16, false);                                \
+    }                                                                       \
   } while (0)
   prof_begin(s, TR_KERNEL_TOPK);
   if (l_is_bf16) {

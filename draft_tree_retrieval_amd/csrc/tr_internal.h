@@ -12,6 +12,8 @@ namespace tr {
 constexpr int kMaxNodes = 128;   // tree nodes, root included
 constexpr int kMaxK = 16;        // candidates per row of M
 constexpr int kHeadDim = 128;    // attention head dimension
+constexpr int kDrawBucket = 512;  // ids per bucket of the sampling draw
+constexpr int kMaxBuckets = 512;  // so sampling takes V <= 262144
 
 // Tree template as kernels see it: passed by value as a kernel argument,
 // so no device allocation is tied to a tree.
@@ -57,6 +59,7 @@ struct TopkPlan {
   int32_t threads;    // 256 (16 vectors per lane) or 512 (8 vectors per lane)
   size_t part_off;    // uint64 [rows][segs][kmax] partial keys (segs > 1)
   size_t ids_off;     // int32  [rows][k] ids when the caller gives no buffer
+  size_t stat_off;    // float2 [rows][segs] softmax statistics (sampling)
   size_t end;
 };
 TopkPlan plan_topk(int64_t rows, int64_t V, int32_t k, int32_t esz);
@@ -84,6 +87,9 @@ struct TailArgs {
   int32_t mode;
   int32_t m_is64;
   int32_t update_mode;     // UpdateMode (TAIL_STEP only)
+  int32_t sample;          // verify by sampling (TAIL_STEP only)
+  float temp_scale;        // log2(e) / temperature
+  const float* uniforms;   // [B][T][2]
   void* M;                 // [B][V][k]
   int32_t* tree_tok;       // [B][T]
   int32_t* root_tok;       // [B]

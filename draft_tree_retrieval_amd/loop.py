@@ -53,5 +53,12 @@ class TRDecoder:
                           v_tree, self.k_cache, self.v_cache, self.prefix_len, self.topk,
                           self.update, self.stream)
 
+    def step_sample(self, logits, k_tree, v_tree, temperature, uniforms):
+        """The step verifying by sampling; uniforms [B][T][2] float32 in [0, 1)."""
+        tr.tr_step_sample(self.tree, logits, temperature, uniforms, self.M, self.tree_tok,
+                          self.root_tok, self.accept_len, self.accept_path, self.emitted, self.ws,
+                          k_tree, v_tree, self.k_cache, self.v_cache, self.prefix_len, self.topk,
+                          self.update, self.stream)
+
     def device_flags(self):
         return tr.tr_read_device_status(self.ws, self.stream)

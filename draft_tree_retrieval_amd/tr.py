@@ -48,6 +48,9 @@ _SIGS = {
                  C.c_int, _P, _P, _P, _P, _I64, _P, _P, _P, _SZ, _P], C.c_int),
     "tr_step_ex": ([_P, _I32, _I64, _I32, _P, C.c_int, _P, C.c_int, _P, _P, _P, _P, _P, _I32,
                     _I32, C.c_int, _P, _P, _P, _P, _I64, _P, _P, C.c_int, _P, _SZ, _P], C.c_int),
+    "tr_step_sample": ([_P, _I32, _I64, _I32, _P, C.c_int, C.c_float, _P, _P, C.c_int, _P, _P,
+                        _P, _P, _P, _I32, _I32, C.c_int, _P, _P, _P, _P, _I64, _P, _P, C.c_int,
+                        _P, _SZ, _P], C.c_int),
     "tr_init_matrix": ([_I32, _I64, _I32, _P, C.c_int, C.c_int, _P, C.c_int, _I32, C.c_uint64,
                         _P], C.c_int),
     "tr_profile_enable": ([_I32], C.c_int),
@@ -244,6 +247,25 @@ def tr_step_ex(tree, logits, M, tree_tok, root_tok, accept_len, accept_path, emi
                              _ptr(accept_path), _ptr(emitted), Hkv, d, kv_dt, _ptr(k_tree),
                              _ptr(v_tree), _ptr(k_cache), _ptr(v_cache), cap, _ptr(prefix_len),
                              _ptr(topk_out), mode, _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def tr_step_sample(tree, logits, temperature, uniforms, M, tree_tok, root_tok, accept_len,
+                   accept_path, emitted, ws, k_tree=None, v_tree=None, k_cache=None, v_cache=None,
+                   prefix_len=None, topk_out=None, update="all", stream=None):
+    """tr_step verifying by sampling at `temperature` with the caller's
+    uniforms [B][T][2] (float32, device)."""
+    mode = _UPDATE_MODES[update] if isinstance(update, str) else int(update)
+    B, T, V = logits.shape
+    if uniforms.dtype != torch.float32 or tuple(uniforms.shape) != (B, T, 2):
+        raise ValueError("uniforms must be float32 [B][T][2]")
+    Hkv, cap, d, kv_dt = _kv_shape(k_cache)
+    _check(load().tr_step_sample(tree.handle, B, V, tree.k, _ptr(logits), _dt(logits),
+                                 float(temperature), _ptr(uniforms), _ptr(M), _dt(M),
+                                 _ptr(tree_tok), _ptr(root_tok), _ptr(accept_len),
+                                 _ptr(accept_path), _ptr(emitted), Hkv, d, kv_dt, _ptr(k_tree),
+                                 _ptr(v_tree), _ptr(k_cache), _ptr(v_cache), cap,
+                                 _ptr(prefix_len), _ptr(topk_out), mode, _ptr(ws), ws.numel(),
+                                 _stream(stream)))
 
 
 # tr_init_mode

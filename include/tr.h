@@ -235,6 +235,38 @@ tr_status tr_step_ex(const tr_tree* t, int32_t B, int64_t V, int32_t k, const vo
                      int64_t cap, int32_t* prefix_len, int32_t* topk_out, tr_update_mode mode,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* tr_step with verification by sampling instead of greedy matching
+ * (speculative-decoding lesson: accept a draft x with min(1, p(x)/q(x)),
+ * else draw from the normalised positive part of p - q and stop; after a
+ * fully accepted draft the bonus is drawn from p; Token Recycling,
+ * Experiment: TR is also evaluated with sampling).
+ *   p_n = softmax(logits[b][n] / temperature), temperature > 0 and finite.
+ *   TR's drafts come from M, so q is a point mass on each drafted token.
+ *   From the root, the children of the current node are tried in rank
+ *   order: child c with token x is accepted when u[b][c][0] < r(x), r the
+ *   current residual (p_n at first; each rejected sibling's token is taken
+ *   out and r renormalised), and the walk moves to c.  When no child is
+ *   accepted (a leaf has none) the bonus is drawn from r with u[b][n][1]:
+ *   the smallest id whose cumulative residual probability, ids in
+ *   increasing order, exceeds u[b][n][1].  The path root..stop node is the
+ *   accepted path (accept_len, accept_path, emitted, commit, next root as
+ *   tr_step).  The update of M (mode) still writes each node's top-k.
+ *   uniforms [B][T][2] float32 in [0, 1), device memory (the caller draws
+ *   them, e.g. from its own generator).  Probabilities are computed in
+ *   float32; a uniform within float32 rounding of a threshold may decide
+ *   either way.
+ * Extra errors: TR_ERR_INVALID_ARGUMENT for a null uniforms pointer or a
+ * temperature that is not positive and finite; TR_ERR_UNSUPPORTED for
+ * V > 262144.  Workspace as tr_step. */
+tr_status tr_step_sample(const tr_tree* t, int32_t B, int64_t V, int32_t k, const void* logits,
+                         tr_dtype l_dtype, float temperature, const float* uniforms, void* M,
+                         tr_dtype m_dtype, int32_t* tree_tok, int32_t* root_tok,
+                         int32_t* accept_len, int32_t* accept_path, int32_t* emitted, int32_t Hkv,
+                         int32_t d, tr_dtype kv_dtype, const void* k_tree, const void* v_tree,
+                         void* k_cache, void* v_cache, int64_t cap, int32_t* prefix_len,
+                         int32_t* topk_out, tr_update_mode mode, void* ws, size_t ws_bytes,
+                         void* stream);
+
 /* Initial contents of M (Token Recycling, Method, first module: a hot start
  * inherits the matrix left by earlier inference instead of an empty one;
  * Experiment, initialisation ablation: all-zero, random ids, and prior

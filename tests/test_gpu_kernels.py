@@ -335,6 +335,110 @@ def test_step_ex_accepted_only_duplicates(tr, m_dtype):
             assert tr.tr_read_device_status(ws) == 0
 
 
+# ------------------------------------------------------------------ sampling verification
+MARGIN = 2e-5      # a uniform this close to a threshold could go either way in float32
+
+
+def clear_uniforms(t, M, tok, z, k, temp, g, update="all"):
+    """Uniforms [T][2] whose every decision clears its threshold by MARGIN
+    in the oracle, and the oracle's step result on them."""
+    for _ in range(50):
+        u = torch.rand((t.n_nodes, 2), generator=g, dtype=torch.float64).to(torch.float32)
+        Mo = M.copy()
+        res, _ = O.step_after_forward(t, Mo, tok, z, k, update_mode=update, temperature=temp,
+                                      uniforms=u.double().numpy())
+        if res.verdict.margin > MARGIN:
+            return u, res, Mo
+    raise AssertionError("no clear uniforms")
+
+
+@pytest.mark.parametrize("l_dtype", [torch.bfloat16, torch.float32])
+def test_step_sample_parity(tr, l_dtype):
+    g = torch.Generator().manual_seed(51)
+    rng = np.random.default_rng(51)
+    lengths = []
+    for li, levels in enumerate(RAND_LEVELS):
+        t = otree(levels)
+        T, D = t.n_nodes, t.max_depth
+        for V, B, temp in ((300, 3, 1.0), (32000, 2, 0.7), (1001, 2, 1.6)):
+            k = 8
+            tree = tr.Tree.from_levels(levels, k)
+            M = torch.randint(0, V, (B, V, k), generator=g, dtype=torch.int32)
+            root = torch.randint(0, V, (B,), generator=g).to(torch.int32)
+            ws = ws_for(tr, tree, B, V, k)
+            dM, droot = M.to(DEV), root.to(DEV)
+            tok = torch.empty((B, T), dtype=torch.int32, device=DEV)
+            tr.tr_retrieve(tree, dM, droot, tok, ws)
+            tok_h = tok.cpu().numpy().astype(np.int64)
+            z = torch.randn((B, T, V), generator=g) * 2.0
+            for b in range(B):                      # deep paths: boost most drafts
+                for n in range(1, T):
+                    if rng.random() < 0.7:
+                        z[b, t.parent[n], tok_h[b, n]] += 10.0
+            z = z.to(l_dtype)
+            zh = z.float().numpy()
+            us, want = [], []
+            for b in range(B):
+                u, res, Mo = clear_uniforms(t, M[b].numpy().astype(np.int64), tok_h[b], zh[b], k,
+                                            temp, g)
+                us.append(u)
+                want.append((res, Mo))
+            U = torch.stack(us).to(DEV)
+            L = torch.empty((B,), dtype=torch.int32, device=DEV)
+            path = torch.empty((B, D + 1), dtype=torch.int32, device=DEV)
+            em = torch.empty((B, D + 1), dtype=torch.int32, device=DEV)
+            topk = torch.empty((B, T, k), dtype=torch.int32, device=DEV)
+            tr.tr_step_sample(tree, z.to(DEV), temp, U, dM, tok, droot, L, path, em, ws,
+                              topk_out=topk)
+            for b, (res, Mo) in enumerate(want):
+                v = res.verdict
+                case = (li, V, b)
+                assert int(L[b]) == v.accept_len, case
+                assert path[b, :v.accept_len + 1].cpu().tolist() == v.path.tolist(), case
+                assert int(droot[b]) == v.bonus, case
+                emw = v.emitted.tolist() + [-1] * (D + 1 - len(v.emitted))
+                assert em[b].cpu().tolist() == emw, case
+                assert (topk[b].cpu().numpy() == res.topk).all(), case
+                assert (dM[b].cpu().numpy().astype(np.int64) == Mo).all(), case
+                assert tok[b].cpu().numpy().tolist() == res.next_tok.tolist(), case
+                lengths.append(v.accept_len)
+            assert tr.tr_read_device_status(ws) == 0
+    # the cases reach past the first layer and also stop at the root
+    assert max(lengths) >= 3 and min(lengths) == 0
+
+
+def test_step_sample_draw_covers_the_row(tr):
+    # one node (a leaf root): the bonus is the inverse-CDF draw from p_root;
+    # uniforms spread over [0, 1) reach ids all over the row, and each
+    # matches the oracle's draw
+    g = torch.Generator().manual_seed(52)
+    tree = tr.Tree.from_levels([], 8)
+    t = otree([])
+    V, B, temp = 5000, 64, 3.0
+    z = (torch.randn((1, 1, V), generator=g) * 0.5).to(torch.bfloat16).repeat(B, 1, 1)
+    zh = z.float().numpy()
+    M = torch.zeros((B, V, 8), dtype=torch.int32)
+    ws = ws_for(tr, tree, B, V, 8)
+    us = []
+    for b in range(B):
+        while True:
+            u = torch.tensor([[0.0, (b + float(torch.rand((), generator=g))) / B]])
+            v = O.verify_sample(t, np.zeros(1, dtype=np.int64), zh[b], temp, u.double().numpy())
+            if v.margin > MARGIN:
+                break
+        us.append((u, v.bonus))
+    U = torch.stack([u for u, _ in us]).to(DEV)
+    tok = torch.zeros((B, 1), dtype=torch.int32, device=DEV)
+    root = torch.zeros((B,), dtype=torch.int32, device=DEV)
+    L = torch.empty((B,), dtype=torch.int32, device=DEV)
+    path = torch.empty((B, 1), dtype=torch.int32, device=DEV)
+    em = torch.empty((B, 1), dtype=torch.int32, device=DEV)
+    tr.tr_step_sample(tree, z.to(DEV), temp, U, M.to(DEV), tok, root, L, path, em, ws)
+    got = root.cpu().tolist()
+    assert got == [bonus for _, bonus in us]
+    assert got == sorted(got) and got[-1] - got[0] > V // 2   # increasing uniforms, increasing ids
+
+
 # ------------------------------------------------------------------ initial M
 @pytest.mark.parametrize("m_dtype", [torch.int32, torch.int64])
 def test_init_matrix_parity(tr, m_dtype):

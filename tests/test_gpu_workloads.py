@@ -42,7 +42,10 @@ def attn_ok(t, out, q, kt, vt, kc, vc, P, dtype):
     return err, err <= 2e-2
 
 
-def run_loop(tr, w, steps, track, attn_steps, update="all"):
+MARGIN = 2e-5      # a uniform this close to a threshold could go either way in float32
+
+
+def run_loop(tr, w, steps, track, attn_steps, update="all", temperature=0.0):
     from draft_tree_retrieval_amd.loop import TRDecoder
     t = O.template_from_levels(w.levels)
     st = W.initial_state(w, DEV)
@@ -76,8 +79,19 @@ def run_loop(tr, w, steps, track, attn_steps, update="all"):
         for b in track:
             gen_tok[b] = torch.from_numpy(otok[b]).to(torch.int32)
         logits = W.step_logits(w, s, gen_tok, DEV)
-        dec.step(logits, kt, vt)
         zl = {b: logits[b].float().cpu().numpy() for b in track}
+        if temperature > 0:
+            # uniforms of every sequence; those of the followed ones redrawn
+            # until every decision clears its threshold
+            ug = torch.Generator().manual_seed(7000 + s)
+            U = torch.rand((w.B, w.T, 2), generator=ug)
+            for b in track:
+                while O.verify_sample(t, otok[b], zl[b], temperature,
+                                      U[b].double().numpy()).margin <= MARGIN:
+                    U[b] = torch.rand((w.T, 2), generator=ug)
+            dec.step_sample(logits, kt, vt, temperature, U.to(DEV))
+        else:
+            dec.step(logits, kt, vt)
         kth = {b: kt[b].float().cpu().numpy() for b in track}
         vth = {b: vt[b].float().cpu().numpy() for b in track}
         gk = dec.topk.cpu().numpy()
@@ -85,7 +99,9 @@ def run_loop(tr, w, steps, track, attn_steps, update="all"):
                                                         dec.prefix_len))
         for b in track:
             res, oP[b] = O.step_after_forward(t, oM[b], otok[b], zl[b], w.k, okc[b], ovc[b],
-                                              kth[b], vth[b], oP[b], update_mode=update)
+                                              kth[b], vth[b], oP[b], update_mode=update,
+                                              temperature=temperature,
+                                              uniforms=U[b].double().numpy() if temperature > 0 else None)
             assert (gk[b] == res.topk).all(), f"step {s} seq {b}: top-k differs"
             v = res.verdict
             assert int(gL[b]) == v.accept_len, f"step {s} seq {b}: accept length"
@@ -132,6 +148,17 @@ def test_tiny_accepted_only_update(tr):
 def test_vicuna7b_accepted_only_update(tr):
     w = W.WORKLOADS["vicuna7b"]
     run_loop(tr, w, 64, [0], {0, 63}, update="accepted")
+
+
+def test_vicuna7b_sampling(tr):
+    # verification by sampling at temperature 1 (tr_step_sample)
+    w = W.WORKLOADS["vicuna7b"]
+    run_loop(tr, w, 48, [0], {0, 47}, temperature=1.0)
+
+
+def test_largevocab_sampling_sampled_sequences(tr):
+    w = W.WORKLOADS["largevocab"]
+    run_loop(tr, w, 16, [0, 31], {0}, temperature=0.8)
 
 
 def test_largevocab_full_sampled_sequences(tr):
