@@ -463,6 +463,53 @@ def commit(k_cache, v_cache, k_tree, v_tree, prefix_len: int, path) -> int:
 
 
 # --------------------------------------------------------------------------
+# paged prefix cache (a storage layout of the same prefix)
+# --------------------------------------------------------------------------
+def page_slot(table_b, page_size: int, pos: int):
+    """(page id, row inside the page) of prefix position pos of one
+    sequence: the block table lists the sequence's pages in order.  READING:
+    the pages fix no cache layout; a paged cache holds the same prefix rows,
+    so every result equals the contiguous cache's."""
+    return int(table_b[pos // page_size]), pos % page_size
+
+
+def gather_pages(pages, table_b, page_size: int, P: int):
+    """The contiguous [Hkv][P][d] prefix of one sequence and one layer from
+    a page pool [num_pages][Hkv][page_size][d]."""
+    Hkv, d = pages.shape[1], pages.shape[3]
+    out = np.zeros((Hkv, P, d), dtype=np.float64)
+    for pos in range(P):
+        pg, r = page_slot(table_b, page_size, pos)
+        out[:, pos, :] = pages[pg, :, r, :]
+    return out
+
+
+def tree_attention_paged(t: Template, q, k_tree, v_tree, k_pages, v_pages, table_b,
+                         page_size: int, prefix_len: int, scale=None) -> np.ndarray:
+    """Tree attention over a paged prefix: the prefix rows gathered in
+    position order, then tree_attention."""
+    kc = gather_pages(k_pages, table_b, page_size, prefix_len)
+    vc = gather_pages(v_pages, table_b, page_size, prefix_len)
+    return tree_attention(t, q, k_tree, v_tree, kc, vc, prefix_len, scale)
+
+
+def commit_paged(k_pages, v_pages, k_tree, v_tree, table_b, page_size: int, prefix_len: int,
+                 path) -> int:
+    """commit() into a paged cache, for every layer: k_pages/v_pages
+    [layers][num_pages][Hkv][page_size][d], k_tree/v_tree [layers][T][Hkv][d].
+    Position prefix_len + i of every layer receives the rows of path[i]."""
+    cap = len(table_b) * page_size
+    if prefix_len + len(path) > cap:
+        raise ValueError("cache capacity exceeded")
+    for layer in range(k_pages.shape[0]):
+        for i, n in enumerate(path):
+            pg, r = page_slot(table_b, page_size, prefix_len + i)
+            k_pages[layer, pg, :, r, :] = k_tree[layer, n]
+            v_pages[layer, pg, :, r, :] = v_tree[layer, n]
+    return prefix_len + len(path)
+
+
+# --------------------------------------------------------------------------
 # one whole step for one sequence
 # --------------------------------------------------------------------------
 @dataclass

@@ -117,6 +117,15 @@ def _sampler(renormalise=True, residual_draw=True, swap_uniforms=False):
     return run
 
 
+def _page_slot_modulo(table_b, page_size, pos):
+    # the page taken by position modulo the table length
+    return int(table_b[pos % len(table_b)]), pos % page_size
+
+
+def _page_slot_swapped(table_b, page_size, pos):
+    return int(table_b[pos % page_size % len(table_b)]), pos // page_size % page_size
+
+
 def _retrieve_rank_off(t, M, root):
     tok = np.empty(t.n_nodes, dtype=np.int64)
     tok[0] = root
@@ -145,7 +154,7 @@ def _attention_wrong_group(t, q, kt, vt, kc, vc, P_, scale=None):
 
 ORIG = {name: getattr(O, name) for name in
         ("verify", "topk_row", "update", "update_accepted", "retrieve", "ancestor_mask",
-         "tree_attention", "splitmix64", "init_matrix", "verify_sample")}
+         "tree_attention", "splitmix64", "init_matrix", "verify_sample", "page_slot")}
 
 CASES = [
     ("verify", _bonus_from_parent, [P.test_worked_example_verify_and_update,
@@ -168,6 +177,10 @@ CASES = [
     ("verify_sample", _sampler(residual_draw=False), [P.test_sample_chain_is_the_speculative_loop,
                                                       P.test_sample_is_lossless]),
     ("verify_sample", _sampler(swap_uniforms=True), [P.test_sample_chain_is_the_speculative_loop]),
+    ("page_slot", _page_slot_modulo, [P.test_paged_attention_equals_contiguous_under_any_page_order,
+                                      P.test_commit_paged_is_commit_per_layer]),
+    ("page_slot", _page_slot_swapped, [P.test_paged_attention_equals_contiguous_under_any_page_order,
+                                       P.test_commit_paged_is_commit_per_layer]),
     ("retrieve", _retrieve_rank_off, [P.test_worked_example_retrieval_gives_merged_sequence,
                                       P.test_retrieve_matches_recursive_definition]),
     ("ancestor_mask", _mask_without_self, [P.test_worked_example_mask,

@@ -560,6 +560,60 @@ def test_attention_matches_per_path_brute_force():
         np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
 
 
+def _paged_copy(rng, caches, page_size, spare=3):
+    """Page pools [num_pages][Hkv][page_size][d] holding each of `caches`
+    [Hkv][cap][d] in the same shuffled pages (spare pages hold junk), and
+    the block table."""
+    Hkv, cap, d = caches[0].shape
+    n = -(-cap // page_size)
+    table = rng.permutation(n + spare)[:n]
+    pools = []
+    for cache in caches:
+        pool = rng.standard_normal((n + spare, Hkv, page_size, d)) * 100.0
+        for pos in range(cap):
+            pool[table[pos // page_size], :, pos % page_size, :] = cache[:, pos, :]
+        pools.append(pool)
+    return pools, table
+
+
+def test_paged_attention_equals_contiguous_under_any_page_order():
+    rng = np.random.default_rng(61)
+    for levels, Hq, Hkv, P, ps in (([[3], [2, 1]], 4, 2, 11, 4), ([[2], [1, 1]], 2, 2, 7, 3),
+                                   ([[1]] * 3, 2, 1, 1, 2), ([[4]], 2, 2, 0, 5)):
+        t = O.template_from_levels(levels)
+        q, kt, vt, kc, vc = rand_attn(rng, t.n_nodes, Hq, Hkv, 8, P, cap=P + 5)
+        (kp, vp), table = _paged_copy(rng, [kc, vc], ps)
+        want = O.tree_attention(t, q, kt, vt, kc, vc, P)
+        got = O.tree_attention_paged(t, q, kt, vt, kp, vp, table, ps, P)
+        np.testing.assert_array_equal(got, want)
+
+
+def test_commit_paged_is_commit_per_layer():
+    rng = np.random.default_rng(62)
+    layers, T, Hkv, d, ps, cap = 3, 7, 2, 4, 4, 16
+    kt = rng.standard_normal((layers, T, Hkv, d))
+    vt = rng.standard_normal((layers, T, Hkv, d))
+    table = rng.permutation(6)[:cap // ps]
+    kp = np.zeros((layers, 6, Hkv, ps, d))
+    vp = np.zeros_like(kp)
+    kc = np.zeros((layers, Hkv, cap, d))
+    vc = np.zeros_like(kc)
+    P, path = 3, [0, 2, 5, 6]                   # rows 3..6 span two pages
+    newP = O.commit_paged(kp, vp, kt, vt, table, ps, P, path)
+    for layer in range(layers):
+        for i, n in enumerate(path):              # position P+i: page table[(P+i) // ps], row (P+i) % ps
+            pg, r = table[(P + i) // ps], (P + i) % ps
+            np.testing.assert_array_equal(kp[layer, pg, :, r], kt[layer, n])
+            np.testing.assert_array_equal(vp[layer, pg, :, r], vt[layer, n])
+        assert O.commit(kc[layer], vc[layer], kt[layer], vt[layer], P, path) == newP == P + 4
+        np.testing.assert_array_equal(O.gather_pages(kp[layer], table, ps, cap), kc[layer])
+        np.testing.assert_array_equal(O.gather_pages(vp[layer], table, ps, cap), vc[layer])
+    unused = [pg for pg in range(6) if pg not in table]
+    assert (kp[:, unused] == 0).all()
+    with pytest.raises(ValueError):
+        O.commit_paged(kp, vp, kt, vt, table, ps, cap - 2, path)
+
+
 def test_chain_tree_is_causal_attention():
     # a chain tree is ordinary causal attention over prefix ++ chain (library SDPA)
     rng = np.random.default_rng(10)
