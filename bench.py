@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--temperature", type=float, default=0.0,
                     help="0: greedy verification (tr_step); above 0: verification by sampling "
                          "at this temperature (tr_step_sample, seeded uniforms)")
+    ap.add_argument("--page-size", type=int, default=0,
+                    help="0: contiguous prefix cache; else a paged cache with pages of this many "
+                         "rows in shuffled order (tr_tree_attn_paged, tr_step_paged)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the CPU oracle baseline (0 disables it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -164,7 +167,10 @@ def main():
     steps = args.steps if args.steps is not None else w.steps
     total = args.warmup + steps
     dev = "cuda"
-    init = W.initial_state(w, dev, cap=w.cap(total))
+    cap = w.cap(total)
+    if args.page_size:
+        cap = -(-cap // args.page_size) * args.page_size
+    init = W.initial_state(w, dev, cap=cap)
     init_host = init.to("cpu")
     tree = tr.Tree.from_levels(w.levels, w.k)
 
@@ -179,7 +185,8 @@ def main():
     # ---- record pass: the trajectory's inputs, kept in HBM
     t0 = time.time()
     st = init.clone()
-    dec = TRDecoder(tree, st.M, st.k_cache, st.v_cache, st.prefix_len, st.root, Hq=w.Hq)
+    dec = TRDecoder(tree, st.M, st.k_cache, st.v_cache, st.prefix_len, st.root, Hq=w.Hq,
+                    page_size=args.page_size or None)
     out = torch.empty((w.B, w.T, w.Hq, w.d), dtype=w.kv_dtype, device=dev)
     ug = torch.Generator(device=dev).manual_seed(w.seed + 77)
     inputs, prefix_hist, accepted = [], [], []
@@ -201,7 +208,8 @@ def main():
 
     # ---- replay: warmup, then the timed region
     st = init.clone()
-    dec = TRDecoder(tree, st.M, st.k_cache, st.v_cache, st.prefix_len, st.root, Hq=w.Hq)
+    dec = TRDecoder(tree, st.M, st.k_cache, st.v_cache, st.prefix_len, st.root, Hq=w.Hq,
+                    page_size=args.page_size or None)
     stream = torch.cuda.current_stream()
     for s in range(args.warmup):
         q, kt, vt, z, U = inputs[s]
@@ -230,7 +238,8 @@ def main():
     # ---- kernel timing: the same steps again, every launch between two HIP
     # events on its stream
     st = init.clone()
-    dec = TRDecoder(tree, st.M, st.k_cache, st.v_cache, st.prefix_len, st.root, Hq=w.Hq)
+    dec = TRDecoder(tree, st.M, st.k_cache, st.v_cache, st.prefix_len, st.root, Hq=w.Hq,
+                    page_size=args.page_size or None)
     for s in range(args.warmup):
         q, kt, vt, z, U = inputs[s]
         dec.attend(q, kt, vt, out)
@@ -319,7 +328,8 @@ def main():
         "config": {"workload": w.description, "V": w.V, "k": w.k, "sequences": w.B,
                    "tree_nodes": w.T, "tree_depth": w.depth, "Hq": w.Hq, "Hkv": w.Hkv,
                    "head_dim": w.d, "prefix": list(w.prefix), "M_dtype": str(w.m_dtype)[6:],
-                   "verification": f"sampling, temperature {temp}" if temp > 0 else "greedy"},
+                   "verification": f"sampling, temperature {temp}" if temp > 0 else "greedy",
+                   "cache": f"paged, {args.page_size} rows per page" if args.page_size else "contiguous"},
         "roofline": roof,
         "per_call": detail,
         "per_kernel": kdetail,

@@ -353,7 +353,9 @@ tr_status step_impl(const tr_tree* t, int32_t B, int64_t V, int32_t k, const voi
                     int32_t* accept_path, int32_t* emitted, int32_t Hkv, int32_t d,
                     tr_dtype kv_dtype, const void* k_tree, const void* v_tree, void* k_cache,
                     void* v_cache, int64_t cap, int32_t* prefix_len, int32_t* topk_out,
-                    tr_update_mode mode, void* ws, size_t ws_bytes, void* stream) {
+                    tr_update_mode mode, void* ws, size_t ws_bytes, void* stream,
+                    const tr::PagedArgs* paged = nullptr, int32_t n_layers = 1,
+                    int64_t tree_layer_bytes = 0, int64_t cache_layer_bytes = 0) {
   TR_CHECK(mode == TR_UPDATE_ALL || mode == TR_UPDATE_ACCEPTED, TR_ERR_INVALID_ARGUMENT,
            "unknown update mode %d", int(mode));
   const bool sample = temperature != 0.f;
@@ -406,6 +408,10 @@ tr_status step_impl(const tr_tree* t, int32_t B, int64_t V, int32_t k, const voi
   tail.cap = cap;
   tail.Hkv = Hkv;
   tail.row_bytes = row_bytes;
+  tail.n_layers = n_layers;
+  tail.tree_layer_bytes = tree_layer_bytes;
+  tail.cache_layer_bytes = cache_layer_bytes;
+  if (paged) tail.paged = *paged;
   return hip_status(tr::launch_topk(t->dev, B, logits, l_dtype == TR_BFLOAT16, V, k, ids, tail, w,
                                     plan, hipStream_t(stream)),
                     "tr_step");
@@ -438,6 +444,86 @@ tr_status tr_step_sample(const tr_tree* t, int32_t B, int64_t V, int32_t k, cons
   return step_impl(t, B, V, k, logits, l_dtype, temperature, uniforms, M, m_dtype, tree_tok,
                    root_tok, accept_len, accept_path, emitted, Hkv, d, kv_dtype, k_tree, v_tree,
                    k_cache, v_cache, cap, prefix_len, topk_out, mode, ws, ws_bytes, stream);
+}
+
+// Checks a paged cache description; fills the kernels' view of it.
+static tr_status check_paged(const tr_paged_kv* kv, int32_t B, tr::PagedArgs* pa) {
+  TR_CHECK(kv != nullptr, TR_ERR_INVALID_ARGUMENT, "kv is null");
+  TR_CHECK(kv->n_layers >= 1 && kv->Hkv >= 1, TR_ERR_INVALID_ARGUMENT, "bad n_layers or Hkv");
+  TR_CHECK(kv->d == tr::kHeadDim, TR_ERR_UNSUPPORTED, "head dimension must be %d", tr::kHeadDim);
+  TR_CHECK(kv->dtype == TR_BFLOAT16, TR_ERR_UNSUPPORTED, "paged caches hold bfloat16");
+  TR_CHECK(kv->page_size >= 64 && (kv->page_size & (kv->page_size - 1)) == 0,
+           TR_ERR_INVALID_ARGUMENT, "page_size must be a power of two >= 64");
+  TR_CHECK(kv->num_pages >= 1 && kv->max_pages >= 1, TR_ERR_INVALID_ARGUMENT,
+           "num_pages and max_pages must be >= 1");
+  TR_CHECK(kv->block_table && kv->k_pages && kv->v_pages && kv->k_tree && kv->v_tree &&
+               kv->prefix_len, TR_ERR_INVALID_ARGUMENT, "null tensor in kv");
+  TR_CHECK(aligned16(kv->k_pages) && aligned16(kv->v_pages) && aligned16(kv->k_tree) &&
+               aligned16(kv->v_tree), TR_ERR_INVALID_ARGUMENT, "kv tensors must be 16-byte aligned");
+  (void)B;
+  pa->table = kv->block_table;
+  pa->max_pages = kv->max_pages;
+  pa->page_size = kv->page_size;
+  pa->ps_log2 = __builtin_ctz(uint32_t(kv->page_size));
+  pa->num_pages = kv->num_pages;
+  return TR_OK;
+}
+
+tr_status tr_tree_attn_paged(const tr_tree* t, int32_t B, int32_t Hq, const void* q,
+                             const tr_paged_kv* kv, int32_t layer, float scale, void* out,
+                             void* ws, size_t ws_bytes, void* stream) {
+  tr::PagedArgs pa{};
+  tr_status st = check_paged(kv, B, &pa);
+  if (st != TR_OK) return st;
+  TR_CHECK(t != nullptr, TR_ERR_INVALID_ARGUMENT, "tree is null");
+  TR_CHECK(B >= 1, TR_ERR_INVALID_ARGUMENT, "B must be >= 1");
+  TR_CHECK(layer >= 0 && layer < kv->n_layers, TR_ERR_INVALID_ARGUMENT, "layer %d outside [0, %d)",
+           layer, kv->n_layers);
+  TR_CHECK(q && out, TR_ERR_INVALID_ARGUMENT, "null tensor");
+  const int32_t Hkv = kv->Hkv;
+  TR_CHECK(Hq >= 1 && Hq % Hkv == 0, TR_ERR_INVALID_ARGUMENT,
+           "Hq (%d) must be a positive multiple of Hkv (%d)", Hq, Hkv);
+  TR_CHECK(scale > 0.f && scale < 1e30f, TR_ERR_INVALID_ARGUMENT, "scale must be positive and finite");
+  TR_CHECK(int64_t(B) * Hkv <= 65535, TR_ERR_UNSUPPORTED, "B*Hkv above 65535");
+  TR_CHECK(aligned16(q) && aligned16(out), TR_ERR_INVALID_ARGUMENT,
+           "attention tensors must be 16-byte aligned");
+  const int64_t cap = int64_t(kv->max_pages) * kv->page_size;
+  const tr::AttnPlan plan = tr::plan_attn(t->dev.T, B, Hq, Hkv, cap, 1);
+  // the longest chunk (at prefix length cap) and the pages it may touch
+  const int64_t cs = ((cap + plan.chunks - 1) / plan.chunks + 63) / 64 * 64;
+  TR_CHECK(cs / kv->page_size + 2 <= tr::kMaxChunkPages, TR_ERR_UNSUPPORTED,
+           "a prefix chunk would span more than %d pages", tr::kMaxChunkPages);
+  st = check_ws(ws, ws_bytes, plan.end);
+  if (st != TR_OK) return st;
+  const size_t row = size_t(Hkv) * tr::kHeadDim * 2;
+  const int64_t T = t->dev.T;
+  const uint8_t* kt = static_cast<const uint8_t*>(kv->k_tree) + layer * int64_t(B) * T * row;
+  const uint8_t* vt = static_cast<const uint8_t*>(kv->v_tree) + layer * int64_t(B) * T * row;
+  const int64_t pool = kv->num_pages * kv->page_size * int64_t(row);
+  const uint8_t* kp = static_cast<const uint8_t*>(kv->k_pages) + layer * pool;
+  const uint8_t* vp = static_cast<const uint8_t*>(kv->v_pages) + layer * pool;
+  return hip_status(tr::launch_attn(t->dev, B, Hq, Hkv, 1, q, kt, vt, kp, vp, cap, kv->prefix_len,
+                                    scale, out, static_cast<uint8_t*>(ws), plan,
+                                    hipStream_t(stream), &pa),
+                    "tr_tree_attn_paged");
+}
+
+tr_status tr_step_paged(const tr_tree* t, int32_t B, int64_t V, int32_t k, const void* logits,
+                        tr_dtype l_dtype, void* M, tr_dtype m_dtype, int32_t* tree_tok,
+                        int32_t* root_tok, int32_t* accept_len, int32_t* accept_path,
+                        int32_t* emitted, const tr_paged_kv* kv, int32_t* topk_out,
+                        tr_update_mode mode, void* ws, size_t ws_bytes, void* stream) {
+  tr::PagedArgs pa{};
+  tr_status st = check_paged(kv, B, &pa);
+  if (st != TR_OK) return st;
+  TR_CHECK(t != nullptr, TR_ERR_INVALID_ARGUMENT, "tree is null");
+  const int64_t row = int64_t(kv->Hkv) * tr::kHeadDim * 2;
+  const int64_t cap = int64_t(kv->max_pages) * kv->page_size;
+  return step_impl(t, B, V, k, logits, l_dtype, 0.f, nullptr, M, m_dtype, tree_tok, root_tok,
+                   accept_len, accept_path, emitted, kv->Hkv, kv->d, kv->dtype, kv->k_tree,
+                   kv->v_tree, kv->k_pages, kv->v_pages, cap, kv->prefix_len, topk_out, mode, ws,
+                   ws_bytes, stream, &pa, kv->n_layers, int64_t(B) * t->dev.T * row,
+                   kv->num_pages * kv->page_size * row);
 }
 
 tr_status tr_step(const tr_tree* t, int32_t B, int64_t V, int32_t k, const void* logits,

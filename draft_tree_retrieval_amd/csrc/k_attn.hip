@@ -99,12 +99,16 @@ __device__ __forceinline__ void mark_empty(float2* part_ml, int64_t unit0, int r
 // sub-block).
 constexpr int kSB = 64;                   // keys per sub-block
 constexpr int kVtS = kSB + 4;             // bf16 per staged V^T row: 136 bytes
-template <int SPW>
+// PAGED: kc and vc are page pools [num_pages][Hkv][page_size][d] reached
+// through the block table; the chunk's page ids are read into LDS first and
+// each 64-key sub-block (inside one page: page sizes are powers of two of
+// at least 64 keys) looks its page up once.
+template <int SPW, bool PAGED>
 __global__ __launch_bounds__(512) void attn_prefix_bf16(
     const uint16_t* __restrict__ q, const uint16_t* kc,
     const uint16_t* vc, int64_t cap, const int32_t* __restrict__ prefix_len, int T,
     int Hq, int Hkv, int G, int R, int chunks, float sl2, uint16_t* __restrict__ part_o,
-    float2* __restrict__ part_ml, uint8_t* ws, int B, int row_tiles) {
+    float2* __restrict__ part_ml, uint8_t* ws, int B, int row_tiles, PagedArgs pg) {
   constexpr int kRows = kWaves * SPW * 16;        // query rows per tile
   // Blocks are dealt to the 8 XCDs round-robin by block index.  The row
   // tiles of one (sequence, kv head, chunk) group read the same keys and
@@ -132,6 +136,20 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
 
   __shared__ __attribute__((aligned(16))) uint16_t Ks2[2][kSB * kKsStride];
   __shared__ __attribute__((aligned(16))) uint16_t Vt2[2][kHeadDim * kVtS];
+  __shared__ int32_t s_pg[PAGED ? kMaxChunkPages : 1];
+  const int p0 = PAGED ? (k0 >> pg.ps_log2) : 0;    // first page of the chunk
+  if constexpr (PAGED) {
+    const int np = ((k1 - 1) >> pg.ps_log2) - p0 + 1;   // <= kMaxChunkPages by the plan
+    for (int i = threadIdx.x; i < np; i += blockDim.x) {
+      int32_t id = pg.table[int64_t(b) * pg.max_pages + p0 + i];
+      if (id < 0 || int64_t(id) >= pg.num_pages) {     // stays inside the pool
+        set_flag(ws, TR_FLAG_BAD_PAGE);
+        id = 0;
+      }
+      s_pg[i] = id;
+    }
+    __syncthreads();
+  }
 
   bf16x8 qb[SPW][4];
 #pragma unroll
@@ -159,7 +177,7 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
     for (int dt = 0; dt < 8; ++dt) acc[s][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int64_t head_off = (int64_t(b) * Hkv + kvh) * cap * kHeadDim;
+  const int64_t head_off = PAGED ? 0 : (int64_t(b) * Hkv + kvh) * cap * kHeadDim;
   const uint16_t* kbase = kc + head_off;
   const uint16_t* vbase = vc + head_off;
   const int cch = tid & 15;     // K: 16-byte column chunk; rows (tid >> 4) + 32 j
@@ -174,12 +192,23 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
   // sub-blocks past the end reload the last sub-block.
   auto load = [&](u32x4 (&kr)[2], u32x4 (&vr)[2], int j) {
     const int kb = k0 + min(j, nsub - 1) * kSB;
+    // rows kb .. kb+63 (and the clamp k1-1 >= kb) lie in one page
+    const uint16_t* kp = kbase;
+    const uint16_t* vp = vbase;
+    int row_base = 0;
+    if constexpr (PAGED) {
+      const int64_t pool_off =
+          (int64_t(s_pg[(kb >> pg.ps_log2) - p0]) * Hkv + kvh) * pg.page_size * kHeadDim;
+      kp = kc + pool_off;
+      vp = vc + pool_off;
+      row_base = (kb >> pg.ps_log2) << pg.ps_log2;   // first position of the page
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int rk = min(kb + rk0 + 32 * i, k1 - 1);
-      kr[i] = *reinterpret_cast<const u32x4*>(kbase + int64_t(rk) * kHeadDim + cch * 8);
-      const int rv = min(kb + 2 * vq + i, k1 - 1);
-      vr[i] = *reinterpret_cast<const u32x4*>(vbase + int64_t(rv) * kHeadDim + vd * 8);
+      const int rk = min(kb + rk0 + 32 * i, k1 - 1) - row_base;
+      kr[i] = *reinterpret_cast<const u32x4*>(kp + int64_t(rk) * kHeadDim + cch * 8);
+      const int rv = min(kb + 2 * vq + i, k1 - 1) - row_base;
+      vr[i] = *reinterpret_cast<const u32x4*>(vp + int64_t(rv) * kHeadDim + vd * 8);
     }
   };
   auto stage = [&](const u32x4 (&kr)[2], const u32x4 (&vr)[2], int buf) {
@@ -644,7 +673,8 @@ __global__ __launch_bounds__(128) void attn_combine(
 hipError_t launch_attn(const TreeDev& tree, int32_t B, int32_t Hq, int32_t Hkv, int is_bf16,
                        const void* q, const void* k_tree, const void* v_tree, const void* k_cache,
                        const void* v_cache, int64_t cap, const int32_t* prefix_len, float scale,
-                       void* out, uint8_t* ws, const AttnPlan& plan, hipStream_t s) {
+                       void* out, uint8_t* ws, const AttnPlan& plan, hipStream_t s,
+                       const PagedArgs* paged) {
   void* part_o = ws + plan.o_off;
   float2* part_ml = reinterpret_cast<float2*>(ws + plan.ml_off);
   const float sl2 = scale * kLog2e;
@@ -656,9 +686,16 @@ hipError_t launch_attn(const TreeDev& tree, int32_t B, int32_t Hq, int32_t Hkv, 
     const auto* qq = reinterpret_cast<const uint16_t*>(q);
     const auto* kk = reinterpret_cast<const uint16_t*>(k_cache);
     const auto* vv = reinterpret_cast<const uint16_t*>(v_cache);
-    hipLaunchKernelGGL(attn_prefix_bf16<2>, grid1, dim3(64 * kWaves), 0, s, qq, kk, vv, cap,
-                       prefix_len, tree.T, Hq, Hkv, plan.G, plan.R, plan.chunks, sl2,
-                       reinterpret_cast<uint16_t*>(part_o), part_ml, ws, B, plan.row_tiles);
+    if (paged)
+      hipLaunchKernelGGL((attn_prefix_bf16<2, true>), grid1, dim3(64 * kWaves), 0, s, qq, kk, vv,
+                         cap, prefix_len, tree.T, Hq, Hkv, plan.G, plan.R, plan.chunks, sl2,
+                         reinterpret_cast<uint16_t*>(part_o), part_ml, ws, B, plan.row_tiles,
+                         *paged);
+    else
+      hipLaunchKernelGGL((attn_prefix_bf16<2, false>), grid1, dim3(64 * kWaves), 0, s, qq, kk, vv,
+                         cap, prefix_len, tree.T, Hq, Hkv, plan.G, plan.R, plan.chunks, sl2,
+                         reinterpret_cast<uint16_t*>(part_o), part_ml, ws, B, plan.row_tiles,
+                         PagedArgs{});
   } else {
     hipLaunchKernelGGL(attn_prefix_f32, grid, dim3(256), 0, s, reinterpret_cast<const float*>(q),
                        reinterpret_cast<const float*>(k_cache), reinterpret_cast<const float*>(v_cache),

@@ -261,7 +261,8 @@ __device__ __forceinline__ void tail_update_store(const TailShared& S, const Tre
 // the threads [first, blockDim.x), R 16-byte units per thread in flight.
 // Returns whether the rows fit (the caller advances the prefix length);
 // they are copied only then.  S.L (verification) and S.P (tail_load) must
-// be visible.
+// be visible.  A paged cache copies every layer's rows, each position into
+// row p % page_size of page table[b][p / page_size] of that layer's pool.
 __device__ __forceinline__ bool tail_commit(const TailShared& S, const TreeDev& tree, int b,
                                             const TailArgs& a, uint8_t* ws, int first) {
   if (!a.k_cache) return false;
@@ -273,9 +274,11 @@ __device__ __forceinline__ bool tail_commit(const TailShared& S, const TreeDev& 
   }
   const int me = int(threadIdx.x) - first, count = int(blockDim.x) - first;
   if (me < 0) return true;
+  const bool paged = a.paged.table != nullptr;
   const int upr = a.row_bytes >> 4;               // 16-byte units per row
   const int per_node = a.Hkv * upr;
-  const int total = 2 * nrows * per_node;          // keys then values
+  const int per_layer = 2 * nrows * per_node;      // keys then values
+  const int total = per_layer * a.n_layers;
   constexpr int R = 4;
   for (int u0 = me; u0 < total; u0 += R * count) {
     u32x4 buf[R];
@@ -284,14 +287,28 @@ __device__ __forceinline__ bool tail_commit(const TailShared& S, const TreeDev& 
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int u = min(u0 + r * count, total - 1);   // clamped: loads stay in bounds
-      const bool isv = u >= total / 2;
-      const int uu = isv ? u - total / 2 : u;
+      const int layer = u / per_layer;
+      const int ul = u - layer * per_layer;
+      const bool isv = ul >= per_layer / 2;
+      const int uu = isv ? ul - per_layer / 2 : ul;
       const int i = uu / per_node, rem = uu - i * per_node;
       const int h = rem / upr, c = rem - h * upr;
       const int node = S.path[i];
-      const uint8_t* src = (isv ? a.v_tree : a.k_tree) +
+      const uint8_t* src = (isv ? a.v_tree : a.k_tree) + layer * a.tree_layer_bytes +
                            ((int64_t(b) * tree.T + node) * a.Hkv + h) * a.row_bytes + c * 16;
-      dst_off[r] = ((int64_t(b) * a.Hkv + h) * a.cap + P + i) * a.row_bytes + c * 16;
+      if (paged) {
+        const int64_t pos = P + i;
+        int64_t pg = a.paged.table[int64_t(b) * a.paged.max_pages + (pos >> a.paged.ps_log2)];
+        if (pg < 0 || pg >= a.paged.num_pages) {       // stays inside the pool
+          set_flag(ws, TR_FLAG_BAD_PAGE);
+          pg = 0;
+        }
+        dst_off[r] = layer * a.cache_layer_bytes +
+                     ((pg * a.Hkv + h) * a.paged.page_size + (pos & (a.paged.page_size - 1))) *
+                         a.row_bytes + c * 16;
+      } else {
+        dst_off[r] = ((int64_t(b) * a.Hkv + h) * a.cap + P + i) * a.row_bytes + c * 16;
+      }
       dst_v[r] = isv;
       buf[r] = *reinterpret_cast<const u32x4*>(src);
     }

@@ -79,6 +79,18 @@ struct AttnPlan {
 AttnPlan plan_attn(int32_t T, int32_t B, int32_t Hq, int32_t Hkv, int64_t cap, int is_bf16);
 
 // ---------------------------------------------------------------- launchers
+// Paged prefix cache: a pool [num_pages][Hkv][page_size][d] per layer and a
+// block table [B][max_pages] of page ids (position p of sequence b is row
+// p % page_size of page table[b][p / page_size]).
+constexpr int kMaxChunkPages = 256;    // pages one prefix chunk may span
+struct PagedArgs {
+  const int32_t* table;
+  int32_t max_pages;
+  int32_t page_size;       // a power of two, at least 64
+  int32_t ps_log2;
+  int64_t num_pages;
+};
+
 enum TailMode : int32_t { TAIL_NONE = 0, TAIL_UPDATE = 1, TAIL_STEP = 2 };
 
 enum UpdateMode : int32_t { UPDATE_ALL = 0, UPDATE_ACCEPTED = 1 };
@@ -105,6 +117,11 @@ struct TailArgs {
   int64_t cap;
   int32_t Hkv;
   int32_t row_bytes;       // d * element size
+  // paged cache (k_cache/v_cache are then the pools of layer 0)
+  PagedArgs paged;         // paged.table null: contiguous [B][Hkv][cap][d]
+  int32_t n_layers;        // layers committed (1 for the contiguous cache)
+  int64_t tree_layer_bytes;   // stride between layers of k_tree/v_tree
+  int64_t cache_layer_bytes;  // stride between layers' pools
 };
 
 // Profiling hooks around each launch (no-ops unless tr_profile_enable).
@@ -128,6 +145,7 @@ hipError_t launch_init_m(int mode, void* M, int m_is64, int32_t B, int64_t V, in
 hipError_t launch_attn(const TreeDev& tree, int32_t B, int32_t Hq, int32_t Hkv, int is_bf16,
                        const void* q, const void* k_tree, const void* v_tree, const void* k_cache,
                        const void* v_cache, int64_t cap, const int32_t* prefix_len, float scale,
-                       void* out, uint8_t* ws, const AttnPlan& plan, hipStream_t s);
+                       void* out, uint8_t* ws, const AttnPlan& plan, hipStream_t s,
+                       const PagedArgs* paged = nullptr);
 
 }  // namespace tr

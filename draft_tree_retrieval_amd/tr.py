@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libtr.so")
 TR_OK, TR_ERR_INVALID_ARGUMENT, TR_ERR_UNSUPPORTED, TR_ERR_INVALID_TREE, \
     TR_ERR_WORKSPACE_TOO_SMALL, TR_ERR_HIP = range(6)
 TR_INT32, TR_INT64, TR_FLOAT32, TR_BFLOAT16 = range(4)
-TR_FLAG_BAD_TOKEN, TR_FLAG_CACHE_FULL, TR_FLAG_BAD_PREFIX = 1, 2, 4
+TR_FLAG_BAD_TOKEN, TR_FLAG_CACHE_FULL, TR_FLAG_BAD_PREFIX, TR_FLAG_BAD_PAGE = 1, 2, 4, 8
 
 _DT = {torch.int32: TR_INT32, torch.int64: TR_INT64, torch.float32: TR_FLOAT32,
        torch.bfloat16: TR_BFLOAT16}
@@ -51,6 +51,9 @@ _SIGS = {
     "tr_step_sample": ([_P, _I32, _I64, _I32, _P, C.c_int, C.c_float, _P, _P, C.c_int, _P, _P,
                         _P, _P, _P, _I32, _I32, C.c_int, _P, _P, _P, _P, _I64, _P, _P, C.c_int,
                         _P, _SZ, _P], C.c_int),
+    "tr_tree_attn_paged": ([_P, _I32, _I32, _P, _P, _I32, C.c_float, _P, _P, _SZ, _P], C.c_int),
+    "tr_step_paged": ([_P, _I32, _I64, _I32, _P, C.c_int, _P, C.c_int, _P, _P, _P, _P, _P, _P, _P,
+                       C.c_int, _P, _SZ, _P], C.c_int),
     "tr_init_matrix": ([_I32, _I64, _I32, _P, C.c_int, C.c_int, _P, C.c_int, _I32, C.c_uint64,
                         _P], C.c_int),
     "tr_profile_enable": ([_I32], C.c_int),
@@ -195,6 +198,48 @@ def tr_tree_attn(tree, q, k_tree, v_tree, k_cache, v_cache, prefix_len, out, ws,
     _check(load().tr_tree_attn(tree.handle, B, Hq, Hkv, d, _dt(q), _ptr(q), _ptr(k_tree),
                                _ptr(v_tree), _ptr(k_cache), _ptr(v_cache), cap, _ptr(prefix_len),
                                float(scale), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+class _PagedKVStruct(C.Structure):
+    _fields_ = [("n_layers", C.c_int32), ("Hkv", C.c_int32), ("d", C.c_int32), ("dtype", C.c_int),
+                ("page_size", C.c_int32), ("num_pages", C.c_int64), ("max_pages", C.c_int32),
+                ("block_table", C.c_void_p), ("k_pages", C.c_void_p), ("v_pages", C.c_void_p),
+                ("k_tree", C.c_void_p), ("v_tree", C.c_void_p), ("prefix_len", C.c_void_p)]
+
+
+class PagedKV:
+    """A tr_paged_kv over caller tensors: pools k_pages/v_pages
+    [layers][num_pages][Hkv][page_size][d], block_table [B][max_pages] int32,
+    tree rows k_tree/v_tree [layers][B][T][Hkv][d], prefix_len [B] int32."""
+
+    def __init__(self, k_pages, v_pages, block_table, k_tree, v_tree, prefix_len):
+        L, npg, Hkv, ps, d = k_pages.shape
+        self.tensors = (k_pages, v_pages, block_table, k_tree, v_tree, prefix_len)
+        self.s = _PagedKVStruct(L, Hkv, d, _dt(k_pages), ps, npg, block_table.shape[1],
+                                _ptr(block_table), _ptr(k_pages), _ptr(v_pages), _ptr(k_tree),
+                                _ptr(v_tree), _ptr(prefix_len))
+
+    @property
+    def ref(self):
+        return C.byref(self.s)
+
+
+def tr_tree_attn_paged(tree, q, kv, layer, out, ws, scale=None, stream=None):
+    B, T, Hq, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check(load().tr_tree_attn_paged(tree.handle, B, Hq, _ptr(q), kv.ref, layer, float(scale),
+                                     _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def tr_step_paged(tree, logits, M, tree_tok, root_tok, accept_len, accept_path, emitted, ws, kv,
+                  topk_out=None, update="all", stream=None):
+    mode = _UPDATE_MODES[update] if isinstance(update, str) else int(update)
+    B, T, V = logits.shape
+    _check(load().tr_step_paged(tree.handle, B, V, tree.k, _ptr(logits), _dt(logits), _ptr(M),
+                                _dt(M), _ptr(tree_tok), _ptr(root_tok), _ptr(accept_len),
+                                _ptr(accept_path), _ptr(emitted), kv.ref, _ptr(topk_out), mode,
+                                _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def tr_update_topk(tree, logits, tree_tok, M, topk_out, ws, stream=None):

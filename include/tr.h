@@ -62,7 +62,8 @@ typedef enum {
 
 typedef enum { TR_INT32 = 0, TR_INT64 = 1, TR_FLOAT32 = 2, TR_BFLOAT16 = 3 } tr_dtype;
 
-enum { TR_FLAG_BAD_TOKEN = 1u, TR_FLAG_CACHE_FULL = 2u, TR_FLAG_BAD_PREFIX = 4u };
+enum { TR_FLAG_BAD_TOKEN = 1u, TR_FLAG_CACHE_FULL = 2u, TR_FLAG_BAD_PREFIX = 4u,
+       TR_FLAG_BAD_PAGE = 8u };
 
 /* Opaque, immutable draft-tree template (host memory, library-owned).
  * Shareable across streams and threads. */
@@ -266,6 +267,54 @@ tr_status tr_step_sample(const tr_tree* t, int32_t B, int64_t V, int32_t k, cons
                          void* k_cache, void* v_cache, int64_t cap, int32_t* prefix_len,
                          int32_t* topk_out, tr_update_mode mode, void* ws, size_t ws_bytes,
                          void* stream);
+
+/* ------------------------------------------------------------------------
+ * Paged prefix cache, all layers of a model.  The pages fix no cache
+ * layout; this one stores the same prefix rows as the contiguous
+ * [B][Hkv][cap][d] cache, so every result equals the contiguous one.
+ * Position p of sequence b is row p % page_size of page
+ * block_table[b][p / page_size].  All pointers inside are device memory
+ * owned by the caller; the struct itself is read on the host during the
+ * call only.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t n_layers;            /* layers in the pools and tree rows, >= 1 */
+  int32_t Hkv;                 /* key/value heads */
+  int32_t d;                   /* head dimension: 128 */
+  tr_dtype dtype;              /* TR_BFLOAT16 */
+  int32_t page_size;           /* rows per page: a power of two, >= 64 */
+  int64_t num_pages;           /* pages in each layer's pool */
+  int32_t max_pages;           /* block-table entries per sequence */
+  const int32_t* block_table;  /* [B][max_pages] page ids in [0, num_pages) */
+  void* k_pages;               /* [n_layers][num_pages][Hkv][page_size][d] */
+  void* v_pages;
+  const void* k_tree;          /* [n_layers][B][T][Hkv][d]: this step's tree rows */
+  const void* v_tree;
+  int32_t* prefix_len;         /* [B], capacity max_pages * page_size */
+} tr_paged_kv;
+
+/* tr_tree_attn for layer `layer` of a paged cache: q [B][T][Hq][d] and out
+ * [B][T][Hq][d] of that layer; the tree rows and the prefix pages are the
+ * layer's slices of kv.  A page id outside [0, num_pages) reads page 0 and
+ * sets TR_FLAG_BAD_PAGE.  Errors as tr_tree_attn, plus
+ * TR_ERR_INVALID_ARGUMENT for a layer outside [0, n_layers) or a page size
+ * that is not a power of two of at least 64, and TR_ERR_UNSUPPORTED for
+ * float32 pages or a prefix chunk spanning more than 256 pages.  Workspace:
+ * tr_workspace_size with cap = max_pages * page_size. */
+tr_status tr_tree_attn_paged(const tr_tree* t, int32_t B, int32_t Hq, const void* q,
+                             const tr_paged_kv* kv, int32_t layer, float scale, void* out,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* tr_step_ex with a paged cache: the commit copies the accepted rows of
+ * every layer (kv->k_tree / v_tree) into positions prefix_len ..
+ * prefix_len+L of each layer's pages; a commit past max_pages * page_size
+ * is skipped with TR_FLAG_CACHE_FULL, a bad page id writes page 0 and sets
+ * TR_FLAG_BAD_PAGE.  Everything else as tr_step_ex. */
+tr_status tr_step_paged(const tr_tree* t, int32_t B, int64_t V, int32_t k, const void* logits,
+                        tr_dtype l_dtype, void* M, tr_dtype m_dtype, int32_t* tree_tok,
+                        int32_t* root_tok, int32_t* accept_len, int32_t* accept_path,
+                        int32_t* emitted, const tr_paged_kv* kv, int32_t* topk_out,
+                        tr_update_mode mode, void* ws, size_t ws_bytes, void* stream);
 
 /* Initial contents of M (Token Recycling, Method, first module: a hot start
  * inherits the matrix left by earlier inference instead of an empty one;

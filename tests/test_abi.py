@@ -115,15 +115,31 @@ def test_host_checks_launch_nothing(tr):
     assert lib.tr_tree_attn(*args(64, 8, 8, tr.TR_BFLOAT16)) == tr.TR_ERR_UNSUPPORTED
     assert lib.tr_tree_attn(*args(128, 6, 4, tr.TR_BFLOAT16)) == tr.TR_ERR_INVALID_ARGUMENT
     assert lib.tr_tree_attn(*args(128, 8, 8, tr.TR_INT32)) == tr.TR_ERR_UNSUPPORTED
-    # tr_workspace_size covers both dtypes (fp32 partials are the larger):
-    # one byte short fails the fp32 call, a bare header fails the bf16 one
+    # tr_workspace_size covers both dtypes (the bf16 plan, 256-row tiles,
+    # needs the more): one byte short fails the bf16 call, a bare header
+    # fails the fp32 one
     need = tr.tr_workspace_size(tree, 1, 0, 0, 8, 8, 128, 64)
-    a = list(args(128, 8, 8, tr.TR_FLOAT32))
+    a = list(args(128, 8, 8, tr.TR_BFLOAT16))
     a[-2] = need - 1
     assert lib.tr_tree_attn(*a) == tr.TR_ERR_WORKSPACE_TOO_SMALL
-    a = list(args(128, 8, 8, tr.TR_BFLOAT16))
+    a = list(args(128, 8, 8, tr.TR_FLOAT32))
     a[-2] = 256 * 1024
     assert lib.tr_tree_attn(*a) == tr.TR_ERR_WORKSPACE_TOO_SMALL
+    # paged: bad page size, layer, dtype (checked before anything launches)
+    pk = tr._PagedKVStruct(2, 8, 128, tr.TR_BFLOAT16, 96, 10, 4, 1 << 20, 1 << 20, 1 << 20,
+                           1 << 20, 1 << 20, 1 << 20)
+    pa = lambda layer: lib.tr_tree_attn_paged(h, 1, 8, fake, C.byref(pk), layer, C.c_float(0.1),
+                                              fake, ws, 1 << 30, None)
+    assert pa(0) == tr.TR_ERR_INVALID_ARGUMENT           # 96 is not a power of two
+    pk.page_size = 64
+    assert pa(2) == tr.TR_ERR_INVALID_ARGUMENT           # layer outside [0, 2)
+    pk.dtype = tr.TR_FLOAT32
+    assert pa(0) == tr.TR_ERR_UNSUPPORTED
+    pk.dtype = tr.TR_BFLOAT16
+    pk.block_table = None
+    assert lib.tr_step_paged(h, 1, 16, 3, fake, tr.TR_BFLOAT16, fake, tr.TR_INT32, fake, fake, fake,
+                             None, None, C.byref(pk), None, 0, ws, 1 << 30, None) == \
+        tr.TR_ERR_INVALID_ARGUMENT                         # null block table
     # top-k / update / step
     assert lib.tr_update_topk(h, 1, fake, tr.TR_BFLOAT16, 2, 3, fake, fake, tr.TR_INT32, None, ws,
                               1 << 30, None) == tr.TR_ERR_INVALID_ARGUMENT        # V < k

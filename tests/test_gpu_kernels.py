@@ -439,6 +439,110 @@ def test_step_sample_draw_covers_the_row(tr):
     assert got == sorted(got) and got[-1] - got[0] > V // 2   # increasing uniforms, increasing ids
 
 
+# ------------------------------------------------------------------ paged cache
+def paged_from_contiguous(g, kc, ps, spare=3, layers=1):
+    """Pools [layers][num_pages][Hkv][ps][d] holding the contiguous caches kc
+    [layers][B][Hkv][cap][d] in shuffled pages (junk in the spare pages) and
+    the block table [B][cap / ps]."""
+    L, B, Hkv, cap, d = kc.shape
+    mp = cap // ps
+    n = B * mp + spare
+    perm = torch.randperm(n, generator=g)
+    table = perm[:B * mp].reshape(B, mp).to(torch.int32)
+    pool = (torch.randn((L, n, Hkv, ps, d), generator=g) * 50).to(kc.dtype)
+    for b in range(B):
+        for j in range(mp):
+            pool[:, table[b, j]] = kc[:, b, :, j * ps:(j + 1) * ps]
+    return pool, table
+
+
+@pytest.mark.parametrize("ps", [64, 128])
+def test_paged_attention_parity(tr, ps):
+    g = torch.Generator().manual_seed(71)
+    levels = RAND_LEVELS[1]
+    t = otree(levels)
+    tree = tr.Tree.from_levels(levels, 8)
+    B, Hq, Hkv, d, cap = 2, 8, 4, 128, 512
+    P = torch.tensor([200, 391], dtype=torch.int32)
+    mk = lambda *sh: torch.randn(sh, generator=g).to(torch.bfloat16)
+    q, kt, vt = mk(B, t.n_nodes, Hq, d), mk(1, B, t.n_nodes, Hkv, d), mk(1, B, t.n_nodes, Hkv, d)
+    kc, vc = mk(1, B, Hkv, cap, d), mk(1, B, Hkv, cap, d)
+    kp, table = paged_from_contiguous(g, kc, ps)
+    vp = torch.empty_like(kp)
+    for b in range(B):
+        for j in range(cap // ps):
+            vp[:, table[b, j]] = vc[:, b, :, j * ps:(j + 1) * ps]
+    D = [x.to(DEV) for x in (q, kt, vt, kc, vc, kp, vp, table, P)]
+    dq, dkt, dvt, dkc, dvc, dkp, dvp, dtab, dP = D
+    ws = ws_for(tr, tree, B, 0, 0, Hq, Hkv, cap)
+    kv = tr.PagedKV(dkp, dvp, dtab, dkt, dvt, dP)
+    out_p = torch.empty_like(dq)
+    tr.tr_tree_attn_paged(tree, dq, kv, 0, out_p, ws)
+    out_c = torch.empty_like(dq)
+    tr.tr_tree_attn(tree, dq, dkt[0], dvt[0], dkc[0], dvc[0], dP, out_c, ws)
+    assert torch.equal(out_p, out_c)                 # the same arithmetic in the same order
+    for b in range(B):
+        want = O.tree_attention_paged(t, q[b].float().numpy(), kt[0, b].float().numpy(),
+                                      vt[0, b].float().numpy(), kp[0].float().numpy(),
+                                      vp[0].float().numpy(), table[b].numpy(), ps, int(P[b]))
+        assert np.abs(out_p[b].float().cpu().numpy() - want).max() <= 2e-2
+    assert tr.tr_read_device_status(ws) == 0
+    # a page id outside the pool reads page 0 and raises the flag
+    bad = dtab.clone()
+    bad[1, 2] = kp.shape[1] + 5
+    kv_bad = tr.PagedKV(dkp, dvp, bad, dkt, dvt, dP)
+    tr.tr_tree_attn_paged(tree, dq, kv_bad, 0, out_p, ws)
+    assert tr.tr_read_device_status(ws) & tr.TR_FLAG_BAD_PAGE
+
+
+def test_step_paged_commits_every_layer(tr):
+    g = torch.Generator().manual_seed(72)
+    levels = RAND_LEVELS[1]
+    t = otree(levels)
+    tree = tr.Tree.from_levels(levels, 8)
+    T, D = t.n_nodes, t.max_depth
+    V, B, Hkv, d, ps, L = 300, 3, 2, 128, 64, 3
+    mp = 3                                          # capacity 192 positions
+    M = torch.randint(0, V, (B, V, 8), generator=g, dtype=torch.int32)
+    root = torch.tensor([3, 4, 5], dtype=torch.int32)
+    P = torch.tensor([5, 62, 189], dtype=torch.int32)   # seq 1 crosses a page, seq 2 overflows
+    kc = torch.zeros((L, B, Hkv, mp * ps, d), dtype=torch.bfloat16)
+    kp, table = paged_from_contiguous(g, kc, ps, layers=L)
+    vp = kp.clone()
+    kt = torch.randn((L, B, T, Hkv, d), generator=g).to(torch.bfloat16)
+    vt = torch.randn((L, B, T, Hkv, d), generator=g).to(torch.bfloat16)
+    ws = ws_for(tr, tree, B, V, 8)
+    dM, droot, dP, dkp, dvp, dtab, dkt, dvt = (x.to(DEV) for x in (M, root, P, kp, vp, table, kt, vt))
+    tok = torch.empty((B, T), dtype=torch.int32, device=DEV)
+    tr.tr_retrieve(tree, dM, droot, tok, ws)
+    tok_h = tok.cpu().numpy().astype(np.int64)
+    z = torch.randn((B, T, V), generator=g)
+    for b in range(B):                              # accept the rank-0 chain 0 -> 1 -> 5 -> 13
+        for a, c in ((0, 1), (1, 5), (5, 13)):
+            z[b, a, tok_h[b, c]] = 50.0
+    Ld = torch.empty((B,), dtype=torch.int32, device=DEV)
+    path = torch.empty((B, D + 1), dtype=torch.int32, device=DEV)
+    em = torch.empty((B, D + 1), dtype=torch.int32, device=DEV)
+    kv = tr.PagedKV(dkp, dvp, dtab, dkt, dvt, dP)
+    tr.tr_step_paged(tree, z.to(DEV), dM, tok, droot, Ld, path, em, ws, kv)
+    flags = tr.tr_read_device_status(ws)
+    assert flags & tr.TR_FLAG_CACHE_FULL            # seq 2: 189 + 4 > 192
+    okp, ovp = kp.float().numpy(), vp.float().numpy()
+    for b in range(B):
+        Mo = M[b].numpy().astype(np.int64).copy()
+        res, _ = O.step_after_forward(t, Mo, tok_h[b], z[b].numpy(), 8)
+        assert int(Ld[b]) == res.verdict.accept_len == 3
+        assert (dM[b].cpu().numpy() == Mo).all()
+        assert tok[b].cpu().numpy().tolist() == res.next_tok.tolist()
+        if b < 2:
+            newP = O.commit_paged(okp, ovp, kt[:, b].float().numpy(), vt[:, b].float().numpy(),
+                                  table[b].numpy(), ps, int(P[b]), res.verdict.path)
+            assert int(dP[b]) == newP
+        else:
+            assert int(dP[b]) == int(P[b])
+    assert (dkp.float().cpu().numpy() == okp).all() and (dvp.float().cpu().numpy() == ovp).all()
+
+
 # ------------------------------------------------------------------ initial M
 @pytest.mark.parametrize("m_dtype", [torch.int32, torch.int64])
 def test_init_matrix_parity(tr, m_dtype):

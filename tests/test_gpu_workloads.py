@@ -161,6 +161,36 @@ def test_largevocab_sampling_sampled_sequences(tr):
     run_loop(tr, w, 16, [0, 31], {0}, temperature=0.8)
 
 
+@pytest.mark.parametrize("wl,ps,steps", [("vicuna7b", 64, 256), ("largevocab", 128, 24)])
+def test_paged_loop_equals_contiguous(tr, wl, ps, steps):
+    # the paged cache (shuffled pages) runs the same trajectory bit for bit:
+    # attention outputs, trees, verdicts, M and the committed rows
+    from draft_tree_retrieval_amd.loop import TRDecoder, from_pages
+    w = W.WORKLOADS[wl]
+    cap = -(-w.cap(steps) // ps) * ps
+    tree = tr.Tree.from_levels(w.levels, w.k)
+    sa, sb = W.initial_state(w, DEV, cap=cap), W.initial_state(w, DEV, cap=cap)
+    da = TRDecoder(tree, sa.M, sa.k_cache, sa.v_cache, sa.prefix_len, sa.root, Hq=w.Hq)
+    db = TRDecoder(tree, sb.M, sb.k_cache, sb.v_cache, sb.prefix_len, sb.root, Hq=w.Hq,
+                   page_size=ps)
+    oa = torch.empty((w.B, w.T, w.Hq, w.d), dtype=w.kv_dtype, device=DEV)
+    ob = torch.empty_like(oa)
+    for s in range(steps):
+        q, kt, vt = W.step_qkv(w, s, DEV)
+        da.attend(q, kt, vt, oa)
+        db.attend(q, kt, vt, ob)
+        assert torch.equal(oa, ob), f"step {s}: attention differs"
+        z = W.step_logits(w, s, da.tree_tok, DEV)
+        da.step(z, kt, vt)
+        db.step(z, kt, vt)
+        assert torch.equal(da.tree_tok, db.tree_tok) and torch.equal(da.prefix_len, db.prefix_len)
+        assert torch.equal(da.emitted, db.emitted), f"step {s}"
+    assert torch.equal(da.M, db.M)
+    assert torch.equal(from_pages(db.k_pages, db.block_table), da.k_cache)
+    assert torch.equal(from_pages(db.v_pages, db.block_table), da.v_cache)
+    assert da.device_flags() == 0 and db.device_flags() == 0
+
+
 def test_largevocab_full_sampled_sequences(tr):
     w = W.WORKLOADS["largevocab"]
     run_loop(tr, w, w.steps, [0, 13, 31], {0, 64, w.steps - 1})
