@@ -51,6 +51,10 @@ def parse():
     ap.add_argument("--page-size", type=int, default=0,
                     help="0: contiguous prefix cache; else a paged cache with pages of this many "
                          "rows in shuffled order (tr_tree_attn_paged, tr_step_paged)")
+    ap.add_argument("--lmhead", type=int, default=0, metavar="H",
+                    help="0: the step takes logits; else it takes hidden states [B][T][H] and a "
+                         "seeded output embedding [V][H] through the fused LM head "
+                         "(tr_step_lmhead); the unfused product + tr_step is timed beside it")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the CPU oracle baseline (0 disables it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -175,10 +179,22 @@ def main():
     tree = tr.Tree.from_levels(w.levels, w.k)
 
     temp = args.temperature
+    Hl = args.lmhead
+    if Hl:
+        gw = torch.Generator(device=dev).manual_seed(w.seed + 91)
+        W_out = (torch.randn((w.V, Hl), generator=gw, device=dev) / Hl ** 0.5).to(torch.bfloat16)
+        lm_ws = {}
 
     def step(dec, z, kt, vt, U):
         if temp > 0:
             dec.step_sample(z, kt, vt, temp, U)
+        elif Hl:
+            key = id(dec)
+            if key not in lm_ws:
+                lm_ws[key] = tr.new_lmhead_workspace(w.B * w.T, w.V, w.k)
+            tr.tr_step_lmhead(tree, z, W_out, dec.M, dec.tree_tok, dec.root_tok, dec.accept_len,
+                              dec.accept_path, dec.emitted, lm_ws[key], kt, vt, dec.k_cache,
+                              dec.v_cache, dec.prefix_len, dec.topk, dec.update)
         else:
             dec.step(z, kt, vt)
 
@@ -192,7 +208,10 @@ def main():
     inputs, prefix_hist, accepted = [], [], []
     for s in range(total):
         q, kt, vt = W.step_qkv(w, s, dev)
-        z = W.step_logits(w, s, dec.tree_tok, dev)
+        if Hl:
+            z = torch.randn((w.B, w.T, Hl), generator=ug, device=dev).to(torch.bfloat16)
+        else:
+            z = W.step_logits(w, s, dec.tree_tok, dev)
         U = torch.rand((w.B, w.T, 2), generator=ug, device=dev) if temp > 0 else None
         prefix_hist.append(dec.prefix_len.clone())
         dec.attend(q, kt, vt, out)
@@ -272,6 +291,12 @@ def main():
     logits_bytes = w.B * w.T * w.V * lsz
     m_bytes = w.B * w.T * w.k * 4 * 2                              # rows written + read back
     step_bytes = logits_bytes + commit_bytes + m_bytes
+    if Hl:
+        # the step reads h and the output embedding instead of logits; the
+        # slice keys (8 per row and 128-id slice) are written and read back
+        lm_bytes = w.V * Hl * 2 + w.B * w.T * Hl * 2
+        part_bytes = w.B * w.T * ((w.V + 127) // 128) * 8 * 8
+        step_bytes = lm_bytes + 2 * part_bytes + commit_bytes + m_bytes
     calls = {
         "tr_tree_attn": (attn_ms, attn_bytes),
         "tr_step": (step_ms, step_bytes),
@@ -284,6 +309,9 @@ def main():
     # the rest of the call
     kbytes = {"attn_prefix": kv_bytes + qo_bytes / 2, "attn_combine": tkv_bytes + qo_bytes / 2,
               "topk": step_bytes}
+    if Hl:
+        kbytes["lmhead"] = lm_bytes + part_bytes
+        kbytes["lmhead_merge"] = part_bytes + commit_bytes + m_bytes
     kdetail = {k: {"avg_us": round(ms * 1e3, 2), "bytes": int(kbytes[k]),
                    "GB_s": round(kbytes[k] / (ms * 1e-3) / 1e9, 1)} for k, ms in kernel_ms.items()}
     log("per kernel:", json.dumps(kdetail))
@@ -291,6 +319,8 @@ def main():
     attn_flops = 4.0 * w.T * w.Hq * w.d * (P_sum.mean().item())
     dtype = "bf16" if w.kv_dtype == torch.bfloat16 else "f32"
     kflops = {"attn_prefix": attn_flops}
+    if Hl:
+        kflops["lmhead"] = 2.0 * w.B * w.T * w.V * Hl
     dom = max(kernel_ms, key=kernel_ms.get)
     dms, dbytes = kernel_ms[dom], kbytes[dom]
     # the binding roof of the dominant kernel: whichever takes longer at peak
@@ -308,8 +338,35 @@ def main():
     roof["traffic"] = measured_traffic(args.workload, dom)
     log(f"mean accepted drafts {L_mean:.3f}, emitted/step {L_mean + 1:.3f}")
 
+    unfused = None
+    if Hl:
+        # the same steps with the product unfused: one bf16 GEMM writing the
+        # logits, then tr_step on them
+        st = init.clone()
+        dec = TRDecoder(tree, st.M, st.k_cache, st.v_cache, st.prefix_len, st.root, Hq=w.Hq,
+                        page_size=args.page_size or None)
+        logits = torch.empty((w.B, w.T, w.V), dtype=torch.bfloat16, device=dev)
+        W_t = W_out.t()
+
+        def unfused_step(i):
+            q, kt, vt, h, _ = inputs[i]
+            dec.attend(q, kt, vt, out)
+            torch.matmul(h.view(-1, Hl), W_t, out=logits.view(-1, w.V))
+            dec.step(logits, kt, vt)
+
+        for i in range(args.warmup):
+            unfused_step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            unfused_step(args.warmup + i)
+        torch.cuda.synchronize()
+        unfused = {"steps_per_s": round(steps / (time.perf_counter() - t0), 2),
+                   "what": "attention + bf16 GEMM writing the logits (torch.matmul) + tr_step"}
+        log("unfused:", json.dumps(unfused))
+
     cpu = None
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and not Hl:
         cpu = cpu_baseline(w, inputs, init_host, args.cpu_seconds, temp)
 
     res = {
@@ -336,6 +393,9 @@ def main():
         "emitted_per_step": round(L_mean + 1, 3),
         "cpu_baseline": cpu,
     }
+    if Hl:
+        res["config"]["lm_head"] = f"fused, H={Hl}, W [V][H] bf16 seeded"
+        res["unfused"] = unfused
     print(json.dumps(res), flush=True)
 
 

@@ -346,6 +346,27 @@ tr_status tr_verify(const tr_tree* t, int32_t B, const int32_t* topk, int32_t k,
 
 namespace {
 
+// LM-head input of the fused step: hidden states h [rows][H] and the output
+// embedding W [V][H], bfloat16.
+struct LmSrc {
+  const void* h;
+  const void* W;
+  int32_t H;
+};
+
+tr_status check_lmhead_args(int64_t rows, int32_t H, int64_t V, int32_t k, const void* h,
+                            const void* W, tr_dtype dtype) {
+  TR_CHECK(rows >= 1, TR_ERR_INVALID_ARGUMENT, "rows must be >= 1");
+  TR_CHECK(rows <= int64_t(tr::kMaxRowCnt), TR_ERR_UNSUPPORTED, "rows above %zu", tr::kMaxRowCnt);
+  TR_CHECK(h && W, TR_ERR_INVALID_ARGUMENT, "h or W is null");
+  TR_CHECK(dtype == TR_BFLOAT16, TR_ERR_UNSUPPORTED, "the LM head takes bfloat16 h and W");
+  TR_CHECK(H >= 128 && H % 128 == 0, TR_ERR_UNSUPPORTED, "H must be a positive multiple of 128");
+  TR_CHECK(k >= 1 && k <= 8, TR_ERR_UNSUPPORTED, "the fused LM head keeps k <= 8");
+  TR_CHECK(V >= k && V <= INT32_MAX, TR_ERR_INVALID_ARGUMENT, "V must be in k..2^31-1");
+  TR_CHECK(aligned16(h) && aligned16(W), TR_ERR_INVALID_ARGUMENT, "h and W must be 16-byte aligned");
+  return TR_OK;
+}
+
 // The fused step; temperature 0 verifies greedily, above 0 by sampling.
 tr_status step_impl(const tr_tree* t, int32_t B, int64_t V, int32_t k, const void* logits,
                     tr_dtype l_dtype, float temperature, const float* uniforms, void* M,
@@ -355,7 +376,8 @@ tr_status step_impl(const tr_tree* t, int32_t B, int64_t V, int32_t k, const voi
                     void* v_cache, int64_t cap, int32_t* prefix_len, int32_t* topk_out,
                     tr_update_mode mode, void* ws, size_t ws_bytes, void* stream,
                     const tr::PagedArgs* paged = nullptr, int32_t n_layers = 1,
-                    int64_t tree_layer_bytes = 0, int64_t cache_layer_bytes = 0) {
+                    int64_t tree_layer_bytes = 0, int64_t cache_layer_bytes = 0,
+                    const LmSrc* lm = nullptr) {
   TR_CHECK(mode == TR_UPDATE_ALL || mode == TR_UPDATE_ACCEPTED, TR_ERR_INVALID_ARGUMENT,
            "unknown update mode %d", int(mode));
   const bool sample = temperature != 0.f;
@@ -366,8 +388,15 @@ tr_status step_impl(const tr_tree* t, int32_t B, int64_t V, int32_t k, const voi
     TR_CHECK(V <= int64_t(tr::kMaxBuckets) * tr::kDrawBucket, TR_ERR_UNSUPPORTED,
              "sampling takes V <= %d", tr::kMaxBuckets * tr::kDrawBucket);
   }
-  tr_status st = check_topk_args(t, B, logits, l_dtype, V, k);
+  tr_status st = lm ? check_lmhead_args(int64_t(B) * (t ? t->dev.T : 0), lm->H, V, k, lm->h, lm->W,
+                                         l_dtype)
+                    : check_topk_args(t, B, logits, l_dtype, V, k);
   if (st != TR_OK) return st;
+  if (lm) {
+    TR_CHECK(t != nullptr, TR_ERR_INVALID_ARGUMENT, "tree is null");
+    TR_CHECK(k == t->k, TR_ERR_INVALID_ARGUMENT, "k %d differs from the tree's %d", k, t->k);
+    TR_CHECK(size_t(B) <= tr::kMaxSeqCnt, TR_ERR_UNSUPPORTED, "B above %zu", tr::kMaxSeqCnt);
+  }
   TR_CHECK(M && tree_tok && root_tok && accept_len, TR_ERR_INVALID_ARGUMENT, "null tensor");
   TR_CHECK(m_dtype == TR_INT32 || m_dtype == TR_INT64, TR_ERR_UNSUPPORTED, "M must be int32 or int64");
   int row_bytes = 0;
@@ -382,11 +411,14 @@ tr_status step_impl(const tr_tree* t, int32_t B, int64_t V, int32_t k, const voi
              TR_ERR_INVALID_ARGUMENT, "key/value tensors must be 16-byte aligned");
     row_bytes = d * (kv_dtype == TR_BFLOAT16 ? 2 : 4);
   }
-  const tr::TopkPlan plan = tr::plan_topk(int64_t(B) * t->dev.T, V, k, l_dtype == TR_BFLOAT16 ? 2 : 4);
-  st = check_ws(ws, ws_bytes, plan.end);
+  const int64_t rows = int64_t(B) * t->dev.T;
+  const tr::TopkPlan plan = tr::plan_topk(rows, V, k, l_dtype == TR_BFLOAT16 ? 2 : 4);
+  const tr::LmheadPlan lplan = tr::plan_lmhead(rows, V, k);
+  st = check_ws(ws, ws_bytes, lm ? lplan.end : plan.end);
   if (st != TR_OK) return st;
   uint8_t* w = static_cast<uint8_t*>(ws);
-  int32_t* ids = topk_out ? topk_out : reinterpret_cast<int32_t*>(w + plan.ids_off);
+  int32_t* ids = topk_out ? topk_out
+                          : reinterpret_cast<int32_t*>(w + (lm ? lplan.ids_off : plan.ids_off));
   tr::TailArgs tail{};
   tail.mode = tr::TAIL_STEP;
   tail.m_is64 = m_dtype == TR_INT64;
@@ -412,6 +444,15 @@ tr_status step_impl(const tr_tree* t, int32_t B, int64_t V, int32_t k, const voi
   tail.tree_layer_bytes = tree_layer_bytes;
   tail.cache_layer_bytes = cache_layer_bytes;
   if (paged) tail.paged = *paged;
+  if (lm) {
+    uint64_t* part = reinterpret_cast<uint64_t*>(w + lplan.part_off);
+    hipError_t e = tr::launch_lmhead(lm->h, lm->W, int32_t(rows), lm->H, V, part, lplan.nvs,
+                                     hipStream_t(stream));
+    if (e == hipSuccess)
+      e = tr::launch_lmhead_merge(t->dev, rows, part, lplan.nvs, V, k, ids, tail, w,
+                                  hipStream_t(stream));
+    return hip_status(e, "tr_step_lmhead");
+  }
   return hip_status(tr::launch_topk(t->dev, B, logits, l_dtype == TR_BFLOAT16, V, k, ids, tail, w,
                                     plan, hipStream_t(stream)),
                     "tr_step");
@@ -524,6 +565,49 @@ tr_status tr_step_paged(const tr_tree* t, int32_t B, int64_t V, int32_t k, const
                    kv->v_tree, kv->k_pages, kv->v_pages, cap, kv->prefix_len, topk_out, mode, ws,
                    ws_bytes, stream, &pa, kv->n_layers, int64_t(B) * t->dev.T * row,
                    kv->num_pages * kv->page_size * row);
+}
+
+size_t tr_lmhead_workspace_size(int64_t rows, int64_t V, int32_t k) {
+  if (rows < 1 || V < 1 || k < 1) return 0;
+  return tr::plan_lmhead(rows, V, k).end;
+}
+
+tr_status tr_lmhead_topk(int32_t rows, int32_t H, int64_t V, int32_t k, const void* h,
+                         const void* W, tr_dtype dtype, int32_t* topk_out, void* ws,
+                         size_t ws_bytes, void* stream) {
+  tr_status st = check_lmhead_args(rows, H, V, k, h, W, dtype);
+  if (st != TR_OK) return st;
+  TR_CHECK(topk_out != nullptr, TR_ERR_INVALID_ARGUMENT, "topk_out is null");
+  const tr::LmheadPlan plan = tr::plan_lmhead(rows, V, k);
+  st = check_ws(ws, ws_bytes, plan.end);
+  if (st != TR_OK) return st;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  uint64_t* part = reinterpret_cast<uint64_t*>(w + plan.part_off);
+  hipError_t e = tr::launch_lmhead(h, W, rows, H, V, part, plan.nvs, hipStream_t(stream));
+  if (e == hipSuccess) {
+    tr::TreeDev none{};
+    none.T = 1;
+    tr::TailArgs tail{};
+    tail.mode = tr::TAIL_NONE;
+    e = tr::launch_lmhead_merge(none, rows, part, plan.nvs, V, k, topk_out, tail, w,
+                                hipStream_t(stream));
+  }
+  return hip_status(e, "tr_lmhead_topk");
+}
+
+tr_status tr_step_lmhead(const tr_tree* t, int32_t B, int32_t H, int64_t V, int32_t k,
+                         const void* h, const void* W, tr_dtype dtype, void* M, tr_dtype m_dtype,
+                         int32_t* tree_tok, int32_t* root_tok, int32_t* accept_len,
+                         int32_t* accept_path, int32_t* emitted, int32_t Hkv, int32_t d,
+                         tr_dtype kv_dtype, const void* k_tree, const void* v_tree, void* k_cache,
+                         void* v_cache, int64_t cap, int32_t* prefix_len, int32_t* topk_out,
+                         tr_update_mode mode, void* ws, size_t ws_bytes, void* stream) {
+  TR_CHECK(t != nullptr && B >= 1, TR_ERR_INVALID_ARGUMENT, "tree is null or B < 1");
+  const LmSrc lm{h, W, H};
+  return step_impl(t, B, V, k, nullptr, dtype, 0.f, nullptr, M, m_dtype, tree_tok, root_tok,
+                   accept_len, accept_path, emitted, Hkv, d, kv_dtype, k_tree, v_tree, k_cache,
+                   v_cache, cap, prefix_len, topk_out, mode, ws, ws_bytes, stream, nullptr, 1, 0,
+                   0, &lm);
 }
 
 tr_status tr_step(const tr_tree* t, int32_t B, int64_t V, int32_t k, const void* logits,

@@ -469,6 +469,58 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SAMPLE ? 3 :
     seq_tail<int32_t, BF16, SAMPLE>(S, tree, b, k, V, topk_b, tok_b, tail, ws, logits, stat, segs);
 }
 
+// Second half of the fused LM head: one block per row merges the 8 best
+// keys of every vocabulary slice (written by lmhead_topk_kernel) into the
+// row's top-k ids; the last row block of a sequence then runs the step's
+// tail as topk_kernel does.  Keys are read eight per thread at a time, all
+// loads of a batch in flight together.
+__global__ __launch_bounds__(512) void lmhead_merge_kernel(const uint64_t* __restrict__ part,
+                                                            int32_t nvs, int64_t V, int32_t k,
+                                                            int32_t* __restrict__ ids_out,
+                                                            uint8_t* ws, TreeDev tree,
+                                                            TailArgs tail) {
+  constexpr int KM = 8, NT = 512, NW = NT / 64, kBatch = 8;
+  __shared__ uint64_t s_keys[NW][KM];
+  __shared__ uint64_t s_best[KM];
+  const int64_t row = blockIdx.x;
+  const int n = nvs * KM;
+  const uint64_t* pr = part + row * int64_t(n);
+  TopList<KM> L;
+  L.clear();
+  for (int i0 = threadIdx.x; i0 < n; i0 += kBatch * NT) {
+    uint64_t v[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) v[j] = pr[min(i0 + j * NT, n - 1)];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (i0 + j * NT < n) L.insert(v[j]);
+  }
+  block_merge<KM, NW>(L, s_keys, s_best);
+  if (threadIdx.x == 0)
+    for (int r = 0; r < k; ++r) put_dev(&ids_out[row * k + r], int32_t(key_id(s_best[r])));
+  if (tail.mode == TAIL_NONE) return;
+  const int b = int(row / tree.T);
+  uint32_t* seq_cnt = reinterpret_cast<uint32_t*>(ws + kSeqCntOff);
+  if (!last_block_arrives(seq_cnt + b, uint32_t(tree.T))) return;
+  __shared__ TailShared S;
+  const int32_t* topk_b = ids_out + int64_t(b) * tree.T * k;
+  int32_t* tok_b = tail.tree_tok + int64_t(b) * tree.T;
+  if (tail.m_is64)
+    seq_tail<int64_t, true, false>(S, tree, b, k, V, topk_b, tok_b, tail, ws, nullptr, nullptr, 1);
+  else
+    seq_tail<int32_t, true, false>(S, tree, b, k, V, topk_b, tok_b, tail, ws, nullptr, nullptr, 1);
+}
+
+hipError_t launch_lmhead_merge(const TreeDev& tree, int64_t rows, const uint64_t* part, int32_t nvs,
+                               int64_t V, int32_t k, int32_t* ids, const TailArgs& tail,
+                               uint8_t* ws, hipStream_t s) {
+  prof_begin(s, TR_KERNEL_LMHEAD_MERGE);
+  hipLaunchKernelGGL(lmhead_merge_kernel, dim3(unsigned(rows)), dim3(512), 0, s, part, nvs, V, k,
+                     ids, ws, tree, tail);
+  prof_end(s);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk(const TreeDev& tree, int32_t B, const void* logits, int l_is_bf16, int64_t V,
                        int32_t k, int32_t* topk_ids, const TailArgs& tail, uint8_t* ws,
                        const TopkPlan& plan, hipStream_t s) {

@@ -131,6 +131,27 @@ void prof_end(hipStream_t s);
 hipError_t launch_topk(const TreeDev& tree, int32_t B, const void* logits, int l_is_bf16, int64_t V,
                        int32_t k, int32_t* topk_ids, const TailArgs& tail, uint8_t* ws,
                        const TopkPlan& plan, hipStream_t s);
+// Fused LM head + top-k: slices of 128 vocabulary rows, 8 keys per (row,
+// slice), then one merge block per row.
+struct LmheadPlan {
+  int32_t nvs;        // vocabulary slices
+  size_t part_off;    // uint64 [rows][nvs][8]
+  size_t ids_off;     // int32 [rows][k] when the caller gives no buffer
+  size_t end;
+};
+inline LmheadPlan plan_lmhead(int64_t rows, int64_t V, int32_t k) {
+  LmheadPlan p{};
+  p.nvs = int32_t((V + 127) / 128);
+  p.part_off = kDataOff;
+  p.ids_off = align256(p.part_off + size_t(rows) * p.nvs * 8 * 8);
+  p.end = align256(p.ids_off + size_t(rows) * k * 4);
+  return p;
+}
+hipError_t launch_lmhead(const void* h, const void* W, int32_t R, int32_t H, int64_t V,
+                         uint64_t* part, int32_t nvs, hipStream_t s);
+hipError_t launch_lmhead_merge(const TreeDev& tree, int64_t rows, const uint64_t* part, int32_t nvs,
+                               int64_t V, int32_t k, int32_t* ids, const TailArgs& tail,
+                               uint8_t* ws, hipStream_t s);
 hipError_t launch_retrieve(const TreeDev& tree, int32_t B, const void* M, int m_is64, int64_t V,
                            int32_t k, const int32_t* root_tok, int32_t* tree_tok, uint8_t* ws,
                            hipStream_t s);

@@ -54,6 +54,11 @@ _SIGS = {
     "tr_tree_attn_paged": ([_P, _I32, _I32, _P, _P, _I32, C.c_float, _P, _P, _SZ, _P], C.c_int),
     "tr_step_paged": ([_P, _I32, _I64, _I32, _P, C.c_int, _P, C.c_int, _P, _P, _P, _P, _P, _P, _P,
                        C.c_int, _P, _SZ, _P], C.c_int),
+    "tr_lmhead_workspace_size": ([_I64, _I64, _I32], _SZ),
+    "tr_lmhead_topk": ([_I32, _I32, _I64, _I32, _P, _P, C.c_int, _P, _P, _SZ, _P], C.c_int),
+    "tr_step_lmhead": ([_P, _I32, _I32, _I64, _I32, _P, _P, C.c_int, _P, C.c_int, _P, _P, _P, _P,
+                        _P, _I32, _I32, C.c_int, _P, _P, _P, _P, _I64, _P, _P, C.c_int, _P, _SZ,
+                        _P], C.c_int),
     "tr_init_matrix": ([_I32, _I64, _I32, _P, C.c_int, C.c_int, _P, C.c_int, _I32, C.c_uint64,
                         _P], C.c_int),
     "tr_profile_enable": ([_I32], C.c_int),
@@ -62,7 +67,7 @@ _SIGS = {
 
 # tr_kernel_id
 KERNEL_NAMES = {1: "attn_prefix", 2: "attn_combine", 3: "topk", 4: "retrieve", 5: "verify", 6: "fill",
-                7: "init"}
+                7: "init", 8: "lmhead", 9: "lmhead_merge"}
 
 
 class _LaunchTime(C.Structure):
@@ -307,6 +312,44 @@ def tr_step_sample(tree, logits, temperature, uniforms, M, tree_tok, root_tok, a
     _check(load().tr_step_sample(tree.handle, B, V, tree.k, _ptr(logits), _dt(logits),
                                  float(temperature), _ptr(uniforms), _ptr(M), _dt(M),
                                  _ptr(tree_tok), _ptr(root_tok), _ptr(accept_len),
+                                 _ptr(accept_path), _ptr(emitted), Hkv, d, kv_dt, _ptr(k_tree),
+                                 _ptr(v_tree), _ptr(k_cache), _ptr(v_cache), cap,
+                                 _ptr(prefix_len), _ptr(topk_out), mode, _ptr(ws), ws.numel(),
+                                 _stream(stream)))
+
+
+def tr_lmhead_workspace_size(rows, V, k):
+    return int(load().tr_lmhead_workspace_size(rows, V, k))
+
+
+def new_lmhead_workspace(rows, V, k, device="cuda", stream=None):
+    """A zeroed workspace for tr_lmhead_topk / tr_step_lmhead."""
+    n = tr_lmhead_workspace_size(rows, V, k)
+    n = (n + 255) // 256 * 256
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    _check(load().tr_workspace_init(_ptr(ws), n, _stream(stream)))
+    return ws
+
+
+def tr_lmhead_topk(h, W, k, topk_out, ws, stream=None):
+    """topk_out [rows][k] = the k best ids of h W^T per row (h [rows][H],
+    W [V][H], bfloat16)."""
+    rows, H = h.shape
+    V = W.shape[0]
+    _check(load().tr_lmhead_topk(rows, H, V, k, _ptr(h), _ptr(W), _dt(h), _ptr(topk_out),
+                                 _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def tr_step_lmhead(tree, h, W, M, tree_tok, root_tok, accept_len, accept_path, emitted, ws,
+                   k_tree=None, v_tree=None, k_cache=None, v_cache=None, prefix_len=None,
+                   topk_out=None, update="all", stream=None):
+    """tr_step_ex with the LM head fused in front: h [B][T][H], W [V][H]."""
+    mode = _UPDATE_MODES[update] if isinstance(update, str) else int(update)
+    B, T, H = h.shape
+    V = W.shape[0]
+    Hkv, cap, d, kv_dt = _kv_shape(k_cache)
+    _check(load().tr_step_lmhead(tree.handle, B, H, V, tree.k, _ptr(h), _ptr(W), _dt(h), _ptr(M),
+                                 _dt(M), _ptr(tree_tok), _ptr(root_tok), _ptr(accept_len),
                                  _ptr(accept_path), _ptr(emitted), Hkv, d, kv_dt, _ptr(k_tree),
                                  _ptr(v_tree), _ptr(k_cache), _ptr(v_cache), cap,
                                  _ptr(prefix_len), _ptr(topk_out), mode, _ptr(ws), ws.numel(),

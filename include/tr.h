@@ -316,6 +316,40 @@ tr_status tr_step_paged(const tr_tree* t, int32_t B, int64_t V, int32_t k, const
                         int32_t* emitted, const tr_paged_kv* kv, int32_t* topk_out,
                         tr_update_mode mode, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * LM head fused with the top-k (the logits are never written).  The update
+ * M[x~_i] = argtopk(p~_{i+1}) needs only the k best ids of each node's
+ * next-token distribution (Token Recycling, Chinese summary, Method), and
+ * softmax is increasing, so they are the k best of the logits z = h W^T:
+ *   h [rows][H] hidden states, W [V][H] output embedding, both bfloat16,
+ *   device memory, 16-byte aligned; products accumulate in float32; ids
+ *   ordered by z descending, ties to the lower id; H a multiple of 128,
+ *   k <= 8.  Built for decode-sized rows (W is streamed once per 96 rows).
+ * Workspace: tr_lmhead_workspace_size(rows, V, k) bytes (rows = B * nodes
+ * for tr_step_lmhead), zeroed once with tr_workspace_init.
+ * ------------------------------------------------------------------------ */
+size_t tr_lmhead_workspace_size(int64_t rows, int64_t V, int32_t k);
+
+/* topk_out [rows][k] int32.  Errors: TR_ERR_INVALID_ARGUMENT (null or
+ * misaligned pointer, V outside k..2^31-1), TR_ERR_UNSUPPORTED (dtype not
+ * bfloat16, H not a multiple of 128, k > 8, rows > 32768),
+ * TR_ERR_WORKSPACE_TOO_SMALL. */
+tr_status tr_lmhead_topk(int32_t rows, int32_t H, int64_t V, int32_t k, const void* h,
+                         const void* W, tr_dtype dtype, int32_t* topk_out, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* tr_step_ex with the LM head in front: the top-k of every node comes from
+ * h [B][T][H] and W instead of a logits tensor; everything after it
+ * (verification, update, commit, next retrieval) and every other argument
+ * as tr_step_ex.  Greedy verification only. */
+tr_status tr_step_lmhead(const tr_tree* t, int32_t B, int32_t H, int64_t V, int32_t k,
+                         const void* h, const void* W, tr_dtype dtype, void* M, tr_dtype m_dtype,
+                         int32_t* tree_tok, int32_t* root_tok, int32_t* accept_len,
+                         int32_t* accept_path, int32_t* emitted, int32_t Hkv, int32_t d,
+                         tr_dtype kv_dtype, const void* k_tree, const void* v_tree, void* k_cache,
+                         void* v_cache, int64_t cap, int32_t* prefix_len, int32_t* topk_out,
+                         tr_update_mode mode, void* ws, size_t ws_bytes, void* stream);
+
 /* Initial contents of M (Token Recycling, Method, first module: a hot start
  * inherits the matrix left by earlier inference instead of an empty one;
  * Experiment, initialisation ablation: all-zero, random ids, and prior
@@ -366,7 +400,9 @@ typedef enum {
   TR_KERNEL_RETRIEVE = 4,      /* tr_retrieve */
   TR_KERNEL_VERIFY = 5,        /* tr_verify */
   TR_KERNEL_FILL = 6,          /* tr_workspace_init */
-  TR_KERNEL_INIT = 7           /* tr_init_matrix */
+  TR_KERNEL_INIT = 7,          /* tr_init_matrix */
+  TR_KERNEL_LMHEAD = 8,        /* tr_lmhead_topk / tr_step_lmhead: product and slice top-k */
+  TR_KERNEL_LMHEAD_MERGE = 9   /* tr_lmhead_topk / tr_step_lmhead: merge (and tail) */
 } tr_kernel_id;
 
 typedef struct {

@@ -243,6 +243,14 @@ def topk_rows(Z, k: int) -> np.ndarray:
     return np.stack([topk_row(Z[i], k) for i in range(Z.shape[0])])
 
 
+def lmhead_logits(h, W) -> np.ndarray:
+    """The target's next-token logits of every node from its last hidden
+    state: z = h W^T (h [rows][H], W [V][H], the output embedding), float64.
+    READING: the pages take the logits as given; the LM head is the plain
+    linear map in front of the softmax whose top-k the update recycles."""
+    return np.asarray(h, dtype=np.float64) @ np.asarray(W, dtype=np.float64).T
+
+
 # --------------------------------------------------------------------------
 # a5: verification (greedy)
 # --------------------------------------------------------------------------

@@ -543,6 +543,123 @@ def test_step_paged_commits_every_layer(tr):
     assert (dkp.float().cpu().numpy() == okp).all() and (dvp.float().cpu().numpy() == ovp).all()
 
 
+# ------------------------------------------------------------------ fused LM head
+def lmhead_tol(H):
+    # twice a worst-case float32 accumulation bound for a length-H dot product
+    # of N(0,1) bf16 entries: (H/32 + 8) roundings (32-term MFMA products,
+    # then one accumulation per k step) of at most eps * sum|h w|, with
+    # sum|h w| ~ 0.64 H
+    return 2 * 6e-8 * (H / 32 + 8) * 0.64 * H
+
+
+def check_lmhead_rows(z, ids, k, tol):
+    """z [rows][V] float64 oracle logits, ids [rows][k] from the GPU: rows
+    whose k+1 best are separated by more than tol must match exactly (value
+    descending, ties to the lower id); the others must be a valid top-k
+    within tol.  Returns the number of rows checked exactly."""
+    exact = 0
+    for r in range(z.shape[0]):
+        order = np.lexsort((np.arange(z.shape[1]), -z[r]))
+        top = z[r][order[:k + 1]]
+        if len(top) <= k or (np.diff(-top) > tol).all():
+            assert ids[r].tolist() == order[:k].tolist(), r
+            exact += 1
+        else:
+            got = z[r][ids[r]]
+            assert len(set(ids[r].tolist())) == k
+            assert (got >= z[r][order[k - 1]] - tol).all() and (np.diff(got) <= tol).all(), r
+    return exact
+
+
+@pytest.mark.parametrize("rows,H,V,k", [(81, 4096, 32000, 8), (5, 256, 1000, 8), (100, 512, 777, 3),
+                                         (1, 128, 130, 1), (200, 256, 4096, 8)])
+def test_lmhead_topk_parity(tr, rows, H, V, k):
+    g = torch.Generator().manual_seed(91 + rows)
+    h = torch.randn((rows, H), generator=g).to(torch.bfloat16)
+    W = torch.randn((V, H), generator=g).to(torch.bfloat16)
+    ws = tr.new_lmhead_workspace(rows, V, k)
+    out = torch.empty((rows, k), dtype=torch.int32, device=DEV)
+    tr.tr_lmhead_topk(h.to(DEV), W.to(DEV), k, out, ws)
+    z = O.lmhead_logits(h.float().numpy(), W.float().numpy())
+    exact = check_lmhead_rows(z, out.cpu().numpy(), k, lmhead_tol(H))
+    assert exact >= rows * 0.6                       # the rest: valid within the bound
+
+
+def test_lmhead_topk_large_vocab_sampled_rows(tr):
+    # 32 sequences x 81 nodes against a 128256 x 4096 output embedding (27
+    # row tiles, W streamed once per tile); the oracle follows sampled rows
+    rows, H, V, k = 2592, 4096, 128256, 8
+    g = torch.Generator(device=DEV).manual_seed(92)
+    h = torch.randn((rows, H), generator=g, device=DEV).to(torch.bfloat16)
+    W = torch.randn((V, H), generator=g, device=DEV).to(torch.bfloat16)
+    ws = tr.new_lmhead_workspace(rows, V, k)
+    out = torch.empty((rows, k), dtype=torch.int32, device=DEV)
+    tr.tr_lmhead_topk(h, W, k, out, ws)
+    pick = [0, 95, 96, 1295, 2591]
+    z = O.lmhead_logits(h[pick].float().cpu().numpy(), W.float().cpu().numpy())
+    check_lmhead_rows(z, out[pick].cpu().numpy(), k, lmhead_tol(H))
+
+
+def test_step_lmhead_parity(tr):
+    levels = RAND_LEVELS[4]
+    t = otree(levels)
+    T, D = t.n_nodes, t.max_depth
+    B, H, V, k = 2, 512, 3000, 8
+    g = torch.Generator().manual_seed(93)
+    tree = tr.Tree.from_levels(levels, k)
+    W = torch.randn((V, H), generator=g).to(torch.bfloat16)
+    M = torch.randint(0, V, (B, V, k), generator=g, dtype=torch.int32)
+    root = torch.randint(0, V, (B,), generator=g).to(torch.int32)
+    ws = tr.new_lmhead_workspace(B * T, V, k)
+    dM, droot, dW = M.to(DEV), root.to(DEV), W.to(DEV)
+    tok = torch.empty((B, T), dtype=torch.int32, device=DEV)
+    tr.tr_retrieve(tree, dM, droot, tok, ws)
+    tok_h = tok.cpu().numpy().astype(np.int64)
+    # hidden states: noise, and for most nodes the W row of their rank-0
+    # child's token (that token then wins by far: accepted paths run deep)
+    rng = np.random.default_rng(93)
+    Wf = W.float().numpy()
+    plant = [[bool(t.children(n)) and rng.random() < 0.85 for n in range(T)] for b in range(B)]
+
+    def draw(b, n):
+        x = torch.randn((H,), generator=g) * (0.02 if plant[b][n] else 1.0)
+        if plant[b][n]:
+            x += W[tok_h[b, t.children(n)[0]]].float() * 0.1
+        return x.to(torch.bfloat16)
+
+    def clear(row):
+        # the k + 1 best oracle logits of the row are separated beyond the bound
+        z = O.lmhead_logits(row.float().numpy()[None], Wf)[0]
+        top = np.sort(z)[::-1][:k + 1]
+        return (np.diff(-top) > lmhead_tol(H)).all()
+
+    h = torch.empty((B, T, H), dtype=torch.bfloat16)
+    for b in range(B):
+        for n in range(T):
+            h[b, n] = draw(b, n)
+            while not clear(h[b, n]):                 # a near tie in the k+1 best: redraw
+                h[b, n] = draw(b, n)
+    L = torch.empty((B,), dtype=torch.int32, device=DEV)
+    path = torch.empty((B, D + 1), dtype=torch.int32, device=DEV)
+    em = torch.empty((B, D + 1), dtype=torch.int32, device=DEV)
+    topk = torch.empty((B, T, k), dtype=torch.int32, device=DEV)
+    tr.tr_step_lmhead(tree, h.to(DEV), dW, dM, tok, droot, L, path, em, ws, topk_out=topk)
+    lengths = []
+    for b in range(B):
+        z = O.lmhead_logits(h[b].float().numpy(), W.float().numpy())
+        assert check_lmhead_rows(z, topk[b].cpu().numpy(), k, lmhead_tol(H)) == T   # all exact
+        Mo = M[b].numpy().astype(np.int64).copy()
+        res, _ = O.step_after_forward(t, Mo, tok_h[b], z, k)
+        assert int(L[b]) == res.verdict.accept_len
+        lengths.append(res.verdict.accept_len)
+        assert path[b, :res.verdict.accept_len + 1].cpu().tolist() == res.verdict.path.tolist()
+        assert int(droot[b]) == res.verdict.bonus
+        assert (dM[b].cpu().numpy().astype(np.int64) == Mo).all()
+        assert tok[b].cpu().numpy().tolist() == res.next_tok.tolist()
+    assert max(lengths) >= 4                          # the planted states reach deep
+    assert tr.tr_read_device_status(ws) == 0
+
+
 # ------------------------------------------------------------------ initial M
 @pytest.mark.parametrize("m_dtype", [torch.int32, torch.int64])
 def test_init_matrix_parity(tr, m_dtype):

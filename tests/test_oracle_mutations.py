@@ -126,6 +126,10 @@ def _page_slot_swapped(table_b, page_size, pos):
     return int(table_b[pos % page_size % len(table_b)]), pos // page_size % page_size
 
 
+def _lmhead_drops_last_coordinate(h, W):
+    return np.asarray(h, dtype=np.float64)[:, :-1] @ np.asarray(W, dtype=np.float64)[:, :-1].T
+
+
 def _retrieve_rank_off(t, M, root):
     tok = np.empty(t.n_nodes, dtype=np.int64)
     tok[0] = root
@@ -154,7 +158,8 @@ def _attention_wrong_group(t, q, kt, vt, kc, vc, P_, scale=None):
 
 ORIG = {name: getattr(O, name) for name in
         ("verify", "topk_row", "update", "update_accepted", "retrieve", "ancestor_mask",
-         "tree_attention", "splitmix64", "init_matrix", "verify_sample", "page_slot")}
+         "tree_attention", "splitmix64", "init_matrix", "verify_sample", "page_slot",
+         "lmhead_logits")}
 
 CASES = [
     ("verify", _bonus_from_parent, [P.test_worked_example_verify_and_update,
@@ -181,6 +186,7 @@ CASES = [
                                       P.test_commit_paged_is_commit_per_layer]),
     ("page_slot", _page_slot_swapped, [P.test_paged_attention_equals_contiguous_under_any_page_order,
                                        P.test_commit_paged_is_commit_per_layer]),
+    ("lmhead_logits", _lmhead_drops_last_coordinate, [P.test_lmhead_logits_brute_force_and_one_hot_rows]),
     ("retrieve", _retrieve_rank_off, [P.test_worked_example_retrieval_gives_merged_sequence,
                                       P.test_retrieve_matches_recursive_definition]),
     ("ancestor_mask", _mask_without_self, [P.test_worked_example_mask,

@@ -396,6 +396,20 @@ def test_sample_low_temperature_is_greedy():
         assert v.emitted.tolist() == g.emitted.tolist()
 
 
+# ---------------------------------------------------------------- LM head
+def test_lmhead_logits_brute_force_and_one_hot_rows():
+    rng = np.random.default_rng(81)
+    h = rng.standard_normal((3, 5))
+    W = rng.standard_normal((7, 5))
+    z = O.lmhead_logits(h, W)
+    for r in range(3):
+        for v in range(7):
+            assert abs(z[r, v] - sum(h[r, j] * W[v, j] for j in range(5))) < 1e-12
+    # one-hot rows of W pick hidden coordinates: row v = e_(v mod 5)
+    E = np.eye(5)[[v % 5 for v in range(7)]]
+    np.testing.assert_array_equal(O.lmhead_logits(h, E), h[:, [v % 5 for v in range(7)]])
+
+
 # ---------------------------------------------------------------- update
 def test_update_last_writer_wins_brute_force():
     rng = np.random.default_rng(8)
