@@ -38,11 +38,11 @@ AttnPlan plan_attn(int32_t T, int32_t B, int32_t Hq, int32_t Hkv, int64_t cap, i
   p.G = Hq / Hkv;
   p.R = T * p.G;
   if (is_bf16) {
-    // two 16-row strips per wave: each key/value operand read from LDS
-    // feeds twice the products (halving the LDS traffic per product), and
-    // with more than 128 rows fewer tiles re-read the same keys.  Measured
-    // faster also for 81 rows, where only three waves then compute.
-    p.spw = 2;
+    // two strips per wave once a head has more than one 128-row tile: each
+    // key/value operand read from LDS then feeds twice the products and
+    // fewer tiles re-read the same keys; one strip per wave below that, so
+    // that more waves compute (one per SIMD at most otherwise)
+    p.spw = p.R > 128 ? 2 : 1;
     p.tile_rows = kWaves * p.spw * 16;
   } else {
     p.spw = kSpw;
@@ -92,17 +92,52 @@ __device__ __forceinline__ void mark_empty(float2* part_ml, int64_t unit0, int r
 }
 
 // ---------------------------------------------------------------- bf16 prefix
-// 8 waves; SPW 16-row strips per wave.  The kernel is bound by memory
-// latency, not arithmetic, so it keeps two or three 64-key sub-blocks
-// (32 KB each) of keys and values loading into a register ring while it
-// computes on another staged in LDS (two LDS buffers, one barrier per
-// sub-block).
+// 8 waves, two 16-row query strips per wave.  The keys and values of the
+// chunk stream HBM -> LDS through the LDS DMA (global_load_lds_dwordx4) in
+// 64-key sub-blocks (16 KB of K and 16 KB of V) into a ring of four LDS
+// slots, three sub-blocks in flight ahead of the one in use; nothing passes
+// through registers and nothing is restaged.
+//  * K is stored [key][d] with the 16-byte column chunk c of row r at
+//    position c ^ (r & 15): the S^T = K Q^T operand reads (16 rows, one
+//    chunk) are conflict-free.
+//  * V is stored [key][d] with chunk c of row r at c ^ 2 (r & 7), and the
+//    O^T = V^T P^T operand is read with ds_read_b64_tr_b16: within each
+//    16-lane group, lane i receives element e from the address of lane
+//    4 e + i / 4 plus i % 4 elements, so lanes pointing at rows k0 ..
+//    k0+3 (four lanes a row, 4 d apart) deliver to lane i the four keys
+//    k0 .. k0+3 of column d0 + i: the V^T layout the product needs.
+// The key order inside the second product's K dimension is permuted
+// consistently on both operands (k-index 8 g + m is key 4 g + m of the
+// first 16-key tile of the 32-key block for m < 4, of the second for
+// m >= 4) so that the probabilities need no cross-lane moves.
+// Waits are explicit: a workgroup fence would wait for every DMA in flight,
+// so the loop synchronises with a bare barrier after vmcnt(8) (the two
+// younger sub-blocks, 4 DMA loads each per wave, may still fly), and each
+// ring slot is its own LDS array named statically (one array would make
+// the compiler wait for DMAs into the other slots before every read).
 constexpr int kSB = 64;                   // keys per sub-block
-constexpr int kVtS = kSB + 4;             // bf16 per staged V^T row: 136 bytes
+constexpr int kRingSlots = 4;
+constexpr int kSubBytes = kSB * kHeadDim * 2;   // 16 KB
 // PAGED: kc and vc are page pools [num_pages][Hkv][page_size][d] reached
 // through the block table; the chunk's page ids are read into LDS first and
 // each 64-key sub-block (inside one page: page sizes are powers of two of
 // at least 64 keys) looks its page up once.
+// Transposed LDS read (ds_read_b64_tr_b16) of the 8 bytes at LDS address
+// p: four 16-bit values, delivered across each 16-lane group as described
+// above.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p));
+}
+// LDS DMA of 16 bytes per lane: lane l's src lands at lds_base + 16 l
+// (lds_base wave-uniform).  These gfx950 builtins sit in plain device
+// functions: inside a kernel template the host compilation pass cannot
+// instantiate them and drops the kernel's launch stub without a word.
+__device__ __forceinline__ void lds_dma16(const void* src, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+}
+
 template <int SPW, bool PAGED>
 __global__ __launch_bounds__(512) void attn_prefix_bf16(
     const uint16_t* __restrict__ q, const uint16_t* kc,
@@ -134,8 +169,16 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
   const int row0 = rt * kRows + w * SPW * 16;      // first query row of this wave
   const bool active = row0 < R;                    // waves past the last row only load
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks2[2][kSB * kKsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt2[2][kHeadDim * kVtS];
+  __shared__ __attribute__((aligned(16))) uint8_t Ks0[kSubBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t Ks1[kSubBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t Ks2[kSubBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t Ks3[kSubBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t Vs0[kSubBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t Vs1[kSubBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t Vs2[kSubBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t Vs3[kSubBytes];
+  auto kslot = [&](int i) -> uint8_t* { return i == 0 ? Ks0 : i == 1 ? Ks1 : i == 2 ? Ks2 : Ks3; };
+  auto vslot = [&](int i) -> uint8_t* { return i == 0 ? Vs0 : i == 1 ? Vs1 : i == 2 ? Vs2 : Vs3; };
   __shared__ int32_t s_pg[PAGED ? kMaxChunkPages : 1];
   const int p0 = PAGED ? (k0 >> pg.ps_log2) : 0;    // first page of the chunk
   if constexpr (PAGED) {
@@ -151,21 +194,20 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
     __syncthreads();
   }
 
+  // (the query fragments are loaded before the DMAs; the compiler waits for
+  // all loads in flight before entering the loop that uses them, so the
+  // first step starts with the prologue's sub-blocks landed)
   bf16x8 qb[SPW][4];
 #pragma unroll
   for (int s = 0; s < SPW; ++s) {
-    const int r = row0 + s * 16 + li;
-    if (r < R) {
-      const int n = r / G, gq = r - n * G;
-      const uint16_t* qp = q + ((int64_t(b) * T + n) * Hq + kvh * G + gq) * kHeadDim;
+    const int r = min(row0 + s * 16 + li, R - 1);     // rows past R: any row, never stored
+    const int n = r / G, gq = r - n * G;
+    const uint16_t* qp = q + ((int64_t(b) * T + n) * Hq + kvh * G + gq) * kHeadDim;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        qb[s][ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32 + g * 8);
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) qb[s][ks] = bf16x8{};
-    }
+    for (int ks = 0; ks < 4; ++ks)
+      qb[s][ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32 + g * 8);
   }
+  asm volatile("" ::: "memory");
 
   floatx4 acc[SPW][8];
   float mrow[SPW], lrow[SPW];
@@ -178,23 +220,15 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
   }
 
   const int64_t head_off = PAGED ? 0 : (int64_t(b) * Hkv + kvh) * cap * kHeadDim;
-  const uint16_t* kbase = kc + head_off;
-  const uint16_t* vbase = vc + head_off;
-  const int cch = tid & 15;     // K: 16-byte column chunk; rows (tid >> 4) + 32 j
-  const int rk0 = tid >> 4;
-  const int vq = tid & 31;      // V: keys 2 vq, 2 vq + 1
-  const int vd = tid >> 5;      // V: d = 8 vd .. 8 vd + 7 (transposed when staged)
-
-  // one ring slot: 2 K units and 2 V units of 16 bytes per thread.  No
-  // branch guards a load, so the compiler can wait for just the slot being
-  // staged and keep the others in flight: rows past the chunk end reload the
-  // chunk's last row (finite data that the key mask gives probability 0) and
-  // sub-blocks past the end reload the last sub-block.
-  auto load = [&](u32x4 (&kr)[2], u32x4 (&vr)[2], int j) {
+  // Sub-block j into ring slot sl: 1024 16-byte slots of K and of V, two
+  // of each per thread (wave w, pass q: slots (8 q + w) * 64 + lane).  Rows
+  // past the chunk end repeat its last row (finite data the key mask gives
+  // probability 0); sub-blocks past the end repeat the last one.
+  auto dma = [&](int j, int sl) {
     const int kb = k0 + min(j, nsub - 1) * kSB;
     // rows kb .. kb+63 (and the clamp k1-1 >= kb) lie in one page
-    const uint16_t* kp = kbase;
-    const uint16_t* vp = vbase;
+    const uint16_t* kp = kc + head_off;
+    const uint16_t* vp = vc + head_off;
     int row_base = 0;
     if constexpr (PAGED) {
       const int64_t pool_off =
@@ -204,66 +238,66 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
       row_base = (kb >> pg.ps_log2) << pg.ps_log2;   // first position of the page
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int rk = min(kb + rk0 + 32 * i, k1 - 1) - row_base;
-      kr[i] = *reinterpret_cast<const u32x4*>(kp + int64_t(rk) * kHeadDim + cch * 8);
-      const int rv = min(kb + 2 * vq + i, k1 - 1) - row_base;
-      vr[i] = *reinterpret_cast<const u32x4*>(vp + int64_t(rv) * kHeadDim + vd * 8);
+    for (int q2 = 0; q2 < 2; ++q2) {
+      const int base = (q2 * kWaves + w) * 64;       // wave-uniform first slot
+      const int p = base + lane;
+      const int r = p >> 4, pos = p & 15;
+      const int64_t row = min(kb + r, k1 - 1) - row_base;
+      const int ck = pos ^ (r & 15), cv = pos ^ ((r & 7) << 1);
+      lds_dma16(kp + row * kHeadDim + ck * 8, kslot(sl) + base * 16);
+      lds_dma16(vp + row * kHeadDim + cv * 8, vslot(sl) + base * 16);
     }
+    asm volatile("" ::: "memory");
   };
-  auto stage = [&](const u32x4 (&kr)[2], const u32x4 (&vr)[2], int buf) {
-    uint16_t* Ks = Ks2[buf];
-    uint16_t* Vt = Vt2[buf];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      *reinterpret_cast<u32x4*>(&Ks[(rk0 + 32 * i) * kKsStride + cch * 8]) = kr[i];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t lo = (e & 1) ? (vr[0][e >> 1] >> 16) : (vr[0][e >> 1] & 0xFFFFu);
-      const uint32_t hi = (e & 1) ? (vr[1][e >> 1] >> 16) : (vr[1][e >> 1] & 0xFFFFu);
-      *reinterpret_cast<uint32_t*>(&Vt[(vd * 8 + e) * kVtS + 2 * vq]) = lo | (hi << 16);
-    }
-  };
-  auto compute = [&](int buf, int nk) {
-    const uint16_t* Ks = Ks2[buf];
-    const uint16_t* Vt = Vt2[buf];
+
+  auto compute = [&](const uint8_t* Ks, const uint8_t* Vs, int nk) {
     const bool ragged = nk < kSB;                  // mask keys past the chunk end
     // S^T = K Q^T for 4 tiles of 16 keys; operands read ahead of the products
-    constexpr int TG = SPW == 1 ? 4 : 2;           // tiles per read group
-    constexpr int VG = SPW == 1 ? 8 : 4;           // V^T tiles per read group
     floatx4 sacc[SPW][4];
 #pragma unroll
     for (int s = 0; s < SPW; ++s)
 #pragma unroll
       for (int t = 0; t < 4; ++t) sacc[s][t] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t0 = 0; t0 < 4; t0 += TG) {
-      bf16x8 ka[TG][4];
+    for (int t0 = 0; t0 < 4; t0 += 2) {
+      bf16x8 ka[2][4];
 #pragma unroll
-      for (int t = 0; t < TG; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-          ka[t][ks] = *reinterpret_cast<const bf16x8*>(&Ks[((t0 + t) * 16 + li) * kKsStride + ks * 32 + g * 8]);
+          ka[t][ks] = *reinterpret_cast<const bf16x8*>(
+              Ks + ((t0 + t) * 16 + li) * 256 + (((4 * ks + g) ^ li) << 4));
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int t = 0; t < TG; ++t)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int s = 0; s < SPW; ++s)
             sacc[s][t0 + t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[t][ks], qb[s][ks], sacc[s][t0 + t], 0, 0, 0);
     }
-    // V^T operands, read while the softmax runs
+    // V^T operands (transposed LDS reads), read while the softmax runs:
+    // rows kr .. kr+3 with kr = 32 pp + 4 g (+16 for the second half),
+    // lane li at row kr + li / 4, columns 16 dt + 4 (li % 4) .. +3
+    constexpr int VG = 2;
     bf16x8 va[VG][2];
     auto read_v = [&](int dt0) {
 #pragma unroll
       for (int i = 0; i < VG; ++i) {
-        const int row = (dt0 + i) * 16 + li;
+        const int dt = dt0 + i;
+        const int cch = 2 * dt + ((li >> 1) & 1), half = (li & 1) * 8;
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(&Vt[row * kVtS + 32 * pp + 4 * g]);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(&Vt[row * kVtS + 32 * pp + 16 + 4 * g]);
-          va[i][pp] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+          uint32_t u[4];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int row = 32 * pp + 16 * hh + 4 * g + (li >> 2);
+            const uint8_t* addr = Vs + row * 256 + ((cch ^ ((row & 7) << 1)) << 4) + half;
+            const u32x2 r2 = lds_read_tr16(addr);
+            u[2 * hh] = r2[0];
+            u[2 * hh + 1] = r2[1];
+          }
+          va[i][pp] = __builtin_bit_cast(bf16x8, u32x4{u[0], u[1], u[2], u[3]});
         }
       }
     };
@@ -326,38 +360,24 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
     }
   };
 
-  // Ring slot j % kRing holds sub-block j; sub-block j is computed from
-  // LDS buffer j & 1.  The loop runs in whole rounds of kRing sub-blocks with
-  // no branch around a load or a stage; only the compute of sub-blocks past
-  // the end is skipped.  Two 16-row strips per wave leave registers for two
-  // slots only.
-  // (compiler memory barriers keep the loads in ring order: the compiler
-  // would otherwise sink them past the first staging and wait for them all;
-  // kc and vc are not __restrict__ for the same reason, loads through such
-  // pointers may move across barriers)
-  constexpr int kRing = SPW == 1 ? 3 : 2;
-  u32x4 kr[kRing][2], vr[kRing][2];
+  // three sub-blocks in flight, then per sub-block: wait, barrier, refill
+  // the slot freed by the previous sub-block, compute
 #pragma unroll
-  for (int j = 0; j < kRing; ++j) {
-    load(kr[j], vr[j], j);
-    asm volatile("" ::: "memory");
-  }
-  stage(kr[0], vr[0], 0);
-  asm volatile("" ::: "memory");
-  load(kr[0], vr[0], kRing);
-  asm volatile("" ::: "memory");
-  __syncthreads();
-  for (int it = 0; it < nsub; it += kRing) {
+  for (int j = 0; j < kRingSlots - 1; ++j) dma(j, j);
+  const int nround = (nsub + kRingSlots - 1) / kRingSlots * kRingSlots;
+  for (int j0 = 0; j0 < nround; j0 += kRingSlots) {
 #pragma unroll
-    for (int r = 0; r < kRing; ++r) {
-      const int cur = it + r;
-      if (active && cur < nsub) compute(cur & 1, min(kSB, k1 - (k0 + cur * kSB)));
-      const int nxt = (r + 1) % kRing;             // slot of sub-block cur + 1
-      stage(kr[nxt], vr[nxt], (cur + 1) & 1);
+    for (int jj = 0; jj < kRingSlots; ++jj) {
+      const int j = j0 + jj;
+      __builtin_amdgcn_s_waitcnt(0x0F78);          // vmcnt(8), lgkm/exp not waited
       asm volatile("" ::: "memory");
-      load(kr[nxt], vr[nxt], cur + 1 + kRing);     // refill it with sub-block cur + 1 + kRing
+      __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      __syncthreads();
+      dma(j + kRingSlots - 1, (jj + kRingSlots - 1) % kRingSlots);
+      if (active && j < nsub) compute(kslot(jj), vslot(jj), min(kSB, k1 - (k0 + j * kSB)));
+      // this step's LDS reads are done before the next barrier
+      __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0), vm/exp not waited
+      asm volatile("" ::: "memory");
     }
   }
 
@@ -686,16 +706,17 @@ hipError_t launch_attn(const TreeDev& tree, int32_t B, int32_t Hq, int32_t Hkv, 
     const auto* qq = reinterpret_cast<const uint16_t*>(q);
     const auto* kk = reinterpret_cast<const uint16_t*>(k_cache);
     const auto* vv = reinterpret_cast<const uint16_t*>(v_cache);
-    if (paged)
-      hipLaunchKernelGGL((attn_prefix_bf16<2, true>), grid1, dim3(64 * kWaves), 0, s, qq, kk, vv,
-                         cap, prefix_len, tree.T, Hq, Hkv, plan.G, plan.R, plan.chunks, sl2,
-                         reinterpret_cast<uint16_t*>(part_o), part_ml, ws, B, plan.row_tiles,
-                         *paged);
-    else
-      hipLaunchKernelGGL((attn_prefix_bf16<2, false>), grid1, dim3(64 * kWaves), 0, s, qq, kk, vv,
-                         cap, prefix_len, tree.T, Hq, Hkv, plan.G, plan.R, plan.chunks, sl2,
-                         reinterpret_cast<uint16_t*>(part_o), part_ml, ws, B, plan.row_tiles,
-                         PagedArgs{});
+    const PagedArgs pa = paged ? *paged : PagedArgs{};
+#define TR_PREFIX(SPWV, PG)                                                                      \
+  hipLaunchKernelGGL((attn_prefix_bf16<SPWV, PG>), grid1, dim3(64 * kWaves), 0, s, qq, kk, vv, cap, \
+                     prefix_len, tree.T, Hq, Hkv, plan.G, plan.R, plan.chunks, sl2,                \
+                     reinterpret_cast<uint16_t*>(part_o), part_ml, ws, B, plan.row_tiles, pa)
+    if (plan.spw == 2) {
+      if (paged) TR_PREFIX(2, true); else TR_PREFIX(2, false);
+    } else {
+      if (paged) TR_PREFIX(1, true); else TR_PREFIX(1, false);
+    }
+#undef TR_PREFIX
   } else {
     hipLaunchKernelGGL(attn_prefix_f32, grid, dim3(256), 0, s, reinterpret_cast<const float*>(q),
                        reinterpret_cast<const float*>(k_cache), reinterpret_cast<const float*>(v_cache),
