@@ -55,6 +55,10 @@ def parse():
                     help="0: the step takes logits; else it takes hidden states [B][T][H] and a "
                          "seeded output embedding [V][H] through the fused LM head "
                          "(tr_step_lmhead); the unfused product + tr_step is timed beside it")
+    ap.add_argument("--launch", choices=("graph", "stream"), default="graph",
+                    help="graph: the timed steps are captured once into a HIP graph and replayed "
+                         "(value); stream: launched one by one from Python.  Both are timed; "
+                         "per-call figures come from the stream pass")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the CPU oracle baseline (0 disables it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -252,6 +256,38 @@ def main():
 
     attn_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
     step_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    stream_wall = wall
+    log(f"stream launches: {steps / wall:.1f} steps/s")
+
+    # ---- graph replay: the timed steps captured once (every library call
+    # launches its kernels on the capturing stream, so each becomes a kernel
+    # node with its arguments fixed) and replayed from the post-warmup state;
+    # the replay must end in the record pass's state as well
+    if args.launch == "graph":
+        st = init.clone()
+        dec = TRDecoder(tree, st.M, st.k_cache, st.v_cache, st.prefix_len, st.root, Hq=w.Hq,
+                        page_size=args.page_size or None)
+        for s in range(args.warmup):
+            q, kt, vt, z, U = inputs[s]
+            dec.attend(q, kt, vt, out)
+            step(dec, z, kt, vt, U)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(steps):
+                q, kt, vt, z, U = inputs[args.warmup + i]
+                dec.attend(q, kt, vt, out)
+                step(dec, z, kt, vt, U)
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+        same = torch.equal(dec.tree_tok, rec_tok) and torch.equal(dec.M, rec_M)
+        assert same, "graph replay diverged from the record pass"
+        assert dec.device_flags() == 0
+        del graph
+        log(f"graph replay: {steps / wall:.1f} steps/s")
     ms_per_step = wall * 1e3 / steps
 
     # ---- kernel timing: the same steps again, every launch between two HIP
@@ -386,8 +422,11 @@ def main():
                    "tree_nodes": w.T, "tree_depth": w.depth, "Hq": w.Hq, "Hkv": w.Hkv,
                    "head_dim": w.d, "prefix": list(w.prefix), "M_dtype": str(w.m_dtype)[6:],
                    "verification": f"sampling, temperature {temp}" if temp > 0 else "greedy",
-                   "cache": f"paged, {args.page_size} rows per page" if args.page_size else "contiguous"},
+                   "cache": f"paged, {args.page_size} rows per page" if args.page_size else "contiguous",
+                   "launch": "one HIP graph of the timed steps" if args.launch == "graph"
+                             else "stream launches"},
         "roofline": roof,
+        "stream_launch_steps_per_s": round(steps / stream_wall, 2),
         "per_call": detail,
         "per_kernel": kdetail,
         "emitted_per_step": round(L_mean + 1, 3),

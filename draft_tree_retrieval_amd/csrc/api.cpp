@@ -101,8 +101,8 @@ tr_status build_tree(int32_t n, const int32_t* parent, const int32_t* rank, int3
   t->dev.parent[0] = 0xFF;
   t->dev.rank[0] = 0xFF;
   t->dev.depth[0] = 0;
-  std::memset(t->anc, 0, sizeof t->anc);
-  t->anc[0][0] = 1;
+  std::memset(t->dev.anc, 0, sizeof t->dev.anc);
+  t->dev.anc[0][0] = 1;
   std::vector<uint32_t> used(size_t(n), 0);   // rank bitmask per parent
   int prev_d = 0, prev_p = -1, prev_r = -1;
   for (int i = 1; i < n; ++i) {
@@ -119,9 +119,9 @@ tr_status build_tree(int32_t n, const int32_t* parent, const int32_t* rank, int3
     t->dev.rank[i] = uint8_t(r);
     t->dev.depth[i] = uint8_t(d);
     if (d > t->dev.D) t->dev.D = d;
-    t->anc[i][0] = t->anc[p][0];
-    t->anc[i][1] = t->anc[p][1];
-    t->anc[i][i >> 6] |= uint64_t(1) << (i & 63);
+    t->dev.anc[i][0] = t->dev.anc[p][0];
+    t->dev.anc[i][1] = t->dev.anc[p][1];
+    t->dev.anc[i][i >> 6] |= uint64_t(1) << (i & 63);
   }
   for (int i = n; i < tr::kMaxNodes; ++i) {
     t->dev.parent[i] = 0xFF;
@@ -203,8 +203,8 @@ tr_status tr_tree_info(const tr_tree* t, int32_t* n_nodes, int32_t* depth, int32
     if (rank_out) rank_out[i] = i ? t->dev.rank[i] : -1;
     if (depth_out) depth_out[i] = t->dev.depth[i];
     if (anc_out) {
-      anc_out[2 * i] = t->anc[i][0];
-      anc_out[2 * i + 1] = t->anc[i][1];
+      anc_out[2 * i] = t->dev.anc[i][0];
+      anc_out[2 * i + 1] = t->dev.anc[i][1];
     }
   }
   return ok();

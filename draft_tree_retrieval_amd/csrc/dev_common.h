@@ -74,10 +74,19 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   }
   return v;
 }
+// Maximum over the wave, in every lane, without the LDS crossbar: DPP
+// within each 16-lane row (swap neighbours, swap pairs, mirror the halves,
+// mirror the row: after each step a lane holds the maximum over 2, 4, 8,
+// 16 lanes), then gfx950's permlane swaps across rows and halves.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = max(v, (uint32_t)__shfl_xor(v, m, 64));
-  return v;
+  v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0xB1, 0xF, 0xF, false)));   // quad_perm 1,0,3,2
+  v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x4E, 0xF, 0xF, false)));   // quad_perm 2,3,0,1
+  v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x141, 0xF, 0xF, false)));  // row_half_mirror
+  v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x140, 0xF, 0xF, false)));  // row_mirror
+  const auto r16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max(uint32_t(r16[0]), uint32_t(r16[1]));
+  const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max(uint32_t(r32[0]), uint32_t(r32[1]));
 }
 // Reductions over lanes l, l^16 (x16) or l, l^32 (x32) with gfx950's
 // permlane swaps (VALU, no trip through the LDS crossbar).  With both

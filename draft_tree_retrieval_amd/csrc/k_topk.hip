@@ -141,7 +141,7 @@ __device__ __forceinline__ void block_merge(TopList<KM>& L, uint64_t (*s_keys)[K
 // while waves 1.. write the verdict, wave 1 the updated rows of M and
 // waves 1.. copy the accepted key/value rows, so retrieval's loads never
 // wait behind their stores.
-template <typename MT, bool BF16, bool SAMPLE>
+template <typename MT, int KM, bool BF16, bool SAMPLE>
 __device__ __forceinline__ void seq_tail(TailShared& S, const TreeDev& tree, int b, int32_t k,
                                          int64_t V, const int32_t* topk_b, int32_t* tok_b,
                                          const TailArgs& tail, uint8_t* ws, const void* logits,
@@ -181,21 +181,33 @@ __device__ __forceinline__ void seq_tail(TailShared& S, const TreeDev& tree, int
     return;
   }
   tail_load(S, tree, tok_b, topk_b, k, tail.k_cache ? tail.prefix_len + b : nullptr);
-  PreRows<MT> pre;
-  if (wave == 0) tail_prefetch<MT>(S, tree, k, M_b, V, pre);   // in flight during verification
-  tail_verify(S, tree, k);
+  // wave 0 verifies while its prefetch is in flight; wave 1 fills the
+  // update map meanwhile unless only the accepted path is recycled (that
+  // map needs the verdict)
+  const bool path_only = tail.update_mode == UPDATE_ACCEPTED;
+  PreRows<MT, KM> pre;
+  Verdict vd{};
+  if (wave == 0) {
+    tail_prefetch<MT, KM>(S, tree, k, M_b, V, pre);
+    vd = tail_verify_wave(S, tree, k);
+    if (path_only) {
+      wave_lds_sync();
+      tail_update_claim(S, tree, V, ws, true);
+    }
+  } else if (wave == 1 && !path_only) {
+    tail_update_claim(S, tree, V, ws, false);
+  }
+  __syncthreads();                                   // verdict and update map complete
   tail_write_verdict(S, tree, b, tail.accept_len, tail.accept_path, nullptr, tail.emitted, 64);
-  if (wave == 0) tail_update_claim(S, tree, V, ws, tail.update_mode == UPDATE_ACCEPTED);
-  __syncthreads();                                   // the LDS map is complete
   const bool fits = tail_commit(S, tree, b, tail, ws, wave == 0 ? 1 << 30 : 64);
   if (wave == 1) tail_update_store<MT>(S, tree, k, M_b, V);
   if (wave != 0) return;
   tail_prefetch_store(S, tree, k, V, pre);
   wave_lds_sync();
-  tail_retrieve<MT>(S, tree, S.bonus, M_b, V, k, tok_b, ws, true, true);
+  tail_retrieve<MT>(S, tree, vd.bonus, M_b, V, k, tok_b, ws, true, true);
   if (threadIdx.x == 0) {
-    tail.root_tok[b] = S.bonus;
-    if (fits) tail.prefix_len[b] = int32_t(S.P + S.L + 1);
+    tail.root_tok[b] = vd.bonus;
+    if (fits) tail.prefix_len[b] = int32_t(S.P + vd.L + 1);
   }
 }
 
@@ -464,9 +476,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SAMPLE ? 3 :
   const int32_t* topk_b = ids_out + int64_t(b) * tree.T * k;
   int32_t* tok_b = tail.tree_tok + int64_t(b) * tree.T;
   if (tail.m_is64)
-    seq_tail<int64_t, BF16, SAMPLE>(S, tree, b, k, V, topk_b, tok_b, tail, ws, logits, stat, segs);
+    seq_tail<int64_t, KM, BF16, SAMPLE>(S, tree, b, k, V, topk_b, tok_b, tail, ws, logits, stat, segs);
   else
-    seq_tail<int32_t, BF16, SAMPLE>(S, tree, b, k, V, topk_b, tok_b, tail, ws, logits, stat, segs);
+    seq_tail<int32_t, KM, BF16, SAMPLE>(S, tree, b, k, V, topk_b, tok_b, tail, ws, logits, stat, segs);
 }
 
 // Second half of the fused LM head: one block per row merges the 8 best
@@ -506,9 +518,9 @@ __global__ __launch_bounds__(512) void lmhead_merge_kernel(const uint64_t* __res
   const int32_t* topk_b = ids_out + int64_t(b) * tree.T * k;
   int32_t* tok_b = tail.tree_tok + int64_t(b) * tree.T;
   if (tail.m_is64)
-    seq_tail<int64_t, true, false>(S, tree, b, k, V, topk_b, tok_b, tail, ws, nullptr, nullptr, 1);
+    seq_tail<int64_t, 8, true, false>(S, tree, b, k, V, topk_b, tok_b, tail, ws, nullptr, nullptr, 1);
   else
-    seq_tail<int32_t, true, false>(S, tree, b, k, V, topk_b, tok_b, tail, ws, nullptr, nullptr, 1);
+    seq_tail<int32_t, 8, true, false>(S, tree, b, k, V, topk_b, tok_b, tail, ws, nullptr, nullptr, 1);
 }
 
 hipError_t launch_lmhead_merge(const TreeDev& tree, int64_t rows, const uint64_t* part, int32_t nvs,

@@ -27,6 +27,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 struct TailShared {
+  uint64_t anc[kMaxNodes][2];           // bit m of anc[n]: m lies on the path root..n (n included)
   uint8_t par[kMaxNodes];               // the template (LDS copy: indexed reads of the
   uint8_t dep[kMaxNodes];               // kernel argument would each be a memory
   uint8_t rnk[kMaxNodes];               // round trip)
@@ -91,9 +92,38 @@ __device__ __forceinline__ void tail_tree(TailShared& S, const TreeDev& tree) {
   }
 }
 
-// tok <- tree_tok_b, the template, the sequence's top-k rows and (when
-// given) its prefix length into LDS.  The rows were handed over by other
-// blocks of the same launch: read them with get_dev, all in flight at once.
+// The template and every node's ancestor set into LDS, by one wave (nodes
+// lane and lane + 64).  Indexed reads of the kernel argument are memory
+// round trips: they leave together with the caller's other loads.
+__device__ __forceinline__ void tail_tree_wave(TailShared& S, const TreeDev& tree) {
+  const int lane = threadIdx.x & 63;
+  uint8_t par[2], dep[2], rnk[2];
+  uint64_t a0[2], a1[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {               // every index < kMaxNodes: no branch
+    const int n = lane + 64 * h;
+    par[h] = tree.parent[n];
+    dep[h] = tree.depth[n];
+    rnk[h] = tree.rank[n];
+    a0[h] = tree.anc[n][0];
+    a1[h] = tree.anc[n][1];
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int n = lane + 64 * h;
+    if (n >= tree.T) continue;
+    S.par[n] = par[h];
+    S.dep[n] = dep[h];
+    S.rnk[n] = rnk[h];
+    S.anc[n][0] = a0[h];
+    S.anc[n][1] = a1[h];
+  }
+}
+
+// tok <- tree_tok_b, the template with its ancestor sets, the sequence's
+// top-k rows and (when given) its prefix length into LDS.  The rows were
+// handed over by other blocks of the same launch: read them with get_dev,
+// all in flight at once, while wave 0 builds the template.
 // Needs blockDim.x >= 256 (T * k <= 2048 ids, at most 8 per thread).
 __device__ __forceinline__ void tail_load(TailShared& S, const TreeDev& tree, const int32_t* tok_b,
                                           const int32_t* topk_b, int32_t k,
@@ -107,7 +137,7 @@ __device__ __forceinline__ void tail_load(TailShared& S, const TreeDev& tree, co
     v[r] = get_dev(topk_b + min(n + r * int(blockDim.x), nk - 1));
   const int32_t t = tok_b[min(n, tree.T - 1)];
   const int32_t P = prefix_len_b ? *prefix_len_b : 0;
-  tail_tree(S, tree);
+  if ((threadIdx.x >> 6) == 0) tail_tree_wave(S, tree);
   map_clear(S);
 #pragma unroll
   for (int r = 0; r < kPer; ++r)
@@ -121,14 +151,15 @@ __device__ __forceinline__ void tail_load(TailShared& S, const TreeDev& tree, co
 // lane and lane + 64: the next tree's root is g(best) for the accepted
 // node best, so its first layer is one of these rows.  The values stay in
 // registers until tail_prefetch_store, so the loads overlap verification.
-template <typename MT>
+// KM >= k bounds the row length (8 or 16).
+template <typename MT, int KM>
 struct PreRows {
-  MT v[2][kMaxK];
+  MT v[2][KM];
   bool ok[2];                               // the node's greedy token is a valid id
 };
-template <typename MT>
+template <typename MT, int KM>
 __device__ __forceinline__ void tail_prefetch(const TailShared& S, const TreeDev& tree, int32_t k,
-                                              const void* M_b, int64_t V, PreRows<MT>& r) {
+                                              const void* M_b, int64_t V, PreRows<MT, KM>& r) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -139,21 +170,21 @@ __device__ __forceinline__ void tail_prefetch(const TailShared& S, const TreeDev
     // (no later write to r.v before tail_prefetch_store, or the compiler
     // would wait for the loads there)
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j)
+    for (int j = 0; j < KM; ++j)
       r.v[h][j] = reinterpret_cast<const MT*>(M_b)[base + min(j, k - 1)];
   }
 }
 // Out-of-range ids become -2 (flagged where used).
-template <typename MT>
+template <typename MT, int KM>
 __device__ __forceinline__ void tail_prefetch_store(TailShared& S, const TreeDev& tree, int32_t k,
-                                                    int64_t V, const PreRows<MT>& r) {
+                                                    int64_t V, const PreRows<MT, KM>& r) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int n = lane + 64 * h;
     if (n >= tree.T) continue;
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
+    for (int j = 0; j < KM; ++j) {
       const int64_t v = int64_t(r.v[h][j]);
       if (j < k) S.pre[n * k + j] = !r.ok[h] ? -1 : (v >= 0 && v < V) ? int32_t(v) : -2;
     }
@@ -163,37 +194,61 @@ __device__ __forceinline__ void tail_prefetch_store(TailShared& S, const TreeDev
 // Greedy verification: node n is accepted when every node m on its path
 // below the root carries the greedy token of its parent, tok(m) == g(par m);
 // best = deepest accepted node, ties to the lowest index; path root..best.
-// Each thread walks its own node's path in LDS (no barrier per level).
-__device__ __forceinline__ void tail_verify(TailShared& S, const TreeDev& tree, int32_t k) {
-  const int tid = threadIdx.x;
+// Run by one wave (nodes lane and lane + 64) without a block barrier: the
+// per-node matches form a 128-bit ballot mask, a node is accepted when its
+// ancestor set lies inside that mask, and the path is best's ancestor set,
+// each member writing itself at its depth.  S.best, S.L, S.bonus and S.path
+// become visible to the other waves at the caller's next barrier; the
+// values are returned for the calling wave.
+struct Verdict {
+  int best, L, bonus;
+};
+__device__ __forceinline__ Verdict tail_verify_wave(TailShared& S, const TreeDev& tree, int32_t k) {
+  const int lane = threadIdx.x & 63;
+  int dep[2];
+  bool match[2];
+  uint64_t a[2][2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int n = lane + 64 * h;
+    const bool in = n < tree.T;
+    const int p = in ? S.par[n] : 0;
+    dep[h] = in ? S.dep[n] : 0;
+    a[h][0] = in ? S.anc[n][0] : 0;
+    a[h][1] = in ? S.anc[n][1] : 0;
+    const int32_t t = in ? S.tok[n] : 0;
+    const int32_t g = (in && n != 0) ? S.topk[p * k] : 0;
+    match[h] = in && (n == 0 || t == g);
+  }
+  const uint64_t m0 = __ballot(match[0]), m1 = __ballot(match[1]);
   uint32_t key = 0;
-  for (int n = tid; n < tree.T; n += blockDim.x) {
-    bool ok = true;
-    for (int m = n; m != 0;) {
-      const int p = S.par[m];
-      ok = ok && (S.tok[m] == S.topk[p * k]);
-      m = p;
-    }
-    if (ok) key = max(key, (uint32_t(S.dep[n]) << 8) | uint32_t(255 - n));
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int n = lane + 64 * h;
+    const bool ok = n < tree.T && ((a[h][0] & ~m0) | (a[h][1] & ~m1)) == 0;
+    if (ok) key = max(key, (uint32_t(dep[h]) << 8) | uint32_t(255 - n));
   }
   key = wave_max_u32(key);
-  const int nw = blockDim.x >> 6;
-  if ((tid & 63) == 0) S.red[tid >> 6] = key;
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t m = S.red[0];
-    for (int w = 1; w < nw; ++w) m = max(m, S.red[w]);
-    const int best = 255 - int(m & 255u);
-    const int L = S.dep[best];
-    int n = best;
-    for (int i = L; i >= 0; --i) {
-      S.path[i] = n;
-      n = S.par[n];
-    }
-    S.best = best;
-    S.L = L;
-    S.bonus = S.topk[best * k];
+  Verdict v;
+  v.best = 255 - int(key & 255u);
+  v.L = int(key >> 8);
+  const uint64_t on0 = S.anc[v.best][0], on1 = S.anc[v.best][1];
+  v.bonus = S.topk[v.best * k];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int n = lane + 64 * h;
+    if (n < tree.T && (((h ? on1 : on0) >> lane) & 1u)) S.path[dep[h]] = n;
   }
+  if (lane == 0) {
+    S.best = v.best;
+    S.L = v.L;
+    S.bonus = v.bonus;
+  }
+  return v;
+}
+// The same for a whole block: wave 0 decides, then every thread sees it.
+__device__ __forceinline__ void tail_verify(TailShared& S, const TreeDev& tree, int32_t k) {
+  if ((threadIdx.x >> 6) == 0) tail_verify_wave(S, tree, k);
   __syncthreads();
 }
 
@@ -331,8 +386,8 @@ __device__ __forceinline__ bool tail_commit(const TailShared& S, const TreeDev& 
 //
 // The layers form a chain of dependent reads, so each layer keeps its
 // chain short: the nodes' template data sit in registers, both nodes of a
-// lane are resolved side by side, and M is read only when some lane needs
-// a row that is neither in the map nor prefetched.
+// lane are resolved side by side, and each layer's M load leaves before
+// the map probe that may make it unnecessary.
 template <typename MT>
 __device__ __forceinline__ void tail_retrieve(TailShared& S, const TreeDev& tree, int32_t root,
                                               const void* M_b, int64_t V, int32_t k,
@@ -353,25 +408,32 @@ __device__ __forceinline__ void tail_retrieve(TailShared& S, const TreeDev& tree
   wave_lds_sync();
   for (int d = 1; d <= tree.D; ++d) {
     int32_t p[2], w[2], src[2];                   // src: 0 none, 1 map, 2 prefetched, 3 M
-#pragma unroll
-    for (int h = 0; h < 2; ++h) p[h] = dep[h] == d ? S.nxt[par[h]] : -1;
+    bool pv[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const bool pv = p[h] >= 0 && int64_t(p[h]) < V;
-      if (p[h] >= 0 && !pv) set_flag(ws, TR_FLAG_BAD_TOKEN);
+      p[h] = dep[h] == d ? S.nxt[par[h]] : -1;
+      pv[h] = p[h] >= 0 && int64_t(p[h]) < V;
+    }
+    // M is read before the map is probed, so the probe's LDS round trips
+    // overlap the load (a map hit discards the value); row 0 stands in for
+    // lanes without a valid parent token.  The first layer comes from the
+    // prefetched row when there is one.
+    MT mv[2] = {MT(0), MT(0)};
+    if (!(use_pre && d == 1)) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        mv[h] = reinterpret_cast<const MT*>(M_b)[pv[h] ? int64_t(p[h]) * k + rnk[h] : 0];
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (p[h] >= 0 && !pv[h]) set_flag(ws, TR_FLAG_BAD_TOKEN);
       w[h] = -1;
-      if (pv && use_map) {                         // first probe inline, collisions in map_get
+      if (pv[h] && use_map) {                      // first probe inline, collisions in map_get
         const uint32_t slot = tok_hash(p[h]);
         const int32_t key = S.hkey[slot];
         w[h] = key == p[h] ? S.hval[slot] : key == -1 ? -1 : map_get(S, p[h]);
       }
-      src[h] = !pv ? 0 : w[h] >= 0 ? 1 : (use_pre && d == 1) ? 2 : 3;
-    }
-    MT mv[2] = {MT(0), MT(0)};
-    if (__ballot(src[0] == 3 || src[1] == 3)) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)                  // row 0 stands in for lanes that need none
-        mv[h] = reinterpret_cast<const MT*>(M_b)[src[h] == 3 ? int64_t(p[h]) * k + rnk[h] : 0];
+      src[h] = !pv[h] ? 0 : w[h] >= 0 ? 1 : (use_pre && d == 1) ? 2 : 3;
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {

@@ -23,6 +23,7 @@ struct TreeDev {
   uint8_t parent[kMaxNodes];     // 0xFF for the root
   uint8_t rank[kMaxNodes];
   uint8_t depth[kMaxNodes];
+  uint64_t anc[kMaxNodes][2];    // bit m of anc[n]: m lies on the path root..n (n included)
 };
 
 }  // namespace tr
@@ -30,7 +31,6 @@ struct TreeDev {
 struct tr_tree {
   tr::TreeDev dev;
   int32_t k;
-  uint64_t anc[tr::kMaxNodes][2];
 };
 
 namespace tr {
