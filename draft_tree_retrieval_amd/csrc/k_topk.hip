@@ -160,10 +160,12 @@ __device__ __forceinline__ void seq_tail(TailShared& S, const TreeDev& tree, int
     tail_write_verdict(S, tree, b, tail.accept_len, tail.accept_path, nullptr, tail.emitted, 64);
     if (wave == 0) tail_update_claim(S, tree, V, ws, tail.update_mode == UPDATE_ACCEPTED);
     __syncthreads();
-    const bool fits = tail_commit(S, tree, b, tail, ws, wave == 0 ? 1 << 30 : 64);
-    if (wave == 1) tail_update_store<MT>(S, tree, k, M_b, V);
-    if (wave != 0) return;
-    wave_lds_sync();
+    if (wave != 0) {
+      tail_commit(S, tree, b, tail, ws, 64);
+      if (wave == 1) tail_update_store<MT>(S, tree, k, M_b, V);
+      return;
+    }
+    const bool fits = tail_commit_fits(S, tail, S.L);
     tail_retrieve<MT>(S, tree, S.bonus, M_b, V, k, tok_b, ws, true, false);
     if (threadIdx.x == 0) {
       tail.root_tok[b] = S.bonus;
@@ -198,10 +200,13 @@ __device__ __forceinline__ void seq_tail(TailShared& S, const TreeDev& tree, int
     tail_update_claim(S, tree, V, ws, false);
   }
   __syncthreads();                                   // verdict and update map complete
-  tail_write_verdict(S, tree, b, tail.accept_len, tail.accept_path, nullptr, tail.emitted, 64);
-  const bool fits = tail_commit(S, tree, b, tail, ws, wave == 0 ? 1 << 30 : 64);
-  if (wave == 1) tail_update_store<MT>(S, tree, k, M_b, V);
-  if (wave != 0) return;
+  if (wave != 0) {                                   // outputs and stores
+    tail_write_verdict(S, tree, b, tail.accept_len, tail.accept_path, nullptr, tail.emitted, 64);
+    tail_commit(S, tree, b, tail, ws, 64);
+    if (wave == 1) tail_update_store<MT>(S, tree, k, M_b, V);
+    return;
+  }
+  const bool fits = tail_commit_fits(S, tail, vd.L);
   tail_prefetch_store(S, tree, k, V, pre);
   wave_lds_sync();
   tail_retrieve<MT>(S, tree, vd.bonus, M_b, V, k, tok_b, ws, true, true);

@@ -26,6 +26,8 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+constexpr int kMapSlots = 512;          // LDS map: 128 groups of 4 slots
+
 struct TailShared {
   uint64_t anc[kMaxNodes][2];           // bit m of anc[n]: m lies on the path root..n (n included)
   uint8_t par[kMaxNodes];               // the template (LDS copy: indexed reads of the
@@ -36,8 +38,8 @@ struct TailShared {
   int32_t pre[kMaxNodes * kMaxK];       // M row of each node's greedy token, as before the update
   int32_t nxt[kMaxNodes];               // next tree tokens
   int32_t path[kMaxNodes];              // accepted path, root first
-  int32_t hkey[256];                    // token -> node whose row M now holds
-  int32_t hval[256];
+  alignas(16) int32_t hkey[kMapSlots];  // token -> node whose row M now holds
+  alignas(16) int32_t hval[kMapSlots];
   uint32_t red[16];
   int32_t best, L, bonus, P;
 };
@@ -56,31 +58,50 @@ __device__ __forceinline__ void m_store(void* M, int64_t idx, int32_t v) {
 
 // Small open-addressing map in LDS from a token to the highest tree node
 // carrying it (the node whose top-k row M holds for that token after this
-// step's update).  At most 128 keys in 256 slots.
-__device__ __forceinline__ uint32_t tok_hash(int32_t t) { return (uint32_t(t) * 2654435761u) >> 24; }
+// step's update): at most 128 keys in 512 slots, linear probing that starts
+// at the first slot of the token's aligned group of four, so a lookup reads
+// a whole group (keys, then values) in one 16-byte LDS access each and
+// rarely needs the next group.
+__device__ __forceinline__ uint32_t tok_group(int32_t t) {
+  return (uint32_t(t) * 2654435761u) >> 25;           // 128 groups
+}
 __device__ __forceinline__ void map_clear(TailShared& S) {
-  for (int i = threadIdx.x; i < 256; i += blockDim.x) {
+  for (int i = threadIdx.x; i < kMapSlots; i += blockDim.x) {
     S.hkey[i] = -1;
     S.hval[i] = -1;
   }
 }
 // Slot of token t, claimed if t is not in the map yet.
 __device__ __forceinline__ uint32_t map_claim(TailShared& S, int32_t t) {
-  uint32_t slot = tok_hash(t);
+  uint32_t slot = tok_group(t) * 4;
   while (true) {
     const int32_t prev = atomicCAS(&S.hkey[slot], -1, t);
     if (prev == -1 || prev == t) return slot;
-    slot = (slot + 1) & 255u;
+    slot = (slot + 1) & uint32_t(kMapSlots - 1);
+  }
+}
+// Lookup within one group: the value of t, -1 when an empty slot ends the
+// probe first, -2 when all four slots hold other keys (go on to the next).
+__device__ __forceinline__ int32_t group_find(const i32x4& keys, const i32x4& vals, int32_t t) {
+  int32_t w = -2;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int32_t hit = keys[j] == t ? vals[j] : keys[j] == -1 ? -1 : -2;
+    w = w == -2 ? hit : w;
+  }
+  return w;
+}
+__device__ __forceinline__ int32_t map_get_from(const TailShared& S, int32_t t, uint32_t g) {
+  while (true) {
+    const i32x4 keys = reinterpret_cast<const i32x4*>(S.hkey)[g];
+    const i32x4 vals = reinterpret_cast<const i32x4*>(S.hval)[g];
+    const int32_t w = group_find(keys, vals, t);
+    if (w != -2) return w;
+    g = (g + 1) & uint32_t(kMapSlots / 4 - 1);
   }
 }
 __device__ __forceinline__ int32_t map_get(const TailShared& S, int32_t t) {
-  uint32_t slot = tok_hash(t);
-  while (true) {
-    const int32_t key = S.hkey[slot];
-    if (key == t) return S.hval[slot];
-    if (key == -1) return -1;
-    slot = (slot + 1) & 255u;
-  }
+  return map_get_from(S, t, tok_group(t));
 }
 
 // The template into LDS; the caller synchronises before use.
@@ -312,23 +333,27 @@ __device__ __forceinline__ void tail_update_store(const TailShared& S, const Tre
   }
 }
 
+// Whether the accepted rows fit in the cache: the prefix length advances
+// (and the rows are copied) only then.
+__device__ __forceinline__ bool tail_commit_fits(const TailShared& S, const TailArgs& a, int L) {
+  return a.k_cache && S.P >= 0 && int64_t(S.P) + L + 1 <= a.cap;
+}
+
 // Copy of the key/value rows of path[0..L] to cache positions P..P+L by
-// the threads [first, blockDim.x), R 16-byte units per thread in flight.
-// Returns whether the rows fit (the caller advances the prefix length);
-// they are copied only then.  S.L (verification) and S.P (tail_load) must
-// be visible.  A paged cache copies every layer's rows, each position into
+// the threads [first, blockDim.x), R 16-byte units per thread in flight;
+// thread first raises the flag when they do not fit (tail_commit_fits).
+// S.L (verification) and S.P (tail_load) must be visible.  A paged cache copies every layer's rows, each position into
 // row p % page_size of page table[b][p / page_size] of that layer's pool.
-__device__ __forceinline__ bool tail_commit(const TailShared& S, const TreeDev& tree, int b,
+__device__ __forceinline__ void tail_commit(const TailShared& S, const TreeDev& tree, int b,
                                             const TailArgs& a, uint8_t* ws, int first) {
-  if (!a.k_cache) return false;
+  const int me = int(threadIdx.x) - first, count = int(blockDim.x) - first;
+  if (!a.k_cache || me < 0) return;
   const int64_t P = S.P;
   const int nrows = S.L + 1;
   if (P < 0 || P + nrows > a.cap) {
-    if (threadIdx.x == 0) set_flag(ws, TR_FLAG_CACHE_FULL);
-    return false;
+    if (me == 0) set_flag(ws, TR_FLAG_CACHE_FULL);
+    return;
   }
-  const int me = int(threadIdx.x) - first, count = int(blockDim.x) - first;
-  if (me < 0) return true;
   const bool paged = a.paged.table != nullptr;
   const int upr = a.row_bytes >> 4;               // 16-byte units per row
   const int per_node = a.Hkv * upr;
@@ -374,7 +399,6 @@ __device__ __forceinline__ bool tail_commit(const TailShared& S, const TreeDev& 
       *reinterpret_cast<u32x4*>(dst) = buf[r];
     }
   }
-  return true;
 }
 
 // Draft tree retrieval: nxt[0] = root; layer by layer
@@ -407,43 +431,54 @@ __device__ __forceinline__ void tail_retrieve(TailShared& S, const TreeDev& tree
   if (lane == 0) S.nxt[0] = root;
   wave_lds_sync();
   for (int d = 1; d <= tree.D; ++d) {
-    int32_t p[2], w[2], src[2];                   // src: 0 none, 1 map, 2 prefetched, 3 M
+    // Three LDS round trips per layer: the parent tokens; the map group of
+    // each (keys and values together) while M is read; the value a map hit
+    // or the prefetched first layer supplies.  The M load leaves before the
+    // probe and is waited for last (a map hit discards it); row 0 stands in
+    // for lanes without a valid parent token.
+    int32_t p[2], w[2], alt[2];
     bool pv[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       p[h] = dep[h] == d ? S.nxt[par[h]] : -1;
       pv[h] = p[h] >= 0 && int64_t(p[h]) < V;
     }
-    // M is read before the map is probed, so the probe's LDS round trips
-    // overlap the load (a map hit discards the value); row 0 stands in for
-    // lanes without a valid parent token.  The first layer comes from the
-    // prefetched row when there is one.
+    const bool first_pre = use_pre && d == 1;
     MT mv[2] = {MT(0), MT(0)};
-    if (!(use_pre && d == 1)) {
+    if (!first_pre) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
         mv[h] = reinterpret_cast<const MT*>(M_b)[pv[h] ? int64_t(p[h]) * k + rnk[h] : 0];
     }
+    if (use_map) {
+      uint32_t g[2];
+      i32x4 keys[2], vals[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        g[h] = tok_group(pv[h] ? p[h] : 0);
+        keys[h] = reinterpret_cast<const i32x4*>(S.hkey)[g[h]];
+        vals[h] = reinterpret_cast<const i32x4*>(S.hval)[g[h]];
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        w[h] = pv[h] ? group_find(keys[h], vals[h], p[h]) : -1;
+        if (w[h] == -2) w[h] = map_get_from(S, p[h], (g[h] + 1) & uint32_t(kMapSlots / 4 - 1));
+      }
+    } else {
+      w[0] = w[1] = -1;
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      if (p[h] >= 0 && !pv[h]) set_flag(ws, TR_FLAG_BAD_TOKEN);
-      w[h] = -1;
-      if (pv[h] && use_map) {                      // first probe inline, collisions in map_get
-        const uint32_t slot = tok_hash(p[h]);
-        const int32_t key = S.hkey[slot];
-        w[h] = key == p[h] ? S.hval[slot] : key == -1 ? -1 : map_get(S, p[h]);
-      }
-      src[h] = !pv[h] ? 0 : w[h] >= 0 ? 1 : (use_pre && d == 1) ? 2 : 3;
+      const int32_t* src = w[h] >= 0 ? S.topk + w[h] * k : S.pre + pre_row;
+      alt[h] = src[rnk[h]];
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       if (dep[h] != d) continue;
-      int64_t v = -1;
-      if (src[h] == 1) v = S.topk[w[h] * k + rnk[h]];
-      else if (src[h] == 2) v = S.pre[pre_row + rnk[h]];
-      else if (src[h] == 3) v = int64_t(mv[h]);
+      if (p[h] >= 0 && !pv[h]) set_flag(ws, TR_FLAG_BAD_TOKEN);
+      const int64_t v = !pv[h] ? -1 : (w[h] >= 0 || first_pre) ? int64_t(alt[h]) : int64_t(mv[h]);
       const bool ok = v >= 0 && v < V;
-      if (src[h] != 0 && !ok) set_flag(ws, TR_FLAG_BAD_TOKEN);
+      if (pv[h] && !ok) set_flag(ws, TR_FLAG_BAD_TOKEN);
       S.nxt[n[h]] = ok ? int32_t(v) : -1;
     }
     wave_lds_sync();
