@@ -240,7 +240,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SAMPLE ? 3 :
   __shared__ uint64_t s_keys[NW][KM];
   __shared__ uint64_t s_best[KM];
   __shared__ uint32_t s_wcnt[NW];
-  __shared__ uint32_t s_lm[NT];
+  __shared__ uint32_t s_top[NW * KM];
   __shared__ float s_wsum[NW];
 
   // aligned vector range [a0, a1) inside [s0, s1); at most VE-1 loose
@@ -286,21 +286,39 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SAMPLE ? 3 :
   if (BF16) mt = max(mt, max(m2 & 0xFFFFu, m2 >> 16) << 16);
 
   // ---- 2. threshold: the largest code reached by at least k lane maxima
-  // of the block (every wave computes the same value)
-  s_lm[tid] = mt;
-  __syncthreads();
-  uint32_t lm[NW];
+  // of the block, i.e. the k-th largest lane maximum.  Each wave bisects
+  // over its own 64 lanes for its k-th largest and puts its k largest lane
+  // maxima into LDS (those above it, then copies of it); the block's k-th
+  // largest is the k-th largest of these NW * k values (the block's k
+  // largest are among them), found by every wave with a second bisection.
+  constexpr int kLowBit = BF16 ? 16 : 0;
+  uint32_t lo = 0;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) lm[w] = s_lm[w * 64 + lane];
+  for (int bit = 31; bit >= kLowBit; --bit) {
+    const uint32_t c = lo | (1u << bit);
+    if (__popcll(__ballot(mt >= c)) >= k) lo = c;
+  }
+  {
+    const uint64_t gt = __ballot(mt > lo);            // fewer than k lanes
+    const int ngt = __popcll(gt);
+    const uint32_t below = __builtin_amdgcn_mbcnt_hi(uint32_t(gt >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(gt), 0u));
+    if (mt > lo) s_top[wave * KM + below] = mt;
+    if (lane >= ngt && lane < k) s_top[wave * KM + lane] = lo;
+  }
+  __syncthreads();
+  constexpr int NTOP = NW * KM;                       // 64 or 128
+  uint32_t tv[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = lane + 64 * h;
+    tv[h] = (i < NTOP && (i % KM) < k) ? s_top[min(i, NTOP - 1)] : 0u;
+  }
 
   // sampling: softmax statistics of the segment, (max, sum of
   // exp2((z - max) * scale)), handed over with the ids
   float seg_max = 0.f;
   if constexpr (SAMPLE) {
-    uint32_t bm = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) bm = max(bm, lm[w]);
-    bm = wave_max_u32(bm);
+    const uint32_t bm = wave_max_u32(max(tv[0], tv[1]));
     seg_max = ord_to_f32(bm);
     const float s2 = tail.temp_scale, off = -seg_max * s2;
     float acc = 0.f;
@@ -327,13 +345,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SAMPLE ? 3 :
     acc = wave_sum_f32(acc);
     if (lane == 0) s_wsum[wave] = acc;
   }
-  uint32_t lo = 0;
+  lo = 0;
 #pragma unroll
-  for (int bit = 31; bit >= (BF16 ? 16 : 0); --bit) {
+  for (int bit = 31; bit >= kLowBit; --bit) {
     const uint32_t c = lo | (1u << bit);
-    int reach = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) reach += __popcll(__ballot(lm[w] >= c));
+    int reach = __popcll(__ballot(tv[0] >= c));
+    if (NTOP > 64) reach += __popcll(__ballot(tv[1] >= c));
     if (reach >= k) lo = c;
   }
 
