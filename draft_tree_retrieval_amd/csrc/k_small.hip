@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) void verify_kernel(TreeDev tree, const int32_t
                                                      int32_t* bonus, int32_t* emitted) {
   __shared__ TailShared S;
   const int b = blockIdx.x;
-  tail_load(S, tree, tree_tok + int64_t(b) * tree.T, topk + int64_t(b) * tree.T * k, k);
+  tail_load<256>(S, tree, tree_tok + int64_t(b) * tree.T, topk + int64_t(b) * tree.T * k, k);
   tail_verify(S, tree, k);
   tail_write_verdict(S, tree, b, accept_len, accept_path, bonus, emitted);
 }

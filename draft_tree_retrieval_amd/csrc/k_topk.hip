@@ -38,8 +38,8 @@ TopkPlan plan_topk(int64_t rows, int64_t V, int32_t k, int32_t esz) {
   TopkPlan p{};
   p.rows = rows;
   p.kmax = k <= 8 ? 8 : 16;
-  p.threads = rows < 256 ? 512 : 256;
-  const int64_t nv = p.threads == 512 ? 8 : 16;           // vectors per lane
+  p.threads = rows < 256 ? 1024 : 256;
+  const int64_t nv = p.threads == 1024 ? 4 : 16;          // vectors per lane
   const int64_t cap = int64_t(p.threads) * nv * (16 / esz);  // largest segment a block holds
   const int64_t max_segs = 256 / p.kmax;                 // the final merge ranks <= 256 keys
   int64_t need = (V + cap - 1) / cap;
@@ -141,7 +141,7 @@ __device__ __forceinline__ void block_merge(TopList<KM>& L, uint64_t (*s_keys)[K
 // while waves 1.. write the verdict, wave 1 the updated rows of M and
 // waves 1.. copy the accepted key/value rows, so retrieval's loads never
 // wait behind their stores.
-template <typename MT, int KM, bool BF16, bool SAMPLE>
+template <typename MT, int KM, int NT, bool BF16, bool SAMPLE>
 __device__ __forceinline__ void seq_tail(TailShared& S, const TreeDev& tree, int b, int32_t k,
                                          int64_t V, const int32_t* topk_b, int32_t* tok_b,
                                          const TailArgs& tail, uint8_t* ws, const void* logits,
@@ -151,7 +151,7 @@ __device__ __forceinline__ void seq_tail(TailShared& S, const TreeDev& tree, int
   if constexpr (SAMPLE) {
     // verification by sampling: no greedy token to prefetch M rows for
     __shared__ SampleShared SS;
-    tail_load(S, tree, tok_b, topk_b, k, tail.k_cache ? tail.prefix_len + b : nullptr);
+    tail_load<NT>(S, tree, tok_b, topk_b, k, tail.k_cache ? tail.prefix_len + b : nullptr);
     sample_prepare<BF16>(S, SS, tree, b, V, logits, stat, segs, tail);
     if (wave == 0) sample_walk(S, SS, tree, V);
     __syncthreads();
@@ -174,7 +174,7 @@ __device__ __forceinline__ void seq_tail(TailShared& S, const TreeDev& tree, int
     return;
   }
   if (tail.mode != TAIL_STEP) {
-    tail_load(S, tree, tok_b, topk_b, k);
+    tail_load<NT>(S, tree, tok_b, topk_b, k);
     if (wave == 0) {
       tail_update_claim(S, tree, V, ws);
       wave_lds_sync();
@@ -182,7 +182,7 @@ __device__ __forceinline__ void seq_tail(TailShared& S, const TreeDev& tree, int
     }
     return;
   }
-  tail_load(S, tree, tok_b, topk_b, k, tail.k_cache ? tail.prefix_len + b : nullptr);
+  tail_load<NT>(S, tree, tok_b, topk_b, k, tail.k_cache ? tail.prefix_len + b : nullptr);
   // wave 0 verifies while its prefetch is in flight; wave 1 fills the
   // update map meanwhile unless only the accepted path is recycled (that
   // map needs the verdict)
@@ -306,10 +306,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SAMPLE ? 3 :
     if (lane >= ngt && lane < k) s_top[wave * KM + lane] = lo;
   }
   __syncthreads();
-  constexpr int NTOP = NW * KM;                       // 64 or 128
-  uint32_t tv[2];
+  constexpr int NTOP = NW * KM;                       // 32 .. 256
+  constexpr int NTV = (NTOP + 63) / 64;
+  uint32_t tv[NTV];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < NTV; ++h) {
     const int i = lane + 64 * h;
     tv[h] = (i < NTOP && (i % KM) < k) ? s_top[min(i, NTOP - 1)] : 0u;
   }
@@ -318,7 +319,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SAMPLE ? 3 :
   // exp2((z - max) * scale)), handed over with the ids
   float seg_max = 0.f;
   if constexpr (SAMPLE) {
-    const uint32_t bm = wave_max_u32(max(tv[0], tv[1]));
+    uint32_t bm = tv[0];
+#pragma unroll
+    for (int h = 1; h < NTV; ++h) bm = max(bm, tv[h]);
+    bm = wave_max_u32(bm);
     seg_max = ord_to_f32(bm);
     const float s2 = tail.temp_scale, off = -seg_max * s2;
     float acc = 0.f;
@@ -349,8 +353,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SAMPLE ? 3 :
 #pragma unroll
   for (int bit = 31; bit >= kLowBit; --bit) {
     const uint32_t c = lo | (1u << bit);
-    int reach = __popcll(__ballot(tv[0] >= c));
-    if (NTOP > 64) reach += __popcll(__ballot(tv[1] >= c));
+    int reach = 0;
+#pragma unroll
+    for (int h = 0; h < NTV; ++h) reach += __popcll(__ballot(tv[h] >= c));
     if (reach >= k) lo = c;
   }
 
@@ -498,9 +503,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SAMPLE ? 3 :
   const int32_t* topk_b = ids_out + int64_t(b) * tree.T * k;
   int32_t* tok_b = tail.tree_tok + int64_t(b) * tree.T;
   if (tail.m_is64)
-    seq_tail<int64_t, KM, BF16, SAMPLE>(S, tree, b, k, V, topk_b, tok_b, tail, ws, logits, stat, segs);
+    seq_tail<int64_t, KM, NT, BF16, SAMPLE>(S, tree, b, k, V, topk_b, tok_b, tail, ws, logits, stat, segs);
   else
-    seq_tail<int32_t, KM, BF16, SAMPLE>(S, tree, b, k, V, topk_b, tok_b, tail, ws, logits, stat, segs);
+    seq_tail<int32_t, KM, NT, BF16, SAMPLE>(S, tree, b, k, V, topk_b, tok_b, tail, ws, logits, stat, segs);
 }
 
 // Second half of the fused LM head: one block per row merges the 8 best
@@ -540,9 +545,9 @@ __global__ __launch_bounds__(512) void lmhead_merge_kernel(const uint64_t* __res
   const int32_t* topk_b = ids_out + int64_t(b) * tree.T * k;
   int32_t* tok_b = tail.tree_tok + int64_t(b) * tree.T;
   if (tail.m_is64)
-    seq_tail<int64_t, 8, true, false>(S, tree, b, k, V, topk_b, tok_b, tail, ws, nullptr, nullptr, 1);
+    seq_tail<int64_t, 8, 512, true, false>(S, tree, b, k, V, topk_b, tok_b, tail, ws, nullptr, nullptr, 1);
   else
-    seq_tail<int32_t, 8, true, false>(S, tree, b, k, V, topk_b, tok_b, tail, ws, nullptr, nullptr, 1);
+    seq_tail<int32_t, 8, 512, true, false>(S, tree, b, k, V, topk_b, tok_b, tail, ws, nullptr, nullptr, 1);
 }
 
 hipError_t launch_lmhead_merge(const TreeDev& tree, int64_t rows, const uint64_t* part, int32_t nvs,
@@ -567,10 +572,10 @@ hipError_t launch_topk(const TreeDev& tree, int32_t B, const void* logits, int l
 #define TR_TOPK_NT(BF, KMV)                                                 \
   do {                                                                      \
     if (tail.sample) {                                                      \
-      if (plan.threads == 512) TR_TOPK(BF, KMV, 512, 8, true);              \
+      if (plan.threads == 1024) TR_TOPK(BF, KMV, 1024, 4, true);            \
       else TR_TOPK(BF, KMV, 256, 16, true);                                 \
     } else {                                                                \
-      if (plan.threads == 512) TR_TOPK(BF, KMV, 512, 8, false);             \
+      if (plan.threads == 1024) TR_TOPK(BF, KMV, 1024, 4, false);           \
       else TR_TOPK(BF, KMV, 256, 16, false);                                \
     }                                                                       \
   } while (0)

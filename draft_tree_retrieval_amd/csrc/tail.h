@@ -145,24 +145,26 @@ __device__ __forceinline__ void tail_tree_wave(TailShared& S, const TreeDev& tre
 // top-k rows and (when given) its prefix length into LDS.  The rows were
 // handed over by other blocks of the same launch: read them with get_dev,
 // all in flight at once, while wave 0 builds the template.
-// Needs blockDim.x >= 256 (T * k <= 2048 ids, at most 8 per thread).
+// NT = blockDim.x >= 256 (T * k <= 2048 ids, at most 8 per thread).
+template <int NT>
 __device__ __forceinline__ void tail_load(TailShared& S, const TreeDev& tree, const int32_t* tok_b,
                                           const int32_t* topk_b, int32_t k,
                                           const int32_t* prefix_len_b = nullptr) {
-  constexpr int kPer = kMaxNodes * kMaxK / 256;
+  static_assert(NT >= 256 && kMaxNodes * kMaxK % NT == 0, "tail_load: 256, 512 or 1024 threads");
+  constexpr int kPer = kMaxNodes * kMaxK / NT;
   const int nk = tree.T * k;
   const int n = threadIdx.x;
   int32_t v[kPer];
 #pragma unroll
   for (int r = 0; r < kPer; ++r)                 // clamped: every load in bounds, none branched
-    v[r] = get_dev(topk_b + min(n + r * int(blockDim.x), nk - 1));
+    v[r] = get_dev(topk_b + min(n + r * NT, nk - 1));
   const int32_t t = tok_b[min(n, tree.T - 1)];
   const int32_t P = prefix_len_b ? *prefix_len_b : 0;
   if ((threadIdx.x >> 6) == 0) tail_tree_wave(S, tree);
   map_clear(S);
 #pragma unroll
   for (int r = 0; r < kPer; ++r)
-    if (n + r * int(blockDim.x) < nk) S.topk[n + r * int(blockDim.x)] = v[r];
+    if (n + r * NT < nk) S.topk[n + r * NT] = v[r];
   if (n < tree.T) S.tok[n] = t;
   if (n == 0) S.P = P;
   __syncthreads();
@@ -342,8 +344,9 @@ __device__ __forceinline__ bool tail_commit_fits(const TailShared& S, const Tail
 // Copy of the key/value rows of path[0..L] to cache positions P..P+L by
 // the threads [first, blockDim.x), R 16-byte units per thread in flight;
 // thread first raises the flag when they do not fit (tail_commit_fits).
-// S.L (verification) and S.P (tail_load) must be visible.  A paged cache copies every layer's rows, each position into
-// row p % page_size of page table[b][p / page_size] of that layer's pool.
+// S.L (verification) and S.P (tail_load) must be visible.  A paged cache
+// copies every layer's rows, each position into row p % page_size of page
+// table[b][p / page_size] of that layer's pool.
 __device__ __forceinline__ void tail_commit(const TailShared& S, const TreeDev& tree, int b,
                                             const TailArgs& a, uint8_t* ws, int first) {
   const int me = int(threadIdx.x) - first, count = int(blockDim.x) - first;
