@@ -574,6 +574,33 @@ __device__ __forceinline__ void load8(const void* base, int64_t elem, float* f) 
   }
 }
 
+// Eight values as loaded (16 bytes of bf16 or 32 of fp32), unpacked only
+// where they are used, so the loads of a batch all leave before the first
+// wait.
+template <bool BF16>
+struct Raw8 {
+  u32x4 u[BF16 ? 1 : 2];
+};
+template <bool BF16>
+__device__ __forceinline__ void load_raw8(const void* base, int64_t elem, Raw8<BF16>& r) {
+  const uint8_t* p = reinterpret_cast<const uint8_t*>(base) + elem * (BF16 ? 2 : 4);
+#pragma unroll
+  for (int i = 0; i < (BF16 ? 1 : 2); ++i) r.u[i] = reinterpret_cast<const u32x4*>(p)[i];
+}
+template <bool BF16>
+__device__ __forceinline__ void unpack8(const Raw8<BF16>& r, float* f) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (BF16) {
+      f[2 * j] = __uint_as_float(r.u[0][j] << 16);
+      f[2 * j + 1] = __uint_as_float(r.u[0][j] & 0xFFFF0000u);
+    } else {
+      f[j] = __uint_as_float(r.u[0][j]);
+      f[4 + j] = __uint_as_float(r.u[1][j]);
+    }
+  }
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(128) void attn_combine(
     TreeDev tree, const void* __restrict__ q, const void* __restrict__ kt,
@@ -581,10 +608,6 @@ __global__ __launch_bounds__(128) void attn_combine(
     const void* __restrict__ part_o, const float2* __restrict__ part_ml, void* __restrict__ out) {
   constexpr int kBatch = 8;
   const int T = tree.T;
-  // parents in LDS: indexed reads of the kernel argument are memory round trips
-  __shared__ uint8_t s_par[kMaxNodes];
-  if (int(threadIdx.x) < T) s_par[threadIdx.x] = tree.parent[threadIdx.x];
-  __syncthreads();
   const int64_t row = int64_t(blockIdx.x) * 8 + (threadIdx.x >> 4);
   if (row >= int64_t(B) * T * Hq) return;          // whole 16-lane groups leave together
   const int li = threadIdx.x & 15;                 // d = 8 li .. 8 li + 7
@@ -609,66 +632,86 @@ __global__ __launch_bounds__(128) void attn_combine(
     m = mn;
   };
   float2 ml[kBatch];
-  float po[kBatch][8];
+  Raw8<BF16> po[kBatch];
   auto load_parts = [&](int c0) {
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const int c = max(0, min(c0 + i, nc - 1));
       const int64_t unit = (int64_t(z) * chunks + c) * Rpad + r;
       ml[i] = part_ml[unit];
-      load8<BF16>(part_o, unit * kHeadDim + 8 * li, po[i]);   // bf16 partials in the bf16 path
+      load_raw8<BF16>(part_o, unit * kHeadDim + 8 * li, po[i]);   // bf16 partials in the bf16 path
     }
   };
-  int j = n;                                       // next path node to visit
+  // the nodes on n's path, n first and the root last: the bits of its
+  // ancestor set (one indexed read of the kernel argument, in flight with
+  // the partials), taken from the highest down
+  uint64_t path[2];
   bool more = true;
   int idx[kBatch];
   int cnt = 0;
-  float kx[kBatch][8], vx[kBatch][8];
+  Raw8<BF16> kx[kBatch], vx[kBatch];
   auto load_tree = [&]() {
     cnt = 0;
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
-      idx[i] = j;
-      if (more) {
+      const bool hi = path[1] != 0;
+      const uint64_t w = hi ? path[1] : path[0];
+      const int bit = w ? 63 - __builtin_clzll(w) : 0;
+      idx[i] = w ? (hi ? 64 : 0) + bit : 0;
+      if (w) {
         ++cnt;
-        if (j == 0) more = false;
-        else j = s_par[j];
+        if (hi) path[1] &= ~(uint64_t(1) << bit);
+        else path[0] &= ~(uint64_t(1) << bit);
       }
     }
+    more = (path[0] | path[1]) != 0;
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const int64_t kv_elem = ((int64_t(b) * T + idx[i]) * Hkv + kvh) * kHeadDim + 8 * li;
-      load8<BF16>(kt, kv_elem, kx[i]);
-      load8<BF16>(vt, kv_elem, vx[i]);
+      load_raw8<BF16>(kt, kv_elem, kx[i]);
+      load_raw8<BF16>(vt, kv_elem, vx[i]);
     }
   };
   auto merge_tree = [&](const float* qv) {
     float sc[kBatch];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
+      float kf[8];
+      unpack8<BF16>(kx[i], kf);
       float d = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) d += qv[e] * kx[i][e];
+      for (int e = 0; e < 8; ++e) d += qv[e] * kf[e];
       sc[i] = row16_sum(d) * sl2;
     }
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i)
-      if (i < cnt) merge(sc[i], 1.f, vx[i]);
+    for (int i = 0; i < kBatch; ++i) {
+      float vf[8];
+      unpack8<BF16>(vx[i], vf);
+      if (i < cnt) merge(sc[i], 1.f, vf);
+    }
   };
 
-  // first batch of everything in flight at once
-  float qv[8];
-  load8<BF16>(q, ((int64_t(b) * T + n) * Hq + h) * kHeadDim + 8 * li, qv);
+  // first batch of everything in flight at once, the ancestor set first
+  // (the tree loads wait for it alone)
+  path[0] = tree.anc[n][0];
+  path[1] = tree.anc[n][1];
+  load_parts(0);                                   // chunks >= 1 (the plan's)
+  Raw8<BF16> qraw;
+  load_raw8<BF16>(q, ((int64_t(b) * T + n) * Hq + h) * kHeadDim + 8 * li, qraw);
   load_tree();
-  if (nc > 0) load_parts(0);
   // prefix chunk partials, chunks in order
   for (int c0 = 0; c0 < nc; c0 += kBatch) {
     if (c0 > 0) load_parts(c0);
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i)
-      if (c0 + i < nc) merge(ml[i].x, ml[i].y, po[i]);
+    for (int i = 0; i < kBatch; ++i) {
+      float pf[8];
+      unpack8<BF16>(po[i], pf);
+      if (c0 + i < nc) merge(ml[i].x, ml[i].y, pf);
+    }
   }
   // tree keys on n's path: n, its parent, ..., the root
+  float qv[8];
+  unpack8<BF16>(qraw, qv);
   merge_tree(qv);
   while (more) {
     load_tree();
