@@ -250,7 +250,7 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
     asm volatile("" ::: "memory");
   };
 
-  auto compute = [&](const uint8_t* Ks, const uint8_t* Vs, int nk) {
+  auto compute = [&](const uint8_t* Ks, const uint8_t* Vs, int nk, bool first) {
     const bool ragged = nk < kSB;                  // mask keys past the chunk end
     // S^T = K Q^T for 4 tiles of 16 keys; operands read ahead of the products
     floatx4 sacc[SPW][4];
@@ -309,15 +309,22 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
       float x[4][4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[t][i] = sacc[s][t][i];
+      if (ragged) {                                // only the chunk's last sub-block
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (t * 16 + 4 * g + i >= nk) x[t][i] = -INFINITY;
+      }
       float mraw = -INFINITY;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = t * 16 + 4 * g + i;
-          x[t][i] = (!ragged || key < nk) ? sacc[s][t][i] : -INFINITY;
-          mraw = fmaxf(mraw, x[t][i]);
-        }
+        for (int i = 0; i < 4; ++i) mraw = fmaxf(mraw, x[t][i]);
       mraw = xmax32(xmax16(mraw));
       const float mnew = fmaxf(mrow[s], mraw * sl2);
       const float alpha = fast_exp2(mrow[s] - mnew);
@@ -334,7 +341,9 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
       psum = xsum32(xsum16(psum));
       lrow[s] = lrow[s] * alpha + psum;
       mrow[s] = mnew;
-      if (__any(alpha != 1.f)) {                   // no lane's maximum moved: nothing to rescale
+      // nothing to rescale on the first sub-block (acc is zero) or when no
+      // lane's maximum moved
+      if (!first && __any(alpha != 1.f)) {
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) acc[s][dt] *= alpha;
       }
@@ -374,7 +383,7 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       dma(j + kRingSlots - 1, (jj + kRingSlots - 1) % kRingSlots);
-      if (active && j < nsub) compute(kslot(jj), vslot(jj), min(kSB, k1 - (k0 + j * kSB)));
+      if (active && j < nsub) compute(kslot(jj), vslot(jj), min(kSB, k1 - (k0 + j * kSB)), j == 0);
       // this step's LDS reads are done before the next barrier
       __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0), vm/exp not waited
       asm volatile("" ::: "memory");
