@@ -116,6 +116,7 @@ __device__ __forceinline__ void mark_empty(float2* part_ml, int64_t unit0, int r
 // ring slot is its own LDS array named statically (one array would make
 // the compiler wait for DMAs into the other slots before every read).
 constexpr int kSB = 64;                   // keys per sub-block
+constexpr float kLazy = 8.f;              // lazy rescaling threshold (log2 units)
 constexpr int kRingSlots = 4;
 constexpr int kSubBytes = kSB * kHeadDim * 2;   // 16 KB
 // PAGED: kc and vc are page pools [num_pages][Hkv][page_size][d] reached
@@ -250,10 +251,8 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
     asm volatile("" ::: "memory");
   };
 
-  auto compute = [&](const uint8_t* Ks, const uint8_t* Vs, int nk, bool first) {
-    const bool ragged = nk < kSB;                  // mask keys past the chunk end
-    // S^T = K Q^T for 4 tiles of 16 keys; operands read ahead of the products
-    floatx4 sacc[SPW][4];
+  // S^T = K Q^T for 4 tiles of 16 keys; operands read ahead of the products
+  auto qk = [&](const uint8_t* Ks, floatx4 (&sacc)[SPW][4]) {
 #pragma unroll
     for (int s = 0; s < SPW; ++s)
 #pragma unroll
@@ -276,87 +275,103 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
           for (int s = 0; s < SPW; ++s)
             sacc[s][t0 + t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[t][ks], qb[s][ks], sacc[s][t0 + t], 0, 0, 0);
     }
-    // V^T operands (transposed LDS reads), read while the softmax runs:
-    // rows kr .. kr+3 with kr = 32 pp + 4 g (+16 for the second half),
-    // lane li at row kr + li / 4, columns 16 dt + 4 (li % 4) .. +3
-    constexpr int VG = 2;
-    bf16x8 va[VG][2];
-    auto read_v = [&](int dt0) {
+  };
+  // V^T operands (transposed LDS reads), read while the softmax runs:
+  // rows kr .. kr+3 with kr = 32 pp + 4 g (+16 for the second half),
+  // lane li at row kr + li / 4, columns 16 dt + 4 (li % 4) .. +3
+  constexpr int VG = 2;
+  bf16x8 va[VG][2];
+  auto read_v = [&](const uint8_t* Vs, int dt0) {
 #pragma unroll
-      for (int i = 0; i < VG; ++i) {
-        const int dt = dt0 + i;
-        const int cch = 2 * dt + ((li >> 1) & 1), half = (li & 1) * 8;
+    for (int i = 0; i < VG; ++i) {
+      const int dt = dt0 + i;
+      const int cch = 2 * dt + ((li >> 1) & 1), half = (li & 1) * 8;
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-          uint32_t u[4];
+      for (int pp = 0; pp < 2; ++pp) {
+        uint32_t u[4];
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int row = 32 * pp + 16 * hh + 4 * g + (li >> 2);
-            const uint8_t* addr = Vs + row * 256 + ((cch ^ ((row & 7) << 1)) << 4) + half;
-            const u32x2 r2 = lds_read_tr16(addr);
-            u[2 * hh] = r2[0];
-            u[2 * hh + 1] = r2[1];
-          }
-          va[i][pp] = __builtin_bit_cast(bf16x8, u32x4{u[0], u[1], u[2], u[3]});
+        for (int hh = 0; hh < 2; ++hh) {
+          const int row = 32 * pp + 16 * hh + 4 * g + (li >> 2);
+          const uint8_t* addr = Vs + row * 256 + ((cch ^ ((row & 7) << 1)) << 4) + half;
+          const u32x2 r2 = lds_read_tr16(addr);
+          u[2 * hh] = r2[0];
+          u[2 * hh + 1] = r2[1];
         }
+        va[i][pp] = __builtin_bit_cast(bf16x8, u32x4{u[0], u[1], u[2], u[3]});
       }
-    };
-    read_v(0);
-    __builtin_amdgcn_sched_barrier(0);
-    // online softmax per query row (the lane's column), on raw scores:
-    // scale > 0, so max(scale s) = scale max(s) and p = 2^(s sl2 - m)
-    bf16x8 pb[SPW][2];
+    }
+  };
+  // keys past the chunk end (its ragged last sub-block) get score -inf
+  auto mask = [&](floatx4 (&sacc)[SPW][4], int nk) {
+    if (nk < kSB) {
 #pragma unroll
-    for (int s = 0; s < SPW; ++s) {
-      float x[4][4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[t][i] = sacc[s][t][i];
-      if (ragged) {                                // only the chunk's last sub-block
+      for (int s = 0; s < SPW; ++s)
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (t * 16 + 4 * g + i >= nk) x[t][i] = -INFINITY;
-      }
+            if (t * 16 + 4 * g + i >= nk) sacc[s][t][i] = -INFINITY;
+    }
+  };
+  // online softmax per query row (the lane's column), on raw scores:
+  // scale > 0, so max(scale s) = scale max(s) and p = 2^(s sl2 - m).
+  // Lazy rescaling: a row's reference maximum moves only when a score
+  // passes it by more than kLazy (log2 units), so the probabilities stay
+  // below 2^kLazy and the accumulators are rarely rescaled; the partial
+  // (m, l, O) stays consistent for any reference m.  No branch: the
+  // rescale of the accumulators is left to the caller (alpha, bump).
+  bf16x8 pb[SPW][2];
+  float alpha[SPW];
+  bool bump[SPW];
+  auto softmax = [&](const floatx4 (&sacc)[SPW][4]) {
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
       float mraw = -INFINITY;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mraw = fmaxf(mraw, x[t][i]);
+        for (int i = 0; i < 4; ++i) mraw = fmaxf(mraw, sacc[s][t][i]);
       mraw = xmax32(xmax16(mraw));
-      const float mnew = fmaxf(mrow[s], mraw * sl2);
-      const float alpha = fast_exp2(mrow[s] - mnew);
+      const float mcand = mraw * sl2;
+      bump[s] = mcand > mrow[s] + kLazy;           // always on the first sub-block
+      const float mnew = bump[s] ? mcand : mrow[s];
+      alpha[s] = bump[s] ? fast_exp2(mrow[s] - mnew) : 1.f;
       float psum = 0.f;
       __bf16 ph[4][4];
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pr = fast_exp2(__builtin_fmaf(x[t][i], sl2, -mnew));
+          const float pr = fast_exp2(__builtin_fmaf(sacc[s][t][i], sl2, -mnew));
           psum += pr;
           ph[t][i] = (__bf16)pr;
         }
       psum = xsum32(xsum16(psum));
-      lrow[s] = lrow[s] * alpha + psum;
+      lrow[s] = lrow[s] * alpha[s] + psum;
       mrow[s] = mnew;
-      // nothing to rescale on the first sub-block (acc is zero) or when no
-      // lane's maximum moved
-      if (!first && __any(alpha != 1.f)) {
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) acc[s][dt] *= alpha;
-      }
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp)
         pb[s][pp] = bf16x8{ph[2 * pp][0], ph[2 * pp][1], ph[2 * pp][2], ph[2 * pp][3],
                            ph[2 * pp + 1][0], ph[2 * pp + 1][1], ph[2 * pp + 1][2], ph[2 * pp + 1][3]};
     }
-    // O^T += V^T P^T over the two 32-key blocks
+  };
+  // nothing to rescale on the first sub-block (acc is zero) or when no
+  // lane's reference moved
+  auto rescale = [&](bool first) {
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
+      if (!first && __any(bump[s])) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) acc[s][dt] *= alpha[s];
+      }
+    }
+  };
+  // O^T += V^T P^T over the two 32-key blocks (va holds dt 0, 1 on entry)
+  auto pv = [&](const uint8_t* Vs) {
 #pragma unroll
     for (int dt0 = 0; dt0 < 8; dt0 += VG) {
       if (dt0 > 0) {
-        read_v(dt0);
+        read_v(Vs, dt0);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
@@ -370,7 +385,10 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
   };
 
   // three sub-blocks in flight, then per sub-block: wait, barrier, refill
-  // the slot freed by the previous sub-block, compute
+  // the slot freed by the previous sub-block, compute.  (A software
+  // pipeline that forms the next sub-block's scores during this one's
+  // softmax measured slower here: the two waves of a SIMD already overlap
+  // each other's matrix and VALU work.)
 #pragma unroll
   for (int j = 0; j < kRingSlots - 1; ++j) dma(j, j);
   const int nround = (nsub + kRingSlots - 1) / kRingSlots * kRingSlots;
@@ -383,7 +401,16 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       dma(j + kRingSlots - 1, (jj + kRingSlots - 1) % kRingSlots);
-      if (active && j < nsub) compute(kslot(jj), vslot(jj), min(kSB, k1 - (k0 + j * kSB)), j == 0);
+      if (active && j < nsub) {
+        floatx4 sc[SPW][4];
+        qk(kslot(jj), sc);
+        mask(sc, min(kSB, k1 - (k0 + j * kSB)));
+        read_v(vslot(jj), 0);
+        __builtin_amdgcn_sched_barrier(0);
+        softmax(sc);
+        rescale(j == 0);
+        pv(vslot(jj));
+      }
       // this step's LDS reads are done before the next barrier
       __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0), vm/exp not waited
       asm volatile("" ::: "memory");
