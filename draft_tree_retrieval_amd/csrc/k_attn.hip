@@ -637,7 +637,9 @@ __device__ __forceinline__ void unpack8(const Raw8<BF16>& r, float* f) {
   }
 }
 
-template <bool BF16>
+// UNIFORM_N: Hq is a multiple of four, so the four rows of a wave share
+// their tree node n.
+template <bool BF16, bool UNIFORM_N>
 __global__ __launch_bounds__(128) void attn_combine(
     TreeDev tree, const void* __restrict__ q, const void* __restrict__ kt,
     const void* __restrict__ vt, int B, int Hq, int Hkv, int G, int chunks, int Rpad, float sl2,
@@ -728,9 +730,12 @@ __global__ __launch_bounds__(128) void attn_combine(
   };
 
   // first batch of everything in flight at once, the ancestor set first
-  // (the tree loads wait for it alone)
-  path[0] = tree.anc[n][0];
-  path[1] = tree.anc[n][1];
+  // (the tree loads wait for it alone).  When the wave's rows share n the
+  // set is a scalar load of the kernel argument, which does not wait
+  // behind the vector loads.
+  const int nw = UNIFORM_N ? __builtin_amdgcn_readfirstlane(n) : n;
+  path[0] = tree.anc[nw][0];
+  path[1] = tree.anc[nw][1];
   load_parts(0);                                   // chunks >= 1 (the plan's)
   Raw8<BF16> qraw;
   load_raw8<BF16>(q, ((int64_t(b) * T + n) * Hq + h) * kHeadDim + 8 * li, qraw);
@@ -809,12 +814,16 @@ hipError_t launch_attn(const TreeDev& tree, int32_t B, int32_t Hq, int32_t Hkv, 
   dim3 cgrid(unsigned((rows + 7) / 8));
   const int Rpad = plan.row_tiles * plan.tile_rows;
   prof_begin(s, TR_KERNEL_ATTN_COMBINE);
-  if (is_bf16)
-    hipLaunchKernelGGL(attn_combine<true>, cgrid, dim3(128), 0, s, tree, q, k_tree, v_tree, B, Hq,
-                       Hkv, plan.G, plan.chunks, Rpad, sl2, part_o, part_ml, out);
-  else
-    hipLaunchKernelGGL(attn_combine<false>, cgrid, dim3(128), 0, s, tree, q, k_tree, v_tree, B, Hq,
-                       Hkv, plan.G, plan.chunks, Rpad, sl2, part_o, part_ml, out);
+#define TR_COMBINE(BF, UN)                                                                  \
+  hipLaunchKernelGGL((attn_combine<BF, UN>), cgrid, dim3(128), 0, s, tree, q, k_tree, v_tree, B, \
+                     Hq, Hkv, plan.G, plan.chunks, Rpad, sl2, part_o, part_ml, out)
+  const bool un = Hq % 4 == 0;
+  if (is_bf16) {
+    if (un) TR_COMBINE(true, true); else TR_COMBINE(true, false);
+  } else {
+    if (un) TR_COMBINE(false, true); else TR_COMBINE(false, false);
+  }
+#undef TR_COMBINE
   prof_end(s);
   return hipGetLastError();
 }
