@@ -530,8 +530,10 @@ tr_status tr_tree_attn_paged(const tr_tree* t, int32_t B, int32_t Hq, const void
            "attention tensors must be 16-byte aligned");
   const int64_t cap = int64_t(kv->max_pages) * kv->page_size;
   const tr::AttnPlan plan = tr::plan_attn(t->dev.T, B, Hq, Hkv, cap, 1);
-  // the longest chunk (at prefix length cap) and the pages it may touch
-  const int64_t cs = ((cap + plan.chunks - 1) / plan.chunks + 63) / 64 * 64;
+  // the longest chunk (at prefix length cap: its share of the 64-key
+  // sub-blocks, the tree's included) and the pages it may touch
+  const int64_t nsub = (cap + 63) / 64 + (plan.tree_keys ? (t->dev.T + 63) / 64 : 0);
+  const int64_t cs = (nsub + plan.chunks - 1) / plan.chunks * 64;
   TR_CHECK(cs / kv->page_size + 2 <= tr::kMaxChunkPages, TR_ERR_UNSUPPORTED,
            "a prefix chunk would span more than %d pages", tr::kMaxChunkPages);
   st = check_ws(ws, ws_bytes, plan.end);

@@ -50,12 +50,18 @@ AttnPlan plan_attn(int32_t T, int32_t B, int32_t Hq, int32_t Hkv, int64_t cap, i
   }
   p.row_tiles = (p.R + p.tile_rows - 1) / p.tile_rows;
   int64_t base = int64_t(B) * Hkv * p.row_tiles;
-  int64_t chunks = (256 + base - 1) / base;        // about one block per CU
-  int64_t by_cap = (cap + kSub - 1) / kSub;
+  // at most one block per CU: a block holds 131+ KB of LDS, so blocks past
+  // the 256th would wait for a whole block to finish
+  int64_t chunks = 256 / base;
+  int64_t by_cap = (cap + kSub - 1) / kSub + (is_bf16 ? (T + kSub - 1) / kSub : 0);
   if (chunks > by_cap) chunks = by_cap;
   if (chunks > 64) chunks = 64;
   if (chunks < 1) chunks = 1;
   p.chunks = int32_t(chunks);
+  // The tree keys go to the prefix pass when there are chunks to spread
+  // them over; with one chunk per (sequence, kv head) they would lengthen
+  // every block, and the combine takes them instead.
+  p.tree_keys = is_bf16 && chunks >= 2 ? 1 : 0;
   const size_t rpad = size_t(p.row_tiles) * p.tile_rows;
   const size_t units = size_t(B) * Hkv * p.chunks * rpad;
   size_t off = kDataOff;
@@ -139,12 +145,17 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint8_t* lds_base) {
   __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
 }
 
-template <int SPW, bool PAGED>
+// TREE: the chunks also take the tree keys (ceil(T / 64) sub-blocks after
+// the prefix's); a template parameter so that without them no branch on
+// the sub-block kind is left in the loop.
+template <int SPW, bool PAGED, bool TREE>
 __global__ __launch_bounds__(512) void attn_prefix_bf16(
     const uint16_t* __restrict__ q, const uint16_t* kc,
-    const uint16_t* vc, int64_t cap, const int32_t* __restrict__ prefix_len, int T,
+    const uint16_t* vc, const uint16_t* kt, const uint16_t* vt, TreeDev tree, int64_t cap,
+    const int32_t* __restrict__ prefix_len,
     int Hq, int Hkv, int G, int R, int chunks, float sl2, uint16_t* __restrict__ part_o,
     float2* __restrict__ part_ml, uint8_t* ws, int B, int row_tiles, PagedArgs pg) {
+  const int T = tree.T;
   constexpr int kRows = kWaves * SPW * 16;        // query rows per tile
   // Blocks are dealt to the 8 XCDs round-robin by block index.  The row
   // tiles of one (sequence, kv head, chunk) group read the same keys and
@@ -156,16 +167,33 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
   if (grp >= B * Hkv * chunks) return;
   const int z = grp / chunks, c = grp - z * chunks;
   const int b = z / Hkv, kvh = z - b * Hkv;
+  // the ancestor set of each of the tile's rows (tree sub-block masks),
+  // read while P is
+  __shared__ uint64_t s_anc[kRows][2];
+  if (TREE && int(threadIdx.x) < kRows) {
+    const int n = min(rt * kRows + int(threadIdx.x), R - 1) / G;
+    const uint64_t a0 = tree.anc[n][0], a1 = tree.anc[n][1];
+    s_anc[threadIdx.x][0] = a0;
+    s_anc[threadIdx.x][1] = a1;
+  }
   const int P = clamp_prefix(prefix_len[b], cap, ws, c == 0 && rt == 0 && kvh == 0 && threadIdx.x == 0);
-  const int cs = chunk_len(P, chunks, kSub);
-  const int k0 = c * cs;
-  const int k1 = min(P, k0 + cs);
+  // The keys of a (sequence, kv head) are the prefix's ntp 64-key
+  // sub-blocks followed by ntt sub-blocks of tree nodes (each row sees the
+  // nodes of its ancestor set, itself included), dealt to the chunks as
+  // evenly as whole sub-blocks allow: chunk c takes global sub-blocks
+  // [s0, s0 + nsub).  The tree keys cost no pass of their own and the
+  // combine merges partials only.
+  const int ntp = (P + kSB - 1) / kSB, ntt = TREE ? (T + kSB - 1) / kSB : 0, ntot = ntp + ntt;
+  const int sbase = ntot / chunks, srem = ntot - sbase * chunks;
+  const int s0 = c * sbase + min(c, srem);
+  const int nsub = sbase + (c < srem ? 1 : 0);
+  const int k0 = s0 * kSB;                          // the chunk's prefix keys: [k0, k1)
+  const int k1 = min(P, (s0 + nsub) * kSB);
   const int Rpad = row_tiles * kRows;
-  if (k0 >= k1) {
+  if (nsub == 0) {
     mark_empty(part_ml, (int64_t(z) * chunks + c) * Rpad + rt * kRows, min(kRows, R - rt * kRows));
     return;
   }
-  const int nsub = (k1 - k0 + kSB - 1) / kSB;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, g = lane >> 4;
   const int row0 = rt * kRows + w * SPW * 16;      // first query row of this wave
   const bool active = row0 < R;                    // waves past the last row only load
@@ -183,7 +211,8 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
   __shared__ int32_t s_pg[PAGED ? kMaxChunkPages : 1];
   const int p0 = PAGED ? (k0 >> pg.ps_log2) : 0;    // first page of the chunk
   if constexpr (PAGED) {
-    const int np = ((k1 - 1) >> pg.ps_log2) - p0 + 1;   // <= kMaxChunkPages by the plan
+    // <= kMaxChunkPages by the plan; none when the chunk holds tree keys only
+    const int np = k1 > k0 ? ((k1 - 1) >> pg.ps_log2) - p0 + 1 : 0;
     for (int i = threadIdx.x; i < np; i += blockDim.x) {
       int32_t id = pg.table[int64_t(b) * pg.max_pages + p0 + i];
       if (id < 0 || int64_t(id) >= pg.num_pages) {     // stays inside the pool
@@ -225,28 +254,48 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
   // of each per thread (wave w, pass q: slots (8 q + w) * 64 + lane).  Rows
   // past the chunk end repeat its last row (finite data the key mask gives
   // probability 0); sub-blocks past the end repeat the last one.
+  // A tree sub-block reads node rows of kt / vt ([B][T][Hkv][d]; nodes past
+  // T repeat the last, masked like the keys past P).
+  const int64_t node_stride = int64_t(Hkv) * kHeadDim;
+  const uint16_t* kt_b = kt + (int64_t(b) * T * Hkv + kvh) * kHeadDim;
+  const uint16_t* vt_b = vt + (int64_t(b) * T * Hkv + kvh) * kHeadDim;
   auto dma = [&](int j, int sl) {
-    const int kb = k0 + min(j, nsub - 1) * kSB;
-    // rows kb .. kb+63 (and the clamp k1-1 >= kb) lie in one page
-    const uint16_t* kp = kc + head_off;
-    const uint16_t* vp = vc + head_off;
-    int row_base = 0;
-    if constexpr (PAGED) {
-      const int64_t pool_off =
-          (int64_t(s_pg[(kb >> pg.ps_log2) - p0]) * Hkv + kvh) * pg.page_size * kHeadDim;
-      kp = kc + pool_off;
-      vp = vc + pool_off;
-      row_base = (kb >> pg.ps_log2) << pg.ps_log2;   // first position of the page
-    }
+    const int gj = s0 + min(j, nsub - 1);
+    if (!TREE || gj < ntp) {
+      const int kb = gj * kSB;
+      // rows kb .. kb+63 (and the clamp P-1 >= kb) lie in one page
+      const uint16_t* kp = kc + head_off;
+      const uint16_t* vp = vc + head_off;
+      int row_base = 0;
+      if constexpr (PAGED) {
+        const int64_t pool_off =
+            (int64_t(s_pg[(kb >> pg.ps_log2) - p0]) * Hkv + kvh) * pg.page_size * kHeadDim;
+        kp = kc + pool_off;
+        vp = vc + pool_off;
+        row_base = (kb >> pg.ps_log2) << pg.ps_log2;   // first position of the page
+      }
 #pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2) {
-      const int base = (q2 * kWaves + w) * 64;       // wave-uniform first slot
-      const int p = base + lane;
-      const int r = p >> 4, pos = p & 15;
-      const int64_t row = min(kb + r, k1 - 1) - row_base;
-      const int ck = pos ^ (r & 15), cv = pos ^ ((r & 7) << 1);
-      lds_dma16(kp + row * kHeadDim + ck * 8, kslot(sl) + base * 16);
-      lds_dma16(vp + row * kHeadDim + cv * 8, vslot(sl) + base * 16);
+      for (int q2 = 0; q2 < 2; ++q2) {
+        const int base = (q2 * kWaves + w) * 64;       // wave-uniform first slot
+        const int p = base + lane;
+        const int r = p >> 4, pos = p & 15;
+        const int64_t row = min(kb + r, P - 1) - row_base;
+        const int ck = pos ^ (r & 15), cv = pos ^ ((r & 7) << 1);
+        lds_dma16(kp + row * kHeadDim + ck * 8, kslot(sl) + base * 16);
+        lds_dma16(vp + row * kHeadDim + cv * 8, vslot(sl) + base * 16);
+      }
+    } else {
+      const int nb = (gj - ntp) * kSB;
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        const int base = (q2 * kWaves + w) * 64;
+        const int p = base + lane;
+        const int r = p >> 4, pos = p & 15;
+        const int64_t node = min(nb + r, T - 1);
+        const int ck = pos ^ (r & 15), cv = pos ^ ((r & 7) << 1);
+        lds_dma16(kt_b + node * node_stride + ck * 8, kslot(sl) + base * 16);
+        lds_dma16(vt_b + node * node_stride + cv * 8, vslot(sl) + base * 16);
+      }
     }
     asm volatile("" ::: "memory");
   };
@@ -257,11 +306,12 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
     for (int s = 0; s < SPW; ++s)
 #pragma unroll
       for (int t = 0; t < 4; ++t) sacc[s][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+    constexpr int KT = 2;                             // key tiles read ahead
 #pragma unroll
-    for (int t0 = 0; t0 < 4; t0 += 2) {
-      bf16x8 ka[2][4];
+    for (int t0 = 0; t0 < 4; t0 += KT) {
+      bf16x8 ka[KT][4];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < KT; ++t)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
           ka[t][ks] = *reinterpret_cast<const bf16x8*>(
@@ -270,7 +320,7 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < KT; ++t)
 #pragma unroll
           for (int s = 0; s < SPW; ++s)
             sacc[s][t0 + t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[t][ks], qb[s][ks], sacc[s][t0 + t], 0, 0, 0);
@@ -301,16 +351,36 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
       }
     }
   };
-  // keys past the chunk end (its ragged last sub-block) get score -inf
-  auto mask = [&](floatx4 (&sacc)[SPW][4], int nk) {
-    if (nk < kSB) {
+  // Global sub-block gj: prefix keys past P (a ragged last sub-block) get
+  // score -inf; in a tree sub-block a row sees only its ancestor set.  (The
+  // comparisons are against per-call values: sixteen loop-invariant key
+  // indices or bit masks hoisted out of the loop would stay live.)
+  auto mask = [&](floatx4 (&sacc)[SPW][4], int gj) {
+    if (!TREE || gj < ntp) {
+      const int nk = P - gj * kSB;
+      if (nk < kSB) {
+        const int nrel = nk - 4 * g;                // keys t*16 + i of the lane's tiles
 #pragma unroll
-      for (int s = 0; s < SPW; ++s)
+        for (int s = 0; s < SPW; ++s)
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+          for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (t * 16 + i >= nrel) sacc[s][t][i] = -INFINITY;
+      }
+    } else {
+      const int hi = gj - ntp > 0 ? 1 : 0;          // nodes 64 .. 127
+#pragma unroll
+      for (int s = 0; s < SPW; ++s) {
+        const uint64_t bits = s_anc[w * SPW * 16 + s * 16 + li][hi] >> (4 * g);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t nib = uint32_t(bits >> (t * 16));   // keys t*16+4g .. +3
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (t * 16 + 4 * g + i >= nk) sacc[s][t][i] = -INFINITY;
+            if (!((nib >> i) & 1u)) sacc[s][t][i] = -INFINITY;
+        }
+      }
     }
   };
   // online softmax per query row (the lane's column), on raw scores:
@@ -336,13 +406,16 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
       bump[s] = mcand > mrow[s] + kLazy;           // always on the first sub-block
       const float mnew = bump[s] ? mcand : mrow[s];
       alpha[s] = bump[s] ? fast_exp2(mrow[s] - mnew) : 1.f;
+      // a row that has seen no visible key yet (a tree sub-block hides all
+      // of them from it) keeps m = -inf: offset 0 gives p = 0, not NaN
+      const float off = mnew == -INFINITY ? 0.f : mnew;
       float psum = 0.f;
       __bf16 ph[4][4];
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pr = fast_exp2(__builtin_fmaf(sacc[s][t][i], sl2, -mnew));
+          const float pr = fast_exp2(__builtin_fmaf(sacc[s][t][i], sl2, -off));
           psum += pr;
           ph[t][i] = (__bf16)pr;
         }
@@ -391,6 +464,9 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
   // each other's matrix and VALU work.)
 #pragma unroll
   for (int j = 0; j < kRingSlots - 1; ++j) dma(j, j);
+  // the ancestor sets in LDS before the first step's barrier
+  __builtin_amdgcn_s_waitcnt(0xC07F);              // lgkmcnt(0)
+  asm volatile("" ::: "memory");
   const int nround = (nsub + kRingSlots - 1) / kRingSlots * kRingSlots;
   for (int j0 = 0; j0 < nround; j0 += kRingSlots) {
 #pragma unroll
@@ -404,7 +480,7 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
       if (active && j < nsub) {
         floatx4 sc[SPW][4];
         qk(kslot(jj), sc);
-        mask(sc, min(kSB, k1 - (k0 + j * kSB)));
+        mask(sc, s0 + j);
         read_v(vslot(jj), 0);
         __builtin_amdgcn_sched_barrier(0);
         softmax(sc);
@@ -638,8 +714,9 @@ __device__ __forceinline__ void unpack8(const Raw8<BF16>& r, float* f) {
 }
 
 // UNIFORM_N: Hq is a multiple of four, so the four rows of a wave share
-// their tree node n.
-template <bool BF16, bool UNIFORM_N>
+// their tree node n.  TREE: the path keys are merged here (the prefix pass
+// did not take them).
+template <bool BF16, bool UNIFORM_N, bool TREE>
 __global__ __launch_bounds__(128) void attn_combine(
     TreeDev tree, const void* __restrict__ q, const void* __restrict__ kt,
     const void* __restrict__ vt, int B, int Hq, int Hkv, int G, int chunks, int Rpad, float sl2,
@@ -733,13 +810,19 @@ __global__ __launch_bounds__(128) void attn_combine(
   // (the tree loads wait for it alone).  When the wave's rows share n the
   // set is a scalar load of the kernel argument, which does not wait
   // behind the vector loads.
+  // When the prefix pass took the tree keys as sub-blocks of its chunks,
+  // its partials already hold them; else (TREE) the path keys are merged
+  // here.
+  constexpr bool kTree = TREE;
   const int nw = UNIFORM_N ? __builtin_amdgcn_readfirstlane(n) : n;
-  path[0] = tree.anc[nw][0];
-  path[1] = tree.anc[nw][1];
+  path[0] = kTree ? tree.anc[nw][0] : 0;
+  path[1] = kTree ? tree.anc[nw][1] : 0;
   load_parts(0);                                   // chunks >= 1 (the plan's)
   Raw8<BF16> qraw;
-  load_raw8<BF16>(q, ((int64_t(b) * T + n) * Hq + h) * kHeadDim + 8 * li, qraw);
-  load_tree();
+  if constexpr (kTree) {
+    load_raw8<BF16>(q, ((int64_t(b) * T + n) * Hq + h) * kHeadDim + 8 * li, qraw);
+    load_tree();
+  }
   // prefix chunk partials, chunks in order
   for (int c0 = 0; c0 < nc; c0 += kBatch) {
     if (c0 > 0) load_parts(c0);
@@ -751,12 +834,14 @@ __global__ __launch_bounds__(128) void attn_combine(
     }
   }
   // tree keys on n's path: n, its parent, ..., the root
-  float qv[8];
-  unpack8<BF16>(qraw, qv);
-  merge_tree(qv);
-  while (more) {
-    load_tree();
+  if constexpr (kTree) {
+    float qv[8];
+    unpack8<BF16>(qraw, qv);
     merge_tree(qv);
+    while (more) {
+      load_tree();
+      merge_tree(qv);
+    }
   }
 
   const float inv = 1.f / l;
@@ -791,15 +876,22 @@ hipError_t launch_attn(const TreeDev& tree, int32_t B, int32_t Hq, int32_t Hkv, 
     const auto* kk = reinterpret_cast<const uint16_t*>(k_cache);
     const auto* vv = reinterpret_cast<const uint16_t*>(v_cache);
     const PagedArgs pa = paged ? *paged : PagedArgs{};
-#define TR_PREFIX(SPWV, PG)                                                                      \
-  hipLaunchKernelGGL((attn_prefix_bf16<SPWV, PG>), grid1, dim3(64 * kWaves), 0, s, qq, kk, vv, cap, \
-                     prefix_len, tree.T, Hq, Hkv, plan.G, plan.R, plan.chunks, sl2,                \
+    const auto* kt = reinterpret_cast<const uint16_t*>(k_tree);
+    const auto* vt = reinterpret_cast<const uint16_t*>(v_tree);
+#define TR_PREFIX(SPWV, PG, TRV)                                                                  \
+  hipLaunchKernelGGL((attn_prefix_bf16<SPWV, PG, TRV>), grid1, dim3(64 * kWaves), 0, s, qq, kk, vv,  \
+                     kt, vt, tree, cap, prefix_len, Hq, Hkv, plan.G, plan.R, plan.chunks, sl2,      \
                      reinterpret_cast<uint16_t*>(part_o), part_ml, ws, B, plan.row_tiles, pa)
+#define TR_PREFIX_T(SPWV, PG)                                                 \
+  do {                                                                        \
+    if (plan.tree_keys) TR_PREFIX(SPWV, PG, true); else TR_PREFIX(SPWV, PG, false); \
+  } while (0)
     if (plan.spw == 2) {
-      if (paged) TR_PREFIX(2, true); else TR_PREFIX(2, false);
+      if (paged) TR_PREFIX_T(2, true); else TR_PREFIX_T(2, false);
     } else {
-      if (paged) TR_PREFIX(1, true); else TR_PREFIX(1, false);
+      if (paged) TR_PREFIX_T(1, true); else TR_PREFIX_T(1, false);
     }
+#undef TR_PREFIX_T
 #undef TR_PREFIX
   } else {
     hipLaunchKernelGGL(attn_prefix_f32, grid, dim3(256), 0, s, reinterpret_cast<const float*>(q),
@@ -814,14 +906,18 @@ hipError_t launch_attn(const TreeDev& tree, int32_t B, int32_t Hq, int32_t Hkv, 
   dim3 cgrid(unsigned((rows + 7) / 8));
   const int Rpad = plan.row_tiles * plan.tile_rows;
   prof_begin(s, TR_KERNEL_ATTN_COMBINE);
-#define TR_COMBINE(BF, UN)                                                                  \
-  hipLaunchKernelGGL((attn_combine<BF, UN>), cgrid, dim3(128), 0, s, tree, q, k_tree, v_tree, B, \
-                     Hq, Hkv, plan.G, plan.chunks, Rpad, sl2, part_o, part_ml, out)
+#define TR_COMBINE(BF, UN, TRV)                                                               \
+  hipLaunchKernelGGL((attn_combine<BF, UN, TRV>), cgrid, dim3(128), 0, s, tree, q, k_tree, v_tree, \
+                     B, Hq, Hkv, plan.G, plan.chunks, Rpad, sl2, part_o, part_ml, out)
   const bool un = Hq % 4 == 0;
   if (is_bf16) {
-    if (un) TR_COMBINE(true, true); else TR_COMBINE(true, false);
+    if (plan.tree_keys) {
+      if (un) TR_COMBINE(true, true, false); else TR_COMBINE(true, false, false);
+    } else {
+      if (un) TR_COMBINE(true, true, true); else TR_COMBINE(true, false, true);
+    }
   } else {
-    if (un) TR_COMBINE(false, true); else TR_COMBINE(false, false);
+    if (un) TR_COMBINE(false, true, true); else TR_COMBINE(false, false, true);
   }
 #undef TR_COMBINE
   prof_end(s);

@@ -115,15 +115,18 @@ def test_host_checks_launch_nothing(tr):
     assert lib.tr_tree_attn(*args(64, 8, 8, tr.TR_BFLOAT16)) == tr.TR_ERR_UNSUPPORTED
     assert lib.tr_tree_attn(*args(128, 6, 4, tr.TR_BFLOAT16)) == tr.TR_ERR_INVALID_ARGUMENT
     assert lib.tr_tree_attn(*args(128, 8, 8, tr.TR_INT32)) == tr.TR_ERR_UNSUPPORTED
-    # tr_workspace_size covers both dtypes.  Here both plans pad the 7 rows
-    # to one 128-row tile and the fp32 plan keeps fp32 partials (the bf16
-    # one bf16), so it needs the more: one byte short fails the fp32 call,
-    # a 256 KiB workspace the bf16 one (8 x 128 partial rows of 264 bytes)
-    need = tr.tr_workspace_size(tree, 1, 0, 0, 8, 8, 128, 64)
-    a = list(args(128, 8, 8, tr.TR_FLOAT32))
+    # tr_workspace_size covers both dtypes.  With a long cache both plans
+    # take 256 / 8 = 32 chunks of one 128-row tile (7 rows) and the fp32
+    # plan keeps fp32 partials (the bf16 one bf16), so it needs the more:
+    # one byte short fails the fp32 call, 256 KiB the bf16 one (32 x 8 x 128
+    # partial rows of 264 bytes)
+    big = lambda d, Hq, Hkv, dt: (h, 1, Hq, Hkv, d, dt, fake, fake, fake, fake, fake, 1 << 16,
+                                  fake, C.c_float(0.1), fake, ws, 1 << 30, None)
+    need = tr.tr_workspace_size(tree, 1, 0, 0, 8, 8, 128, 1 << 16)
+    a = list(big(128, 8, 8, tr.TR_FLOAT32))
     a[-2] = need - 1
     assert lib.tr_tree_attn(*a) == tr.TR_ERR_WORKSPACE_TOO_SMALL
-    a = list(args(128, 8, 8, tr.TR_BFLOAT16))
+    a = list(big(128, 8, 8, tr.TR_BFLOAT16))
     a[-2] = 256 * 1024
     assert lib.tr_tree_attn(*a) == tr.TR_ERR_WORKSPACE_TOO_SMALL
     # paged: bad page size, layer, dtype (checked before anything launches)
