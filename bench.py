@@ -341,10 +341,21 @@ def main():
                   "GB_s": round(b / (ms * 1e-3) / 1e9, 1)} for c, (ms, b) in calls.items()}
     log("per call:", json.dumps(detail))
     # per kernel: the prefix pass reads the cache and the queries, the combine
-    # reads the tree keys/values and writes the output, the step kernel does
-    # the rest of the call
-    kbytes = {"attn_prefix": kv_bytes + qo_bytes / 2, "attn_combine": tkv_bytes + qo_bytes / 2,
-              "topk": step_bytes}
+    # writes the output (and reads the tree keys/values unless the prefix pass
+    # took them), the step kernel does the rest of the call
+    # With two or more key chunks per (sequence, kv head) the bf16 prefix pass
+    # also takes the tree keys (the library's plan: floor(256 / (B * Hkv *
+    # row tiles)) chunks, row tiles of 128 query rows up to 128 rows per kv
+    # head, else of 256), and the combine merges partials only.
+    R = w.T * (w.Hq // w.Hkv)
+    tiles = -(-R // (128 if R <= 128 else 256))
+    tree_in_prefix = w.kv_dtype == torch.bfloat16 and 256 // (w.B * w.Hkv * tiles) >= 2
+    if tree_in_prefix:
+        kbytes = {"attn_prefix": kv_bytes + tkv_bytes + qo_bytes / 2, "attn_combine": qo_bytes / 2,
+                  "topk": step_bytes}
+    else:
+        kbytes = {"attn_prefix": kv_bytes + qo_bytes / 2, "attn_combine": tkv_bytes + qo_bytes / 2,
+                  "topk": step_bytes}
     if Hl:
         kbytes["lmhead"] = lm_bytes + part_bytes
         kbytes["lmhead_merge"] = part_bytes + commit_bytes + m_bytes
