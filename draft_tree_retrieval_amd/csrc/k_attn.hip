@@ -145,6 +145,11 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint8_t* lds_base) {
   __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
 }
 
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+
 // TREE: the chunks also take the tree keys (ceil(T / 64) sub-blocks after
 // the prefix's); a template parameter so that without them no branch on
 // the sub-block kind is left in the loop.
@@ -195,7 +200,18 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
     return;
   }
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, g = lane >> 4;
-  const int row0 = rt * kRows + w * SPW * 16;      // first query row of this wave
+  // Strips of 16 query rows: wave w takes strip w.  With one strip per
+  // wave and 5 or 6 strips in the tile, waves 4..7 instead split strips 4
+  // and 5 by key halves (waves 4 + 2h and 5 + 2h take keys 32h .. 32h+31 of
+  // every sub-block), so each SIMD (wave w runs on SIMD w % 4) carries 1.5
+  // strips rather than two of them carrying 2; the halves merge at the end.
+  const int tile_strips = (min(kRows, R - rt * kRows) + 15) / 16;
+  const bool split = SPW == 1 && (tile_strips == 5 || tile_strips == 6);
+  const bool hw = split && w >= 4;                  // a half-key wave
+  const int kh = hw ? (w >> 1) & 1 : 0;             // its key half
+  const int strip = hw ? 4 + (w & 1) : w;
+  const int srow0 = strip * SPW * 16;               // the wave's first row in the tile
+  const int row0 = rt * kRows + srow0;              // first query row of this wave
   const bool active = row0 < R;                    // waves past the last row only load
 
   __shared__ __attribute__((aligned(16))) uint8_t Ks0[kSubBytes];
@@ -300,22 +316,24 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
     asm volatile("" ::: "memory");
   };
 
-  // S^T = K Q^T for 4 tiles of 16 keys; operands read ahead of the products
-  auto qk = [&](const uint8_t* Ks, floatx4 (&sacc)[SPW][4]) {
+  // S^T = K Q^T for NTL tiles of 16 keys from tile tb on (sacc[s][t] holds
+  // tile tb + t); operands read ahead of the products
+  auto qk = [&](const uint8_t* Ks, floatx4 (&sacc)[SPW][4], auto ntl, int tb) {
+    constexpr int NTL = decltype(ntl)::value;
 #pragma unroll
     for (int s = 0; s < SPW; ++s)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) sacc[s][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < NTL; ++t) sacc[s][t] = floatx4{0.f, 0.f, 0.f, 0.f};
     constexpr int KT = 2;                             // key tiles read ahead
 #pragma unroll
-    for (int t0 = 0; t0 < 4; t0 += KT) {
+    for (int t0 = 0; t0 < NTL; t0 += KT) {
       bf16x8 ka[KT][4];
 #pragma unroll
       for (int t = 0; t < KT; ++t)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
           ka[t][ks] = *reinterpret_cast<const bf16x8*>(
-              Ks + ((t0 + t) * 16 + li) * 256 + (((4 * ks + g) ^ li) << 4));
+              Ks + ((tb + t0 + t) * 16 + li) * 256 + (((4 * ks + g) ^ li) << 4));
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
@@ -328,16 +346,19 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
   };
   // V^T operands (transposed LDS reads), read while the softmax runs:
   // rows kr .. kr+3 with kr = 32 pp + 4 g (+16 for the second half),
-  // lane li at row kr + li / 4, columns 16 dt + 4 (li % 4) .. +3
+  // lane li at row kr + li / 4, columns 16 dt + 4 (li % 4) .. +3.  NPP
+  // 32-key blocks from block pb0 on (va[i][p] holds block pb0 + p).
   constexpr int VG = 2;
   bf16x8 va[VG][2];
-  auto read_v = [&](const uint8_t* Vs, int dt0) {
+  auto read_v = [&](const uint8_t* Vs, int dt0, auto npp, int pb0) {
+    constexpr int NPP = decltype(npp)::value;
 #pragma unroll
     for (int i = 0; i < VG; ++i) {
       const int dt = dt0 + i;
       const int cch = 2 * dt + ((li >> 1) & 1), half = (li & 1) * 8;
 #pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
+      for (int p = 0; p < NPP; ++p) {
+        const int pp = pb0 + p;
         uint32_t u[4];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
@@ -347,7 +368,7 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
           u[2 * hh] = r2[0];
           u[2 * hh + 1] = r2[1];
         }
-        va[i][pp] = __builtin_bit_cast(bf16x8, u32x4{u[0], u[1], u[2], u[3]});
+        va[i][p] = __builtin_bit_cast(bf16x8, u32x4{u[0], u[1], u[2], u[3]});
       }
     }
   };
@@ -355,15 +376,16 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
   // score -inf; in a tree sub-block a row sees only its ancestor set.  (The
   // comparisons are against per-call values: sixteen loop-invariant key
   // indices or bit masks hoisted out of the loop would stay live.)
-  auto mask = [&](floatx4 (&sacc)[SPW][4], int gj) {
+  auto mask = [&](floatx4 (&sacc)[SPW][4], int gj, auto ntl, int tb) {
+    constexpr int NTL = decltype(ntl)::value;
     if (!TREE || gj < ntp) {
       const int nk = P - gj * kSB;
       if (nk < kSB) {
-        const int nrel = nk - 4 * g;                // keys t*16 + i of the lane's tiles
+        const int nrel = nk - 4 * g - 16 * tb;      // keys t*16 + i of the lane's tiles
 #pragma unroll
         for (int s = 0; s < SPW; ++s)
 #pragma unroll
-          for (int t = 0; t < 4; ++t)
+          for (int t = 0; t < NTL; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
               if (t * 16 + i >= nrel) sacc[s][t][i] = -INFINITY;
@@ -372,10 +394,10 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
       const int hi = gj - ntp > 0 ? 1 : 0;          // nodes 64 .. 127
 #pragma unroll
       for (int s = 0; s < SPW; ++s) {
-        const uint64_t bits = s_anc[w * SPW * 16 + s * 16 + li][hi] >> (4 * g);
+        const uint64_t bits = s_anc[srow0 + s * 16 + li][hi] >> (4 * g + 16 * tb);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const uint32_t nib = uint32_t(bits >> (t * 16));   // keys t*16+4g .. +3
+        for (int t = 0; t < NTL; ++t) {
+          const uint32_t nib = uint32_t(bits >> (t * 16));   // keys (tb+t)*16+4g .. +3
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             if (!((nib >> i) & 1u)) sacc[s][t][i] = -INFINITY;
@@ -393,12 +415,13 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
   bf16x8 pb[SPW][2];
   float alpha[SPW];
   bool bump[SPW];
-  auto softmax = [&](const floatx4 (&sacc)[SPW][4]) {
+  auto softmax = [&](const floatx4 (&sacc)[SPW][4], auto ntl) {
+    constexpr int NTL = decltype(ntl)::value;
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
       float mraw = -INFINITY;
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < NTL; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mraw = fmaxf(mraw, sacc[s][t][i]);
       mraw = xmax32(xmax16(mraw));
@@ -412,7 +435,7 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
       float psum = 0.f;
       __bf16 ph[4][4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < NTL; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float pr = fast_exp2(__builtin_fmaf(sacc[s][t][i], sl2, -off));
@@ -423,7 +446,7 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
       lrow[s] = lrow[s] * alpha[s] + psum;
       mrow[s] = mnew;
 #pragma unroll
-      for (int pp = 0; pp < 2; ++pp)
+      for (int pp = 0; pp < NTL / 2; ++pp)
         pb[s][pp] = bf16x8{ph[2 * pp][0], ph[2 * pp][1], ph[2 * pp][2], ph[2 * pp][3],
                            ph[2 * pp + 1][0], ph[2 * pp + 1][1], ph[2 * pp + 1][2], ph[2 * pp + 1][3]};
     }
@@ -439,16 +462,18 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
       }
     }
   };
-  // O^T += V^T P^T over the two 32-key blocks (va holds dt 0, 1 on entry)
-  auto pv = [&](const uint8_t* Vs) {
+  // O^T += V^T P^T over NPP 32-key blocks from pb0 on (va holds dt 0, 1 on
+  // entry)
+  auto pv = [&](const uint8_t* Vs, auto npp, int pb0) {
+    constexpr int NPP = decltype(npp)::value;
 #pragma unroll
     for (int dt0 = 0; dt0 < 8; dt0 += VG) {
       if (dt0 > 0) {
-        read_v(Vs, dt0);
+        read_v(Vs, dt0, npp, pb0);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
-      for (int pp = 0; pp < 2; ++pp)
+      for (int pp = 0; pp < NPP; ++pp)
 #pragma unroll
         for (int i = 0; i < VG; ++i)
 #pragma unroll
@@ -479,13 +504,23 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
       dma(j + kRingSlots - 1, (jj + kRingSlots - 1) % kRingSlots);
       if (active && j < nsub) {
         floatx4 sc[SPW][4];
-        qk(kslot(jj), sc);
-        mask(sc, s0 + j);
-        read_v(vslot(jj), 0);
-        __builtin_amdgcn_sched_barrier(0);
-        softmax(sc);
-        rescale(j == 0);
-        pv(vslot(jj));
+        if (!hw) {                                   // all 64 keys
+          qk(kslot(jj), sc, IntC<4>{}, 0);
+          mask(sc, s0 + j, IntC<4>{}, 0);
+          read_v(vslot(jj), 0, IntC<2>{}, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          softmax(sc, IntC<4>{});
+          rescale(j == 0);
+          pv(vslot(jj), IntC<2>{}, 0);
+        } else {                                     // keys 32 kh .. 32 kh + 31
+          qk(kslot(jj), sc, IntC<2>{}, 2 * kh);
+          mask(sc, s0 + j, IntC<2>{}, 2 * kh);
+          read_v(vslot(jj), 0, IntC<1>{}, kh);
+          __builtin_amdgcn_sched_barrier(0);
+          softmax(sc, IntC<2>{});
+          rescale(j == 0);
+          pv(vslot(jj), IntC<1>{}, kh);
+        }
       }
       // this step's LDS reads are done before the next barrier
       __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0), vm/exp not waited
@@ -493,7 +528,42 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
     }
   }
 
-  if (!active) return;
+  if (split) {
+    // the second key half of strips 4 and 5 hands its (m, l, O) to the
+    // first through LDS; the first merges and stores
+    __shared__ float s_mo[SPW == 1 ? 2 : 1][64][36];
+    __shared__ float2 s_ml[SPW == 1 ? 2 : 1][64];
+    if (hw && kh == 1 && active) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        *reinterpret_cast<floatx4*>(&s_mo[w & 1][lane][4 * dt]) = acc[0][dt];
+      s_ml[w & 1][lane] = make_float2(mrow[0], lrow[0]);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (hw && kh == 0 && active) {
+      const float2 ml1 = s_ml[w & 1][lane];
+      if (ml1.y > 0.f) {
+        if (!(lrow[0] > 0.f)) {
+          mrow[0] = ml1.x;
+          lrow[0] = ml1.y;
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) acc[0][dt] = *reinterpret_cast<const floatx4*>(&s_mo[w & 1][lane][4 * dt]);
+        } else {
+          const float mn = fmaxf(mrow[0], ml1.x);
+          const float a0 = fast_exp2(mrow[0] - mn), a1 = fast_exp2(ml1.x - mn);
+          lrow[0] = lrow[0] * a0 + ml1.y * a1;
+          mrow[0] = mn;
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt)
+            acc[0][dt] = acc[0][dt] * a0 + *reinterpret_cast<const floatx4*>(&s_mo[w & 1][lane][4 * dt]) * a1;
+        }
+      }
+    }
+  }
+  if (!active || (hw && kh == 1)) return;
 #pragma unroll
   for (int s = 0; s < SPW; ++s) {
     const int r = row0 + s * 16 + li;
