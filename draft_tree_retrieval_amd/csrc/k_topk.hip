@@ -146,6 +146,7 @@ __device__ __forceinline__ void seq_tail(TailShared& S, const TreeDev& tree, int
                                          int64_t V, const int32_t* topk_b, int32_t* tok_b,
                                          const TailArgs& tail, uint8_t* ws, const void* logits,
                                          const uint64_t* stat, int32_t segs) {
+  static_assert(NT >= 256, "the tail's roles take four waves");
   void* M_b = reinterpret_cast<MT*>(tail.M) + int64_t(b) * V * k;
   const int wave = threadIdx.x >> 6;
   if constexpr (SAMPLE) {
@@ -183,23 +184,23 @@ __device__ __forceinline__ void seq_tail(TailShared& S, const TreeDev& tree, int
     return;
   }
   tail_load<NT>(S, tree, tok_b, topk_b, k, tail.k_cache ? tail.prefix_len + b : nullptr);
-  // wave 0 verifies while its prefetch is in flight; wave 1 fills the
-  // update map meanwhile unless only the accepted path is recycled (that
-  // map needs the verdict)
+  // wave 0 verifies while waves 2 and 3 fetch the rows the next tree's
+  // first layer may take; wave 1 fills the update map meanwhile unless only
+  // the accepted path is recycled (that map needs the verdict)
   const bool path_only = tail.update_mode == UPDATE_ACCEPTED;
-  PreRows<MT, KM> pre;
   Verdict vd{};
   if (wave == 0) {
-    tail_prefetch<MT, KM>(S, tree, k, M_b, V, pre);
     vd = tail_verify_wave(S, tree, k);
     if (path_only) {
       wave_lds_sync();
       tail_update_claim(S, tree, V, ws, true);
     }
-  } else if (wave == 1 && !path_only) {
-    tail_update_claim(S, tree, V, ws, false);
+  } else if (wave == 1) {
+    if (!path_only) tail_update_claim(S, tree, V, ws, false);
+  } else if (wave < 4) {
+    tail_prefetch<MT, KM>(S, tree, k, M_b, V, int(threadIdx.x) - 128);
   }
-  __syncthreads();                                   // verdict and update map complete
+  __syncthreads();                                   // verdict, update map, prefetched rows
   if (wave != 0) {                                   // outputs and stores
     tail_write_verdict(S, tree, b, tail.accept_len, tail.accept_path, nullptr, tail.emitted, 64);
     tail_commit(S, tree, b, tail, ws, 64);
@@ -207,8 +208,6 @@ __device__ __forceinline__ void seq_tail(TailShared& S, const TreeDev& tree, int
     return;
   }
   const bool fits = tail_commit_fits(S, tail, vd.L);
-  tail_prefetch_store(S, tree, k, V, pre);
-  wave_lds_sync();
   tail_retrieve<MT>(S, tree, vd.bonus, M_b, V, k, tok_b, ws, true, true);
   if (threadIdx.x == 0) {
     tail.root_tok[b] = vd.bonus;

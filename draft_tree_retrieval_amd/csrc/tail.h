@@ -170,47 +170,37 @@ __device__ __forceinline__ void tail_load(TailShared& S, const TreeDev& tree, co
   __syncthreads();
 }
 
-// Loads of M[g(n)] (g = the node's greedy token), by wave 0 for nodes
-// lane and lane + 64: the next tree's root is g(best) for the accepted
-// node best, so its first layer is one of these rows.  The values stay in
-// registers until tail_prefetch_store, so the loads overlap verification.
+// S.pre[n] = M[g(n)] as before the update (g = the node's greedy token),
+// for node n by the calling thread: the next tree's root is g(best) for
+// the accepted node best, so its first layer is one of these rows.  Run by
+// waves that are idle during verification, so the loads overlap it and
+// the rows are in LDS at the barrier that publishes the verdict.
+// Out-of-range ids become -2 (flagged where used), rows of invalid tokens -1.
 // KM >= k bounds the row length (8 or 16).
 template <typename MT, int KM>
-struct PreRows {
-  MT v[2][KM];
-  bool ok[2];                               // the node's greedy token is a valid id
-};
-template <typename MT, int KM>
-__device__ __forceinline__ void tail_prefetch(const TailShared& S, const TreeDev& tree, int32_t k,
-                                              const void* M_b, int64_t V, PreRows<MT, KM>& r) {
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ void tail_prefetch(TailShared& S, const TreeDev& tree, int32_t k,
+                                              const void* M_b, int64_t V, int n) {
+  if (n >= tree.T) return;
+  const int32_t g = S.topk[n * k];
+  const bool ok = g >= 0 && int64_t(g) < V;
+  const int64_t base = ok ? int64_t(g) * k : 0;          // row 0 stands in: no branch
+  MT v[KM];
+  if (KM == 8 && sizeof(MT) == 4 && k == 8) {            // two aligned 16-byte loads
+    const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const MT*>(M_b) + base);
+    const u32x4 x = p[0], y = p[1];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int n = lane + 64 * h;
-    const int32_t g = n < tree.T ? S.topk[n * k] : -1;
-    r.ok[h] = g >= 0 && int64_t(g) < V;
-    const int64_t base = r.ok[h] ? int64_t(g) * k : 0;   // row 0 stands in: no branch
-    // (no later write to r.v before tail_prefetch_store, or the compiler
-    // would wait for the loads there)
-#pragma unroll
-    for (int j = 0; j < KM; ++j)
-      r.v[h][j] = reinterpret_cast<const MT*>(M_b)[base + min(j, k - 1)];
-  }
-}
-// Out-of-range ids become -2 (flagged where used).
-template <typename MT, int KM>
-__device__ __forceinline__ void tail_prefetch_store(TailShared& S, const TreeDev& tree, int32_t k,
-                                                    int64_t V, const PreRows<MT, KM>& r) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int n = lane + 64 * h;
-    if (n >= tree.T) continue;
-#pragma unroll
-    for (int j = 0; j < KM; ++j) {
-      const int64_t v = int64_t(r.v[h][j]);
-      if (j < k) S.pre[n * k + j] = !r.ok[h] ? -1 : (v >= 0 && v < V) ? int32_t(v) : -2;
+    for (int j = 0; j < 4; ++j) {
+      v[j] = MT(x[j]);
+      v[4 + j] = MT(y[j]);
     }
+  } else {
+#pragma unroll
+    for (int j = 0; j < KM; ++j) v[j] = reinterpret_cast<const MT*>(M_b)[base + min(j, k - 1)];
+  }
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    const int64_t x = int64_t(v[j]);
+    if (j < k) S.pre[n * k + j] = !ok ? -1 : (x >= 0 && x < V) ? int32_t(x) : -2;
   }
 }
 
