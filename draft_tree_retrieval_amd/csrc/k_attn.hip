@@ -172,8 +172,10 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
   if (grp >= B * Hkv * chunks) return;
   const int z = grp / chunks, c = grp - z * chunks;
   const int b = z / Hkv, kvh = z - b * Hkv;
-  // the ancestor set of each of the tile's rows (tree sub-block masks),
-  // read while P is
+  // P gates every key load, so its load leaves first; the ancestor set of
+  // each of the tile's rows (tree sub-block masks) is read while P is in
+  // flight
+  const int32_t p_raw = prefix_len[b];
   __shared__ uint64_t s_anc[kRows][2];
   if (TREE && int(threadIdx.x) < kRows) {
     const int n = min(rt * kRows + int(threadIdx.x), R - 1) / G;
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
     s_anc[threadIdx.x][0] = a0;
     s_anc[threadIdx.x][1] = a1;
   }
-  const int P = clamp_prefix(prefix_len[b], cap, ws, c == 0 && rt == 0 && kvh == 0 && threadIdx.x == 0);
+  const int P = clamp_prefix(p_raw, cap, ws, c == 0 && rt == 0 && kvh == 0 && threadIdx.x == 0);
   // The keys of a (sequence, kv head) are the prefix's ntp 64-key
   // sub-blocks followed by ntt sub-blocks of tree nodes (each row sees the
   // nodes of its ancestor set, itself included), dealt to the chunks as
