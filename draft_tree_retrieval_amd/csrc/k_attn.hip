@@ -57,11 +57,13 @@ AttnPlan plan_attn(int32_t T, int32_t B, int32_t Hq, int32_t Hkv, int64_t cap, i
   if (chunks > by_cap) chunks = by_cap;
   if (chunks > 64) chunks = 64;
   if (chunks < 1) chunks = 1;
+  // bf16: at least two chunks, so that the tree keys always go to the
+  // prefix pass (folded into the chunks' sub-blocks); left to the combine,
+  // its per-row loop over them costs more than the extra chunk (32
+  // sequences x 8 kv heads: combine 35 -> 17 us, prefix 234 -> 245 us)
+  if (is_bf16 && chunks < 2) chunks = 2;
   p.chunks = int32_t(chunks);
-  // The tree keys go to the prefix pass when there are chunks to spread
-  // them over; with one chunk per (sequence, kv head) they would lengthen
-  // every block, and the combine takes them instead.
-  p.tree_keys = is_bf16 && chunks >= 2 ? 1 : 0;
+  p.tree_keys = is_bf16 ? 1 : 0;
   const size_t rpad = size_t(p.row_tiles) * p.tile_rows;
   const size_t units = size_t(B) * Hkv * p.chunks * rpad;
   size_t off = kDataOff;
@@ -150,10 +152,9 @@ struct IntC {
   static constexpr int value = N;
 };
 
-// TREE: the chunks also take the tree keys (ceil(T / 64) sub-blocks after
-// the prefix's); a template parameter so that without them no branch on
-// the sub-block kind is left in the loop.
-template <int SPW, bool PAGED, bool TREE>
+// The chunks take the tree keys too: ceil(T / 64) sub-blocks after the
+// prefix's, each row masked to its ancestor set.
+template <int SPW, bool PAGED>
 __global__ __launch_bounds__(512) void attn_prefix_bf16(
     const uint16_t* __restrict__ q, const uint16_t* kc,
     const uint16_t* vc, const uint16_t* kt, const uint16_t* vt, TreeDev tree, int64_t cap,
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
   // flight
   const int32_t p_raw = prefix_len[b];
   __shared__ uint64_t s_anc[kRows][2];
-  if (TREE && int(threadIdx.x) < kRows) {
+  if (int(threadIdx.x) < kRows) {
     const int n = min(rt * kRows + int(threadIdx.x), R - 1) / G;
     const uint64_t a0 = tree.anc[n][0], a1 = tree.anc[n][1];
     s_anc[threadIdx.x][0] = a0;
@@ -190,7 +191,7 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
   // evenly as whole sub-blocks allow: chunk c takes global sub-blocks
   // [s0, s0 + nsub).  The tree keys cost no pass of their own and the
   // combine merges partials only.
-  const int ntp = (P + kSB - 1) / kSB, ntt = TREE ? (T + kSB - 1) / kSB : 0, ntot = ntp + ntt;
+  const int ntp = (P + kSB - 1) / kSB, ntt = (T + kSB - 1) / kSB, ntot = ntp + ntt;
   const int sbase = ntot / chunks, srem = ntot - sbase * chunks;
   const int s0 = c * sbase + min(c, srem);
   const int nsub = sbase + (c < srem ? 1 : 0);
@@ -279,7 +280,7 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
   const uint16_t* vt_b = vt + (int64_t(b) * T * Hkv + kvh) * kHeadDim;
   auto dma = [&](int j, int sl) {
     const int gj = s0 + min(j, nsub - 1);
-    if (!TREE || gj < ntp) {
+    if (gj < ntp) {
       const int kb = gj * kSB;
       // rows kb .. kb+63 (and the clamp P-1 >= kb) lie in one page
       const uint16_t* kp = kc + head_off;
@@ -380,7 +381,7 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
   // indices or bit masks hoisted out of the loop would stay live.)
   auto mask = [&](floatx4 (&sacc)[SPW][4], int gj, auto ntl, int tb) {
     constexpr int NTL = decltype(ntl)::value;
-    if (!TREE || gj < ntp) {
+    if (gj < ntp) {
       const int nk = P - gj * kSB;
       if (nk < kSB) {
         const int nrel = nk - 4 * g - 16 * tb;      // keys t*16 + i of the lane's tiles
@@ -786,8 +787,8 @@ __device__ __forceinline__ void unpack8(const Raw8<BF16>& r, float* f) {
 }
 
 // UNIFORM_N: Hq is a multiple of four, so the four rows of a wave share
-// their tree node n.  TREE: the path keys are merged here (the prefix pass
-// did not take them).
+// their tree node n.  TREE: the path keys are merged here (the fp32 path,
+// whose prefix pass does not take them; the bf16 prefix pass always does).
 template <bool BF16, bool UNIFORM_N, bool TREE>
 __global__ __launch_bounds__(128) void attn_combine(
     TreeDev tree, const void* __restrict__ q, const void* __restrict__ kt,
@@ -882,9 +883,9 @@ __global__ __launch_bounds__(128) void attn_combine(
   // (the tree loads wait for it alone).  When the wave's rows share n the
   // set is a scalar load of the kernel argument, which does not wait
   // behind the vector loads.
-  // When the prefix pass took the tree keys as sub-blocks of its chunks,
-  // its partials already hold them; else (TREE) the path keys are merged
-  // here.
+  // When the prefix pass took the tree keys as sub-blocks of its chunks
+  // (bf16), its partials already hold them; else (TREE) the path keys are
+  // merged here.
   constexpr bool kTree = TREE;
   const int nw = UNIFORM_N ? __builtin_amdgcn_readfirstlane(n) : n;
   path[0] = kTree ? tree.anc[nw][0] : 0;
@@ -950,20 +951,15 @@ hipError_t launch_attn(const TreeDev& tree, int32_t B, int32_t Hq, int32_t Hkv, 
     const PagedArgs pa = paged ? *paged : PagedArgs{};
     const auto* kt = reinterpret_cast<const uint16_t*>(k_tree);
     const auto* vt = reinterpret_cast<const uint16_t*>(v_tree);
-#define TR_PREFIX(SPWV, PG, TRV)                                                                  \
-  hipLaunchKernelGGL((attn_prefix_bf16<SPWV, PG, TRV>), grid1, dim3(64 * kWaves), 0, s, qq, kk, vv,  \
+#define TR_PREFIX(SPWV, PG)                                                                       \
+  hipLaunchKernelGGL((attn_prefix_bf16<SPWV, PG>), grid1, dim3(64 * kWaves), 0, s, qq, kk, vv,  \
                      kt, vt, tree, cap, prefix_len, Hq, Hkv, plan.G, plan.R, plan.chunks, sl2,      \
                      reinterpret_cast<uint16_t*>(part_o), part_ml, ws, B, plan.row_tiles, pa)
-#define TR_PREFIX_T(SPWV, PG)                                                 \
-  do {                                                                        \
-    if (plan.tree_keys) TR_PREFIX(SPWV, PG, true); else TR_PREFIX(SPWV, PG, false); \
-  } while (0)
     if (plan.spw == 2) {
-      if (paged) TR_PREFIX_T(2, true); else TR_PREFIX_T(2, false);
+      if (paged) TR_PREFIX(2, true); else TR_PREFIX(2, false);
     } else {
-      if (paged) TR_PREFIX_T(1, true); else TR_PREFIX_T(1, false);
+      if (paged) TR_PREFIX(1, true); else TR_PREFIX(1, false);
     }
-#undef TR_PREFIX_T
 #undef TR_PREFIX
   } else {
     hipLaunchKernelGGL(attn_prefix_f32, grid, dim3(256), 0, s, reinterpret_cast<const float*>(q),
@@ -982,12 +978,8 @@ hipError_t launch_attn(const TreeDev& tree, int32_t B, int32_t Hq, int32_t Hkv, 
   hipLaunchKernelGGL((attn_combine<BF, UN, TRV>), cgrid, dim3(128), 0, s, tree, q, k_tree, v_tree, \
                      B, Hq, Hkv, plan.G, plan.chunks, Rpad, sl2, part_o, part_ml, out)
   const bool un = Hq % 4 == 0;
-  if (is_bf16) {
-    if (plan.tree_keys) {
-      if (un) TR_COMBINE(true, true, false); else TR_COMBINE(true, false, false);
-    } else {
-      if (un) TR_COMBINE(true, true, true); else TR_COMBINE(true, false, true);
-    }
+  if (is_bf16) {                                    // the prefix pass took the tree keys
+    if (un) TR_COMBINE(true, true, false); else TR_COMBINE(true, false, false);
   } else {
     if (un) TR_COMBINE(false, true, true); else TR_COMBINE(false, false, true);
   }

@@ -72,7 +72,7 @@ struct AttnPlan {
   int32_t tile_rows;  // query rows per block
   int32_t row_tiles;  // ceil(R / tile_rows)
   int32_t chunks;     // prefix chunks per (sequence, kv head)
-  int32_t tree_keys;  // the bf16 prefix pass also takes the tree keys (else the combine)
+  int32_t tree_keys;  // the prefix pass takes the tree keys (bf16; fp32: the combine)
   size_t o_off;       // float [B*Hkv][chunks][row_tiles*tile_rows][128]
   size_t ml_off;      // float2 [B*Hkv][chunks][row_tiles*tile_rows]
   size_t end;
