@@ -240,6 +240,10 @@ ATTN_CASES = [
     (RAND_LEVELS[2], 2, 8, 8, [130, 64], 200),
     (RAND_LEVELS[3], 2, 8, 1, [77, 3000], 3100),
     (RAND_LEVELS[4], 1, 64, 8, [1500], 1600),
+    # 64 x 4 (sequence, kv head) pairs fill 256 blocks with one chunk each:
+    # the bf16 plan still splits the keys in two so the prefix pass takes
+    # the tree keys; ragged prefixes, 0 and the full capacity among them
+    (RAND_LEVELS[2], 64, 8, 4, [0, 300] + [(37 * i) % 301 for i in range(62)], 300),
 ]
 
 
