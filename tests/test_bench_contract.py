@@ -33,9 +33,9 @@ def test_traffic_follows_the_record():
             assert b is None
     # the scale factors come from the plain-copy calibration runs
     cal = rec["copy_calibration"]
-    mib = cal["bytes_per_launch"] / 1024
-    assert cal["fetch_scale"] == pytest.approx(mib / cal["fetch_kib"], rel=1e-3)
-    assert cal["write_scale"] == pytest.approx(mib / cal["write_kib"], rel=1e-3)
+    kib = cal["bytes_per_launch"] / 1024
+    assert cal["fetch_scale"] == pytest.approx(kib / cal["fetch_kib"], rel=1e-3)
+    assert cal["write_scale"] == pytest.approx(kib / cal["write_kib"], rel=1e-3)
 
 
 def test_traffic_is_dropped_when_stale(monkeypatch):
