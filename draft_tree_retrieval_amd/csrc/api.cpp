@@ -663,7 +663,7 @@ tr_status tr_profile_enable(int32_t on) {
       const hipError_t err = hipEventCreate(&e);
       if (err != hipSuccess) {
         for (auto& f : P.ev)
-          if (f) hipEventDestroy(f);
+          if (f) (void)hipEventDestroy(f);   // already failing: keep the first error
         P.ev.clear();
         P.id.clear();
         return hip_status(err, "tr_profile_enable");

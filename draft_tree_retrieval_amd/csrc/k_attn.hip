@@ -25,10 +25,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSub = 64;          // chunk boundaries are multiples of this many keys
-constexpr int kSubB = 128;        // keys per staged sub-block (bf16 kernel)
 constexpr int kWaves = 8;         // waves per bf16 prefix block
-constexpr int kKsStride = 136;    // bf16 per staged K row: 272 bytes, conflict-free b128 reads
-constexpr int kVtStride = 132;    // bf16 per staged V^T row (128 keys + 4): 264 bytes
 constexpr int kSpw = 2;           // 16-row strips per wave (fp32 kernel)
 constexpr int kRowsPerTile = 4 * kSpw * 16;   // fp32 kernel: 4 waves
 constexpr float kLog2e = 1.4426950408889634f;
