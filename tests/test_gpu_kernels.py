@@ -307,7 +307,8 @@ def test_step_ex_accepted_only_duplicates(tr, m_dtype):
         t = otree(levels)
         T, D = t.n_nodes, t.max_depth
         widest = max((max(l) for l in levels), default=0)
-        for V, k, B in ((5, 3, 4), (9, 8, 3), (300, 8, 2)):
+        # k = 16: the 16-wide tail (row prefetch of 16 ids per node)
+        for V, k, B in ((5, 3, 4), (9, 8, 3), (300, 8, 2), (40, 16, 2)):
             if k < widest:
                 continue
             tree = tr.Tree.from_levels(levels, k)
