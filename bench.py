@@ -340,17 +340,12 @@ def main():
     detail = {c: {"avg_us": round(ms * 1e3, 2), "bytes": int(b),
                   "GB_s": round(b / (ms * 1e-3) / 1e9, 1)} for c, (ms, b) in calls.items()}
     log("per call:", json.dumps(detail))
-    # per kernel: the prefix pass reads the cache and the queries, the combine
-    # writes the output (and reads the tree keys/values unless the prefix pass
-    # took them), the step kernel does the rest of the call
-    # With two or more key chunks per (sequence, kv head) the bf16 prefix pass
-    # also takes the tree keys (the library's plan: floor(256 / (B * Hkv *
-    # row tiles)) chunks, row tiles of 128 query rows up to 128 rows per kv
-    # head, else of 256), and the combine merges partials only.
-    R = w.T * (w.Hq // w.Hkv)
-    tiles = -(-R // (128 if R <= 128 else 256))
-    tree_in_prefix = w.kv_dtype == torch.bfloat16 and 256 // (w.B * w.Hkv * tiles) >= 2
-    if tree_in_prefix:
+    # per kernel: in the bf16 path the prefix pass reads the cache, the tree
+    # keys/values and the queries and writes the output of every (sequence,
+    # kv head) that one block finishes; the merge writes the rest, so the
+    # output bytes are booked to the merge (its upper bound).  In the fp32
+    # path the combine reads the tree keys/values and writes the output.
+    if w.kv_dtype == torch.bfloat16:
         kbytes = {"attn_prefix": kv_bytes + tkv_bytes + qo_bytes / 2, "attn_combine": qo_bytes / 2,
                   "topk": step_bytes}
     else:

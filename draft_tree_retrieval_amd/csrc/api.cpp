@@ -132,6 +132,16 @@ tr_status build_tree(int32_t n, const int32_t* parent, const int32_t* rank, int3
   return ok();
 }
 
+// Limits of the bf16 attention pass: every block scans the sequences'
+// prefix lengths in LDS, and the flat sub-block count fits 32 bits.
+tr_status check_bf16_attn(const tr_tree* t, int32_t B, int32_t Hkv, int64_t cap) {
+  TR_CHECK(B <= tr::kMaxAttnSeq, TR_ERR_UNSUPPORTED, "bf16 attention takes B <= %d", tr::kMaxAttnSeq);
+  const int64_t per_seq = (cap + 63) / 64 + (t->dev.T + 63) / 64;
+  TR_CHECK(int64_t(B) * per_seq * Hkv <= INT32_MAX, TR_ERR_UNSUPPORTED,
+           "B x Hkv x 64-key blocks of the cache above 2^31-1");
+  return TR_OK;
+}
+
 size_t topk_need(const tr_tree* t, int32_t B, int64_t V, int32_t k) {
   const int64_t rows = int64_t(B) * t->dev.T;
   const size_t a = tr::plan_topk(rows, V, k, 2).end, b = tr::plan_topk(rows, V, k, 4).end;
@@ -280,6 +290,10 @@ tr_status tr_tree_attn(const tr_tree* t, int32_t B, int32_t Hq, int32_t Hkv, int
   TR_CHECK(aligned16(q) && aligned16(k_tree) && aligned16(v_tree) && aligned16(k_cache) &&
                aligned16(v_cache) && aligned16(out), TR_ERR_INVALID_ARGUMENT,
            "attention tensors must be 16-byte aligned");
+  if (dt == TR_BFLOAT16) {
+    tr_status st = check_bf16_attn(t, B, Hkv, cap);
+    if (st != TR_OK) return st;
+  }
   const tr::AttnPlan plan = tr::plan_attn(t->dev.T, B, Hq, Hkv, cap, dt == TR_BFLOAT16);
   tr_status st = check_ws(ws, ws_bytes, plan.end);
   if (st != TR_OK) return st;
@@ -529,13 +543,9 @@ tr_status tr_tree_attn_paged(const tr_tree* t, int32_t B, int32_t Hq, const void
   TR_CHECK(aligned16(q) && aligned16(out), TR_ERR_INVALID_ARGUMENT,
            "attention tensors must be 16-byte aligned");
   const int64_t cap = int64_t(kv->max_pages) * kv->page_size;
+  st = check_bf16_attn(t, B, Hkv, cap);
+  if (st != TR_OK) return st;
   const tr::AttnPlan plan = tr::plan_attn(t->dev.T, B, Hq, Hkv, cap, 1);
-  // the longest chunk (at prefix length cap: its share of the 64-key
-  // sub-blocks, the tree's included) and the pages it may touch
-  const int64_t nsub = (cap + 63) / 64 + (plan.tree_keys ? (t->dev.T + 63) / 64 : 0);
-  const int64_t cs = (nsub + plan.chunks - 1) / plan.chunks * 64;
-  TR_CHECK(cs / kv->page_size + 2 <= tr::kMaxChunkPages, TR_ERR_UNSUPPORTED,
-           "a prefix chunk would span more than %d pages", tr::kMaxChunkPages);
   st = check_ws(ws, ws_bytes, plan.end);
   if (st != TR_OK) return st;
   const size_t row = size_t(Hkv) * tr::kHeadDim * 2;

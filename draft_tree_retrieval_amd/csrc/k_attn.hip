@@ -2,70 +2,131 @@
 //
 // Every tree node attends to the whole prefix and to its own ancestors
 // (itself included), never to a sibling branch ("Token Recycling" summary,
-// Method, third module; walk-through, workflow step 3).  The prefix part is
-// the same dense product for every query row of a key/value head, so it is
-// computed with matrix cores over prefix chunks (split-K over the prefix,
-// one block per (sequence, kv head, 128-row tile, chunk)); the tree part
-// touches at most depth+1 keys per row and is folded into the combine pass
-// that merges the chunk partials with an online softmax in a fixed order.
+// Method, third module; walk-through, workflow step 3).  Per (sequence, kv
+// head) the query rows are the (node, query head) pairs of that kv head; the
+// keys are the prefix followed by the tree nodes, and a tree key is visible to
+// a row exactly when it lies in the row's ancestor set.
 //
-// Prefix pass layout (bf16).  Per 64-key sub-block the block stages K as
-// [key][d] and V transposed as [d][key] in LDS.  Each wave owns 16-row
-// query strips and computes S^T = K Q^T and O^T = V^T P^T with
-// v_mfma_f32_16x16x32_bf16: in both products the lane's output column is
-// its query row, so softmax statistics, the probabilities fed to the second
-// product and the accumulator rows all stay in the same lane.  The key
-// order inside the second product's K dimension is permuted consistently
-// on both operands so that the probabilities need no cross-lane moves.
+// bf16 path: one pass over the keys with matrix cores, then a merge.
+//  * The keys of every (sequence, kv head) unit are cut into 64-key
+//    sub-blocks, the prefix's first and then ceil(T / 64) sub-blocks of tree
+//    nodes, each row masked to its ancestor set there.  The flat list of all
+//    units' sub-blocks is cut into equal contiguous ranges, one per block, and
+//    the blocks stay resident (one per CU), so every CU does the same amount
+//    of work whatever the prefix lengths.  The cut is computed on the device
+//    from the prefix lengths at every call.
+//  * A unit's query rows are split into equal row tiles of at most sixteen
+//    16-row strips; every tile has its own set of blocks ("lane"), and the
+//    blocks of the lanes that read the same keys at the same time share an XCD
+//    (and its L2).
+//  * A unit that lies wholly inside one block's range is finished there and
+//    written out.  A unit cut by range boundaries leaves one (m, l, O) partial
+//    per block; the merge kernel combines them in block order.
+//  * Inside a block the keys and values stream HBM -> LDS by LDS DMA through a
+//    four-slot ring; each wave holds one or two 16-row query strips and
+//    computes S^T = K Q^T and O^T = V^T P^T with v_mfma_f32_16x16x32_bf16, so
+//    a lane's output column is its query row and the softmax statistics stay
+//    in the lane.  K sits in LDS as [key][d] (16-byte chunks XOR-swizzled by
+//    row); V also as [key][d], read with the transposed LDS read
+//    ds_read_b64_tr_b16, which delivers the V^T operand directly.
+//
+// fp32 path (the small fp32 workload): split-K prefix chunks on
+// v_mfma_f32_16x16x4_f32, the tree keys merged in the combine pass together
+// with the chunk partials.
 #include "dev_common.h"
 
 namespace tr {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kSub = 64;          // chunk boundaries are multiples of this many keys
+constexpr int kSub = 64;          // fp32 chunk boundaries are multiples of this many keys
 constexpr int kWaves = 8;         // waves per bf16 prefix block
 constexpr int kSpw = 2;           // 16-row strips per wave (fp32 kernel)
 constexpr int kRowsPerTile = 4 * kSpw * 16;   // fp32 kernel: 4 waves
+constexpr int kTileStrips = 16;   // bf16: strips per row tile (8 waves x 2)
+constexpr int kBlocks = 256;      // bf16: resident blocks (one per CU)
+constexpr size_t kLdsBytes = 160 * 1024;           // LDS of a CU (gfx950)
+// static LDS of the bf16 prefix kernel (ring 8 x 16 KB, ancestor sets
+// 256 x 16 B, wave sums) and a margin
+constexpr size_t kAttnStaticLds = 8 * 16384 + 256 * 16 + 32 + 1024;
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Cost of one 64-key sub-block for a bf16 row tile of ns strips, in units
+// of ~0.1 strip-times: wave w holds strips w and w + 8 (w + 4 when ns <= 8,
+// waves 4..7 then only stream keys) and runs on SIMD w % 4, so SIMD s
+// carries strips s, s+4, s+8, s+12 (matrix and vector work of a strip: 10);
+// every computing wave reads the whole K and V sub-block from LDS (3 on the
+// CU's LDS port).  The larger of the two bounds the step.
+static int tile_cost(int ns) {
+  const int simd = (ns + 3) / 4;
+  const int waves = ns > 8 ? 8 : (ns < 4 ? ns : 4);
+  return 10 * simd > 3 * waves ? 10 * simd : 3 * waves;
+}
 
 AttnPlan plan_attn(int32_t T, int32_t B, int32_t Hq, int32_t Hkv, int64_t cap, int is_bf16) {
   AttnPlan p{};
   p.G = Hq / Hkv;
   p.R = T * p.G;
   if (is_bf16) {
-    // two strips per wave once a head has more than one 128-row tile: each
-    // key/value operand read from LDS then feeds twice the products and
-    // fewer tiles re-read the same keys; one strip per wave below that, so
-    // that more waves compute (one per SIMD at most otherwise)
-    p.spw = p.R > 128 ? 2 : 1;
-    p.tile_rows = kWaves * p.spw * 16;
-  } else {
-    p.spw = kSpw;
-    p.tile_rows = kRowsPerTile;
+    // row tiles: the fewest that minimise tiles x per-tile step cost, the
+    // time of the pass with every tile's lane running side by side
+    const int S = (p.R + 15) / 16;
+    int best = 0, cost = 0;
+    for (int nt = (S + kTileStrips - 1) / kTileStrips; nt <= S; ++nt) {
+      const int c = nt * tile_cost((S + nt - 1) / nt);
+      if (best == 0 || c < cost) { best = nt; cost = c; }
+      if (nt >= kBlocks) break;
+    }
+    p.nt = best;
+    p.S = S;
+    p.tstrips = (S + best - 1) / best;
+    // blocks per lane: with the lanes' blocks of one index on one XCD, at
+    // most 32 per XCD (its CUs), else a block would wait for a whole one
+    if (best <= 32) {
+      p.xpair = 1;
+      p.gl = 8 * (32 / best);
+    } else {
+      p.xpair = 0;
+      p.gl = kBlocks / best > 0 ? kBlocks / best : 1;
+    }
+    p.grid = best * p.gl;
+    // dynamic LDS: the per-sequence scan (2 B + 1 ints, 16-byte padded) and,
+    // for 5- or 6-strip tiles when it fits, the key halves' hand-over
+    const size_t scan = size_t(2 * B + 1 + 3) / 4 * 16;
+    const size_t hand = size_t(2) * 64 * 36 * 4;
+    p.split = kAttnStaticLds + scan + hand <= kLdsBytes ? 1 : 0;
+    p.lds_dyn = scan + (p.split ? hand : 0);
+    p.tree_keys = 1;
+    const size_t slots = size_t(best) * 2 * p.gl * p.tstrips * 16;   // 2 partials per block
+    size_t off = kDataOff;
+    p.o_off = off;                                   // bf16 [nt][2 gl][tstrips*16][128]
+    off = align256(off + slots * kHeadDim * 2);
+    p.ml_off = off;                                  // float2 [nt][2 gl][tstrips*16]
+    off = align256(off + slots * 8);
+    p.rec_off = off;                                 // int4 [nt][gl] merge records
+    off = align256(off + size_t(best) * p.gl * 16);
+    p.end = off;
+    return p;
   }
+  p.spw = kSpw;
+  p.tile_rows = kRowsPerTile;
   p.row_tiles = (p.R + p.tile_rows - 1) / p.tile_rows;
   int64_t base = int64_t(B) * Hkv * p.row_tiles;
-  // at most one block per CU: a block holds 131+ KB of LDS, so blocks past
-  // the 256th would wait for a whole block to finish
-  int64_t chunks = 256 / base;
-  int64_t by_cap = (cap + kSub - 1) / kSub + (is_bf16 ? (T + kSub - 1) / kSub : 0);
+  // at most one block per CU; the combine merges the chunks and the tree keys
+  int64_t chunks = kBlocks / base;
+  int64_t by_cap = (cap + kSub - 1) / kSub;
   if (chunks > by_cap) chunks = by_cap;
   if (chunks > 64) chunks = 64;
   if (chunks < 1) chunks = 1;
-  // bf16: at least two chunks, so that the tree keys always go to the
-  // prefix pass (folded into the chunks' sub-blocks); left to the combine,
-  // its per-row loop over them costs more than the extra chunk (32
-  // sequences x 8 kv heads: combine 35 -> 17 us, prefix 234 -> 245 us)
-  if (is_bf16 && chunks < 2) chunks = 2;
   p.chunks = int32_t(chunks);
-  p.tree_keys = is_bf16 ? 1 : 0;
+  p.tree_keys = 0;
   const size_t rpad = size_t(p.row_tiles) * p.tile_rows;
   const size_t units = size_t(B) * Hkv * p.chunks * rpad;
   size_t off = kDataOff;
-  p.o_off = off;                                    // bf16 path: bf16 partials
-  off = align256(off + units * kHeadDim * (is_bf16 ? 2 : 4));
+  p.o_off = off;                                    // fp32 partials
+  off = align256(off + units * kHeadDim * 4);
   p.ml_off = off;
   off = align256(off + units * 8);
   p.end = off;
@@ -97,11 +158,11 @@ __device__ __forceinline__ void mark_empty(float2* part_ml, int64_t unit0, int r
 }
 
 // ---------------------------------------------------------------- bf16 prefix
-// 8 waves, two 16-row query strips per wave.  The keys and values of the
-// chunk stream HBM -> LDS through the LDS DMA (global_load_lds_dwordx4) in
-// 64-key sub-blocks (16 KB of K and 16 KB of V) into a ring of four LDS
-// slots, three sub-blocks in flight ahead of the one in use; nothing passes
-// through registers and nothing is restaged.
+// 8 waves.  The keys and values of a block's range stream HBM -> LDS through
+// the LDS DMA (global_load_lds_dwordx4) in 64-key sub-blocks (16 KB of K and
+// 16 KB of V) into a ring of four LDS slots, three sub-blocks in flight ahead
+// of the one in use; nothing passes through registers and nothing is
+// restaged.
 //  * K is stored [key][d] with the 16-byte column chunk c of row r at
 //    position c ^ (r & 15): the S^T = K Q^T operand reads (16 rows, one
 //    chunk) are conflict-free.
@@ -116,18 +177,14 @@ __device__ __forceinline__ void mark_empty(float2* part_ml, int64_t unit0, int r
 // first 16-key tile of the 32-key block for m < 4, of the second for
 // m >= 4) so that the probabilities need no cross-lane moves.
 // Waits are explicit: a workgroup fence would wait for every DMA in flight,
-// so the loop synchronises with a bare barrier after vmcnt(8) (the two
-// younger sub-blocks, 4 DMA loads each per wave, may still fly), and each
-// ring slot is its own LDS array named statically (one array would make
+// so the loop synchronises with a bare barrier after a vmcnt wait that
+// leaves the younger sub-blocks' DMA (4 loads each per wave) in flight, and
+// each ring slot is its own LDS array named statically (one array would make
 // the compiler wait for DMAs into the other slots before every read).
 constexpr int kSB = 64;                   // keys per sub-block
 constexpr float kLazy = 8.f;              // lazy rescaling threshold (log2 units)
 constexpr int kRingSlots = 4;
 constexpr int kSubBytes = kSB * kHeadDim * 2;   // 16 KB
-// PAGED: kc and vc are page pools [num_pages][Hkv][page_size][d] reached
-// through the block table; the chunk's page ids are read into LDS first and
-// each 64-key sub-block (inside one page: page sizes are powers of two of
-// at least 64 keys) looks its page up once.
 // Transposed LDS read (ds_read_b64_tr_b16) of the 8 bytes at LDS address
 // p: four 16-bit values, delivered across each 16-lane group as described
 // above.
@@ -143,76 +200,233 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
 __device__ __forceinline__ void lds_dma16(const void* src, uint8_t* lds_base) {
   __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
 }
+// Sum of two bf16 values added to c (v_dot2c_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float add_bf16x2(bf16x2 p, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(p, bf16x2{(__bf16)1.f, (__bf16)1.f}, c, false);
+}
+// Page id of the sub-block of sequence b that starts at key kb, read
+// through the scalar cache (a wave-uniform address); an id outside the pool
+// reads page 0 and raises the sticky flag.
+__device__ __forceinline__ int32_t page_id(const PagedArgs& pg, int b, int kb, uint8_t* ws) {
+  typedef const __attribute__((address_space(4))) int32_t* cptr;
+  const cptr tb = (cptr)pg.table;
+  int32_t id = tb[int64_t(b) * pg.max_pages + (kb >> pg.ps_log2)];
+  if (id < 0 || int64_t(id) >= pg.num_pages) {
+    set_flag(ws, TR_FLAG_BAD_PAGE);
+    id = 0;
+  }
+  return id;
+}
 
 template <int N>
 struct IntC {
   static constexpr int value = N;
 };
 
-// The chunks take the tree keys too: ceil(T / 64) sub-blocks after the
-// prefix's, each row masked to its ancestor set.
-template <int SPW, bool PAGED>
+// Rows of row tile t: strips [st0, st0 + ns) of the unit's S strips
+// (tiles as equal as whole strips allow, the larger ones first).
+__device__ __forceinline__ void tile_rows_of(int t, int nt, int S, int R, int& row0, int& rows) {
+  const int Sb = S / nt, Sr = S - Sb * nt;
+  const int ns = Sb + (t < Sr ? 1 : 0);
+  row0 = (t * Sb + min(t, Sr)) * 16;
+  rows = min(ns * 16, R - row0);
+}
+// The block of a lane whose range [beg(i), beg(i+1)), beg(i) =
+// floor(i W / nb), holds flat position x.
+__device__ __forceinline__ int block_of(int64_t x, int64_t W, int nb) {
+  return int(((x + 1) * nb - 1) / W);
+}
+
+// Position of the walk over a lane's flat (sequence, kv head, sub-block)
+// order: sub-block s of unit (b, kvh), whose sequence has n sub-blocks and
+// prefix length P.  All fields are wave-uniform.
+struct Walk {
+  int b, kvh, s, n, P;
+};
+
+// Merge record of a block: the unit whose partials it gathers (the block
+// after the one a cut unit starts in): {b * Hkv + kvh, first block, blocks,
+// 1 if the unit starts inside the first block (its partial is that
+// block's second)}; x = -1: none.
+template <bool PAGED>
 __global__ __launch_bounds__(512) void attn_prefix_bf16(
-    const uint16_t* __restrict__ q, const uint16_t* kc,
-    const uint16_t* vc, const uint16_t* kt, const uint16_t* vt, TreeDev tree, int64_t cap,
-    const int32_t* __restrict__ prefix_len,
-    int Hq, int Hkv, int G, int R, int chunks, float sl2, uint16_t* __restrict__ part_o,
-    float2* __restrict__ part_ml, uint8_t* ws, int B, int row_tiles, PagedArgs pg) {
+    const uint16_t* __restrict__ q, const uint16_t* kc, const uint16_t* vc, const uint16_t* kt,
+    const uint16_t* vt, TreeDev tree, int64_t cap, const int32_t* __restrict__ prefix_len, int B,
+    int Hq, int Hkv, int G, int R, int nt, int S, int tstrips, int gl, int xpair, int split,
+    float sl2, uint16_t* __restrict__ part_o, float2* __restrict__ part_ml,
+    int4* __restrict__ rec, uint16_t* __restrict__ out, uint8_t* ws, PagedArgs pg) {
   const int T = tree.T;
-  constexpr int kRows = kWaves * SPW * 16;        // query rows per tile
-  // Blocks are dealt to the 8 XCDs round-robin by block index.  The row
-  // tiles of one (sequence, kv head, chunk) group read the same keys and
-  // values, so they are given consecutive slots on the same XCD and share
-  // its L2: block i runs on XCD i % 8, slot i / 8 of that XCD.
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int rt = slot % row_tiles;
-  const int grp = (slot / row_tiles) * 8 + xcd;    // (sequence, kv head, chunk) group
-  if (grp >= B * Hkv * chunks) return;
-  const int z = grp / chunks, c = grp - z * chunks;
-  const int b = z / Hkv, kvh = z - b * Hkv;
-  // P gates every key load, so its load leaves first; the ancestor set of
-  // each of the tile's rows (tree sub-block masks) is read while P is in
-  // flight
-  const int32_t p_raw = prefix_len[b];
-  __shared__ uint64_t s_anc[kRows][2];
-  if (int(threadIdx.x) < kRows) {
-    const int n = min(rt * kRows + int(threadIdx.x), R - 1) / G;
-    const uint64_t a0 = tree.anc[n][0], a1 = tree.anc[n][1];
-    s_anc[threadIdx.x][0] = a0;
-    s_anc[threadIdx.x][1] = a1;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, g = lane >> 4;
+  // Blocks are dealt to the 8 XCDs round-robin by block index.  With xpair,
+  // block (lane t, index i) gets grid slot 8 (nt (i / 8) + t) + i % 8, so the
+  // lanes' blocks of the same index, which read the same keys at the same
+  // time, run on the same XCD and share its L2 (gl = 8 floor(32 / nt): no
+  // XCD gets more than its 32 CUs); else slot i nt + t.
+  int t, bil;
+  if (xpair) {
+    const int xcd = blockIdx.x & 7, qd = blockIdx.x >> 3;
+    t = qd % nt;
+    bil = (qd / nt) * 8 + xcd;
+  } else {
+    t = blockIdx.x % nt;
+    bil = blockIdx.x / nt;
   }
-  const int P = clamp_prefix(p_raw, cap, ws, c == 0 && rt == 0 && kvh == 0 && threadIdx.x == 0);
-  // The keys of a (sequence, kv head) are the prefix's ntp 64-key
-  // sub-blocks followed by ntt sub-blocks of tree nodes (each row sees the
-  // nodes of its ancestor set, itself included), dealt to the chunks as
-  // evenly as whole sub-blocks allow: chunk c takes global sub-blocks
-  // [s0, s0 + nsub).  The tree keys cost no pass of their own and the
-  // combine merges partials only.
-  const int ntp = (P + kSB - 1) / kSB, ntt = (T + kSB - 1) / kSB, ntot = ntp + ntt;
-  const int sbase = ntot / chunks, srem = ntot - sbase * chunks;
-  const int s0 = c * sbase + min(c, srem);
-  const int nsub = sbase + (c < srem ? 1 : 0);
-  const int k0 = s0 * kSB;                          // the chunk's prefix keys: [k0, k1)
-  const int k1 = min(P, (s0 + nsub) * kSB);
-  const int Rpad = row_tiles * kRows;
-  if (nsub == 0) {
-    mark_empty(part_ml, (int64_t(z) * chunks + c) * Rpad + rt * kRows, min(kRows, R - rt * kRows));
+  if (bil >= gl) return;
+  int trow0, trows;
+  tile_rows_of(t, nt, S, R, trow0, trows);
+  const int ns = (trows + 15) / 16;                 // strips of this tile
+  const int ntt = (T + kSB - 1) / kSB;              // tree sub-blocks of a unit
+
+  // ---- sub-blocks per sequence and their running sum (every block does
+  // the same scan, so the cut needs no other launch)
+  // dynamic LDS: s_cb [B + 1] sub-blocks of sequences < b, s_p [B] clamped
+  // prefix lengths, then (split) the key halves' hand-over buffer
+  extern __shared__ __attribute__((aligned(16))) int32_t s_dyn[];
+  int32_t* s_cb = s_dyn;
+  int32_t* s_p = s_dyn + B + 1;
+  float* s_mo = reinterpret_cast<float*>(s_dyn + ((2 * B + 1 + 3) & ~3));   // [2][64][36]
+  __shared__ int32_t s_wsum[kWaves];
+  __shared__ uint64_t s_anc[kTileStrips * 16][2];   // ancestor sets of the tile's rows
+  if (tid < ns * 16) {
+    const int n = min(trow0 + tid, R - 1) / G;
+    s_anc[tid][0] = tree.anc[n][0];
+    s_anc[tid][1] = tree.anc[n][1];
+  }
+  int carry = 0;
+  bool same = true;                                 // every sequence has as many sub-blocks
+  int n_first;                                      // sub-blocks of sequence 0
+  if (B <= 64) {
+    // one wave scans; one barrier
+    if (w == 0) {
+      int nsub = 0;
+      if (lane < B) {
+        // prefix_len outside [0, cap] is a caller error: clamped (no read
+        // leaves the cache), flagged once
+        const int P = clamp_prefix(prefix_len[lane], cap, ws, blockIdx.x == 0);
+        s_p[lane] = P;
+        nsub = (P + kSB - 1) / kSB + ntt;
+      }
+      const int x = int(wave_incl_scan(uint32_t(nsub)));
+      if (lane < B) s_cb[lane] = x - nsub;
+      if (lane == B - 1) s_cb[B] = x;
+      const int n0 = __builtin_amdgcn_readfirstlane(nsub);
+      s_wsum[0] = __all(lane >= B || nsub == n0) ? 1 : 0;
+    }
+    __syncthreads();
+    carry = s_cb[B];
+    n_first = s_cb[1];
+    same = s_wsum[0] != 0;
+  } else {
+    n_first = (clamp_prefix(prefix_len[0], cap, ws, false) + kSB - 1) / kSB + ntt;
+    for (int base = 0; base < B; base += 64 * kWaves) {
+      const int bb = base + tid;
+      int nsub = 0;
+      if (bb < B) {
+        const int P = clamp_prefix(prefix_len[bb], cap, ws, blockIdx.x == 0);
+        s_p[bb] = P;
+        nsub = (P + kSB - 1) / kSB + ntt;
+      }
+      const int x = int(wave_incl_scan(uint32_t(nsub)));
+      if (lane == 63) s_wsum[w] = x;
+      __syncthreads();
+      int off = carry, tot = 0;
+#pragma unroll
+      for (int i = 0; i < kWaves; ++i) {
+        const int v = s_wsum[i];
+        off += i < w ? v : 0;
+        tot += v;
+      }
+      if (bb < B) s_cb[bb] = off + x - nsub;
+      carry += tot;
+      same = same && (bb >= B || nsub == n_first);
+      __syncthreads();
+    }
+    if (tid == 0) s_cb[B] = carry;
+    same = __syncthreads_and(same);
+  }
+
+  // ---- this block's range of the lane's W sub-blocks (no block empty).
+  // Units of equal length, no more of them than blocks: as many blocks as
+  // fit whole per unit, so no block crosses from one unit into the next.
+  // Merge records are kept per unit when units are no more than blocks
+  // (each cut unit's record at its index, a whole unit's cleared by the
+  // block that finishes it), else per block.
+  const int64_t W = int64_t(carry) * Hkv;
+  const int U = B * Hkv;
+  const bool byunit = U <= gl;
+  const int nb = same && byunit ? U * min(gl / U, n_first) : int(min<int64_t>(gl, W));
+  if (bil >= nb) {
+    if (tid == 0 && !byunit) rec[t * gl + bil] = make_int4(-1, 0, 0, 0);
     return;
   }
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, g = lane >> 4;
-  // Strips of 16 query rows: wave w takes strip w.  With one strip per
-  // wave and 5 or 6 strips in the tile, waves 4..7 instead split strips 4
-  // and 5 by key halves (waves 4 + 2h and 5 + 2h take keys 32h .. 32h+31 of
-  // every sub-block), so each SIMD (wave w runs on SIMD w % 4) carries 1.5
-  // strips rather than two of them carrying 2; the halves merge at the end.
-  const int tile_strips = (min(kRows, R - rt * kRows) + 15) / 16;
-  const bool split = SPW == 1 && (tile_strips == 5 || tile_strips == 6);
+  const int64_t g0 = int64_t(bil) * W / nb, g1 = int64_t(bil + 1) * W / nb;
+  const int nj = int(g1 - g0);
+  // the unit holding g0: the last sequence whose first sub-block is <= g0
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (int64_t(s_cb[mid]) * Hkv <= g0) lo = mid; else hi = mid - 1;
+  }
+  Walk w0;
+  w0.b = __builtin_amdgcn_readfirstlane(lo);
+  w0.n = __builtin_amdgcn_readfirstlane(s_cb[w0.b + 1] - s_cb[w0.b]);
+  w0.P = __builtin_amdgcn_readfirstlane(s_p[w0.b]);
+  {
+    const int64_t rel = g0 - int64_t(s_cb[w0.b]) * Hkv;
+    w0.kvh = __builtin_amdgcn_readfirstlane(int(rel / w0.n));
+    w0.s = __builtin_amdgcn_readfirstlane(int(rel - int64_t(w0.kvh) * w0.n));
+  }
+  if (tid == 0) {
+    // this block merges its first unit when that unit started in the block
+    // before it
+    int4 r = make_int4(-1, 0, 0, 0);
+    const int64_t ustart = g0 - w0.s;
+    if (w0.s > 0 && block_of(ustart, W, nb) == bil - 1) {
+      const int first = bil - 1;
+      const int last = block_of(ustart + w0.n - 1, W, nb);
+      r = make_int4(w0.b * Hkv + w0.kvh, first, last - first + 1,
+                    ustart > int64_t(first) * W / nb ? 1 : 0);
+    }
+    if (!byunit) rec[t * gl + bil] = r;
+    else if (r.x >= 0) rec[t * gl + r.x] = r;
+  }
+  auto advance = [&](Walk& it) {
+    if (++it.s == it.n) {
+      it.s = 0;
+      if (++it.kvh == Hkv) {
+        it.kvh = 0;
+        ++it.b;
+        const int bb = min(it.b, B - 1);
+        it.n = __builtin_amdgcn_readfirstlane(s_cb[bb + 1] - s_cb[bb]);
+        it.P = __builtin_amdgcn_readfirstlane(s_p[bb]);
+      }
+    }
+  };
+
+  // ---- the wave's query strips.  Tiles of more than 8 strips: wave w holds
+  // strips w and w + 8.  5 or 6 strips with the key split: waves 0..3 hold
+  // strip w; waves 4..7 hold strip 4 + (w & 1) over key half (w >> 1) & 1
+  // (keys 32 h .. 32 h + 31 of every sub-block), so each SIMD (wave w runs on
+  // SIMD w % 4) carries 1.5 strips rather than two of them carrying 2; the
+  // halves merge through LDS when a unit ends.  Else wave w < 4 holds
+  // strips w and w + 4 and waves 4..7 only stream keys.
+  split = split && (ns == 5 || ns == 6);            // LDS for the hand-over fits
   const bool hw = split && w >= 4;                  // a half-key wave
   const int kh = hw ? (w >> 1) & 1 : 0;             // its key half
-  const int strip = hw ? 4 + (w & 1) : w;
-  const int srow0 = strip * SPW * 16;               // the wave's first row in the tile
-  const int row0 = rt * kRows + srow0;              // first query row of this wave
-  const bool active = row0 < R;                    // waves past the last row only load
+  int stride, strip0, nstr;
+  if (ns > 8) {
+    stride = 8;
+    strip0 = w;
+    nstr = w + 8 < ns ? 2 : 1;
+  } else if (split) {
+    stride = 0;
+    strip0 = w < 4 ? w : 4 + (w & 1);
+    nstr = strip0 < ns ? 1 : 0;
+  } else {
+    stride = 4;
+    strip0 = w;
+    nstr = w < 4 ? (w + 4 < ns ? 2 : (w < ns ? 1 : 0)) : 0;
+  }
 
   __shared__ __attribute__((aligned(16))) uint8_t Ks0[kSubBytes];
   __shared__ __attribute__((aligned(16))) uint8_t Ks1[kSubBytes];
@@ -224,90 +438,52 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
   __shared__ __attribute__((aligned(16))) uint8_t Vs3[kSubBytes];
   auto kslot = [&](int i) -> uint8_t* { return i == 0 ? Ks0 : i == 1 ? Ks1 : i == 2 ? Ks2 : Ks3; };
   auto vslot = [&](int i) -> uint8_t* { return i == 0 ? Vs0 : i == 1 ? Vs1 : i == 2 ? Vs2 : Vs3; };
-  __shared__ int32_t s_pg[PAGED ? kMaxChunkPages : 1];
-  const int p0 = PAGED ? (k0 >> pg.ps_log2) : 0;    // first page of the chunk
-  if constexpr (PAGED) {
-    // <= kMaxChunkPages by the plan; none when the chunk holds tree keys only
-    const int np = k1 > k0 ? ((k1 - 1) >> pg.ps_log2) - p0 + 1 : 0;
-    for (int i = threadIdx.x; i < np; i += blockDim.x) {
-      int32_t id = pg.table[int64_t(b) * pg.max_pages + p0 + i];
-      if (id < 0 || int64_t(id) >= pg.num_pages) {     // stays inside the pool
-        set_flag(ws, TR_FLAG_BAD_PAGE);
-        id = 0;
-      }
-      s_pg[i] = id;
-    }
-    __syncthreads();
-  }
 
-  // (the query fragments are loaded before the DMAs; the compiler waits for
-  // all loads in flight before entering the loop that uses them, so the
-  // first step starts with the prologue's sub-blocks landed)
-  bf16x8 qb[SPW][4];
-#pragma unroll
-  for (int s = 0; s < SPW; ++s) {
-    const int r = min(row0 + s * 16 + li, R - 1);     // rows past R: any row, never stored
-    const int n = r / G, gq = r - n * G;
-    const uint16_t* qp = q + ((int64_t(b) * T + n) * Hq + kvh * G + gq) * kHeadDim;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      qb[s][ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32 + g * 8);
-  }
-  asm volatile("" ::: "memory");
-
-  floatx4 acc[SPW][8];
-  float mrow[SPW], lrow[SPW];
-#pragma unroll
-  for (int s = 0; s < SPW; ++s) {
-    mrow[s] = -INFINITY;
-    lrow[s] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) acc[s][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  const int64_t head_off = PAGED ? 0 : (int64_t(b) * Hkv + kvh) * cap * kHeadDim;
-  // Sub-block j into ring slot sl: 1024 16-byte slots of K and of V, two
-  // of each per thread (wave w, pass q: slots (8 q + w) * 64 + lane).  Rows
-  // past the chunk end repeat its last row (finite data the key mask gives
-  // probability 0); sub-blocks past the end repeat the last one.
-  // A tree sub-block reads node rows of kt / vt ([B][T][Hkv][d]; nodes past
-  // T repeat the last, masked like the keys past P).
-  const int64_t node_stride = int64_t(Hkv) * kHeadDim;
-  const uint16_t* kt_b = kt + (int64_t(b) * T * Hkv + kvh) * kHeadDim;
-  const uint16_t* vt_b = vt + (int64_t(b) * T * Hkv + kvh) * kHeadDim;
-  auto dma = [&](int j, int sl) {
-    const int gj = s0 + min(j, nsub - 1);
-    if (gj < ntp) {
-      const int kb = gj * kSB;
-      // rows kb .. kb+63 (and the clamp P-1 >= kb) lie in one page
-      const uint16_t* kp = kc + head_off;
-      const uint16_t* vp = vc + head_off;
+  // Sub-block `it` into ring slot sl: 1024 16-byte slots of K and of V, two
+  // of each per thread (wave w, pass q: slots (8 q + w) * 64 + lane).
+  // Prefix rows past P repeat row P-1 (finite data the key mask gives
+  // probability 0); a tree sub-block reads node rows of kt / vt
+  // ([B][T][Hkv][d]; nodes past T repeat the last, masked like keys past P).
+  // PAGED: kc / vc are page pools [num_pages][Hkv][page_size][d]; pid is the
+  // page of the sub-block's rows (a 64-key sub-block never straddles pages).
+  auto dma = [&](const Walk& it, int pid, int sl) {
+    const int ntp = (it.P + kSB - 1) / kSB;
+    if (it.s < ntp) {
+      const int kb = it.s * kSB;
+      const uint16_t* kp;
+      const uint16_t* vp;
       int row_base = 0;
       if constexpr (PAGED) {
-        const int64_t pool_off =
-            (int64_t(s_pg[(kb >> pg.ps_log2) - p0]) * Hkv + kvh) * pg.page_size * kHeadDim;
+        const int64_t pool_off = (int64_t(pid) * Hkv + it.kvh) * pg.page_size * kHeadDim;
         kp = kc + pool_off;
         vp = vc + pool_off;
         row_base = (kb >> pg.ps_log2) << pg.ps_log2;   // first position of the page
+      } else {
+        const int64_t head_off = (int64_t(it.b) * Hkv + it.kvh) * cap * kHeadDim;
+        kp = kc + head_off;
+        vp = vc + head_off;
       }
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2) {
         const int base = (q2 * kWaves + w) * 64;       // wave-uniform first slot
         const int p = base + lane;
         const int r = p >> 4, pos = p & 15;
-        const int64_t row = min(kb + r, P - 1) - row_base;
+        const int64_t row = min(kb + r, it.P - 1) - row_base;
         const int ck = pos ^ (r & 15), cv = pos ^ ((r & 7) << 1);
         lds_dma16(kp + row * kHeadDim + ck * 8, kslot(sl) + base * 16);
         lds_dma16(vp + row * kHeadDim + cv * 8, vslot(sl) + base * 16);
       }
     } else {
-      const int nb = (gj - ntp) * kSB;
+      const int nb0 = (it.s - ntp) * kSB;
+      const int64_t node_stride = int64_t(Hkv) * kHeadDim;
+      const uint16_t* kt_b = kt + (int64_t(it.b) * T * Hkv + it.kvh) * kHeadDim;
+      const uint16_t* vt_b = vt + (int64_t(it.b) * T * Hkv + it.kvh) * kHeadDim;
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2) {
         const int base = (q2 * kWaves + w) * 64;
         const int p = base + lane;
         const int r = p >> 4, pos = p & 15;
-        const int64_t node = min(nb + r, T - 1);
+        const int64_t node = min(nb0 + r, T - 1);
         const int ck = pos ^ (r & 15), cv = pos ^ ((r & 7) << 1);
         lds_dma16(kt_b + node * node_stride + ck * 8, kslot(sl) + base * 16);
         lds_dma16(vt_b + node * node_stride + cv * 8, vslot(sl) + base * 16);
@@ -315,272 +491,468 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
     }
     asm volatile("" ::: "memory");
   };
+  // page of a prefix sub-block (0 for tree sub-blocks and unpaged caches)
+  auto page = [&](const Walk& it) -> int {
+    if constexpr (PAGED) {
+      if (it.b < B && it.s * kSB < it.P) return __builtin_amdgcn_readfirstlane(page_id(pg, it.b, it.s * kSB, ws));
+    }
+    return 0;
+  };
 
-  // S^T = K Q^T for NTL tiles of 16 keys from tile tb on (sacc[s][t] holds
-  // tile tb + t); operands read ahead of the products
-  auto qk = [&](const uint8_t* Ks, floatx4 (&sacc)[SPW][4], auto ntl, int tb) {
-    constexpr int NTL = decltype(ntl)::value;
+  // The compute for waves holding NS strips (1 or 2); waves without a strip
+  // run it with `active` false and only stream keys.
+  auto body = [&](auto ns_c) {
+    constexpr int NS = decltype(ns_c)::value;
+    const bool active = nstr > 0;
+    int srow[NS];                                   // the strips' first rows in the tile
 #pragma unroll
-    for (int s = 0; s < SPW; ++s)
+    for (int s = 0; s < NS; ++s) srow[s] = (strip0 + s * stride) * 16;
+
+    bf16x8 qb[NS][4];
+    floatx4 acc[NS][8];
+    float mrow[NS], lrow[NS], moff[NS], thr[NS];
+    // queries of the unit (b, kvh): rows past the tile read any row, never stored
+    auto qload = [&](int b, int kvh) {
 #pragma unroll
-      for (int t = 0; t < NTL; ++t) sacc[s][t] = floatx4{0.f, 0.f, 0.f, 0.f};
-    constexpr int KT = 2;                             // key tiles read ahead
-#pragma unroll
-    for (int t0 = 0; t0 < NTL; t0 += KT) {
-      bf16x8 ka[KT][4];
-#pragma unroll
-      for (int t = 0; t < KT; ++t)
+      for (int s = 0; s < NS; ++s) {
+        const int r = trow0 + min(srow[s] + li, trows - 1);
+        const int n = r / G, gq = r - n * G;
+        const uint16_t* qp = q + ((int64_t(b) * T + n) * Hq + kvh * G + gq) * kHeadDim;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-          ka[t][ks] = *reinterpret_cast<const bf16x8*>(
-              Ks + ((tb + t0 + t) * 16 + li) * 256 + (((4 * ks + g) ^ li) << 4));
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int t = 0; t < KT; ++t)
-#pragma unroll
-          for (int s = 0; s < SPW; ++s)
-            sacc[s][t0 + t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[t][ks], qb[s][ks], sacc[s][t0 + t], 0, 0, 0);
-    }
-  };
-  // V^T operands (transposed LDS reads), read while the softmax runs:
-  // rows kr .. kr+3 with kr = 32 pp + 4 g (+16 for the second half),
-  // lane li at row kr + li / 4, columns 16 dt + 4 (li % 4) .. +3.  NPP
-  // 32-key blocks from block pb0 on (va[i][p] holds block pb0 + p).
-  constexpr int VG = 2;
-  bf16x8 va[VG][2];
-  auto read_v = [&](const uint8_t* Vs, int dt0, auto npp, int pb0) {
-    constexpr int NPP = decltype(npp)::value;
-#pragma unroll
-    for (int i = 0; i < VG; ++i) {
-      const int dt = dt0 + i;
-      const int cch = 2 * dt + ((li >> 1) & 1), half = (li & 1) * 8;
-#pragma unroll
-      for (int p = 0; p < NPP; ++p) {
-        const int pp = pb0 + p;
-        uint32_t u[4];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int row = 32 * pp + 16 * hh + 4 * g + (li >> 2);
-          const uint8_t* addr = Vs + row * 256 + ((cch ^ ((row & 7) << 1)) << 4) + half;
-          const u32x2 r2 = lds_read_tr16(addr);
-          u[2 * hh] = r2[0];
-          u[2 * hh + 1] = r2[1];
-        }
-        va[i][p] = __builtin_bit_cast(bf16x8, u32x4{u[0], u[1], u[2], u[3]});
+          qb[s][ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32 + g * 8);
       }
-    }
-  };
-  // Global sub-block gj: prefix keys past P (a ragged last sub-block) get
-  // score -inf; in a tree sub-block a row sees only its ancestor set.  (The
-  // comparisons are against per-call values: sixteen loop-invariant key
-  // indices or bit masks hoisted out of the loop would stay live.)
-  auto mask = [&](floatx4 (&sacc)[SPW][4], int gj, auto ntl, int tb) {
-    constexpr int NTL = decltype(ntl)::value;
-    if (gj < ntp) {
-      const int nk = P - gj * kSB;
-      if (nk < kSB) {
-        const int nrel = nk - 4 * g - 16 * tb;      // keys t*16 + i of the lane's tiles
+    };
+    auto reset = [&]() {
 #pragma unroll
-        for (int s = 0; s < SPW; ++s)
+      for (int s = 0; s < NS; ++s) {
+        mrow[s] = -INFINITY;
+        moff[s] = 0.f;
+        thr[s] = -INFINITY;
+        lrow[s] = 0.f;
 #pragma unroll
-          for (int t = 0; t < NTL; ++t)
+        for (int dt = 0; dt < 8; ++dt) acc[s][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+    };
+    // S^T = K Q^T for NTL 16-key tiles from tile tb on (sacc[s][t] holds
+    // tile tb + t); operands read two tiles ahead of the products
+    auto qk = [&](const uint8_t* Ks, floatx4 (&sacc)[NS][4], auto ntl, int tb) {
+      constexpr int NTL = decltype(ntl)::value;
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int t4 = 0; t4 < NTL; ++t4) sacc[s][t4] = floatx4{0.f, 0.f, 0.f, 0.f};
+      constexpr int KT = 2;
+#pragma unroll
+      for (int t0 = 0; t0 < NTL; t0 += KT) {
+        bf16x8 ka[KT][4];
+#pragma unroll
+        for (int tt = 0; tt < KT; ++tt)
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+            ka[tt][ks] = *reinterpret_cast<const bf16x8*>(
+                Ks + ((tb + t0 + tt) * 16 + li) * 256 + (((4 * ks + g) ^ li) << 4));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int tt = 0; tt < KT; ++tt)
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+              sacc[s][t0 + tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tt][ks], qb[s][ks], sacc[s][t0 + tt], 0, 0, 0);
+      }
+    };
+    // V^T operands (transposed LDS reads), read while the softmax runs:
+    // rows kr .. kr+3 with kr = 32 pp + 4 g (+16 for the second half),
+    // lane li at row kr + li / 4, columns 16 dt + 4 (li % 4) .. +3.  NPP
+    // 32-key blocks from block pb0 on (va[i][p] holds block pb0 + p).
+    constexpr int VG = 2;
+    bf16x8 va[VG][2];
+    auto read_v = [&](const uint8_t* Vs, int dt0, auto npp, int pb0) {
+      constexpr int NPP = decltype(npp)::value;
+#pragma unroll
+      for (int i = 0; i < VG; ++i) {
+        const int dt = dt0 + i;
+        const int cch = 2 * dt + ((li >> 1) & 1), half = (li & 1) * 8;
+#pragma unroll
+        for (int pp = 0; pp < NPP; ++pp) {
+          uint32_t u[4];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int row = 32 * (pb0 + pp) + 16 * hh + 4 * g + (li >> 2);
+            const uint8_t* addr = Vs + row * 256 + ((cch ^ ((row & 7) << 1)) << 4) + half;
+            const u32x2 r2 = lds_read_tr16(addr);
+            u[2 * hh] = r2[0];
+            u[2 * hh + 1] = r2[1];
+          }
+          va[i][pp] = __builtin_bit_cast(bf16x8, u32x4{u[0], u[1], u[2], u[3]});
+        }
+      }
+    };
+    // Sub-block s of a unit with prefix length P: prefix keys past P (a
+    // ragged last sub-block) get score -inf; in a tree sub-block a row sees
+    // only its ancestor set.
+    auto mask = [&](floatx4 (&sacc)[NS][4], int s, int P, auto ntl, int tb) {
+      constexpr int NTL = decltype(ntl)::value;
+      const int ntp = (P + kSB - 1) / kSB;
+      if (s < ntp) {
+        const int nk = P - s * kSB;
+        if (nk < kSB) {
+          const int nrel = nk - 4 * g - 16 * tb;      // keys t*16 + i of the lane's tiles
+#pragma unroll
+          for (int ss = 0; ss < NS; ++ss)
+#pragma unroll
+            for (int t4 = 0; t4 < NTL; ++t4)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (t4 * 16 + i >= nrel) sacc[ss][t4][i] = -INFINITY;
+        }
+      } else {
+        const int hi = s - ntp > 0 ? 1 : 0;           // nodes 64 .. 127
+#pragma unroll
+        for (int ss = 0; ss < NS; ++ss) {
+          const uint64_t bits = s_anc[srow[ss] + li][hi] >> (4 * g + 16 * tb);
+#pragma unroll
+          for (int t4 = 0; t4 < NTL; ++t4) {
+            const uint32_t nib = uint32_t(bits >> (t4 * 16));   // keys (tb+t4)*16+4g .. +3
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              if (t * 16 + i >= nrel) sacc[s][t][i] = -INFINITY;
+              if (!((nib >> i) & 1u)) sacc[ss][t4][i] = -INFINITY;
+          }
+        }
       }
-    } else {
-      const int hi = gj - ntp > 0 ? 1 : 0;          // nodes 64 .. 127
+    };
+    // Online softmax per query row (the lane's column) on raw scores:
+    // scale > 0, so max(scale s) = scale max(s) and p = 2^(s sl2 - m).
+    // Lazy rescaling: a row's reference maximum m moves only when a score
+    // passes it by more than kLazy (log2 units), so the probabilities stay
+    // below 2^kLazy and the accumulators are rarely rescaled; the partial
+    // (m, l, O) is consistent for any reference m.  A lane compares its own
+    // maximum with the raw-score threshold (m + kLazy) / sl2; only when some
+    // lane passes it does the wave reduce the maxima over the column's four
+    // lane groups and move m.  l is summed per lane (over its own keys) and
+    // over the lane groups when the unit ends; it adds the probabilities as
+    // rounded to bf16, the weights the second product uses.
+    bf16x8 pb[NS][2];
+    auto softmax = [&](const floatx4 (&sacc)[NS][4], auto ntl, bool fresh) {
+      constexpr int NTL = decltype(ntl)::value;
+      float lm[NS];
+      bool pass = false;
 #pragma unroll
-      for (int s = 0; s < SPW; ++s) {
-        const uint64_t bits = s_anc[srow0 + s * 16 + li][hi] >> (4 * g + 16 * tb);
+      for (int s = 0; s < NS; ++s) {
+        float mt[NTL];
 #pragma unroll
-        for (int t = 0; t < NTL; ++t) {
-          const uint32_t nib = uint32_t(bits >> (t * 16));   // keys (tb+t)*16+4g .. +3
+        for (int t4 = 0; t4 < NTL; ++t4)
+          mt[t4] = fmaxf(fmaxf(sacc[s][t4][0], sacc[s][t4][1]), fmaxf(sacc[s][t4][2], sacc[s][t4][3]));
+        float m = mt[0];
+#pragma unroll
+        for (int t4 = 1; t4 < NTL; ++t4) m = fmaxf(m, mt[t4]);
+        lm[s] = m;
+        pass |= m > thr[s];
+      }
+      if (__any(pass)) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const float mcand = xmax32(xmax16(lm[s])) * sl2;
+          const bool bump = mcand > mrow[s] + kLazy;
+          const float mnew = bump ? mcand : mrow[s];
+          const float alpha = bump ? fast_exp2(mrow[s] - mnew) : 1.f;
+          mrow[s] = mnew;
+          // a row that has seen no visible key yet keeps m = -inf: offset 0
+          // gives p = 2^-inf = 0 for its masked scores, not NaN
+          moff[s] = mnew == -INFINITY ? 0.f : mnew;
+          thr[s] = (mnew + kLazy) / sl2;
+          lrow[s] *= alpha;
+          if (!fresh && __any(bump)) {
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) acc[s][dt] *= alpha;
+          }
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        __bf16 ph[4][4];
+#pragma unroll
+        for (int t4 = 0; t4 < NTL; ++t4)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (!((nib >> i) & 1u)) sacc[s][t][i] = -INFINITY;
+            ph[t4][i] = (__bf16)fast_exp2(__builtin_fmaf(sacc[s][t4][i], sl2, -moff[s]));
+        float ls = lrow[s];
+#pragma unroll
+        for (int t4 = 0; t4 < NTL; ++t4) {
+          ls = add_bf16x2(bf16x2{ph[t4][0], ph[t4][1]}, ls);
+          ls = add_bf16x2(bf16x2{ph[t4][2], ph[t4][3]}, ls);
         }
+        lrow[s] = ls;
+#pragma unroll
+        for (int pp = 0; pp < NTL / 2; ++pp)
+          pb[s][pp] = bf16x8{ph[2 * pp][0], ph[2 * pp][1], ph[2 * pp][2], ph[2 * pp][3],
+                             ph[2 * pp + 1][0], ph[2 * pp + 1][1], ph[2 * pp + 1][2], ph[2 * pp + 1][3]};
       }
-    }
-  };
-  // online softmax per query row (the lane's column), on raw scores:
-  // scale > 0, so max(scale s) = scale max(s) and p = 2^(s sl2 - m).
-  // Lazy rescaling: a row's reference maximum moves only when a score
-  // passes it by more than kLazy (log2 units), so the probabilities stay
-  // below 2^kLazy and the accumulators are rarely rescaled; the partial
-  // (m, l, O) stays consistent for any reference m.  No branch: the
-  // rescale of the accumulators is left to the caller (alpha, bump).
-  bf16x8 pb[SPW][2];
-  float alpha[SPW];
-  bool bump[SPW];
-  auto softmax = [&](const floatx4 (&sacc)[SPW][4], auto ntl) {
-    constexpr int NTL = decltype(ntl)::value;
+    };
+    // O^T += V^T P^T over NPP 32-key blocks from pb0 on (va holds dt 0, 1
+    // on entry)
+    auto pv = [&](const uint8_t* Vs, auto npp, int pb0) {
+      constexpr int NPP = decltype(npp)::value;
 #pragma unroll
-    for (int s = 0; s < SPW; ++s) {
-      float mraw = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < NTL; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mraw = fmaxf(mraw, sacc[s][t][i]);
-      mraw = xmax32(xmax16(mraw));
-      const float mcand = mraw * sl2;
-      bump[s] = mcand > mrow[s] + kLazy;           // always on the first sub-block
-      const float mnew = bump[s] ? mcand : mrow[s];
-      alpha[s] = bump[s] ? fast_exp2(mrow[s] - mnew) : 1.f;
-      // a row that has seen no visible key yet (a tree sub-block hides all
-      // of them from it) keeps m = -inf: offset 0 gives p = 0, not NaN
-      const float off = mnew == -INFINITY ? 0.f : mnew;
-      float psum = 0.f;
-      __bf16 ph[4][4];
-#pragma unroll
-      for (int t = 0; t < NTL; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pr = fast_exp2(__builtin_fmaf(sacc[s][t][i], sl2, -off));
-          psum += pr;
-          ph[t][i] = (__bf16)pr;
+      for (int dt0 = 0; dt0 < 8; dt0 += VG) {
+        if (dt0 > 0) {
+          read_v(Vs, dt0, npp, pb0);
+          __builtin_amdgcn_sched_barrier(0);
         }
-      psum = xsum32(xsum16(psum));
-      lrow[s] = lrow[s] * alpha[s] + psum;
-      mrow[s] = mnew;
 #pragma unroll
-      for (int pp = 0; pp < NTL / 2; ++pp)
-        pb[s][pp] = bf16x8{ph[2 * pp][0], ph[2 * pp][1], ph[2 * pp][2], ph[2 * pp][3],
-                           ph[2 * pp + 1][0], ph[2 * pp + 1][1], ph[2 * pp + 1][2], ph[2 * pp + 1][3]};
-    }
-  };
-  // nothing to rescale on the first sub-block (acc is zero) or when no
-  // lane's reference moved
-  auto rescale = [&](bool first) {
+        for (int pp = 0; pp < NPP; ++pp)
 #pragma unroll
-    for (int s = 0; s < SPW; ++s) {
-      if (!first && __any(bump[s])) {
+          for (int i = 0; i < VG; ++i)
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) acc[s][dt] *= alpha[s];
+            for (int s = 0; s < NS; ++s)
+              acc[s][dt0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[i][pp], pb[s][pp], acc[s][dt0 + i], 0, 0, 0);
       }
-    }
-  };
-  // O^T += V^T P^T over NPP 32-key blocks from pb0 on (va holds dt 0, 1 on
-  // entry)
-  auto pv = [&](const uint8_t* Vs, auto npp, int pb0) {
-    constexpr int NPP = decltype(npp)::value;
-#pragma unroll
-    for (int dt0 = 0; dt0 < 8; dt0 += VG) {
-      if (dt0 > 0) {
-        read_v(Vs, dt0, npp, pb0);
+    };
+    // one sub-block: all 64 keys, or (half-key waves) keys 32 kh .. 32 kh + 31
+    auto compute = [&](const uint8_t* Ks, const uint8_t* Vs, int s, int P, bool fresh) {
+      floatx4 sc[NS][4];
+      if (NS == 2 || !hw) {
+        qk(Ks, sc, IntC<4>{}, 0);
+        mask(sc, s, P, IntC<4>{}, 0);
+        read_v(Vs, 0, IntC<2>{}, 0);
         __builtin_amdgcn_sched_barrier(0);
+        softmax(sc, IntC<4>{}, fresh);
+        pv(Vs, IntC<2>{}, 0);
+      } else {
+        qk(Ks, sc, IntC<2>{}, 2 * kh);
+        mask(sc, s, P, IntC<2>{}, 2 * kh);
+        read_v(Vs, 0, IntC<1>{}, kh);
+        __builtin_amdgcn_sched_barrier(0);
+        softmax(sc, IntC<2>{}, fresh);
+        pv(Vs, IntC<1>{}, kh);
+      }
+    };
+    // The unit (b, kvh) ends in this block: a unit wholly inside the range
+    // is normalised and written out; a cut one leaves its partial in the
+    // block's slot (0 for the block's first unit, 1 for its last).  With the
+    // key split the second key half first hands (m, l, O) of its strip to
+    // the first through LDS (every wave meets the barrier).
+    auto finish = [&](int b, int kvh, bool whole, int slot) {
+      if (NS == 1 && split) {
+        float* mo = s_mo + ((w & 1) * 64 + lane) * 36;
+        if (hw && kh == 1 && active) {
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<floatx4*>(mo + 4 * dt) = acc[0][dt];
+          mo[32] = mrow[0];
+          mo[33] = lrow[0];
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0)
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (hw && kh == 0 && active) {
+          const float m1 = mo[32], l1 = mo[33];
+          if (m1 != -INFINITY) {                    // the second half saw a visible key
+            if (mrow[0] == -INFINITY) {
+              mrow[0] = m1;
+              lrow[0] = l1;
+#pragma unroll
+              for (int dt = 0; dt < 8; ++dt) acc[0][dt] = *reinterpret_cast<const floatx4*>(mo + 4 * dt);
+            } else {
+              const float mn = fmaxf(mrow[0], m1);
+              const float a0 = fast_exp2(mrow[0] - mn), a1 = fast_exp2(m1 - mn);
+              lrow[0] = lrow[0] * a0 + l1 * a1;
+              mrow[0] = mn;
+#pragma unroll
+              for (int dt = 0; dt < 8; ++dt)
+                acc[0][dt] = acc[0][dt] * a0 + *reinterpret_cast<const floatx4*>(mo + 4 * dt) * a1;
+            }
+          }
+        }
       }
 #pragma unroll
-      for (int pp = 0; pp < NPP; ++pp)
+      for (int s = 0; s < NS; ++s) {
+        const float l = xsum32(xsum16(lrow[s]));
+        int rt = srow[s] + li;                        // row in the tile
+        // (opaque, so the output-address arithmetic of this rare path is not
+        // hoisted out of the loop into long-lived registers)
+        asm volatile("" : "+v"(rt));
+        if (!active || (hw && kh == 1) || rt >= trows) continue;
+        if (whole) {
+          const float inv = __builtin_amdgcn_rcpf(l);  // 1 ulp: far below the bf16 rounding
+          const int r = trow0 + rt;
+          const int n = r / G, gq = r - n * G;
+          uint16_t* po = out + ((int64_t(b) * T + n) * Hq + kvh * G + gq) * kHeadDim;
 #pragma unroll
-        for (int i = 0; i < VG; ++i)
+          for (int dt = 0; dt < 8; ++dt) {
+            const u32x2 v = {uint32_t(__builtin_bit_cast(uint16_t, (__bf16)(acc[s][dt][0] * inv))) |
+                                 (uint32_t(__builtin_bit_cast(uint16_t, (__bf16)(acc[s][dt][1] * inv))) << 16),
+                             uint32_t(__builtin_bit_cast(uint16_t, (__bf16)(acc[s][dt][2] * inv))) |
+                                 (uint32_t(__builtin_bit_cast(uint16_t, (__bf16)(acc[s][dt][3] * inv))) << 16)};
+            *reinterpret_cast<u32x2*>(po + dt * 16 + 4 * g) = v;
+          }
+        } else {
+          const int64_t unit = (int64_t(t) * 2 * gl + 2 * bil + slot) * (tstrips * 16) + rt;
+          uint16_t* po = part_o + unit * kHeadDim;   // bf16: the partial sums round once
 #pragma unroll
-          for (int s = 0; s < SPW; ++s)
-            acc[s][dt0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[i][pp], pb[s][pp], acc[s][dt0 + i], 0, 0, 0);
+          for (int dt = 0; dt < 8; ++dt) {
+            const u32x2 v = {uint32_t(__builtin_bit_cast(uint16_t, (__bf16)acc[s][dt][0])) |
+                                 (uint32_t(__builtin_bit_cast(uint16_t, (__bf16)acc[s][dt][1])) << 16),
+                             uint32_t(__builtin_bit_cast(uint16_t, (__bf16)acc[s][dt][2])) |
+                                 (uint32_t(__builtin_bit_cast(uint16_t, (__bf16)acc[s][dt][3])) << 16)};
+            *reinterpret_cast<u32x2*>(po + dt * 16 + 4 * g) = v;
+          }
+          if (g == 0) part_ml[unit] = make_float2(mrow[s], l);
+        }
+      }
+    };
+
+    int pnext = 0;                                  // page of the next sub-block to stream
+    Walk wc = w0;                                   // the sub-block being computed
+    Walk wd = w0;                                   // the next sub-block to stream
+    bool whole = wc.s == 0;                         // the unit starts in this block
+    int slot = 0;                                   // the block's first unit: slot 0
+    bool fresh = true;
+    reset();
+    // three sub-blocks in flight (the pages of the first four looked up at once)
+    {
+      Walk w1 = wd, w2, w3;
+      advance(w1);
+      w2 = w1;
+      advance(w2);
+      w3 = w2;
+      advance(w3);
+      const int p0 = page(wd), p1 = nj > 1 ? page(w1) : 0, p2 = nj > 2 ? page(w2) : 0;
+      const int p3 = nj > 3 ? page(w3) : 0;
+      dma(wd, p0, 0);
+      if (nj > 1) dma(w1, p1, 1);
+      if (nj > 2) dma(w2, p2, 2);
+      wd = w3;
+      pnext = p3;
+    }
+    // the first unit's queries, then everything landed before the loop (an
+    // explicit wait: otherwise the compiler waits for all loads in flight,
+    // the ring's DMA included, before every step's products)
+    if (active) qload(wc.b, wc.kvh);
+    __builtin_amdgcn_s_waitcnt(0x0070);            // vmcnt(0) lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    const int nround = (nj + kRingSlots - 1) / kRingSlots * kRingSlots;
+    for (int j0 = 0; j0 < nround; j0 += kRingSlots) {
+#pragma unroll
+      for (int jj = 0; jj < kRingSlots; ++jj) {
+        const int j = j0 + jj;
+        // sub-block j landed: only the younger ones' loads may still fly
+        if (j + 2 < nj) {
+          __builtin_amdgcn_s_waitcnt(0x0F78);      // vmcnt(8)
+        } else if (j + 1 < nj) {
+          __builtin_amdgcn_s_waitcnt(0x0F74);      // vmcnt(4)
+        } else {
+          __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0)
+        }
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (j + 3 < nj) {
+          const int pid = pnext;
+          dma(wd, pid, (jj + 3) % kRingSlots);
+          advance(wd);
+          if (j + 4 < nj) pnext = page(wd);
+        }
+        if (j < nj) {
+          if (active) compute(kslot(jj), vslot(jj), wc.s, wc.P, fresh);
+          fresh = false;
+          if (wc.s == wc.n - 1 || j == nj - 1) {
+            const bool unit_whole = whole && wc.s == wc.n - 1;
+            finish(wc.b, wc.kvh, unit_whole, slot);
+            if (byunit && unit_whole && tid == 0) rec[t * gl + wc.b * Hkv + wc.kvh] = make_int4(-1, 0, 0, 0);
+            slot = 1;
+            if (j < nj - 1) {                       // the next unit starts here
+              advance(wc);
+              if (active) qload(wc.b, wc.kvh);
+              reset();
+              whole = true;
+              fresh = true;
+            }
+            // the stores (and the next unit's queries) complete here, on
+            // this rare path: left pending, the compiler would make every
+            // later step wait for all loads in flight, the ring's DMA
+            // included, before reusing the stores' source registers or
+            // reading the queries
+            __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0)
+            asm volatile("" ::: "memory");
+          } else {
+            advance(wc);
+          }
+        }
+        // this step's LDS reads (and page lookups) are done before the next barrier
+        __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0), vm/exp not waited
+        asm volatile("" ::: "memory");
+      }
     }
   };
+  if (nstr == 2) body(IntC<2>{});
+  else body(IntC<1>{});
+}
 
-  // three sub-blocks in flight, then per sub-block: wait, barrier, refill
-  // the slot freed by the previous sub-block, compute.  (A software
-  // pipeline that forms the next sub-block's scores during this one's
-  // softmax measured slower here: the two waves of a SIMD already overlap
-  // each other's matrix and VALU work.)
+// ---------------------------------------------------------------- bf16 merge
+// One block of 256 threads per (lane, merge record, 16 rows of the tile):
+// the record (one per unit when units are no more than blocks, else one
+// per block boundary) names a unit cut by block ranges and the blocks
+// holding its partials; 16 lanes per output row (8 head-dimension
+// values each) merge them in block order with an online softmax (run-to-run
+// bit identical) and write the normalised row.
+__global__ __launch_bounds__(256) void attn_merge_bf16(
+    const int4* __restrict__ rec, int nt, int gl, int B_Hkv, int S, int tstrips, int R, int T, int G,
+    int Hq, int Hkv, const uint16_t* __restrict__ part_o, const float2* __restrict__ part_ml,
+    uint16_t* __restrict__ out) {
+  constexpr int kBatch = 8;
+  const int rg = blockIdx.x % tstrips;             // 16-row group of the tile
+  const int li_rec = blockIdx.x / tstrips;         // t * records per lane + record
+  const int nrec = B_Hkv <= gl ? B_Hkv : gl;
+  const int t = li_rec / nrec;
+  const int4 rc = rec[t * gl + li_rec % nrec];
+  if (rc.x < 0) return;
+  int trow0, trows;
+  tile_rows_of(t, nt, S, R, trow0, trows);
+  const int rt = rg * 16 + (threadIdx.x >> 4);     // row in the tile
+  if (rt >= trows) return;                          // whole 16-lane groups leave together
+  const int li = threadIdx.x & 15;                 // d = 8 li .. 8 li + 7
+  const int b = rc.x / Hkv, kvh = rc.x - b * Hkv;
+  const int first = rc.y, nc = rc.z, s0 = rc.w;
+  const int64_t rows_t = int64_t(tstrips) * 16;
+  float m = -INFINITY, l = 0.f, o[8];
 #pragma unroll
-  for (int j = 0; j < kRingSlots - 1; ++j) dma(j, j);
-  // the ancestor sets in LDS before the first step's barrier
-  __builtin_amdgcn_s_waitcnt(0xC07F);              // lgkmcnt(0)
-  asm volatile("" ::: "memory");
-  const int nround = (nsub + kRingSlots - 1) / kRingSlots * kRingSlots;
-  for (int j0 = 0; j0 < nround; j0 += kRingSlots) {
+  for (int e = 0; e < 8; ++e) o[e] = 0.f;
+  float2 ml[kBatch];
+  u32x4 po[kBatch];
+  for (int c0 = 0; c0 < nc; c0 += kBatch) {
 #pragma unroll
-    for (int jj = 0; jj < kRingSlots; ++jj) {
-      const int j = j0 + jj;
-      __builtin_amdgcn_s_waitcnt(0x0F78);          // vmcnt(8), lgkm/exp not waited
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      dma(j + kRingSlots - 1, (jj + kRingSlots - 1) % kRingSlots);
-      if (active && j < nsub) {
-        floatx4 sc[SPW][4];
-        if (!hw) {                                   // all 64 keys
-          qk(kslot(jj), sc, IntC<4>{}, 0);
-          mask(sc, s0 + j, IntC<4>{}, 0);
-          read_v(vslot(jj), 0, IntC<2>{}, 0);
-          __builtin_amdgcn_sched_barrier(0);
-          softmax(sc, IntC<4>{});
-          rescale(j == 0);
-          pv(vslot(jj), IntC<2>{}, 0);
-        } else {                                     // keys 32 kh .. 32 kh + 31
-          qk(kslot(jj), sc, IntC<2>{}, 2 * kh);
-          mask(sc, s0 + j, IntC<2>{}, 2 * kh);
-          read_v(vslot(jj), 0, IntC<1>{}, kh);
-          __builtin_amdgcn_sched_barrier(0);
-          softmax(sc, IntC<2>{});
-          rescale(j == 0);
-          pv(vslot(jj), IntC<1>{}, kh);
-        }
+    for (int i = 0; i < kBatch; ++i) {
+      const int c = min(c0 + i, nc - 1);
+      const int slot = 2 * (first + c) + (c == 0 ? s0 : 0);
+      const int64_t unit = (int64_t(t) * 2 * gl + slot) * rows_t + rt;
+      ml[i] = part_ml[unit];
+      po[i] = *reinterpret_cast<const u32x4*>(part_o + unit * kHeadDim + 8 * li);
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (c0 + i >= nc || !(ml[i].y > 0.f)) continue;   // past the list, or no visible key
+      const float mn = fmaxf(m, ml[i].x);
+      const float a = fast_exp2(m - mn), e = fast_exp2(ml[i].x - mn);
+      l = l * a + ml[i].y * e;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        o[2 * j] = o[2 * j] * a + __uint_as_float(po[i][j] << 16) * e;
+        o[2 * j + 1] = o[2 * j + 1] * a + __uint_as_float(po[i][j] & 0xFFFF0000u) * e;
       }
-      // this step's LDS reads are done before the next barrier
-      __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0), vm/exp not waited
-      asm volatile("" ::: "memory");
+      m = mn;
     }
   }
-
-  if (split) {
-    // the second key half of strips 4 and 5 hands its (m, l, O) to the
-    // first through LDS; the first merges and stores
-    __shared__ float s_mo[SPW == 1 ? 2 : 1][64][36];
-    __shared__ float2 s_ml[SPW == 1 ? 2 : 1][64];
-    if (hw && kh == 1 && active) {
+  const float inv = 1.f / l;
+  const int r = trow0 + rt;
+  const int n = r / G, gq = r - n * G;
+  const int64_t oe = ((int64_t(b) * T + n) * Hq + kvh * G + gq) * kHeadDim + 8 * li;
+  u32x4 u;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-        *reinterpret_cast<floatx4*>(&s_mo[w & 1][lane][4 * dt]) = acc[0][dt];
-      s_ml[w & 1][lane] = make_float2(mrow[0], lrow[0]);
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0)
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (hw && kh == 0 && active) {
-      const float2 ml1 = s_ml[w & 1][lane];
-      if (ml1.y > 0.f) {
-        if (!(lrow[0] > 0.f)) {
-          mrow[0] = ml1.x;
-          lrow[0] = ml1.y;
-#pragma unroll
-          for (int dt = 0; dt < 8; ++dt) acc[0][dt] = *reinterpret_cast<const floatx4*>(&s_mo[w & 1][lane][4 * dt]);
-        } else {
-          const float mn = fmaxf(mrow[0], ml1.x);
-          const float a0 = fast_exp2(mrow[0] - mn), a1 = fast_exp2(ml1.x - mn);
-          lrow[0] = lrow[0] * a0 + ml1.y * a1;
-          mrow[0] = mn;
-#pragma unroll
-          for (int dt = 0; dt < 8; ++dt)
-            acc[0][dt] = acc[0][dt] * a0 + *reinterpret_cast<const floatx4*>(&s_mo[w & 1][lane][4 * dt]) * a1;
-        }
-      }
-    }
-  }
-  if (!active || (hw && kh == 1)) return;
-#pragma unroll
-  for (int s = 0; s < SPW; ++s) {
-    const int r = row0 + s * 16 + li;
-    if (r < R) {
-      const int64_t unit = (int64_t(z) * chunks + c) * Rpad + r;
-      uint16_t* po = part_o + unit * kHeadDim;     // bf16: the partial sums round once
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const u32x2 v = {uint32_t(__builtin_bit_cast(uint16_t, (__bf16)acc[s][dt][0])) |
-                             (uint32_t(__builtin_bit_cast(uint16_t, (__bf16)acc[s][dt][1])) << 16),
-                         uint32_t(__builtin_bit_cast(uint16_t, (__bf16)acc[s][dt][2])) |
-                             (uint32_t(__builtin_bit_cast(uint16_t, (__bf16)acc[s][dt][3])) << 16)};
-        *reinterpret_cast<u32x2*>(po + dt * 16 + 4 * g) = v;
-      }
-      if (g == 0) part_ml[unit] = make_float2(mrow[s], lrow[s]);
-    }
-  }
+  for (int e = 0; e < 4; ++e)
+    u[e] = uint32_t(f32_to_bf16(o[2 * e] * inv)) | (uint32_t(f32_to_bf16(o[2 * e + 1] * inv)) << 16);
+  *reinterpret_cast<u32x4*>(out + oe) = u;
 }
 
 // ---------------------------------------------------------------- fp32 prefix
@@ -937,33 +1309,42 @@ hipError_t launch_attn(const TreeDev& tree, int32_t B, int32_t Hq, int32_t Hkv, 
   void* part_o = ws + plan.o_off;
   float2* part_ml = reinterpret_cast<float2*>(ws + plan.ml_off);
   const float sl2 = scale * kLog2e;
-  dim3 grid(plan.chunks, plan.row_tiles, B * Hkv);
-  const int64_t groups = int64_t(B) * Hkv * plan.chunks;
-  dim3 grid1(unsigned((groups + 7) / 8 * 8 * plan.row_tiles));
-  prof_begin(s, TR_KERNEL_ATTN_PREFIX);
   if (is_bf16) {
     const auto* qq = reinterpret_cast<const uint16_t*>(q);
     const auto* kk = reinterpret_cast<const uint16_t*>(k_cache);
     const auto* vv = reinterpret_cast<const uint16_t*>(v_cache);
-    const PagedArgs pa = paged ? *paged : PagedArgs{};
     const auto* kt = reinterpret_cast<const uint16_t*>(k_tree);
     const auto* vt = reinterpret_cast<const uint16_t*>(v_tree);
-#define TR_PREFIX(SPWV, PG)                                                                       \
-  hipLaunchKernelGGL((attn_prefix_bf16<SPWV, PG>), grid1, dim3(64 * kWaves), 0, s, qq, kk, vv,  \
-                     kt, vt, tree, cap, prefix_len, Hq, Hkv, plan.G, plan.R, plan.chunks, sl2,      \
-                     reinterpret_cast<uint16_t*>(part_o), part_ml, ws, B, plan.row_tiles, pa)
-    if (plan.spw == 2) {
-      if (paged) TR_PREFIX(2, true); else TR_PREFIX(2, false);
-    } else {
-      if (paged) TR_PREFIX(1, true); else TR_PREFIX(1, false);
-    }
+    auto* po = reinterpret_cast<uint16_t*>(part_o);
+    auto* rec = reinterpret_cast<int4*>(ws + plan.rec_off);
+    auto* o = reinterpret_cast<uint16_t*>(out);
+    const PagedArgs pa = paged ? *paged : PagedArgs{};
+    prof_begin(s, TR_KERNEL_ATTN_PREFIX);
+#define TR_PREFIX(PG)                                                                             \
+  hipLaunchKernelGGL((attn_prefix_bf16<PG>), dim3(plan.grid), dim3(64 * kWaves), plan.lds_dyn, s, qq, \
+                     kk, vv, kt, vt, tree, cap, prefix_len, B, Hq, Hkv, plan.G, plan.R, plan.nt,     \
+                     plan.S, plan.tstrips, plan.gl, plan.xpair, plan.split, sl2, po, part_ml, rec, o, \
+                     ws, pa)
+    if (paged) TR_PREFIX(true); else TR_PREFIX(false);
 #undef TR_PREFIX
-  } else {
-    hipLaunchKernelGGL(attn_prefix_f32, grid, dim3(256), 0, s, reinterpret_cast<const float*>(q),
-                       reinterpret_cast<const float*>(k_cache), reinterpret_cast<const float*>(v_cache),
-                       cap, prefix_len, tree.T, Hq, Hkv, plan.G, plan.R, plan.chunks, sl2,
-                       reinterpret_cast<float*>(part_o), part_ml, ws);
+    prof_end(s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    prof_begin(s, TR_KERNEL_ATTN_COMBINE);
+    const int64_t U = int64_t(B) * Hkv;
+    const int64_t recs = U <= plan.gl ? U : plan.gl;    // records per lane (per unit or per block)
+    hipLaunchKernelGGL(attn_merge_bf16, dim3(unsigned(plan.nt * recs * plan.tstrips)), dim3(256), 0,
+                       s, rec, plan.nt, plan.gl, int(U), plan.S, plan.tstrips, plan.R, tree.T, plan.G,
+                       Hq, Hkv, po, part_ml, o);
+    prof_end(s);
+    return hipGetLastError();
   }
+  dim3 grid(plan.chunks, plan.row_tiles, B * Hkv);
+  prof_begin(s, TR_KERNEL_ATTN_PREFIX);
+  hipLaunchKernelGGL(attn_prefix_f32, grid, dim3(256), 0, s, reinterpret_cast<const float*>(q),
+                     reinterpret_cast<const float*>(k_cache), reinterpret_cast<const float*>(v_cache),
+                     cap, prefix_len, tree.T, Hq, Hkv, plan.G, plan.R, plan.chunks, sl2,
+                     reinterpret_cast<float*>(part_o), part_ml, ws);
   prof_end(s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -971,15 +1352,10 @@ hipError_t launch_attn(const TreeDev& tree, int32_t B, int32_t Hq, int32_t Hkv, 
   dim3 cgrid(unsigned((rows + 7) / 8));
   const int Rpad = plan.row_tiles * plan.tile_rows;
   prof_begin(s, TR_KERNEL_ATTN_COMBINE);
-#define TR_COMBINE(BF, UN, TRV)                                                               \
-  hipLaunchKernelGGL((attn_combine<BF, UN, TRV>), cgrid, dim3(128), 0, s, tree, q, k_tree, v_tree, \
+#define TR_COMBINE(UN)                                                                        \
+  hipLaunchKernelGGL((attn_combine<false, UN, true>), cgrid, dim3(128), 0, s, tree, q, k_tree, v_tree, \
                      B, Hq, Hkv, plan.G, plan.chunks, Rpad, sl2, part_o, part_ml, out)
-  const bool un = Hq % 4 == 0;
-  if (is_bf16) {                                    // the prefix pass took the tree keys
-    if (un) TR_COMBINE(true, true, false); else TR_COMBINE(true, false, false);
-  } else {
-    if (un) TR_COMBINE(false, true, true); else TR_COMBINE(false, false, true);
-  }
+  if (Hq % 4 == 0) TR_COMBINE(true); else TR_COMBINE(false);
 #undef TR_COMBINE
   prof_end(s);
   return hipGetLastError();

@@ -65,25 +65,44 @@ struct TopkPlan {
 TopkPlan plan_topk(int64_t rows, int64_t V, int32_t k, int32_t esz);
 
 // Attention launch shape.
+//  bf16: a resident grid (one block per CU) over the flat (sequence, kv
+//  head, 64-key sub-block) order, cut into equal ranges on the device; the
+//  query rows of a (sequence, kv head) split into nt row tiles of at most
+//  16 strips of 16 rows, each tile with its own gl blocks ("lane").
+//  fp32: split-K chunks per (sequence, kv head, row tile) and a combine.
 struct AttnPlan {
   int32_t G;          // query heads per key/value head
   int32_t R;          // query rows per (sequence, kv head) = T * G
+  int32_t tree_keys;  // the prefix pass takes the tree keys (bf16; fp32: the combine)
+  // bf16
+  int32_t nt;         // row tiles (lanes)
+  int32_t S;          // 16-row strips per (sequence, kv head)
+  int32_t tstrips;    // strips of the largest tile
+  int32_t gl;         // blocks per lane
+  int32_t grid;       // blocks launched (nt gl)
+  int32_t xpair;      // the lanes' blocks of one index share an XCD
+  int32_t split;      // 5- and 6-strip tiles split strips 4, 5 by key halves
+  size_t lds_dyn;     // dynamic LDS bytes of the prefix kernel
+  size_t rec_off;     // int4 [nt][gl] merge records
+  // fp32
   int32_t spw;        // 16-row strips per wave
   int32_t tile_rows;  // query rows per block
   int32_t row_tiles;  // ceil(R / tile_rows)
   int32_t chunks;     // prefix chunks per (sequence, kv head)
-  int32_t tree_keys;  // the prefix pass takes the tree keys (bf16; fp32: the combine)
-  size_t o_off;       // float [B*Hkv][chunks][row_tiles*tile_rows][128]
-  size_t ml_off;      // float2 [B*Hkv][chunks][row_tiles*tile_rows]
+  // both: partials (bf16 path: bf16 O [nt][2 gl][tstrips*16][128] and
+  // float2 (m, l) [nt][2 gl][tstrips*16]; fp32 path: fp32 O
+  // [B*Hkv][chunks][row_tiles*tile_rows][128] and (m, l) likewise)
+  size_t o_off;
+  size_t ml_off;
   size_t end;
 };
+constexpr int kMaxAttnSeq = 2048;     // sequences of one bf16 attention call
 AttnPlan plan_attn(int32_t T, int32_t B, int32_t Hq, int32_t Hkv, int64_t cap, int is_bf16);
 
 // ---------------------------------------------------------------- launchers
 // Paged prefix cache: a pool [num_pages][Hkv][page_size][d] per layer and a
 // block table [B][max_pages] of page ids (position p of sequence b is row
 // p % page_size of page table[b][p / page_size]).
-constexpr int kMaxChunkPages = 256;    // pages one prefix chunk may span
 struct PagedArgs {
   const int32_t* table;
   int32_t max_pages;

@@ -115,11 +115,11 @@ def test_host_checks_launch_nothing(tr):
     assert lib.tr_tree_attn(*args(64, 8, 8, tr.TR_BFLOAT16)) == tr.TR_ERR_UNSUPPORTED
     assert lib.tr_tree_attn(*args(128, 6, 4, tr.TR_BFLOAT16)) == tr.TR_ERR_INVALID_ARGUMENT
     assert lib.tr_tree_attn(*args(128, 8, 8, tr.TR_INT32)) == tr.TR_ERR_UNSUPPORTED
-    # tr_workspace_size covers both dtypes.  With a long cache both plans
-    # take 256 / 8 = 32 chunks of one 128-row tile (7 rows) and the fp32
-    # plan keeps fp32 partials (the bf16 one bf16), so it needs the more:
-    # one byte short fails the fp32 call, 256 KiB the bf16 one (32 x 8 x 128
-    # partial rows of 264 bytes)
+    # tr_workspace_size covers both dtypes.  With a long cache the fp32 plan
+    # takes 256 / 8 = 32 chunks of one 128-row tile (7 rows) per kv head with
+    # fp32 partials, more than the bf16 plan's two bf16 partials per block
+    # (256 blocks x 2 x 16 rows x 264 bytes): one byte short fails the fp32
+    # call, 256 KiB (the counters alone) the bf16 one
     big = lambda d, Hq, Hkv, dt: (h, 1, Hq, Hkv, d, dt, fake, fake, fake, fake, fake, 1 << 16,
                                   fake, C.c_float(0.1), fake, ws, 1 << 30, None)
     need = tr.tr_workspace_size(tree, 1, 0, 0, 8, 8, 128, 1 << 16)
