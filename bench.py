@@ -4,20 +4,28 @@
 One step = tr_tree_attn (tree attention of the merged sequence against the
 prefix cache, one layer) + tr_step (top-k of every node's logits,
 verification, update of M, commit of the accepted path, retrieval of the
-next tree).  Default workload: the Vicuna-7B-shaped step loop (V=32000,
-k=8, 81-node depth-6 tree, 32 heads x d=128 bf16, 2048-token prefix, 256
-steps).
+next tree).  Default workload: the large-vocabulary batch (32 independent
+sequences, V=128256, k=8, 81-node depth-6 trees, GQA 32/8 x d=128 bf16,
+prefixes uniform in [1024, 4096], 128 steps), the largest configuration
+that fits one GPU; `--workload` picks another.
 
 Protocol: a record pass runs the whole trajectory once and keeps every
 step's synthetic inputs (queries, tree keys/values, logits with the planted
 continuation of that step's tree) in HBM.  The state is then reset to the
 start and the same trajectory is replayed: `--warmup` steps untimed, then
-`--steps` steps timed between two device synchronisations, with HIP events
-around every call on the launch stream.  The replay must end in the same
-state as the record pass (checked).  A second replay of the same steps runs
-with the library's launch profiling on (two HIP events around every kernel,
-on the stream it runs on) and gives each kernel's average duration for the
-roofline; the headline rate comes from the first, unprofiled replay.
+`--steps` steps timed.  Passes over the same steps:
+  * stream replay: launched one by one from Python between two device
+    synchronisations, HIP events around every call (per-call figures);
+  * graph replay (the headline `value`): the timed steps captured once into
+    a HIP graph and replayed between two synchronisations;
+  * warm kernel timing: the library's launch profiling on (two HIP events
+    around every kernel, on the stream it runs on);
+  * cold kernel timing: the same, with a 1 GiB scrub buffer written before
+    every library call, so no kernel finds its inputs in the 256 MB
+    Infinity Cache or the L2s; the roofline is taken from this pass.
+Every replay must end in the record pass's state (checked).  Also measured:
+the achievable streaming-read bandwidth (tr_read_probe over 2 GiB, a sanity
+denominator), and the CPU oracle on the same trajectory (cpu_baseline).
 Prints one JSON line.
 """
 import argparse
@@ -33,6 +41,8 @@ if ROOT not in sys.path:
 METRIC = "TR steps/sec (retrieve+tree-attn+verify+top-k update); achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}     # dense matrix-core peaks
+SCRUB_BYTES = 1 << 30                                  # cold pass: written before every call
+PROBE_BYTES = 2 << 30                                  # read probe buffer
 
 
 def log(*a):
@@ -44,7 +54,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default: the workload's)")
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--workload", default="vicuna7b")
+    ap.add_argument("--workload", default="largevocab")
     ap.add_argument("--temperature", type=float, default=0.0,
                     help="0: greedy verification (tr_step); above 0: verification by sampling "
                          "at this temperature (tr_step_sample, seeded uniforms)")
@@ -59,47 +69,75 @@ def parse():
                     help="graph: the timed steps are captured once into a HIP graph and replayed "
                          "(value); stream: launched one by one from Python.  Both are timed; "
                          "per-call figures come from the stream pass")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="budget of the CPU oracle baseline (0 disables it)")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache kernel timing")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="budget of the CPU oracle baseline, split between a 1-thread and an "
+                         "all-threads run (0 disables it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (reference for "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
 
 
-def kernel_sources_sha256():
-    """Hash of the HIP sources: traffic counters taken on other sources are stale."""
+# Kernels of the library (profiling names), the kernel name prefix they
+# carry in counter records, and the sources they are built from: a counter
+# record taken on other sources of a kernel is stale for that kernel.
+KERNEL_SOURCES = {
+    "attn_prefix": ("attn_prefix", ["k_attn.hip", "dev_common.h", "tr_internal.h"]),
+    "attn_combine": ("attn_merge", ["k_attn.hip", "dev_common.h", "tr_internal.h"]),
+    "topk": ("topk_kernel", ["k_topk.hip", "tail.h", "sample.h", "dev_common.h", "tr_internal.h"]),
+}
+
+
+def kernel_sources_sha256(kernel):
+    """Hash of the HIP sources `kernel` is built from."""
     import hashlib
     d = os.path.join(ROOT, "draft_tree_retrieval_amd", "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(d)):
+    for name in sorted(KERNEL_SOURCES[kernel][1]):
         with open(os.path.join(d, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
-# profiling names of the library's kernels -> kernel name prefixes in the
-# counter record
-TRAFFIC_KERNEL = {"attn_prefix": "attn_prefix", "attn_combine": "attn_combine", "topk": "topk_kernel"}
+def counter_record(kind, workload, kernel):
+    """The committed counter record `profiles/<kind>_<workload>.json` entry
+    of `kernel`, or None when there is none or the kernel's sources changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_{workload}.json")
+    if kernel not in KERNEL_SOURCES or not os.path.exists(path):
+        return None, None
+    with open(path) as f:
+        rec = json.load(f)
+    prefix = KERNEL_SOURCES[kernel][0]
+    if rec.get("sources_sha256", {}).get(prefix) != kernel_sources_sha256(kernel):
+        return None, rec
+    return rec.get("per_kernel", {}).get(prefix), rec
 
 
 def measured_traffic(workload, kernel):
     """HBM bytes per launch of `kernel` from the committed counter record of
-    this workload (FETCH_SIZE and WRITE_SIZE runs, each scaled by what it
-    reads for a plain copy), or None when there is no record or the kernels
-    changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
-    if not os.path.exists(path):
+    this workload (a FETCH_SIZE run and a WRITE_SIZE run, each scaled by what
+    it reads for a plain copy of known size), or None when there is no
+    record or the kernel changed since it was taken."""
+    k, rec = counter_record("traffic", workload, kernel)
+    if not k:
         return None
-    with open(path) as f:
-        rec = json.load(f)
-    if rec.get("sources_sha256") != kernel_sources_sha256():
-        return None
-    k = rec.get("per_kernel_kib", {}).get(TRAFFIC_KERNEL.get(kernel, kernel))
     cal = rec.get("copy_calibration", {})
-    if not k or not cal:
+    if not cal:
         return None
     return int(round((k["FETCH_SIZE"] * cal["fetch_scale"] + k["WRITE_SIZE"] * cal["write_scale"]) * 1024))
+
+
+def measured_mfma(workload, kernel):
+    """Matrix-core figures of `kernel` from the committed counter record:
+    busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs) and
+    the matrix-core work per launch (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512
+    flops), or None."""
+    k, rec = counter_record("mfma", workload, kernel)
+    if not k:
+        return None
+    return {"busy_frac": k["busy_frac"], "mops_flops": k["mops_flops"]}
 
 
 def copy_calibration(mib):
@@ -114,43 +152,105 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes_per_launch": mib << 20, "launches": 5}), flush=True)
 
 
-def cpu_baseline(w, inputs, init_host, seconds, temperature=0.0):
-    """The CPU oracle, as it stands, on the first steps of the same trajectory."""
-    import numpy as np
-    from oracle import tr_oracle as O
+def read_probe(tr):
+    """Achievable streaming-read bandwidth: the median of five
+    tr_read_probe launches over 2 GiB (GB/s)."""
+    import torch
+    src = torch.ones(PROBE_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    sink = torch.zeros(2048, dtype=torch.int32, device="cuda")
+    tr.tr_read_probe(src, sink)
+    torch.cuda.synchronize()
+    tr.tr_profile_enable(True)
+    for _ in range(5):
+        tr.tr_read_probe(src, sink)
+    ms = sorted(m for n, m in tr.tr_profile_read() if n == "read_probe")
+    tr.tr_profile_enable(False)
+    del src
+    return round(PROBE_BYTES / (ms[len(ms) // 2] * 1e-3) / 1e9, 1)
+
+
+def cpu_info():
+    model = ""
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
-    t = O.template_from_levels(w.levels)
-    b = 0
-    M = init_host.M[b].numpy().astype(np.int64).copy()
-    kc = init_host.k_cache[b].float().numpy().copy()
-    vc = init_host.v_cache[b].float().numpy().copy()
-    P = int(init_host.prefix_len[b])
-    tok = O.retrieve(t, M, int(init_host.root[b]))
-    done, elapsed = 0, 0.0
-    for (q, kt, vt, z, U) in inputs:
-        if elapsed >= seconds:
-            break
-        qh, kth, vth, zh = (x[b].float().cpu().numpy() for x in (q, kt, vt, z))
-        uh = U[b].double().cpu().numpy() if U is not None else None
-        t0 = time.perf_counter()
-        O.tree_attention(t, qh, kth, vth, kc, vc, P)
-        res, P = O.step_after_forward(t, M, tok, zh, w.k, kc, vc, kth, vth, P,
-                                      temperature=temperature, uniforms=uh)
-        tok = res.next_tok
-        elapsed += time.perf_counter() - t0
-        done += 1
-    # a step of the batch is w.B sequences' work: the rate of sequence 0 alone
-    # divided by the batch size
-    return {"value": done / elapsed / w.B if elapsed else None, "unit": "steps/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"first {done} steps of the same trajectory, sequence 0 of {w.B} "
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count()
+    return model, os.cpu_count(), affinity
+
+
+def _oracle_run(w, inputs, init_host, seconds, temperature, threads):
+    """The CPU oracle, as it stands, stepping sequence 0 of the trajectory
+    with `threads` BLAS threads (None: the pool's default) for about
+    `seconds`: per-phase seconds and the steps done."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from oracle import tr_oracle as O
+    phases = ["attention", "topk", "verify", "update", "commit", "retrieve"]
+    acc = {p: 0.0 for p in phases}
+    with threadpool_limits(limits=threads):
+        used = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        t = O.template_from_levels(w.levels)
+        b = 0
+        M = init_host.M[b].numpy().astype(np.int64).copy()
+        kc = init_host.k_cache[b].float().numpy().copy()
+        vc = init_host.v_cache[b].float().numpy().copy()
+        P = int(init_host.prefix_len[b])
+        tok = O.retrieve(t, M, int(init_host.root[b]))
+        done, elapsed = 0, 0.0
+        for (q, kt, vt, z, U) in inputs:
+            if elapsed >= seconds:
+                break
+            qh, kth, vth, zh = (x[b].float().cpu().numpy() for x in (q, kt, vt, z))
+            uh = U[b].double().cpu().numpy() if U is not None else None
+            c0 = time.perf_counter()
+            O.tree_attention(t, qh, kth, vth, kc, vc, P)
+            c1 = time.perf_counter()
+            top = O.topk_rows(zh, w.k)
+            c2 = time.perf_counter()
+            v = (O.verify_sample(t, tok, zh, temperature, uh) if temperature > 0
+                 else O.verify(t, tok, top[:, 0]))
+            c3 = time.perf_counter()
+            O.update(M, tok, top)
+            c4 = time.perf_counter()
+            P = O.commit(kc, vc, kth, vth, P, v.path)
+            c5 = time.perf_counter()
+            tok = O.retrieve(t, M, v.bonus)
+            c6 = time.perf_counter()
+            for p, dt in zip(phases, (c1 - c0, c2 - c1, c3 - c2, c4 - c3, c5 - c4, c6 - c5)):
+                acc[p] += dt
+            elapsed += c6 - c0
+            done += 1
+    return acc, done, elapsed, used
+
+
+def cpu_baseline(w, inputs, init_host, seconds, temperature=0.0):
+    """The CPU oracle (float64 numpy, as it stands) on the first steps of
+    the same trajectory, sequence 0, once with one BLAS thread and once with
+    the pool's default thread count; a step of the batch is B sequences'
+    work, so each rate is the sequence rate divided by B."""
+    model, nproc, affinity = cpu_info()
+    runs = {}
+    for name, threads in (("one_thread", 1), ("all_threads", None)):
+        acc, done, elapsed, used = _oracle_run(w, inputs, init_host, seconds / 2, temperature, threads)
+        runs[name] = {"value": round(done / elapsed / w.B, 4) if elapsed else None, "threads": used,
+                      "steps": done, "seconds": round(elapsed, 2),
+                      "per_phase_ms": {p: round(s * 1e3 / max(done, 1), 3) for p, s in acc.items()}}
+    best = runs["all_threads"]
+    return {"value": best["value"], "unit": "steps/s", "cores": best["threads"], "kind": "oracle",
+            "sample": f"first {best['steps']} steps of the same trajectory, sequence 0 of {w.B} "
                       f"(tree attention + top-k + verify + update + commit + retrieve, float64 "
-                      f"numpy), {elapsed:.1f} s of CPU time; value = that rate / {w.B} "
-                      f"(steps of the whole batch)"}
+                      f"numpy), {best['seconds']} s of CPU time; value = that rate / {w.B} "
+                      f"(steps of the whole batch)",
+            "one_thread": runs["one_thread"], "all_threads": runs["all_threads"],
+            "nproc": nproc, "affinity_cpus": affinity, "cpu_model": model}
 
 
 def main():
@@ -202,11 +302,14 @@ def main():
         else:
             dec.step(z, kt, vt)
 
+    def fresh_decoder():
+        st = init.clone()
+        return TRDecoder(tree, st.M, st.k_cache, st.v_cache, st.prefix_len, st.root, Hq=w.Hq,
+                         page_size=args.page_size or None)
+
     # ---- record pass: the trajectory's inputs, kept in HBM
     t0 = time.time()
-    st = init.clone()
-    dec = TRDecoder(tree, st.M, st.k_cache, st.v_cache, st.prefix_len, st.root, Hq=w.Hq,
-                    page_size=args.page_size or None)
+    dec = fresh_decoder()
     out = torch.empty((w.B, w.T, w.Hq, w.d), dtype=w.kv_dtype, device=dev)
     ug = torch.Generator(device=dev).manual_seed(w.seed + 77)
     inputs, prefix_hist, accepted = [], [], []
@@ -229,17 +332,19 @@ def main():
     accepted = torch.stack(accepted).cpu()
     log(f"record pass: {total} steps in {time.time() - t0:.1f} s")
 
-    # ---- replay: warmup, then the timed region
-    st = init.clone()
-    dec = TRDecoder(tree, st.M, st.k_cache, st.v_cache, st.prefix_len, st.root, Hq=w.Hq,
-                    page_size=args.page_size or None)
+    def warmed():
+        d = fresh_decoder()
+        for s in range(args.warmup):
+            q, kt, vt, z, U = inputs[s]
+            d.attend(q, kt, vt, out)
+            step(d, z, kt, vt, U)
+        torch.cuda.synchronize()
+        return d
+
+    # ---- stream replay: warmup, then the timed region
+    dec = warmed()
     stream = torch.cuda.current_stream()
-    for s in range(args.warmup):
-        q, kt, vt, z, U = inputs[s]
-        dec.attend(q, kt, vt, out)
-        step(dec, z, kt, vt, U)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(steps):
         q, kt, vt, z, U = inputs[args.warmup + i]
@@ -264,14 +369,7 @@ def main():
     # node with its arguments fixed) and replayed from the post-warmup state;
     # the replay must end in the record pass's state as well
     if args.launch == "graph":
-        st = init.clone()
-        dec = TRDecoder(tree, st.M, st.k_cache, st.v_cache, st.prefix_len, st.root, Hq=w.Hq,
-                        page_size=args.page_size or None)
-        for s in range(args.warmup):
-            q, kt, vt, z, U = inputs[s]
-            dec.attend(q, kt, vt, out)
-            step(dec, z, kt, vt, U)
-        torch.cuda.synchronize()
+        dec = warmed()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             for i in range(steps):
@@ -291,27 +389,30 @@ def main():
     ms_per_step = wall * 1e3 / steps
 
     # ---- kernel timing: the same steps again, every launch between two HIP
-    # events on its stream
-    st = init.clone()
-    dec = TRDecoder(tree, st.M, st.k_cache, st.v_cache, st.prefix_len, st.root, Hq=w.Hq,
-                    page_size=args.page_size or None)
-    for s in range(args.warmup):
-        q, kt, vt, z, U = inputs[s]
-        dec.attend(q, kt, vt, out)
-        step(dec, z, kt, vt, U)
-    torch.cuda.synchronize()
-    tr.tr_profile_enable(True)
-    for i in range(steps):
-        q, kt, vt, z, U = inputs[args.warmup + i]
-        dec.attend(q, kt, vt, out)
-        step(dec, z, kt, vt, U)
-    launches = tr.tr_profile_read()
-    tr.tr_profile_enable(False)
-    assert torch.equal(dec.tree_tok, rec_tok), "profiled replay diverged from the record pass"
-    kernel_ms = {}
-    for name, ms in launches:
-        kernel_ms.setdefault(name, []).append(ms)
-    kernel_ms = {k: sum(v) / len(v) for k, v in kernel_ms.items() if len(v) == steps}
+    # events on its stream; warm, then cold (a 1 GiB scrub written before
+    # every library call, outside the events)
+    def kernel_pass(cold):
+        d = warmed()
+        scrub = torch.empty(SCRUB_BYTES // 4, dtype=torch.int32, device=dev) if cold else None
+        tr.tr_profile_enable(True)
+        for i in range(steps):
+            q, kt, vt, z, U = inputs[args.warmup + i]
+            if cold:
+                scrub.fill_(2 * i)
+            d.attend(q, kt, vt, out)
+            if cold:
+                scrub.fill_(2 * i + 1)
+            step(d, z, kt, vt, U)
+        launches = tr.tr_profile_read()
+        tr.tr_profile_enable(False)
+        assert torch.equal(d.tree_tok, rec_tok), "profiled replay diverged from the record pass"
+        ks = {}
+        for name, ms in launches:
+            ks.setdefault(name, []).append(ms)
+        return {k: sum(v) / len(v) for k, v in ks.items() if len(v) == steps}
+
+    kernel_ms = kernel_pass(False)
+    cold_ms = kernel_pass(True) if not args.no_cold else None
 
     # ---- algorithmic bytes per call (what the method must move)
     esz = torch.tensor([], dtype=w.kv_dtype).element_size()
@@ -354,18 +455,27 @@ def main():
     if Hl:
         kbytes["lmhead"] = lm_bytes + part_bytes
         kbytes["lmhead_merge"] = part_bytes + commit_bytes + m_bytes
-    kdetail = {k: {"avg_us": round(ms * 1e3, 2), "bytes": int(kbytes[k]),
-                   "GB_s": round(kbytes[k] / (ms * 1e-3) / 1e9, 1)} for k, ms in kernel_ms.items()}
-    log("per kernel:", json.dumps(kdetail))
+
+    def per_kernel(ms_map):
+        return {k: {"avg_us": round(ms * 1e3, 2), "bytes": int(kbytes[k]),
+                    "GB_s": round(kbytes[k] / (ms * 1e-3) / 1e9, 1)} for k, ms in ms_map.items()}
+
+    kdetail = per_kernel(kernel_ms)
+    log("per kernel (warm):", json.dumps(kdetail))
+    cdetail = per_kernel(cold_ms) if cold_ms else None
+    if cdetail:
+        log("per kernel (cold):", json.dumps(cdetail))
     # matrix-core work of the prefix pass: two products of rows x keys x d
     attn_flops = 4.0 * w.T * w.Hq * w.d * (P_sum.mean().item())
     dtype = "bf16" if w.kv_dtype == torch.bfloat16 else "f32"
     kflops = {"attn_prefix": attn_flops}
     if Hl:
         kflops["lmhead"] = 2.0 * w.B * w.T * w.V * Hl
-    dom = max(kernel_ms, key=kernel_ms.get)
-    dms, dbytes = kernel_ms[dom], kbytes[dom]
-    # the binding roof of the dominant kernel: whichever takes longer at peak
+    # the roofline of the dominant kernel, from the cold pass when there is
+    # one: its binding roof is whichever takes longer at peak
+    roof_ms = cold_ms or kernel_ms
+    dom = max(roof_ms, key=roof_ms.get)
+    dms, dbytes = roof_ms[dom], kbytes[dom]
     t_hbm = dbytes / (HBM_PEAK_GBS * 1e9)
     t_mfma = kflops.get(dom, 0.0) / (MFMA_PEAK_TFLOPS[dtype] * 1e12)
     if t_mfma > t_hbm:
@@ -378,15 +488,21 @@ def main():
         roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
     roof["traffic"] = measured_traffic(args.workload, dom)
-    log(f"mean accepted drafts {L_mean:.3f}, emitted/step {L_mean + 1:.3f}")
+    roof["timing"] = "cold (1 GiB scrub before every call)" if cold_ms else "warm"
+    # both roofs of the dominant kernel, and its matrix-core counters
+    roof["hbm_GB_s"] = round(dbytes / (dms * 1e-3) / 1e9, 1)
+    if dom in kflops:
+        roof["mfma_TFLOP_s"] = round(kflops[dom] / (dms * 1e-3) / 1e12, 1)
+    roof["mfma_counters"] = measured_mfma(args.workload, dom)
+    probe = read_probe(tr)
+    roof["achievable_read_GB_s"] = probe
+    log(f"read probe: {probe} GB/s; mean accepted drafts {L_mean:.3f}, emitted/step {L_mean + 1:.3f}")
 
     unfused = None
     if Hl:
         # the same steps with the product unfused: one bf16 GEMM writing the
         # logits, then tr_step on them
-        st = init.clone()
-        dec = TRDecoder(tree, st.M, st.k_cache, st.v_cache, st.prefix_len, st.root, Hq=w.Hq,
-                        page_size=args.page_size or None)
+        dec = fresh_decoder()
         logits = torch.empty((w.B, w.T, w.V), dtype=torch.bfloat16, device=dev)
         W_t = W_out.t()
 
@@ -435,6 +551,9 @@ def main():
         "stream_launch_steps_per_s": round(steps / stream_wall, 2),
         "per_call": detail,
         "per_kernel": kdetail,
+        "per_kernel_cold": cdetail,
+        "kernel_sum_steps_per_s": {"warm": round(1e3 / sum(kernel_ms.values()), 2),
+                                   "cold": round(1e3 / sum(cold_ms.values()), 2) if cold_ms else None},
         "emitted_per_step": round(L_mean + 1, 3),
         "cpu_baseline": cpu,
     }

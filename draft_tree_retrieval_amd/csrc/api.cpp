@@ -685,6 +685,14 @@ tr_status tr_profile_enable(int32_t on) {
   return ok();
 }
 
+tr_status tr_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  TR_CHECK(src && sink, TR_ERR_INVALID_ARGUMENT, "null pointer");
+  TR_CHECK(aligned16(src) && (reinterpret_cast<uintptr_t>(sink) & 3) == 0, TR_ERR_INVALID_ARGUMENT,
+           "src must be 16-byte aligned, sink 4-byte aligned");
+  TR_CHECK(bytes > 0 && bytes % 16 == 0, TR_ERR_INVALID_ARGUMENT, "bytes must be a positive multiple of 16");
+  return hip_status(tr::launch_read_probe(src, bytes, sink, hipStream_t(stream)), "tr_read_probe");
+}
+
 int32_t tr_profile_read(tr_launch_time* out, int32_t max) {
   auto& P = tr::g_prof;
   int32_t w = 0;

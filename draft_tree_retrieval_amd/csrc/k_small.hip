@@ -42,6 +42,39 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint4* p, size_t n16) {
     p[i] = make_uint4(0, 0, 0, 0);
 }
 
+// Read-bandwidth probe (a profiling aid, not a TR step): every 16-byte word
+// of the buffer is read once with non-temporal loads, four independent
+// loads in flight per thread, folded into one word per block and written to
+// sink[block] so the loads cannot be elided.
+constexpr int kProbeThreads = 512;
+constexpr int kProbeBlocks = 2048;
+__global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(const u32x4* __restrict__ p,
+                                                                 size_t n16, uint32_t* sink) {
+  const size_t stride = size_t(gridDim.x) * kProbeThreads;
+  size_t i = size_t(blockIdx.x) * kProbeThreads + threadIdx.x;
+  u32x4 acc = {0, 0, 0, 0};
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4 a = __builtin_nontemporal_load(p + i);
+    const u32x4 b = __builtin_nontemporal_load(p + i + stride);
+    const u32x4 c = __builtin_nontemporal_load(p + i + 2 * stride);
+    const u32x4 d = __builtin_nontemporal_load(p + i + 3 * stride);
+    acc ^= a ^ b ^ c ^ d;
+  }
+  for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(p + i);
+  uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  x = wave_max_u32(x);
+  if ((threadIdx.x & 63) == 0) atomicXor(sink + blockIdx.x, x);
+}
+
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  prof_begin(s, TR_KERNEL_READ_PROBE);
+  hipLaunchKernelGGL(read_probe_kernel, dim3(kProbeBlocks), dim3(kProbeThreads), 0, s,
+                     reinterpret_cast<const u32x4*>(src), n16, sink);
+  prof_end(s);
+  return hipGetLastError();
+}
+
 hipError_t launch_retrieve(const TreeDev& tree, int32_t B, const void* M, int m_is64, int64_t V,
                            int32_t k, const int32_t* root_tok, int32_t* tree_tok, uint8_t* ws,
                            hipStream_t s) {

@@ -179,6 +179,7 @@ hipError_t launch_verify(const TreeDev& tree, int32_t B, const int32_t* topk, in
                          const int32_t* tree_tok, int32_t* accept_len, int32_t* accept_path,
                          int32_t* bonus, int32_t* emitted, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
 enum InitMode : int32_t { INIT_ZERO = 0, INIT_RANDOM = 1, INIT_PRIOR = 2 };
 hipError_t launch_init_m(int mode, void* M, int m_is64, int32_t B, int64_t V, int32_t k,
                          const void* prior, int prior_is64, int prior_bcast, uint64_t seed,

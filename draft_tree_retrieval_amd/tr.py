@@ -63,11 +63,12 @@ _SIGS = {
                         _P], C.c_int),
     "tr_profile_enable": ([_I32], C.c_int),
     "tr_profile_read": ([_P, _I32], _I32),
+    "tr_read_probe": ([_P, _SZ, _P, _P], C.c_int),
 }
 
 # tr_kernel_id
 KERNEL_NAMES = {1: "attn_prefix", 2: "attn_combine", 3: "topk", 4: "retrieve", 5: "verify", 6: "fill",
-                7: "init", 8: "lmhead", 9: "lmhead_merge"}
+                7: "init", 8: "lmhead", 9: "lmhead_merge", 10: "read_probe"}
 
 
 class _LaunchTime(C.Structure):
@@ -383,3 +384,9 @@ def tr_profile_read(max_records=16384):
     buf = (_LaunchTime * max_records)()
     n = load().tr_profile_read(buf, max_records)
     return [(KERNEL_NAMES.get(buf[i].kernel, str(buf[i].kernel)), float(buf[i].ms)) for i in range(n)]
+
+
+def tr_read_probe(src, sink, stream=None):
+    """One streaming read of every byte of src (a profiling aid)."""
+    _check(load().tr_read_probe(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                                _stream(stream)))

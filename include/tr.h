@@ -402,7 +402,8 @@ typedef enum {
   TR_KERNEL_FILL = 6,          /* tr_workspace_init */
   TR_KERNEL_INIT = 7,          /* tr_init_matrix */
   TR_KERNEL_LMHEAD = 8,        /* tr_lmhead_topk / tr_step_lmhead: product and slice top-k */
-  TR_KERNEL_LMHEAD_MERGE = 9   /* tr_lmhead_topk / tr_step_lmhead: merge (and tail) */
+  TR_KERNEL_LMHEAD_MERGE = 9,  /* tr_lmhead_topk / tr_step_lmhead: merge (and tail) */
+  TR_KERNEL_READ_PROBE = 10    /* tr_read_probe */
 } tr_kernel_id;
 
 typedef struct {
@@ -412,6 +413,15 @@ typedef struct {
 
 tr_status tr_profile_enable(int32_t on);
 int32_t tr_profile_read(tr_launch_time* out, int32_t max);
+
+/* Achievable streaming-read bandwidth (a sanity denominator for the
+ * kernels' HBM figures, not a TR step): one kernel reads every byte of
+ * src [bytes] once with non-temporal 16-byte loads and folds them into
+ * sink [2048] uint32 (device memory, XOR-accumulated, contents meaningless).
+ * Time it with tr_profile_enable (kernel TR_KERNEL_READ_PROBE).  Errors:
+ * TR_ERR_INVALID_ARGUMENT for a null or misaligned pointer or a size that
+ * is not a positive multiple of 16. */
+tr_status tr_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }
