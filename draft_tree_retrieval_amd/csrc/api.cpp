@@ -150,6 +150,40 @@ size_t topk_need(const tr_tree* t, int32_t B, int64_t V, int32_t k) {
 
 }  // namespace
 
+namespace tr {
+
+tr_status set_error(tr_status s, const char* what) { return fail(s, "%s", what); }
+
+tr_status hip_error(hipError_t e, const char* what) { return hip_status(e, what); }
+
+tr_status attn_prepare(const tr_tree* t, int32_t B, int32_t Hq, int32_t Hkv, int32_t d, tr_dtype dt,
+                       const void* q, const void* k_tree, const void* v_tree, const void* k_cache,
+                       const void* v_cache, int64_t cap, const int32_t* prefix_len, float scale,
+                       const void* out, AttnPlan* plan) {
+  TR_CHECK(t != nullptr, TR_ERR_INVALID_ARGUMENT, "tree is null");
+  TR_CHECK(B >= 1, TR_ERR_INVALID_ARGUMENT, "B must be >= 1");
+  TR_CHECK(q && k_tree && v_tree && k_cache && v_cache && prefix_len && out,
+           TR_ERR_INVALID_ARGUMENT, "null tensor");
+  TR_CHECK(dt == TR_FLOAT32 || dt == TR_BFLOAT16, TR_ERR_UNSUPPORTED, "attention dtype must be float32 or bfloat16");
+  TR_CHECK(d == kHeadDim, TR_ERR_UNSUPPORTED, "head dimension must be %d", kHeadDim);
+  TR_CHECK(Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0, TR_ERR_INVALID_ARGUMENT,
+           "Hq (%d) must be a positive multiple of Hkv (%d)", Hq, Hkv);
+  TR_CHECK(cap >= 0, TR_ERR_INVALID_ARGUMENT, "negative capacity");
+  TR_CHECK(scale > 0.f && scale < 1e30f, TR_ERR_INVALID_ARGUMENT, "scale must be positive and finite");
+  TR_CHECK(int64_t(B) * Hkv <= 65535, TR_ERR_UNSUPPORTED, "B*Hkv above 65535");
+  TR_CHECK(aligned16(q) && aligned16(k_tree) && aligned16(v_tree) && aligned16(k_cache) &&
+               aligned16(v_cache) && aligned16(out), TR_ERR_INVALID_ARGUMENT,
+           "attention tensors must be 16-byte aligned");
+  if (dt == TR_BFLOAT16) {
+    tr_status st = check_bf16_attn(t, B, Hkv, cap);
+    if (st != TR_OK) return st;
+  }
+  *plan = plan_attn(t->dev.T, B, Hq, Hkv, cap, dt == TR_BFLOAT16);
+  return ok();
+}
+
+}  // namespace tr
+
 extern "C" {
 
 const char* tr_status_string(tr_status s) {
@@ -276,26 +310,11 @@ tr_status tr_tree_attn(const tr_tree* t, int32_t B, int32_t Hq, int32_t Hkv, int
                        const void* q, const void* k_tree, const void* v_tree, const void* k_cache,
                        const void* v_cache, int64_t cap, const int32_t* prefix_len, float scale,
                        void* out, void* ws, size_t ws_bytes, void* stream) {
-  TR_CHECK(t != nullptr, TR_ERR_INVALID_ARGUMENT, "tree is null");
-  TR_CHECK(B >= 1, TR_ERR_INVALID_ARGUMENT, "B must be >= 1");
-  TR_CHECK(q && k_tree && v_tree && k_cache && v_cache && prefix_len && out,
-           TR_ERR_INVALID_ARGUMENT, "null tensor");
-  TR_CHECK(dt == TR_FLOAT32 || dt == TR_BFLOAT16, TR_ERR_UNSUPPORTED, "attention dtype must be float32 or bfloat16");
-  TR_CHECK(d == tr::kHeadDim, TR_ERR_UNSUPPORTED, "head dimension must be %d", tr::kHeadDim);
-  TR_CHECK(Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0, TR_ERR_INVALID_ARGUMENT,
-           "Hq (%d) must be a positive multiple of Hkv (%d)", Hq, Hkv);
-  TR_CHECK(cap >= 0, TR_ERR_INVALID_ARGUMENT, "negative capacity");
-  TR_CHECK(scale > 0.f && scale < 1e30f, TR_ERR_INVALID_ARGUMENT, "scale must be positive and finite");
-  TR_CHECK(int64_t(B) * Hkv <= 65535, TR_ERR_UNSUPPORTED, "B*Hkv above 65535");
-  TR_CHECK(aligned16(q) && aligned16(k_tree) && aligned16(v_tree) && aligned16(k_cache) &&
-               aligned16(v_cache) && aligned16(out), TR_ERR_INVALID_ARGUMENT,
-           "attention tensors must be 16-byte aligned");
-  if (dt == TR_BFLOAT16) {
-    tr_status st = check_bf16_attn(t, B, Hkv, cap);
-    if (st != TR_OK) return st;
-  }
-  const tr::AttnPlan plan = tr::plan_attn(t->dev.T, B, Hq, Hkv, cap, dt == TR_BFLOAT16);
-  tr_status st = check_ws(ws, ws_bytes, plan.end);
+  tr::AttnPlan plan;
+  tr_status st = tr::attn_prepare(t, B, Hq, Hkv, d, dt, q, k_tree, v_tree, k_cache, v_cache, cap,
+                                  prefix_len, scale, out, &plan);
+  if (st != TR_OK) return st;
+  st = check_ws(ws, ws_bytes, plan.end);
   if (st != TR_OK) return st;
   return hip_status(tr::launch_attn(t->dev, B, Hq, Hkv, dt == TR_BFLOAT16, q, k_tree, v_tree, k_cache,
                                     v_cache, cap, prefix_len, scale, out, static_cast<uint8_t*>(ws),

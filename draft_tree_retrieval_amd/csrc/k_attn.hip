@@ -1305,7 +1305,8 @@ hipError_t launch_attn(const TreeDev& tree, int32_t B, int32_t Hq, int32_t Hkv, 
                        const void* q, const void* k_tree, const void* v_tree, const void* k_cache,
                        const void* v_cache, int64_t cap, const int32_t* prefix_len, float scale,
                        void* out, uint8_t* ws, const AttnPlan& plan, hipStream_t s,
-                       const PagedArgs* paged) {
+                       const PagedArgs* paged, uint8_t* flags) {
+  uint8_t* fl = flags ? flags : ws;                 // sticky flags
   void* part_o = ws + plan.o_off;
   float2* part_ml = reinterpret_cast<float2*>(ws + plan.ml_off);
   const float sl2 = scale * kLog2e;
@@ -1324,7 +1325,7 @@ hipError_t launch_attn(const TreeDev& tree, int32_t B, int32_t Hq, int32_t Hkv, 
   hipLaunchKernelGGL((attn_prefix_bf16<PG>), dim3(plan.grid), dim3(64 * kWaves), plan.lds_dyn, s, qq, \
                      kk, vv, kt, vt, tree, cap, prefix_len, B, Hq, Hkv, plan.G, plan.R, plan.nt,     \
                      plan.S, plan.tstrips, plan.gl, plan.xpair, plan.split, sl2, po, part_ml, rec, o, \
-                     ws, pa)
+                     fl, pa)
     if (paged) TR_PREFIX(true); else TR_PREFIX(false);
 #undef TR_PREFIX
     prof_end(s);
@@ -1344,7 +1345,7 @@ hipError_t launch_attn(const TreeDev& tree, int32_t B, int32_t Hq, int32_t Hkv, 
   hipLaunchKernelGGL(attn_prefix_f32, grid, dim3(256), 0, s, reinterpret_cast<const float*>(q),
                      reinterpret_cast<const float*>(k_cache), reinterpret_cast<const float*>(v_cache),
                      cap, prefix_len, tree.T, Hq, Hkv, plan.G, plan.R, plan.chunks, sl2,
-                     reinterpret_cast<float*>(part_o), part_ml, ws);
+                     reinterpret_cast<float*>(part_o), part_ml, fl);
   prof_end(s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -184,10 +184,22 @@ enum InitMode : int32_t { INIT_ZERO = 0, INIT_RANDOM = 1, INIT_PRIOR = 2 };
 hipError_t launch_init_m(int mode, void* M, int m_is64, int32_t B, int64_t V, int32_t k,
                          const void* prior, int prior_is64, int prior_bcast, uint64_t seed,
                          hipStream_t s);
+// ws: the scratch of the call (partials at the plan's offsets); flags: where
+// the kernels raise sticky TR_FLAG_* bits (null: the status word of ws).
 hipError_t launch_attn(const TreeDev& tree, int32_t B, int32_t Hq, int32_t Hkv, int is_bf16,
                        const void* q, const void* k_tree, const void* v_tree, const void* k_cache,
                        const void* v_cache, int64_t cap, const int32_t* prefix_len, float scale,
                        void* out, uint8_t* ws, const AttnPlan& plan, hipStream_t s,
-                       const PagedArgs* paged = nullptr);
+                       const PagedArgs* paged = nullptr, uint8_t* flags = nullptr);
+
+// Host-side helpers of the entry points (api.cpp): every check of a
+// tr_tree_attn call except its workspace, and the plan; the last-error
+// text of a status.
+tr_status attn_prepare(const tr_tree* t, int32_t B, int32_t Hq, int32_t Hkv, int32_t d, tr_dtype dt,
+                       const void* q, const void* k_tree, const void* v_tree, const void* k_cache,
+                       const void* v_cache, int64_t cap, const int32_t* prefix_len, float scale,
+                       const void* out, AttnPlan* plan);
+tr_status set_error(tr_status s, const char* what);
+tr_status hip_error(hipError_t e, const char* what);
 
 }  // namespace tr

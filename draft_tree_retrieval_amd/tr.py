@@ -64,6 +64,8 @@ _SIGS = {
     "tr_profile_enable": ([_I32], C.c_int),
     "tr_profile_read": ([_P, _I32], _I32),
     "tr_read_probe": ([_P, _SZ, _P, _P], C.c_int),
+    "tr_tree_attn_noalloc": ([_P, _I32, _I32, _I32, _I32, C.c_int, _P, _P, _P, _P, _P, _I64, _P,
+                              C.c_float, _P, _P, _P], C.c_int),
 }
 
 # tr_kernel_id
@@ -204,6 +206,21 @@ def tr_tree_attn(tree, q, k_tree, v_tree, k_cache, v_cache, prefix_len, out, ws,
     _check(load().tr_tree_attn(tree.handle, B, Hq, Hkv, d, _dt(q), _ptr(q), _ptr(k_tree),
                                _ptr(v_tree), _ptr(k_cache), _ptr(v_cache), cap, _ptr(prefix_len),
                                float(scale), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def tr_tree_attn_noalloc(tree, q, k_tree, v_tree, k_cache, v_cache, prefix_len, out, flags=None,
+                         scale=None, stream=None):
+    """tr_tree_attn without a workspace (the library's per-GPU scratch);
+    flags: an optional device int32 [1] the sticky TR_FLAG_* bits are OR-ed into."""
+    B, T, Hq, d = q.shape
+    Hkv = k_tree.shape[2]
+    cap = k_cache.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check(load().tr_tree_attn_noalloc(tree.handle, B, Hq, Hkv, d, _dt(q), _ptr(q), _ptr(k_tree),
+                                       _ptr(v_tree), _ptr(k_cache), _ptr(v_cache), cap,
+                                       _ptr(prefix_len), float(scale), _ptr(out), _ptr(flags),
+                                       _stream(stream)))
 
 
 class _PagedKVStruct(C.Structure):

@@ -166,6 +166,25 @@ tr_status tr_tree_attn(const tr_tree* t, int32_t B, int32_t Hq, int32_t Hkv, int
                        const void* v_cache, int64_t cap, const int32_t* prefix_len, float scale,
                        void* out, void* ws, size_t ws_bytes, void* stream);
 
+/* tr_tree_attn for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, arithmetic, results and errors as
+ * tr_tree_attn, without ws / ws_bytes: the call's scratch (prefix partials,
+ * merge records) lives in a 48 MiB array of device memory that the library
+ * holds on every GPU it runs on from the first call there until the process
+ * ends; the call itself allocates nothing.  A call needing more scratch than
+ * that (tr_workspace_size's attention part above 48 MiB) returns
+ * TR_ERR_UNSUPPORTED and launches nothing.  Every call on one GPU shares that
+ * GPU's array, so calls that overlap on one GPU (different streams or host
+ * threads without ordering) race: order them on one stream.
+ *   flags  device uint32 (nullable): the sticky TR_FLAG_* bits of the call
+ *          are OR-ed into it (TR_FLAG_BAD_PREFIX); the caller clears it. */
+tr_status tr_tree_attn_noalloc(const tr_tree* t, int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
+                               tr_dtype dt, const void* q, const void* k_tree, const void* v_tree,
+                               const void* k_cache, const void* v_cache, int64_t cap,
+                               const int32_t* prefix_len, float scale, void* out, uint32_t* flags,
+                               void* stream);
+
 /* argtopk of every node's next-token logits and the recycling update
  * M[tree_tok[b][n]] = argtopk(logits[b][n]) for every node n, in merged
  * order (Chinese summary, Method, update equation; walk-through "why it is

@@ -169,6 +169,18 @@ def test_host_checks_launch_nothing(tr):
     assert init(1, 1 << 31, 8, fake, tr.TR_INT32, tr.TR_INIT_ZERO, None, 0, 0) == tr.TR_ERR_INVALID_ARGUMENT
     assert lib.tr_verify(h, 1, None, 3, fake, fake, None, fake, None, None) == tr.TR_ERR_INVALID_ARGUMENT
     assert "null" in tr.load().tr_last_error().decode()
+    # allocation-free attention: the workspace call's checks, then its scratch
+    # limit (an fp32 plan of 512 x 8 (sequence, kv head) pairs needs one
+    # 128-row tile of fp32 partials each, about 270 MB), before any device call
+    na = lambda B, Hq, Hkv, d, dt, q: lib.tr_tree_attn_noalloc(
+        h, B, Hq, Hkv, d, dt, q, fake, fake, fake, fake, 64, fake, C.c_float(0.1), fake, None, None)
+    assert na(1, 8, 8, 128, tr.TR_BFLOAT16, None) == tr.TR_ERR_INVALID_ARGUMENT     # null tensor
+    assert na(1, 8, 8, 64, tr.TR_BFLOAT16, fake) == tr.TR_ERR_UNSUPPORTED           # head dim
+    assert na(512, 8, 8, 128, tr.TR_FLOAT32, fake) == tr.TR_ERR_UNSUPPORTED         # scratch limit
+    assert "48 MiB" in tr.load().tr_last_error().decode()
+    assert lib.tr_tree_attn_noalloc(h, 1, 8, 8, 128, tr.TR_BFLOAT16, fake, fake, fake, fake, fake,
+                                    64, fake, C.c_float(0.1), fake, C.c_void_p((1 << 20) + 2),
+                                    None) == tr.TR_ERR_INVALID_ARGUMENT             # misaligned flags
 
 
 def test_workspace_size_grows_with_problem(tr):
