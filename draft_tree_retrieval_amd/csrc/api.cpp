@@ -322,6 +322,15 @@ tr_status tr_tree_attn(const tr_tree* t, int32_t B, int32_t Hq, int32_t Hkv, int
                     "tr_tree_attn");
 }
 
+// A row longer than the plan's segments can hold in registers is refused
+// (the scan would otherwise leave its tail unread).
+static tr_status check_topk_len(const tr::TopkPlan& plan, int64_t V) {
+  TR_CHECK(plan.seg_len <= plan.seg_cap, TR_ERR_UNSUPPORTED,
+           "V = %lld above the top-k limit of %lld for this logit dtype and k",
+           (long long)V, (long long)plan.max_v);
+  return TR_OK;
+}
+
 static tr_status check_topk_args(const tr_tree* t, int32_t B, const void* logits, tr_dtype l_dtype,
                                  int64_t V, int32_t k) {
   TR_CHECK(t != nullptr, TR_ERR_INVALID_ARGUMENT, "tree is null");
@@ -351,6 +360,8 @@ tr_status tr_update_topk(const tr_tree* t, int32_t B, const void* logits, tr_dty
     TR_CHECK(m_dtype == TR_INT32 || m_dtype == TR_INT64, TR_ERR_UNSUPPORTED, "M must be int32 or int64");
   }
   const tr::TopkPlan plan = tr::plan_topk(int64_t(B) * t->dev.T, V, k, l_dtype == TR_BFLOAT16 ? 2 : 4);
+  st = check_topk_len(plan, V);
+  if (st != TR_OK) return st;
   st = check_ws(ws, ws_bytes, plan.end);
   if (st != TR_OK) return st;
   uint8_t* w = static_cast<uint8_t*>(ws);
@@ -447,6 +458,10 @@ tr_status step_impl(const tr_tree* t, int32_t B, int64_t V, int32_t k, const voi
   const int64_t rows = int64_t(B) * t->dev.T;
   const tr::TopkPlan plan = tr::plan_topk(rows, V, k, l_dtype == TR_BFLOAT16 ? 2 : 4);
   const tr::LmheadPlan lplan = tr::plan_lmhead(rows, V, k);
+  if (!lm) {
+    st = check_topk_len(plan, V);
+    if (st != TR_OK) return st;
+  }
   st = check_ws(ws, ws_bytes, lm ? lplan.end : plan.end);
   if (st != TR_OK) return st;
   uint8_t* w = static_cast<uint8_t*>(ws);

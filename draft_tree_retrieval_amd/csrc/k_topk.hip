@@ -42,6 +42,8 @@ TopkPlan plan_topk(int64_t rows, int64_t V, int32_t k, int32_t esz) {
   const int64_t nv = p.threads == 1024 ? 4 : 16;          // vectors per lane
   const int64_t cap = int64_t(p.threads) * nv * (16 / esz);  // largest segment a block holds
   const int64_t max_segs = 256 / p.kmax;                 // the final merge ranks <= 256 keys
+  p.seg_cap = cap;
+  p.max_v = max_segs * cap;                              // longer rows are refused on the host
   int64_t need = (V + cap - 1) / cap;
   // Few rows: one block per row when a row fits, so no segment hand-over
   // (a round trip through device memory) stands between the scan and the

@@ -56,7 +56,9 @@ struct TopkPlan {
   int32_t segs;       // segments per row (1..64)
   int64_t seg_len;    // elements per segment (multiple of 8)
   int32_t kmax;       // 8 or 16 (list length kept per thread)
-  int32_t threads;    // 256 (16 vectors per lane) or 512 (8 vectors per lane)
+  int32_t threads;    // 256 (16 vectors per lane) or 1024 (4 vectors per lane)
+  int64_t seg_cap;    // the longest segment a block holds (elements)
+  int64_t max_v;      // the largest row length the plan supports (segments x seg_cap)
   size_t part_off;    // uint64 [rows][segs][kmax] partial keys (segs > 1)
   size_t ids_off;     // int32  [rows][k] ids when the caller gives no buffer
   size_t stat_off;    // float2 [rows][segs] softmax statistics (sampling)

@@ -39,7 +39,11 @@
  *   - Logits must not be NaN (+-inf are fine).
  *
  * Limits: 1 <= k <= 16, 1 <= tree nodes <= 128, head dimension d = 128,
- * Hq a multiple of Hkv.
+ * Hq a multiple of Hkv.  The top-k of a logits row (tr_update_topk, tr_step
+ * and its variants) holds V <= 1,048,576 (bfloat16 logits, k <= 8),
+ * 524,288 (bfloat16 with k > 8, or float32 with k <= 8) or 262,144 (float32,
+ * k > 8); a longer row is TR_ERR_UNSUPPORTED.  bf16 tree attention takes
+ * B <= 2048 sequences.
  */
 #ifndef TR_H
 #define TR_H
@@ -200,7 +204,10 @@ tr_status tr_update_topk(const tr_tree* t, int32_t B, const void* logits, tr_dty
 
 /* Greedy verification (Method, third module: the longest correct sequence
  * is the step's output; walk-through step 4: the target's own token follows
- * it).  g(n) = topk[b][n][0]; node n > 0 is accepted iff its parent is and
+ * it).  It reads the target's greedy token of every node from topk; a caller
+ * holding only the logits gets them first with tr_update_topk (M = NULL,
+ * topk_out given), then calls this (tr_step does both in one launch).
+ * g(n) = topk[b][n][0]; node n > 0 is accepted iff its parent is and
  * tree_tok[b][n] == g(parent).  best = deepest accepted node (ties: lowest
  * index).  Outputs (Dmax = tree depth):
  *   accept_len  [B]         L = depth(best)

@@ -147,6 +147,14 @@ def test_host_checks_launch_nothing(tr):
     # top-k / update / step
     assert lib.tr_update_topk(h, 1, fake, tr.TR_BFLOAT16, 2, 3, fake, fake, tr.TR_INT32, None, ws,
                               1 << 30, None) == tr.TR_ERR_INVALID_ARGUMENT        # V < k
+    # rows longer than the segments hold: float32 k <= 8 holds 524288, bf16 1048576
+    for dt, V in ((tr.TR_FLOAT32, 524289), (tr.TR_FLOAT32, 600000), (tr.TR_BFLOAT16, 1048577)):
+        assert lib.tr_update_topk(h, 1, fake, dt, V, 3, fake, fake, tr.TR_INT32, None, ws,
+                                  1 << 40, None) == tr.TR_ERR_UNSUPPORTED, (dt, V)
+        assert "top-k limit" in tr.load().tr_last_error().decode()
+        assert lib.tr_step(h, 1, V, 3, fake, dt, fake, tr.TR_INT32, fake, fake, fake, None, None, 2,
+                           128, tr.TR_BFLOAT16, fake, fake, fake, fake, 64, fake, None, ws,
+                           1 << 40, None) == tr.TR_ERR_UNSUPPORTED, (dt, V)
     assert lib.tr_update_topk(h, 1, fake, tr.TR_BFLOAT16, 16, 3, fake, None, tr.TR_INT32, None, ws,
                               1 << 30, None) == tr.TR_ERR_INVALID_ARGUMENT        # nothing to write
     assert lib.tr_step(h, 1, 16, 3, fake, tr.TR_BFLOAT16, fake, tr.TR_INT32, fake, fake, fake, None,

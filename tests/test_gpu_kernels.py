@@ -165,6 +165,34 @@ def test_topk_unaligned_rows(tr):
     assert (out[0].cpu().numpy() == want).all()
 
 
+@pytest.mark.parametrize("dtype,V,k,rows", [(torch.float32, 524288, 8, 3),
+                                             (torch.bfloat16, 1048576, 8, 3),
+                                             (torch.bfloat16, 524288, 16, 2),
+                                             (torch.float32, 262144, 16, 300)])
+def test_topk_at_row_limit(tr, dtype, V, k, rows):
+    # the longest rows the plan holds (one row per block and many rows per
+    # launch): the best values sit in the last elements of each row, where a
+    # segment that dropped its tail would miss them; a tie at the very end
+    # goes to the lower id
+    g = torch.Generator().manual_seed(V + k)
+    z = (torch.randn((rows, V), generator=g) * 3).to(dtype)
+    for r in range(rows):
+        z[r, V - 1] = 100.0
+        z[r, V - 3] = 90.0
+        z[r, V - 2] = 90.0
+        z[r, (r * 7919) % (V // 2)] = 95.0
+    T = min(rows, 100)                              # B sequences of a T-node chain
+    B = rows // T
+    tree = tr.Tree.from_levels([[1]] * (T - 1), k)
+    ws = ws_for(tr, tree, B, V, k)
+    out = torch.empty((B, T, k), dtype=torch.int32, device=DEV)
+    tr.tr_update_topk(tree, z.view(B, T, V).to(DEV), None, None, out, ws)
+    want = O.topk_rows(z.float().numpy(), k)
+    got = out.view(rows, k).cpu().numpy()
+    assert (got == want).all()
+    assert (got[:, 0] == V - 1).all() and (got[:, 2] == V - 3).all() and (got[:, 3] == V - 2).all()
+
+
 # ------------------------------------------------------------------ verify + update
 def test_verify_parity_duplicates(tr):
     rng = np.random.default_rng(4)
@@ -498,6 +526,46 @@ def test_paged_attention_parity(tr, ps):
     kv_bad = tr.PagedKV(dkp, dvp, bad, dkt, dvt, dP)
     tr.tr_tree_attn_paged(tree, dq, kv_bad, 0, out_p, ws)
     assert tr.tr_read_device_status(ws) & tr.TR_FLAG_BAD_PAGE
+
+
+@pytest.mark.parametrize("ps", [64, 256])
+def test_paged_attention_later_layers(tr, ps):
+    # a model's cache of 4 layers in shared page pools; attention at layer 1
+    # and at the last layer reads that layer's pages and tree rows only
+    # (every layer's data differs), checked against the oracle's paged
+    # attention on that layer's pool and bit for bit against the contiguous
+    # call on that layer's slices
+    g = torch.Generator().manual_seed(73)
+    levels = RAND_LEVELS[4]
+    t = otree(levels)
+    tree = tr.Tree.from_levels(levels, 8)
+    L, B, Hq, Hkv, d, cap = 4, 3, 16, 4, 128, 1024
+    P = torch.tensor([1000, 0, 517], dtype=torch.int32)
+    mk = lambda *sh: torch.randn(sh, generator=g).to(torch.bfloat16)
+    kt, vt = mk(L, B, t.n_nodes, Hkv, d), mk(L, B, t.n_nodes, Hkv, d)
+    kc, vc = mk(L, B, Hkv, cap, d), mk(L, B, Hkv, cap, d)
+    kp, table = paged_from_contiguous(g, kc, ps, layers=L)
+    vp = torch.empty_like(kp)
+    for b in range(B):
+        for j in range(cap // ps):
+            vp[:, table[b, j]] = vc[:, b, :, j * ps:(j + 1) * ps]
+    dkt, dvt, dkc, dvc, dkp, dvp, dtab, dP = (x.to(DEV) for x in (kt, vt, kc, vc, kp, vp, table, P))
+    ws = ws_for(tr, tree, B, 0, 0, Hq, Hkv, cap)
+    kv = tr.PagedKV(dkp, dvp, dtab, dkt, dvt, dP)
+    for layer in (1, L - 1):
+        q = mk(B, t.n_nodes, Hq, d)
+        dq = q.to(DEV)
+        out_p = torch.empty_like(dq)
+        tr.tr_tree_attn_paged(tree, dq, kv, layer, out_p, ws)
+        out_c = torch.empty_like(dq)
+        tr.tr_tree_attn(tree, dq, dkt[layer], dvt[layer], dkc[layer], dvc[layer], dP, out_c, ws)
+        assert torch.equal(out_p, out_c), layer
+        for b in range(B):
+            want = O.tree_attention_paged(t, q[b].float().numpy(), kt[layer, b].float().numpy(),
+                                          vt[layer, b].float().numpy(), kp[layer].float().numpy(),
+                                          vp[layer].float().numpy(), table[b].numpy(), ps, int(P[b]))
+            assert np.abs(out_p[b].float().cpu().numpy() - want).max() <= 2e-2, (layer, b)
+    assert tr.tr_read_device_status(ws) == 0
 
 
 def test_step_paged_commits_every_layer(tr):
