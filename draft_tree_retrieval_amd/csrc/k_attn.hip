@@ -248,9 +248,11 @@ struct Walk {
 // after the one a cut unit starts in): {b * Hkv + kvh, first block, blocks,
 // 1 if the unit starts inside the first block (its partial is that
 // block's second)}; x = -1: none.
+// (q is not __restrict__: loads through a const __restrict__ pointer may be
+// moved across the explicit waits below, which must cover them.)
 template <bool PAGED>
 __global__ __launch_bounds__(512) void attn_prefix_bf16(
-    const uint16_t* __restrict__ q, const uint16_t* kc, const uint16_t* vc, const uint16_t* kt,
+    const uint16_t* q, const uint16_t* kc, const uint16_t* vc, const uint16_t* kt,
     const uint16_t* vt, TreeDev tree, int64_t cap, const int32_t* __restrict__ prefix_len, int B,
     int Hq, int Hkv, int G, int R, int nt, int S, int tstrips, int gl, int xpair, int split,
     float sl2, uint16_t* __restrict__ part_o, float2* __restrict__ part_ml,
@@ -446,10 +448,21 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
   // ([B][T][Hkv][d]; nodes past T repeat the last, masked like keys past P).
   // PAGED: kc / vc are page pools [num_pages][Hkv][page_size][d]; pid is the
   // page of the sub-block's rows (a 64-key sub-block never straddles pages).
+  // A full prefix sub-block (the common case) is a wave-uniform base plus
+  // each lane's fixed byte offset (row r = p / 16 of the sub-block, its
+  // swizzled 16-byte chunk), computed once here; the second pass is 32 rows
+  // on with the same swizzle, 8 KB further.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  uint32_t offk, offv;
+  {
+    const int r = (w * 64 + lane) >> 4, pos = lane & 15;
+    offk = uint32_t(r * 256 + ((pos ^ (r & 15)) << 4));
+    offv = uint32_t(r * 256 + ((pos ^ ((r & 7) << 1)) << 4));
+  }
   auto dma = [&](const Walk& it, int pid, int sl) {
     const int ntp = (it.P + kSB - 1) / kSB;
+    const int kb = it.s * kSB;
     if (it.s < ntp) {
-      const int kb = it.s * kSB;
       const uint16_t* kp;
       const uint16_t* vp;
       int row_base = 0;
@@ -463,15 +476,26 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
         kp = kc + head_off;
         vp = vc + head_off;
       }
+      if (kb + kSB <= it.P) {
+        const uint8_t* kbase = reinterpret_cast<const uint8_t*>(kp + int64_t(kb - row_base) * kHeadDim);
+        const uint8_t* vbase = reinterpret_cast<const uint8_t*>(vp + int64_t(kb - row_base) * kHeadDim);
 #pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
-        const int base = (q2 * kWaves + w) * 64;       // wave-uniform first slot
-        const int p = base + lane;
-        const int r = p >> 4, pos = p & 15;
-        const int64_t row = min(kb + r, it.P - 1) - row_base;
-        const int ck = pos ^ (r & 15), cv = pos ^ ((r & 7) << 1);
-        lds_dma16(kp + row * kHeadDim + ck * 8, kslot(sl) + base * 16);
-        lds_dma16(vp + row * kHeadDim + cv * 8, vslot(sl) + base * 16);
+        for (int q2 = 0; q2 < 2; ++q2) {
+          const int base = (q2 * kWaves + wu) * 64;    // wave-uniform first slot
+          lds_dma16(kbase + q2 * 8192 + offk, kslot(sl) + base * 16);
+          lds_dma16(vbase + q2 * 8192 + offv, vslot(sl) + base * 16);
+        }
+      } else {
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) {
+          const int base = (q2 * kWaves + wu) * 64;
+          const int p = base + lane;
+          const int r = p >> 4, pos = p & 15;
+          const int64_t row = min(kb + r, it.P - 1) - row_base;
+          const int ck = pos ^ (r & 15), cv = pos ^ ((r & 7) << 1);
+          lds_dma16(kp + row * kHeadDim + ck * 8, kslot(sl) + base * 16);
+          lds_dma16(vp + row * kHeadDim + cv * 8, vslot(sl) + base * 16);
+        }
       }
     } else {
       const int nb0 = (it.s - ntp) * kSB;
@@ -480,7 +504,7 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
       const uint16_t* vt_b = vt + (int64_t(it.b) * T * Hkv + it.kvh) * kHeadDim;
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2) {
-        const int base = (q2 * kWaves + w) * 64;
+        const int base = (q2 * kWaves + wu) * 64;
         const int p = base + lane;
         const int r = p >> 4, pos = p & 15;
         const int64_t node = min(nb0 + r, T - 1);
@@ -709,8 +733,10 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
               acc[s][dt0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[i][pp], pb[s][pp], acc[s][dt0 + i], 0, 0, 0);
       }
     };
-    // one sub-block: all 64 keys, or (half-key waves) keys 32 kh .. 32 kh + 31
-    auto compute = [&](const uint8_t* Ks, const uint8_t* Vs, int s, int P, bool fresh) {
+    // one sub-block: all 64 keys, or (half-key waves) keys 32 kh .. 32 kh + 31:
+    // scores and probabilities first, then (after the step's DMA has been
+    // issued, while the scores are no longer live) the second product
+    auto probs = [&](const uint8_t* Ks, const uint8_t* Vs, int s, int P, bool fresh) {
       floatx4 sc[NS][4];
       if (NS == 2 || !hw) {
         qk(Ks, sc, IntC<4>{}, 0);
@@ -718,15 +744,17 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
         read_v(Vs, 0, IntC<2>{}, 0);
         __builtin_amdgcn_sched_barrier(0);
         softmax(sc, IntC<4>{}, fresh);
-        pv(Vs, IntC<2>{}, 0);
       } else {
         qk(Ks, sc, IntC<2>{}, 2 * kh);
         mask(sc, s, P, IntC<2>{}, 2 * kh);
         read_v(Vs, 0, IntC<1>{}, kh);
         __builtin_amdgcn_sched_barrier(0);
         softmax(sc, IntC<2>{}, fresh);
-        pv(Vs, IntC<1>{}, kh);
       }
+    };
+    auto weigh = [&](const uint8_t* Vs) {
+      if (NS == 2 || !hw) pv(Vs, IntC<2>{}, 0);
+      else pv(Vs, IntC<1>{}, kh);
     };
     // The unit (b, kvh) ends in this block: a unit wholly inside the range
     // is normalised and written out; a cut one leaves its partial in the
@@ -830,6 +858,7 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
     // explicit wait: otherwise the compiler waits for all loads in flight,
     // the ring's DMA included, before every step's products)
     if (active) qload(wc.b, wc.kvh);
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0x0070);            // vmcnt(0) lgkmcnt(0)
     asm volatile("" ::: "memory");
     const int nround = (nj + kRingSlots - 1) / kRingSlots * kRingSlots;
@@ -848,6 +877,10 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
+        // this step's DMA is issued after the scores and probabilities, so
+        // its issue overlaps the matrix cores instead of holding every wave
+        // back right after the barrier
+        if (j < nj && active) probs(kslot(jj), vslot(jj), wc.s, wc.P, fresh);
         if (j + 3 < nj) {
           const int pid = pnext;
           dma(wd, pid, (jj + 3) % kRingSlots);
@@ -855,7 +888,7 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
           if (j + 4 < nj) pnext = page(wd);
         }
         if (j < nj) {
-          if (active) compute(kslot(jj), vslot(jj), wc.s, wc.P, fresh);
+          if (active) weigh(vslot(jj));
           fresh = false;
           if (wc.s == wc.n - 1 || j == nj - 1) {
             const bool unit_whole = whole && wc.s == wc.n - 1;
@@ -874,6 +907,7 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
             // later step wait for all loads in flight, the ring's DMA
             // included, before reusing the stores' source registers or
             // reading the queries
+            asm volatile("" ::: "memory");
             __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0)
             asm volatile("" ::: "memory");
           } else {
