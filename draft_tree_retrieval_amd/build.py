@@ -13,8 +13,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtr.so")
-SOURCES = ["api.cpp", "k_topk.hip", "k_small.hip", "k_attn.hip", "k_init.hip", "k_lmhead.hip",
-           "noalloc.hip"]
+SOURCES = ["api.cpp", "k_topk.hip", "k_step.hip", "k_small.hip", "k_attn.hip", "k_init.hip",
+           "k_lmhead.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -1,6 +1,7 @@
 // extern "C" entry points of libtr: argument checks on the host, then the
 // kernel launches.  No call here allocates device memory.
 #include <cmath>
+#include <cstdlib>
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -324,6 +325,14 @@ tr_status tr_tree_attn(const tr_tree* t, int32_t B, int32_t Hq, int32_t Hkv, int
 
 // A row longer than the plan's segments can hold in registers is refused
 // (the scan would otherwise leave its tail unread).
+// The few-row greedy step kernel (k_step.hip) is used where it applies
+// unless the environment sets TR_FEW_ROW_STEP=0 (a diagnostic switch: the
+// general kernel computes the same results).
+static bool few_row_step_enabled() {
+  const char* v = std::getenv("TR_FEW_ROW_STEP");
+  return !(v && v[0] == '0' && v[1] == 0);
+}
+
 static tr_status check_topk_len(const tr::TopkPlan& plan, int64_t V) {
   TR_CHECK(plan.seg_len <= plan.seg_cap, TR_ERR_UNSUPPORTED,
            "V = %lld above the top-k limit of %lld for this logit dtype and k",
@@ -371,6 +380,13 @@ tr_status tr_update_topk(const tr_tree* t, int32_t B, const void* logits, tr_dty
   tail.m_is64 = m_dtype == TR_INT64;
   tail.M = M;
   tail.tree_tok = const_cast<int32_t*>(tree_tok);
+  if (M && few_row_step_enabled()) {
+    const tr::StepPlan sp = tr::plan_step(B, t->dev, V, k, l_dtype == TR_BFLOAT16 ? 2 : 4, false, tail);
+    if (sp.use)
+      return hip_status(tr::launch_step(t->dev, logits, l_dtype == TR_BFLOAT16, V, k, ids, tail, w,
+                                        sp, hipStream_t(stream)),
+                        "tr_update_topk");
+  }
   return hip_status(tr::launch_topk(t->dev, B, logits, l_dtype == TR_BFLOAT16, V, k, ids, tail, w,
                                     plan, hipStream_t(stream)),
                     "tr_update_topk");
@@ -500,6 +516,13 @@ tr_status step_impl(const tr_tree* t, int32_t B, int64_t V, int32_t k, const voi
       e = tr::launch_lmhead_merge(t->dev, rows, part, lplan.nvs, V, k, ids, tail, w,
                                   hipStream_t(stream));
     return hip_status(e, "tr_step_lmhead");
+  }
+  if (few_row_step_enabled()) {
+    const tr::StepPlan sp = tr::plan_step(B, t->dev, V, k, l_dtype == TR_BFLOAT16 ? 2 : 4, sample, tail);
+    if (sp.use)
+      return hip_status(tr::launch_step(t->dev, logits, l_dtype == TR_BFLOAT16, V, k, ids, tail, w,
+                                        sp, hipStream_t(stream)),
+                        "tr_step");
   }
   return hip_status(tr::launch_topk(t->dev, B, logits, l_dtype == TR_BFLOAT16, V, k, ids, tail, w,
                                     plan, hipStream_t(stream)),

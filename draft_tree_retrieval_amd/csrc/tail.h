@@ -27,6 +27,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 constexpr int kMapSlots = 512;          // LDS map: 128 groups of 4 slots
+constexpr int kSpinLimit = 1 << 22;     // polls before a hand-over wait gives up (seconds)
 
 struct TailShared {
   uint64_t anc[kMaxNodes][2];           // bit m of anc[n]: m lies on the path root..n (n included)
@@ -331,22 +332,15 @@ __device__ __forceinline__ bool tail_commit_fits(const TailShared& S, const Tail
   return a.k_cache && S.P >= 0 && int64_t(S.P) + L + 1 <= a.cap;
 }
 
-// Copy of the key/value rows of path[0..L] to cache positions P..P+L by
-// the threads [first, blockDim.x), R 16-byte units per thread in flight;
-// thread first raises the flag when they do not fit (tail_commit_fits).
-// S.L (verification) and S.P (tail_load) must be visible.  A paged cache
+// Copy of the key/value rows of path[0..L] (LDS) to cache positions
+// P..P+L: 16-byte units me, me + count, ... of the copy, R units per thread
+// in flight.  The caller has checked that the rows fit.  A paged cache
 // copies every layer's rows, each position into row p % page_size of page
 // table[b][p / page_size] of that layer's pool.
-__device__ __forceinline__ void tail_commit(const TailShared& S, const TreeDev& tree, int b,
-                                            const TailArgs& a, uint8_t* ws, int first) {
-  const int me = int(threadIdx.x) - first, count = int(blockDim.x) - first;
-  if (!a.k_cache || me < 0) return;
-  const int64_t P = S.P;
-  const int nrows = S.L + 1;
-  if (P < 0 || P + nrows > a.cap) {
-    if (me == 0) set_flag(ws, TR_FLAG_CACHE_FULL);
-    return;
-  }
+__device__ __forceinline__ void commit_rows(const int32_t* path, int L, int64_t P,
+                                            const TreeDev& tree, int b, const TailArgs& a,
+                                            uint8_t* ws, int me, int count) {
+  const int nrows = L + 1;
   const bool paged = a.paged.table != nullptr;
   const int upr = a.row_bytes >> 4;               // 16-byte units per row
   const int per_node = a.Hkv * upr;
@@ -366,7 +360,7 @@ __device__ __forceinline__ void tail_commit(const TailShared& S, const TreeDev& 
       const int uu = isv ? ul - per_layer / 2 : ul;
       const int i = uu / per_node, rem = uu - i * per_node;
       const int h = rem / upr, c = rem - h * upr;
-      const int node = S.path[i];
+      const int node = path[i];
       const uint8_t* src = (isv ? a.v_tree : a.k_tree) + layer * a.tree_layer_bytes +
                            ((int64_t(b) * tree.T + node) * a.Hkv + h) * a.row_bytes + c * 16;
       if (paged) {
@@ -394,6 +388,21 @@ __device__ __forceinline__ void tail_commit(const TailShared& S, const TreeDev& 
   }
 }
 
+// The commit of sequence b by the threads [first, blockDim.x); thread first
+// raises the flag when the rows do not fit (tail_commit_fits).  S.L
+// (verification) and S.P (tail_load) must be visible.
+__device__ __forceinline__ void tail_commit(const TailShared& S, const TreeDev& tree, int b,
+                                            const TailArgs& a, uint8_t* ws, int first) {
+  const int me = int(threadIdx.x) - first, count = int(blockDim.x) - first;
+  if (!a.k_cache || me < 0) return;
+  const int64_t P = S.P;
+  if (P < 0 || P + S.L + 1 > a.cap) {
+    if (me == 0) set_flag(ws, TR_FLAG_CACHE_FULL);
+    return;
+  }
+  commit_rows(S.path, S.L, P, tree, b, a, ws, me, count);
+}
+
 // Draft tree retrieval: nxt[0] = root; layer by layer
 // nxt[n] = M[nxt[parent n]][rank n].  Run by one wave (nodes lane and
 // lane + 64).  With use_map, rows written by this block's update come from
@@ -405,11 +414,17 @@ __device__ __forceinline__ void tail_commit(const TailShared& S, const TreeDev& 
 // chain short: the nodes' template data sit in registers, both nodes of a
 // lane are resolved side by side, and each layer's M load leaves before
 // the map probe that may make it unnecessary.
+//
+// With mail (the few-row step kernel), S.topk holds only each node's
+// greedy token (rank 0) when the retrieval starts: a map hit's other ranks
+// are read from the mailbox word its row block publishes (bit 31 set once
+// written), waiting for it if need be (bounded: TR_FLAG_HANDOVER).
 template <typename MT>
 __device__ __forceinline__ void tail_retrieve(TailShared& S, const TreeDev& tree, int32_t root,
                                               const void* M_b, int64_t V, int32_t k,
                                               int32_t* out_b, uint8_t* ws, bool use_map,
-                                              bool use_pre = false) {
+                                              bool use_pre = false,
+                                              const uint32_t* mail = nullptr) {
   const int lane = threadIdx.x & 63;
   int n[2], dep[2], par[2], rnk[2];
 #pragma unroll
@@ -443,8 +458,11 @@ __device__ __forceinline__ void tail_retrieve(TailShared& S, const TreeDev& tree
       for (int h = 0; h < 2; ++h)
         mv[h] = reinterpret_cast<const MT*>(M_b)[pv[h] ? int64_t(p[h]) * k + rnk[h] : 0];
     }
+    // the home group only; a full group without the token (rare) is
+    // probed further below, after the M load has been waited for: a loop
+    // here would make the compiler wait for that load before entering it
+    uint32_t g[2] = {0u, 0u};
     if (use_map) {
-      uint32_t g[2];
       i32x4 keys[2], vals[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -453,10 +471,7 @@ __device__ __forceinline__ void tail_retrieve(TailShared& S, const TreeDev& tree
         vals[h] = reinterpret_cast<const i32x4*>(S.hval)[g[h]];
       }
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        w[h] = pv[h] ? group_find(keys[h], vals[h], p[h]) : -1;
-        if (w[h] == -2) w[h] = map_get_from(S, p[h], (g[h] + 1) & uint32_t(kMapSlots / 4 - 1));
-      }
+      for (int h = 0; h < 2; ++h) w[h] = pv[h] ? group_find(keys[h], vals[h], p[h]) : -1;
     } else {
       w[0] = w[1] = -1;
     }
@@ -464,6 +479,27 @@ __device__ __forceinline__ void tail_retrieve(TailShared& S, const TreeDev& tree
     for (int h = 0; h < 2; ++h) {
       const int32_t* src = w[h] >= 0 ? S.topk + w[h] * k : S.pre + pre_row;
       alt[h] = src[rnk[h]];
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (w[h] == -2) {
+        w[h] = map_get_from(S, p[h], (g[h] + 1) & uint32_t(kMapSlots / 4 - 1));
+        alt[h] = (w[h] >= 0 ? S.topk + w[h] * k : S.pre + pre_row)[rnk[h]];
+      }
+    }
+    if (mail) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (dep[h] != d || w[h] < 0 || rnk[h] == 0) continue;
+        const uint32_t* word = mail + w[h] * k + rnk[h];
+        uint32_t v = 0;
+        for (int spin = 0; spin <= kSpinLimit; ++spin) {
+          v = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (v >> 31) break;
+        }
+        if ((v >> 31) == 0u) set_flag(ws, TR_FLAG_HANDOVER);
+        alt[h] = (v >> 31) ? int32_t(v & 0x7FFFFFFFu) : -1;
+      }
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {

@@ -46,7 +46,12 @@ constexpr size_t kSeqCntOff = 256;                    // uint32 [<= 4096]
 constexpr size_t kMaxSeqCnt = 4096;
 constexpr size_t kRowCntOff = kSeqCntOff + 4 * kMaxSeqCnt;   // uint32 [<= 32768]
 constexpr size_t kMaxRowCnt = 32768;
+// the greedy step for few rows (k_step.hip):
+constexpr size_t kMailOff = kRowCntOff + 4 * kMaxRowCnt;       // uint32 [< 256 rows][k]: ids | 1 << 31
+constexpr size_t kVerdictOff = kMailOff + 4 * 256 * 16;        // uint64 [<= 256 sequences]
+constexpr size_t kCommitCntOff = kVerdictOff + 8 * 256;        // uint32 [<= 256 sequences]
 constexpr size_t kDataOff = 256 * 1024;
+static_assert(kCommitCntOff + 4 * 256 <= kDataOff, "workspace counter region");
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -153,6 +158,22 @@ void prof_end(hipStream_t s);
 hipError_t launch_topk(const TreeDev& tree, int32_t B, const void* logits, int l_is_bf16, int64_t V,
                        int32_t k, int32_t* topk_ids, const TailArgs& tail, uint8_t* ws,
                        const TopkPlan& plan, hipStream_t s);
+// The greedy step for few rows: one block per logit row, one tail block per
+// sequence, `commit` commit blocks per sequence (0 without a cache), then
+// M-prefetch helpers on each tail block's XCD.
+constexpr int kMaxStepSeq = 256;
+constexpr int64_t kStepMaxV = 32768;
+struct StepPlan {
+  bool use;
+  int32_t rows, B, commit;
+  int32_t helpers, help_base;   // M-prefetch helper blocks per sequence, first helper-region block
+  int32_t grid;
+};
+StepPlan plan_step(int32_t B, const TreeDev& tree, int64_t V, int32_t k, int32_t esz, bool sample,
+                   const TailArgs& tail);
+hipError_t launch_step(const TreeDev& tree, const void* logits, int l_is_bf16, int64_t V,
+                       int32_t k, int32_t* topk_ids, const TailArgs& tail, uint8_t* ws,
+                       const StepPlan& plan, hipStream_t s);
 // Fused LM head + top-k: slices of 128 vocabulary rows, 8 keys per (row,
 // slice), then one merge block per row.
 struct LmheadPlan {

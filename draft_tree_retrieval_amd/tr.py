@@ -21,6 +21,7 @@ TR_OK, TR_ERR_INVALID_ARGUMENT, TR_ERR_UNSUPPORTED, TR_ERR_INVALID_TREE, \
     TR_ERR_WORKSPACE_TOO_SMALL, TR_ERR_HIP = range(6)
 TR_INT32, TR_INT64, TR_FLOAT32, TR_BFLOAT16 = range(4)
 TR_FLAG_BAD_TOKEN, TR_FLAG_CACHE_FULL, TR_FLAG_BAD_PREFIX, TR_FLAG_BAD_PAGE = 1, 2, 4, 8
+TR_FLAG_HANDOVER = 16
 
 _DT = {torch.int32: TR_INT32, torch.int64: TR_INT64, torch.float32: TR_FLOAT32,
        torch.bfloat16: TR_BFLOAT16}

@@ -30,7 +30,11 @@
  *     a token outside [0, V) (TR_FLAG_BAD_TOKEN), a commit that would
  *     overflow the cache capacity (TR_FLAG_CACHE_FULL) and a prefix_len
  *     outside [0, cap] given to tr_tree_attn (TR_FLAG_BAD_PREFIX; the
- *     length is clamped to that range).
+ *     length is clamped to that range).  TR_FLAG_HANDOVER reports that a
+ *     wait of one block of a launch for another gave up (bounded at about
+ *     seconds; it does not occur in normal operation): that call's outputs
+ *     are unspecified and the workspace must be zeroed again
+ *     (tr_workspace_init).
  *   - Tie and duplicate rules (fixed here; the pages leave them open):
  *     top-k orders by value descending, then token id ascending, with
  *     -0.0 == +0.0; when two tree nodes carry the same token, the node with
@@ -67,7 +71,7 @@ typedef enum {
 typedef enum { TR_INT32 = 0, TR_INT64 = 1, TR_FLOAT32 = 2, TR_BFLOAT16 = 3 } tr_dtype;
 
 enum { TR_FLAG_BAD_TOKEN = 1u, TR_FLAG_CACHE_FULL = 2u, TR_FLAG_BAD_PREFIX = 4u,
-       TR_FLAG_BAD_PAGE = 8u };
+       TR_FLAG_BAD_PAGE = 8u, TR_FLAG_HANDOVER = 16u };
 
 /* Opaque, immutable draft-tree template (host memory, library-owned).
  * Shareable across streams and threads. */
@@ -232,7 +236,13 @@ tr_status tr_verify(const tr_tree* t, int32_t B, const int32_t* topk, int32_t k,
  *   kv_dtype; prefix_len [B] in/out: rows path[0..L] are copied to cache
  *   positions prefix_len .. prefix_len+L and prefix_len grows by L+1.
  *   If k_cache is NULL no commit is done.
- *   topk_out  [B][T][k] (nullable). */
+ *   topk_out  [B][T][k] (nullable).
+ * With fewer than 256 logit rows (B*T) of at most 32768 logits, the step
+ * runs as one launch of row blocks, a tail block per sequence and copy
+ * blocks that wait for one another through the workspace; setting the
+ * environment variable TR_FEW_ROW_STEP=0 selects the general kernel
+ * instead (same results; a diagnostic switch).  tr_update_topk with M
+ * follows the same rule. */
 tr_status tr_step(const tr_tree* t, int32_t B, int64_t V, int32_t k, const void* logits,
                   tr_dtype l_dtype, void* M, tr_dtype m_dtype, int32_t* tree_tok, int32_t* root_tok,
                   int32_t* accept_len, int32_t* accept_path, int32_t* emitted, int32_t Hkv,
