@@ -85,8 +85,20 @@ def parse():
 KERNEL_SOURCES = {
     "attn_prefix": ("attn_prefix", ["k_attn.hip", "dev_common.h", "tr_internal.h"]),
     "attn_combine": ("attn_merge", ["k_attn.hip", "dev_common.h", "tr_internal.h"]),
-    "topk": ("topk_kernel", ["k_topk.hip", "tail.h", "sample.h", "dev_common.h", "tr_internal.h"]),
+    "topk": ("topk_kernel", ["k_topk.hip", "select.h", "tail.h", "sample.h", "dev_common.h",
+                             "tr_internal.h"]),
+    "step": ("step_kernel", ["k_step.hip", "select.h", "tail.h", "dev_common.h", "tr_internal.h"]),
 }
+STEP_MAX_V = 32768          # the few-row step kernel: fewer than 256 rows of at most this many logits
+
+
+def record_kernel(w, kernel):
+    """The counter-record name of timed kernel `kernel` on workload w: the
+    step's top-k launch is the few-row step kernel when B*T < 256 and
+    V <= 32768 (greedy verification), the general top-k kernel otherwise."""
+    if kernel == "topk" and w.B * w.T < 256 and w.V <= STEP_MAX_V:
+        return "step"
+    return kernel
 
 
 def kernel_sources_sha256(kernel):
@@ -487,13 +499,13 @@ def main():
         achieved = dbytes / (dms * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    roof["traffic"] = measured_traffic(args.workload, dom)
+    roof["traffic"] = measured_traffic(args.workload, record_kernel(w, dom))
     roof["timing"] = "cold (1 GiB scrub before every call)" if cold_ms else "warm"
     # both roofs of the dominant kernel, and its matrix-core counters
     roof["hbm_GB_s"] = round(dbytes / (dms * 1e-3) / 1e9, 1)
     if dom in kflops:
         roof["mfma_TFLOP_s"] = round(kflops[dom] / (dms * 1e-3) / 1e12, 1)
-    roof["mfma_counters"] = measured_mfma(args.workload, dom)
+    roof["mfma_counters"] = measured_mfma(args.workload, record_kernel(w, dom))
     probe = read_probe(tr)
     roof["achievable_read_GB_s"] = probe
     log(f"read probe: {probe} GB/s; mean accepted drafts {L_mean:.3f}, emitted/step {L_mean + 1:.3f}")

@@ -85,6 +85,16 @@ def test_kernel_trace_summaries_name_their_command():
     for path in paths:
         text = open(path).read()
         assert "rocprofv3 --kernel-trace --stats" in text and "bench.py" in text
-        # the three kernels of a step appear in it
-        for name in ("attn_prefix_bf16", "topk_kernel", "attn_merge_bf16"):
+        # the three kernels of a step appear in it (the top-k launch is the
+        # few-row step kernel on the single-sequence workloads)
+        for name in ("attn_prefix_bf16", "attn_merge_bf16"):
             assert name in text, (path, name)
+        assert "topk_kernel" in text or "step_kernel" in text, path
+
+
+def test_top_k_launch_maps_to_its_kernel_record():
+    from synth import workloads as W
+    assert bench.record_kernel(W.WORKLOADS["vicuna7b"], "topk") == "step"
+    assert bench.record_kernel(W.WORKLOADS["codellama34b"], "topk") == "step"
+    assert bench.record_kernel(W.WORKLOADS["largevocab"], "topk") == "topk"     # 2592 rows
+    assert bench.record_kernel(W.WORKLOADS["vicuna7b"], "attn_prefix") == "attn_prefix"
