@@ -387,6 +387,234 @@ __device__ __forceinline__ void step_row(const void* __restrict__ logits, int64_
 }
 
 // ---------------------------------------------------------------- tail
+// Per-launch LDS of the tail block beyond the shared tail state: the
+// update map as a direct table (token -> node whose top-k row M now holds
+// for it; 0xFF none), the nodes in layer order as packed descriptors
+// (node | parent << 8 | rank << 16) with each layer's first index, and a
+// flag per node once its whole top-k row is in S.topk.
+struct StepShared {
+  alignas(16) uint8_t wtab[kStepMaxV];
+  uint32_t desc[kMaxNodes];
+  int32_t lst[kMaxNodes + 2];
+  uint8_t pos[kMaxNodes];        // a node's index within its layer's list
+  uint32_t rowok[kMaxNodes];
+  int32_t narrow;                // every layer fits in one wave (and D + 2 <= 64)
+};
+
+// The direct map table from the hash map the claims built (one wave; nodes
+// lane, lane+64): the winner of each token writes itself.
+__device__ __forceinline__ void step_map_table(const TailShared& S, StepShared& X,
+                                               const TreeDev& tree, int64_t V) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int n = lane + 64 * h;
+    const int32_t t = n < tree.T ? S.tok[n] : -1;
+    if (t >= 0 && int64_t(t) < V && map_get(S, t) == n) X.wtab[t] = uint8_t(n);
+  }
+}
+
+// The layer lists from the template in LDS (wave 0; nodes lane, lane+64).
+__device__ __forceinline__ void step_layers(const TailShared& S, StepShared& X, const TreeDev& tree) {
+  const int lane = threadIdx.x & 63;
+  int dep[2];
+  uint32_t dsc[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int n = lane + 64 * h;
+    const bool in = n < tree.T;
+    dep[h] = in ? S.dep[n] : -1;
+    dsc[h] = in ? uint32_t(n) | (uint32_t(S.par[n] == 0xFF ? 0 : S.par[n]) << 8) |
+                      (uint32_t(S.rnk[n]) << 16) : 0u;
+  }
+  int at = 0, widest = 0;
+  int idx[2] = {-1, -1};                               // each node's place in the lists
+  for (int d = 1; d <= tree.D; ++d) {
+    if (lane == 0) X.lst[d] = at;
+    const int start = at;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint64_t m = __ballot(dep[h] == d);
+      const int below = int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
+      if (dep[h] == d) {
+        idx[h] = at + below;
+        X.pos[lane + 64 * h] = uint8_t(at + below - start);
+      }
+      at += __popcll(m);
+    }
+    widest = max(widest, at - start);
+  }
+  if (lane == 0) {
+    X.lst[tree.D + 1] = at;
+    X.pos[0] = 0;
+    X.narrow = (widest <= 64 && tree.D + 2 <= 64) ? 1 : 0;
+  }
+  wave_lds_sync();
+  // descriptors, with the parent's place in its layer in bits 24..31
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    if (idx[h] >= 0) X.desc[idx[h]] = dsc[h] | (uint32_t(X.pos[(dsc[h] >> 8) & 0xFFu]) << 24);
+}
+
+// The value of node n at layer d > 1 from its parent token p (valid or
+// not), its rank, and the M entry mv loaded for it: a map hit's row (from
+// LDS once its flag is set, else from the mailbox), the root's prefetched
+// row at layer 1, else M.  Shared by both retrieval loops.
+template <typename MT>
+__device__ __forceinline__ int32_t step_value(TailShared& S, const StepShared& X, int d, int32_t p,
+                                              bool pv, int rnk, MT mv, int pre_row, int32_t k,
+                                              int64_t V, const uint32_t* mail, uint8_t* ws,
+                                              bool& bad) {
+  const uint32_t wt = X.wtab[pv ? p : 0];
+  const int w = pv && wt != 0xFFu ? int(wt) : -1;
+  const bool late = w >= 0 && rnk > 0 &&
+                    __hip_atomic_load(&X.rowok[w], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0u;
+  int32_t alt = (w >= 0 ? S.topk + w * k : S.pre + pre_row)[rnk];
+  if (__ballot(late) != 0 && late) {
+    // the row may have reached LDS since the first look: read it there
+    // then (the value read before its flag was set is not the row's)
+    if (__hip_atomic_load(&X.rowok[w], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 0u) {
+      alt = S.topk[w * k + rnk];
+    } else {
+      const uint32_t* word = mail + w * k + rnk;
+      uint32_t v = 0;
+      for (int spin = 0; spin <= kSpinLimit; ++spin) {
+        v = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (v >> 31) break;
+      }
+      if ((v >> 31) == 0u) set_flag(ws, TR_FLAG_HANDOVER);
+      alt = (v >> 31) ? int32_t(v & 0x7FFFFFFFu) : -1;
+    }
+  }
+  const int64_t v = !pv ? -1 : (w >= 0 || d == 1) ? int64_t(alt) : int64_t(mv);
+  const bool ok = v >= 0 && v < V;
+  bad = bad || (p >= 0 && !pv) || (pv && !ok);
+  return ok ? int32_t(v) : -1;
+}
+
+// The next draft tree when every layer fits in one wave: lane i holds the
+// value of the i-th node of the current layer in a register, and a node
+// takes its parent's token from the parent's lane (a cross-lane permute),
+// so a layer's chain is: permute, then the M entry and the map table
+// together, then the hit's value.  The tokens also go to S.nxt for the
+// output, off the chain.
+template <typename MT>
+__device__ __forceinline__ void step_retrieve_narrow(TailShared& S, const StepShared& X,
+                                                     const TreeDev& tree, int32_t root,
+                                                     const void* M_b, int64_t V, int32_t k,
+                                                     int32_t* out_b, uint8_t* ws,
+                                                     const uint32_t* mail) {
+  const int lane = threadIdx.x & 63;
+  const int pre_row = S.best * k;
+  const int D = tree.D;
+  const int lstv = lane <= D + 1 ? X.lst[lane] : 0;     // lane d: layer d's first index
+  bool bad = lane == 0 && (root < 0 || int64_t(root) >= V);
+  if (lane == 0) S.nxt[0] = root;
+  int32_t val = root;                                  // the previous layer's tokens, by place
+  int beg = __builtin_amdgcn_readlane(lstv, 1), end = __builtin_amdgcn_readlane(lstv, 2);
+  uint32_t desc = D >= 1 && lane < end - beg ? X.desc[beg + lane] : 0u;
+  for (int d = 1; d <= D; ++d) {
+    const bool act = lane < end - beg;
+    const uint32_t dsc = desc;
+    // the next layer's descriptors, off the chain
+    if (d < D) {
+      const int nb = __builtin_amdgcn_readlane(lstv, d + 1), ne = __builtin_amdgcn_readlane(lstv, d + 2);
+      desc = lane < ne - nb ? X.desc[nb + lane] : 0u;
+      beg = nb;
+      end = ne;
+    }
+    const int n = int(dsc & 0xFFu), rnk = int((dsc >> 16) & 0xFFu), ppos = int(dsc >> 24);
+    const int32_t pp = __shfl(val, ppos, 64);
+    const int32_t p = act ? (d == 1 ? root : pp) : -1;
+    const bool pv = p >= 0 && int64_t(p) < V;
+    MT mv = MT(0);
+    if (d > 1) mv = reinterpret_cast<const MT*>(M_b)[pv ? int64_t(p) * k + rnk : 0];
+    const int32_t v = step_value<MT>(S, X, d, p, pv, rnk, mv, pre_row, k, V, mail, ws, bad);
+    if (act) S.nxt[n] = v;
+    val = v;
+  }
+  if (bad) set_flag(ws, TR_FLAG_BAD_TOKEN);
+  wave_lds_sync();
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    if (lane + 64 * h < tree.T) out_b[lane + 64 * h] = S.nxt[lane + 64 * h];
+}
+
+// The next draft tree: nxt[0] = root, then layer by layer nxt[n] =
+// M'[nxt[parent n]][rank n], M' = M after this step's update (Chinese
+// summary, Method, draft retrieval).  Wave 0, one node of the layer per
+// lane (more passes for a layer wider than 64).
+//
+// The layers are a chain of dependent reads, so a layer's common path is
+// short: the node's descriptor (read ahead, off the chain); the parent's
+// token; then, together, its M row entry (from the L2 the helper blocks
+// filled) and its entry in the direct map table; then the value a map hit
+// or the root's prefetched row supplies.  A map hit's row is in LDS once
+// waves 1..3 have it (rowok set after the row); a hit whose row is not in
+// yet reads its word from the mailbox (the slow path: one wave-uniform
+// branch).  Bad tokens set the flag once, after the loop.
+template <typename MT>
+__device__ __forceinline__ void step_retrieve(TailShared& S, const StepShared& X,
+                                              const TreeDev& tree, int32_t root, const void* M_b,
+                                              int64_t V, int32_t k, int32_t* out_b, uint8_t* ws,
+                                              const uint32_t* mail) {
+  const int lane = threadIdx.x & 63;
+  const int pre_row = S.best * k;
+  if (lane == 0) S.nxt[0] = root;
+  bool bad = lane == 0 && (root < 0 || int64_t(root) >= V);
+  uint32_t desc = 0u;
+  if (tree.D >= 1) desc = X.lst[1] + lane < X.lst[2] ? X.desc[X.lst[1] + lane] : 0u;
+  wave_lds_sync();
+  for (int d = 1; d <= tree.D; ++d) {
+    const int beg = X.lst[d], end = X.lst[d + 1];
+    for (int base = beg; base < end; base += 64) {
+      const bool act = base + lane < end;
+      const uint32_t dsc = base == beg ? desc : (act ? X.desc[base + lane] : 0u);
+      const int n = int(dsc & 0xFFu), par = int((dsc >> 8) & 0xFFu), rnk = int((dsc >> 16) & 0xFFu);
+      const int32_t p = act ? S.nxt[par] : -1;
+      const bool pv = p >= 0 && int64_t(p) < V;
+      MT mv = MT(0);
+      if (d > 1) mv = reinterpret_cast<const MT*>(M_b)[pv ? int64_t(p) * k + rnk : 0];
+      const uint32_t wt = X.wtab[pv ? p : 0];
+      const int w = pv && wt != 0xFFu ? int(wt) : -1;
+      const bool late = w >= 0 && rnk > 0 &&
+                        __hip_atomic_load(&X.rowok[w], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0u;
+      int32_t alt = (w >= 0 ? S.topk + w * k : S.pre + pre_row)[rnk];
+      if (__ballot(late) != 0 && late) {
+        // the row may have reached LDS since the first look: read it there
+        // then (the value read before its flag was set is not the row's)
+        if (__hip_atomic_load(&X.rowok[w], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 0u) {
+          alt = S.topk[w * k + rnk];
+        } else {
+          const uint32_t* word = mail + w * k + rnk;
+          uint32_t v = 0;
+          for (int spin = 0; spin <= kSpinLimit; ++spin) {
+            v = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (v >> 31) break;
+          }
+          if ((v >> 31) == 0u) set_flag(ws, TR_FLAG_HANDOVER);
+          alt = (v >> 31) ? int32_t(v & 0x7FFFFFFFu) : -1;
+        }
+      }
+      if (act) {
+        const int64_t v = !pv ? -1 : (w >= 0 || d == 1) ? int64_t(alt) : int64_t(mv);
+        const bool ok = v >= 0 && v < V;
+        bad = bad || (p >= 0 && !pv) || (pv && !ok);
+        S.nxt[n] = ok ? int32_t(v) : -1;
+      }
+    }
+    if (d < tree.D) {                                   // the next layer's first descriptors, off the chain
+      const int nb = X.lst[d + 1], ne = X.lst[d + 2];
+      desc = nb + lane < ne ? X.desc[nb + lane] : 0u;
+    }
+    wave_lds_sync();
+  }
+  if (bad) set_flag(ws, TR_FLAG_BAD_TOKEN);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    if (lane + 64 * h < tree.T) out_b[lane + 64 * h] = S.nxt[lane + 64 * h];
+}
+
 // Verdict word handed to the commit blocks: bit 63 set once written, bit 62
 // whether the accepted rows fit in the cache, bits 32..38 the accepted
 // (deepest) node, bits 0..31 the prefix length before the commit.
@@ -399,6 +627,7 @@ __device__ __forceinline__ void step_tail(const TreeDev& tree, int b, int32_t k,
                                           uint32_t* mail, const TailArgs& tail, uint8_t* ws,
                                           uint64_t* verdict, bool commit) {
   __shared__ TailShared S;
+  __shared__ StepShared X;
   const int tid = threadIdx.x, wave = tid >> 6;
   const int T = tree.T;
   const bool step = tail.mode == TAIL_STEP;
@@ -414,9 +643,24 @@ __device__ __forceinline__ void step_tail(const TreeDev& tree, int b, int32_t k,
   if (wave == 0) tail_tree_wave(S, tree);
   map_clear(S);
   if (tid < T) S.tok[tid] = tok;
+  if (tid < kMaxNodes) X.rowok[tid] = 0u;
+  if (step) {
+    for (int i = tid; i < kStepMaxV / 16; i += kStepNT)
+      reinterpret_cast<u32x4*>(X.wtab)[i] = u32x4{~0u, ~0u, ~0u, ~0u};
+  }
   if (tid == 0) S.P = P;
   __syncthreads();
-  if (wave == 1 && !path_only) tail_update_claim(S, tree, V, ws, false);
+  if (wave == 1 && !path_only) {
+    tail_update_claim(S, tree, V, ws, false);
+    if (step) {
+      wave_lds_sync();
+      step_map_table(S, X, tree, V);
+    }
+  }
+  if (wave == 0 && step) {
+    wave_lds_sync();                                   // the template tail_tree_wave wrote
+    step_layers(S, X, tree);
+  }
 
   // ---- the rows.  Whole step: thread n waits for row n's greedy token
   // g(n) (rank 0, published first), then fetches the row of M the next
@@ -476,6 +720,8 @@ __device__ __forceinline__ void step_tail(const TreeDev& tree, int b, int32_t k,
     if (path_only) {
       wave_lds_sync();
       tail_update_claim(S, tree, V, ws, true);
+      wave_lds_sync();
+      step_map_table(S, X, tree, V);
     }
   }
   if (tid < T) {
@@ -490,7 +736,10 @@ __device__ __forceinline__ void step_tail(const TreeDev& tree, int b, int32_t k,
   if (wave == 0) {
     // the next tree (loads only); a map hit's ranks come from the mailbox
     const bool fits = tail_commit_fits(S, tail, vd.L);
-    tail_retrieve<MT>(S, tree, vd.bonus, M_b, V, k, tok_b, ws, true, true, mseq);
+    if (X.narrow)
+      step_retrieve_narrow<MT>(S, X, tree, vd.bonus, M_b, V, k, tok_b, ws, mseq);
+    else
+      step_retrieve<MT>(S, X, tree, vd.bonus, M_b, V, k, tok_b, ws, mseq);
     if (tid == 0) {
       tail.root_tok[b] = vd.bonus;
       if (fits) tail.prefix_len[b] = int32_t(S.P + vd.L + 1);
@@ -520,6 +769,12 @@ __device__ __forceinline__ void step_tail(const TreeDev& tree, int b, int32_t k,
         if (ok || spin == kSpinLimit) break;
       }
       if (!ok) set_flag(ws, TR_FLAG_HANDOVER);
+      if (ok) {                                        // the row for the retrieval, then its flag
+#pragma unroll
+        for (int j = 1; j < KM; ++j)
+          if (j < k) S.topk[n * k + j] = int32_t(v[j] & 0x7FFFFFFFu);
+        __hip_atomic_store(&X.rowok[n], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
       const int32_t t = S.tok[n];
       if (ok && t >= 0 && int64_t(t) < V && map_get(S, t) == n) {
         m_store<MT>(M_b, int64_t(t) * k, S.topk[n * k]);
