@@ -1,10 +1,13 @@
 """Python binding of libtr (the C ABI in include/tr.h).
 
 Argument marshalling only: every function takes torch tensors (device
-memory), checks nothing the library does not check itself beyond deriving
-sizes from tensor shapes, and calls the entry point of the same name.  All
-work runs in the HIP kernels of libtr.so; there is no fallback.  A missing
-or unloadable library raises at import of this module's first call.
+memory), derives the sizes the C call takes from their shapes, checks that
+every tensor has the shape, dtype, layout (contiguous) and device the call
+assumes (ValueError before anything reaches the library: a mismatched
+tensor would otherwise be read or written out of bounds on the device), and
+calls the entry point of the same name.  All work runs in the HIP kernels
+of libtr.so; there is no fallback.  A missing or unloadable library raises
+at the first call.
 """
 from __future__ import annotations
 
@@ -112,7 +115,14 @@ def _check(status):
 
 
 def _ptr(t):
-    return None if t is None else C.c_void_p(t.data_ptr())
+    """The device address of t for the C call (None: NULL); every tensor the
+    library receives passes here, after the call's shape checks."""
+    if t is None:
+        return None
+    if t.device.type != "cuda":
+        raise ValueError(f"a {list(t.shape)} {t.dtype} tensor is in {t.device} memory; "
+                         "libtr takes GPU memory")
+    return C.c_void_p(t.data_ptr())
 
 
 def _stream(stream):
@@ -123,6 +133,72 @@ def _stream(stream):
 
 def _dt(t):
     return _DT[t.dtype]
+
+
+_INT = (torch.int32, torch.int64)
+_FLT = (torch.float32, torch.bfloat16)
+_BF16 = (torch.bfloat16,)
+_I32T = (torch.int32,)
+
+
+def _arg(t, name, shape, dtypes, nullable=False):
+    """Checks tensor argument `name`: shape (ints; None matches any extent),
+    dtype and contiguity (the device when it is marshalled, in _ptr).  None
+    passes only where nullable."""
+    if t is None:
+        if nullable:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if len(t.shape) != len(shape) or any(w is not None and int(g) != int(w)
+                                         for g, w in zip(t.shape, shape)):
+        want = "[" + "][".join("*" if w is None else str(int(w)) for w in shape) + "]"
+        raise ValueError(f"{name} has shape {list(t.shape)}, expected {want}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {[str(d) for d in dtypes]}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _same_dtype(*named):
+    """All non-None tensors of (name, tensor) pairs share the first one's dtype."""
+    ts = [(n, t) for n, t in named if t is not None]
+    for n, t in ts[1:]:
+        if t.dtype != ts[0][1].dtype:
+            raise ValueError(f"{n} has dtype {t.dtype}, {ts[0][0]} has {ts[0][1].dtype}")
+
+
+def _ws(ws):
+    _arg(ws, "ws", [None], (torch.uint8,))
+
+
+def _step_args(tree, logits, M, tree_tok, root_tok, accept_len, accept_path, emitted, topk_out,
+               k_tree=None, v_tree=None, k_cache=None, v_cache=None, prefix_len=None):
+    """The tensors of a tr_step-family call; returns (B, T, V)."""
+    if not isinstance(logits, torch.Tensor) or logits.dim() != 3:
+        raise ValueError("logits must be a [B][T][V] tensor")
+    B, T, V = logits.shape
+    if T != tree.n_nodes:
+        raise ValueError(f"logits has {T} rows per sequence, the tree {tree.n_nodes} nodes")
+    W = tree.depth + 1
+    _arg(logits, "logits", [B, T, V], _FLT)
+    _arg(M, "M", [B, V, tree.k], _INT)
+    _arg(tree_tok, "tree_tok", [B, T], _I32T)
+    _arg(root_tok, "root_tok", [B], _I32T)
+    _arg(accept_len, "accept_len", [B], _I32T)
+    _arg(accept_path, "accept_path", [B, W], _I32T, nullable=True)
+    _arg(emitted, "emitted", [B, W], _I32T, nullable=True)
+    _arg(topk_out, "topk_out", [B, T, tree.k], _I32T, nullable=True)
+    if k_cache is not None:
+        _arg(k_cache, "k_cache", [B, None, None, None], _FLT)
+        Hkv, cap, d = k_cache.shape[1:]
+        _arg(v_cache, "v_cache", [B, Hkv, cap, d], _FLT)
+        _arg(k_tree, "k_tree", [B, T, Hkv, d], _FLT)
+        _arg(v_tree, "v_tree", [B, T, Hkv, d], _FLT)
+        _arg(prefix_len, "prefix_len", [B], _I32T)
+        _same_dtype(("k_cache", k_cache), ("v_cache", v_cache), ("k_tree", k_tree), ("v_tree", v_tree))
+    return B, T, V
 
 
 class Tree:
@@ -174,6 +250,7 @@ def tr_workspace_size(tree, B, V=0, k=0, Hq=0, Hkv=0, d=0, cap=0):
 
 
 def tr_workspace_init(ws, stream=None):
+    _ws(ws)
     _check(load().tr_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
@@ -186,22 +263,45 @@ def new_workspace(tree, B, V=0, k=0, Hq=0, Hkv=0, d=0, cap=0, device="cuda", str
 
 
 def tr_read_device_status(ws, stream=None):
+    _ws(ws)
     flags = C.c_uint32()
     _check(load().tr_read_device_status(_ptr(ws), C.byref(flags), _stream(stream)))
     return flags.value
 
 
 def tr_retrieve(tree, M, root_tok, tree_tok, ws, stream=None):
+    if not isinstance(M, torch.Tensor) or M.dim() != 3:
+        raise ValueError("M must be a [B][V][k] tensor")
     B, V, k = M.shape
+    _arg(M, "M", [B, V, tree.k], _INT)
+    _arg(root_tok, "root_tok", [B], _I32T)
+    _arg(tree_tok, "tree_tok", [B, tree.n_nodes], _I32T)
+    _ws(ws)
     _check(load().tr_retrieve(tree.handle, B, _ptr(M), _dt(M), V, k, _ptr(root_tok), _ptr(tree_tok),
                               _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def tr_tree_attn(tree, q, k_tree, v_tree, k_cache, v_cache, prefix_len, out, ws, scale=None,
                  stream=None):
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a [B][T][Hq][d] tensor")
+    if not isinstance(k_cache, torch.Tensor) or k_cache.dim() != 4:
+        raise ValueError("k_cache must be a [B][Hkv][cap][d] tensor")
     B, T, Hq, d = q.shape
-    Hkv = k_tree.shape[2]
+    Hkv = k_cache.shape[1]
     cap = k_cache.shape[2]
+    if T != tree.n_nodes:
+        raise ValueError(f"q has {T} rows per sequence, the tree {tree.n_nodes} nodes")
+    _arg(q, "q", [B, T, Hq, d], _FLT)
+    _arg(k_tree, "k_tree", [B, T, Hkv, d], _FLT)
+    _arg(v_tree, "v_tree", [B, T, Hkv, d], _FLT)
+    _arg(k_cache, "k_cache", [B, Hkv, cap, d], _FLT)
+    _arg(v_cache, "v_cache", [B, Hkv, cap, d], _FLT)
+    _arg(prefix_len, "prefix_len", [B], _I32T)
+    _arg(out, "out", [B, T, Hq, d], _FLT)
+    _same_dtype(("q", q), ("k_tree", k_tree), ("v_tree", v_tree), ("k_cache", k_cache),
+                ("v_cache", v_cache), ("out", out))
+    _ws(ws)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     _check(load().tr_tree_attn(tree.handle, B, Hq, Hkv, d, _dt(q), _ptr(q), _ptr(k_tree),
@@ -213,9 +313,25 @@ def tr_tree_attn_noalloc(tree, q, k_tree, v_tree, k_cache, v_cache, prefix_len, 
                          scale=None, stream=None):
     """tr_tree_attn without a workspace (the library's per-GPU scratch);
     flags: an optional device int32 [1] the sticky TR_FLAG_* bits are OR-ed into."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a [B][T][Hq][d] tensor")
+    if not isinstance(k_cache, torch.Tensor) or k_cache.dim() != 4:
+        raise ValueError("k_cache must be a [B][Hkv][cap][d] tensor")
     B, T, Hq, d = q.shape
-    Hkv = k_tree.shape[2]
+    Hkv = k_cache.shape[1]
     cap = k_cache.shape[2]
+    if T != tree.n_nodes:
+        raise ValueError(f"q has {T} rows per sequence, the tree {tree.n_nodes} nodes")
+    _arg(q, "q", [B, T, Hq, d], _FLT)
+    _arg(k_tree, "k_tree", [B, T, Hkv, d], _FLT)
+    _arg(v_tree, "v_tree", [B, T, Hkv, d], _FLT)
+    _arg(k_cache, "k_cache", [B, Hkv, cap, d], _FLT)
+    _arg(v_cache, "v_cache", [B, Hkv, cap, d], _FLT)
+    _arg(prefix_len, "prefix_len", [B], _I32T)
+    _arg(out, "out", [B, T, Hq, d], _FLT)
+    _same_dtype(("q", q), ("k_tree", k_tree), ("v_tree", v_tree), ("k_cache", k_cache),
+                ("v_cache", v_cache), ("out", out))
+    _arg(flags, "flags", [None], (torch.int32, torch.uint32), nullable=True)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     _check(load().tr_tree_attn_noalloc(tree.handle, B, Hq, Hkv, d, _dt(q), _ptr(q), _ptr(k_tree),
@@ -237,7 +353,19 @@ class PagedKV:
     tree rows k_tree/v_tree [layers][B][T][Hkv][d], prefix_len [B] int32."""
 
     def __init__(self, k_pages, v_pages, block_table, k_tree, v_tree, prefix_len):
+        if not isinstance(k_pages, torch.Tensor) or k_pages.dim() != 5:
+            raise ValueError("k_pages must be a [layers][num_pages][Hkv][page_size][d] tensor")
+        if not isinstance(k_tree, torch.Tensor) or k_tree.dim() != 5:
+            raise ValueError("k_tree must be a [layers][B][T][Hkv][d] tensor")
         L, npg, Hkv, ps, d = k_pages.shape
+        B, T = k_tree.shape[1], k_tree.shape[2]
+        _arg(k_pages, "k_pages", [L, npg, Hkv, ps, d], _BF16)
+        _arg(v_pages, "v_pages", [L, npg, Hkv, ps, d], _BF16)
+        _arg(block_table, "block_table", [B, None], _I32T)
+        _arg(k_tree, "k_tree", [L, B, T, Hkv, d], _BF16)
+        _arg(v_tree, "v_tree", [L, B, T, Hkv, d], _BF16)
+        _arg(prefix_len, "prefix_len", [B], _I32T)
+        self.B, self.T, self.L = B, T, L
         self.tensors = (k_pages, v_pages, block_table, k_tree, v_tree, prefix_len)
         self.s = _PagedKVStruct(L, Hkv, d, _dt(k_pages), ps, npg, block_table.shape[1],
                                 _ptr(block_table), _ptr(k_pages), _ptr(v_pages), _ptr(k_tree),
@@ -249,7 +377,15 @@ class PagedKV:
 
 
 def tr_tree_attn_paged(tree, q, kv, layer, out, ws, scale=None, stream=None):
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a [B][T][Hq][d] tensor")
     B, T, Hq, d = q.shape
+    if (B, T) != (kv.B, kv.T) or T != tree.n_nodes:
+        raise ValueError(f"q is [{B}][{T}][..], the cache holds {kv.B} sequences of {kv.T} nodes, "
+                         f"the tree {tree.n_nodes} nodes")
+    _arg(q, "q", [B, T, Hq, d], _BF16)
+    _arg(out, "out", [B, T, Hq, d], _BF16)
+    _ws(ws)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     _check(load().tr_tree_attn_paged(tree.handle, B, Hq, _ptr(q), kv.ref, layer, float(scale),
@@ -259,7 +395,11 @@ def tr_tree_attn_paged(tree, q, kv, layer, out, ws, scale=None, stream=None):
 def tr_step_paged(tree, logits, M, tree_tok, root_tok, accept_len, accept_path, emitted, ws, kv,
                   topk_out=None, update="all", stream=None):
     mode = _UPDATE_MODES[update] if isinstance(update, str) else int(update)
-    B, T, V = logits.shape
+    B, T, V = _step_args(tree, logits, M, tree_tok, root_tok, accept_len, accept_path, emitted,
+                         topk_out)
+    if (B, T) != (kv.B, kv.T):
+        raise ValueError(f"logits are [{B}][{T}][..], the cache holds {kv.B} sequences of {kv.T} nodes")
+    _ws(ws)
     _check(load().tr_step_paged(tree.handle, B, V, tree.k, _ptr(logits), _dt(logits), _ptr(M),
                                 _dt(M), _ptr(tree_tok), _ptr(root_tok), _ptr(accept_len),
                                 _ptr(accept_path), _ptr(emitted), kv.ref, _ptr(topk_out), mode,
@@ -267,15 +407,33 @@ def tr_step_paged(tree, logits, M, tree_tok, root_tok, accept_len, accept_path, 
 
 
 def tr_update_topk(tree, logits, tree_tok, M, topk_out, ws, stream=None):
+    if not isinstance(logits, torch.Tensor) or logits.dim() != 3:
+        raise ValueError("logits must be a [B][T][V] tensor")
     B, T, V = logits.shape
     k = tree.k
+    if T != tree.n_nodes:
+        raise ValueError(f"logits has {T} rows per sequence, the tree {tree.n_nodes} nodes")
+    _arg(logits, "logits", [B, T, V], _FLT)
+    _arg(M, "M", [B, V, k], _INT, nullable=True)
+    _arg(tree_tok, "tree_tok", [B, T], _I32T, nullable=M is None)
+    _arg(topk_out, "topk_out", [B, T, k], _I32T, nullable=M is not None)
+    _ws(ws)
     _check(load().tr_update_topk(tree.handle, B, _ptr(logits), _dt(logits), V, k, _ptr(tree_tok),
                                  _ptr(M), _dt(M) if M is not None else TR_INT32, _ptr(topk_out),
                                  _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def tr_verify(tree, topk, tree_tok, accept_len, accept_path, bonus, emitted, stream=None):
+    if not isinstance(topk, torch.Tensor) or topk.dim() != 3:
+        raise ValueError("topk must be a [B][T][k] tensor")
     B = topk.shape[0]
+    T, W = tree.n_nodes, tree.depth + 1
+    _arg(topk, "topk", [B, T, tree.k], _I32T)
+    _arg(tree_tok, "tree_tok", [B, T], _I32T)
+    _arg(accept_len, "accept_len", [B], _I32T)
+    _arg(accept_path, "accept_path", [B, W], _I32T, nullable=True)
+    _arg(bonus, "bonus", [B], _I32T)
+    _arg(emitted, "emitted", [B, W], _I32T, nullable=True)
     _check(load().tr_verify(tree.handle, B, _ptr(topk), topk.shape[2], _ptr(tree_tok),
                             _ptr(accept_len), _ptr(accept_path), _ptr(bonus), _ptr(emitted),
                             _stream(stream)))
@@ -290,7 +448,9 @@ def _kv_shape(k_cache):
 def tr_step(tree, logits, M, tree_tok, root_tok, accept_len, accept_path, emitted, ws,
             k_tree=None, v_tree=None, k_cache=None, v_cache=None, prefix_len=None, topk_out=None,
             stream=None):
-    B, T, V = logits.shape
+    B, T, V = _step_args(tree, logits, M, tree_tok, root_tok, accept_len, accept_path, emitted,
+                         topk_out, k_tree, v_tree, k_cache, v_cache, prefix_len)
+    _ws(ws)
     Hkv, cap, d, kv_dt = _kv_shape(k_cache)
     _check(load().tr_step(tree.handle, B, V, tree.k, _ptr(logits), _dt(logits), _ptr(M), _dt(M),
                           _ptr(tree_tok), _ptr(root_tok), _ptr(accept_len), _ptr(accept_path),
@@ -309,7 +469,9 @@ def tr_step_ex(tree, logits, M, tree_tok, root_tok, accept_len, accept_path, emi
                topk_out=None, update="all", stream=None):
     """tr_step with the update chosen by name: "all" or "accepted"."""
     mode = _UPDATE_MODES[update] if isinstance(update, str) else int(update)
-    B, T, V = logits.shape
+    B, T, V = _step_args(tree, logits, M, tree_tok, root_tok, accept_len, accept_path, emitted,
+                         topk_out, k_tree, v_tree, k_cache, v_cache, prefix_len)
+    _ws(ws)
     Hkv, cap, d, kv_dt = _kv_shape(k_cache)
     _check(load().tr_step_ex(tree.handle, B, V, tree.k, _ptr(logits), _dt(logits), _ptr(M),
                              _dt(M), _ptr(tree_tok), _ptr(root_tok), _ptr(accept_len),
@@ -324,9 +486,10 @@ def tr_step_sample(tree, logits, temperature, uniforms, M, tree_tok, root_tok, a
     """tr_step verifying by sampling at `temperature` with the caller's
     uniforms [B][T][2] (float32, device)."""
     mode = _UPDATE_MODES[update] if isinstance(update, str) else int(update)
-    B, T, V = logits.shape
-    if uniforms.dtype != torch.float32 or tuple(uniforms.shape) != (B, T, 2):
-        raise ValueError("uniforms must be float32 [B][T][2]")
+    B, T, V = _step_args(tree, logits, M, tree_tok, root_tok, accept_len, accept_path, emitted,
+                         topk_out, k_tree, v_tree, k_cache, v_cache, prefix_len)
+    _arg(uniforms, "uniforms", [B, T, 2], (torch.float32,))
+    _ws(ws)
     Hkv, cap, d, kv_dt = _kv_shape(k_cache)
     _check(load().tr_step_sample(tree.handle, B, V, tree.k, _ptr(logits), _dt(logits),
                                  float(temperature), _ptr(uniforms), _ptr(M), _dt(M),
@@ -353,8 +516,14 @@ def new_lmhead_workspace(rows, V, k, device="cuda", stream=None):
 def tr_lmhead_topk(h, W, k, topk_out, ws, stream=None):
     """topk_out [rows][k] = the k best ids of h W^T per row (h [rows][H],
     W [V][H], bfloat16)."""
+    if not isinstance(h, torch.Tensor) or h.dim() != 2 or not isinstance(W, torch.Tensor) or W.dim() != 2:
+        raise ValueError("h must be [rows][H] and W [V][H]")
     rows, H = h.shape
     V = W.shape[0]
+    _arg(h, "h", [rows, H], _BF16)
+    _arg(W, "W", [V, H], _BF16)
+    _arg(topk_out, "topk_out", [rows, k], _I32T)
+    _ws(ws)
     _check(load().tr_lmhead_topk(rows, H, V, k, _ptr(h), _ptr(W), _dt(h), _ptr(topk_out),
                                  _ptr(ws), ws.numel(), _stream(stream)))
 
@@ -364,8 +533,31 @@ def tr_step_lmhead(tree, h, W, M, tree_tok, root_tok, accept_len, accept_path, e
                    topk_out=None, update="all", stream=None):
     """tr_step_ex with the LM head fused in front: h [B][T][H], W [V][H]."""
     mode = _UPDATE_MODES[update] if isinstance(update, str) else int(update)
+    if not isinstance(h, torch.Tensor) or h.dim() != 3 or not isinstance(W, torch.Tensor) or W.dim() != 2:
+        raise ValueError("h must be [B][T][H] and W [V][H]")
     B, T, H = h.shape
     V = W.shape[0]
+    if T != tree.n_nodes:
+        raise ValueError(f"h has {T} rows per sequence, the tree {tree.n_nodes} nodes")
+    _arg(h, "h", [B, T, H], _BF16)
+    _arg(W, "W", [V, H], _BF16)
+    Wd = tree.depth + 1
+    _arg(M, "M", [B, V, tree.k], _INT)
+    _arg(tree_tok, "tree_tok", [B, T], _I32T)
+    _arg(root_tok, "root_tok", [B], _I32T)
+    _arg(accept_len, "accept_len", [B], _I32T)
+    _arg(accept_path, "accept_path", [B, Wd], _I32T, nullable=True)
+    _arg(emitted, "emitted", [B, Wd], _I32T, nullable=True)
+    _arg(topk_out, "topk_out", [B, T, tree.k], _I32T, nullable=True)
+    if k_cache is not None:
+        _arg(k_cache, "k_cache", [B, None, None, None], _FLT)
+        Hk, cp, dd = k_cache.shape[1:]
+        _arg(v_cache, "v_cache", [B, Hk, cp, dd], _FLT)
+        _arg(k_tree, "k_tree", [B, T, Hk, dd], _FLT)
+        _arg(v_tree, "v_tree", [B, T, Hk, dd], _FLT)
+        _arg(prefix_len, "prefix_len", [B], _I32T)
+        _same_dtype(("k_cache", k_cache), ("v_cache", v_cache), ("k_tree", k_tree), ("v_tree", v_tree))
+    _ws(ws)
     Hkv, cap, d, kv_dt = _kv_shape(k_cache)
     _check(load().tr_step_lmhead(tree.handle, B, H, V, tree.k, _ptr(h), _ptr(W), _dt(h), _ptr(M),
                                  _dt(M), _ptr(tree_tok), _ptr(root_tok), _ptr(accept_len),
@@ -383,7 +575,14 @@ _INIT_MODES = {"zero": TR_INIT_ZERO, "random": TR_INIT_RANDOM, "prior": TR_INIT_
 def tr_init_matrix(M, mode="zero", prior=None, seed=0, stream=None):
     """Fills M [B][V][k] on the device: "zero", "random" (SplitMix64 ids,
     seeded) or "prior" (prior [1 or B][V][k] copied into every slot)."""
+    if not isinstance(M, torch.Tensor) or M.dim() != 3:
+        raise ValueError("M must be a [B][V][k] tensor")
     B, V, k = M.shape
+    _arg(M, "M", [B, V, k], _INT)
+    if prior is not None:
+        if prior.dim() != 3 or prior.shape[0] not in (1, B):
+            raise ValueError(f"prior has shape {list(prior.shape)}, expected [1 or {B}][{V}][{k}]")
+        _arg(prior, "prior", [prior.shape[0], V, k], _INT)
     m = _INIT_MODES[mode] if isinstance(mode, str) else int(mode)
     pb = prior.shape[0] if prior is not None else 0
     _check(load().tr_init_matrix(B, V, k, _ptr(M), _dt(M), m, _ptr(prior),
@@ -406,5 +605,7 @@ def tr_profile_read(max_records=16384):
 
 def tr_read_probe(src, sink, stream=None):
     """One streaming read of every byte of src (a profiling aid)."""
+    _arg(src, "src", [None] * src.dim(), None)
+    _arg(sink, "sink", [None] * sink.dim(), None)
     _check(load().tr_read_probe(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
                                 _stream(stream)))
