@@ -22,23 +22,9 @@
 // ends.  The waits are bounded all the same (TR_FLAG_HANDOVER).
 //
 // A row block (256 threads, one row of up to 32768 elements, every element
-// read once into registers) selects in four steps:
-//   1. every element becomes a flip code (an unsigned integer in the order
-//      of the values: negative values bit-inverted, others with the sign bit
-//      set; -0.0 sits one below +0.0) and every 16-byte vector keeps its
-//      largest code;
-//   2. each wave bisects over its 64 lane maxima for the k-th largest and
-//      keeps its k largest lane maxima; the block's largest code gives the
-//      greedy token (rank 0), published at once;
-//   3. T = the k-th largest of all the waves' kept maxima (lowered by one
-//      when it is +0.0's code, so that -0.0 passes with +0.0) is reached by
-//      k elements, so every one of the k best reaches it: only vectors whose
-//      maximum reaches T are looked into, and their elements at or above T
-//      go to per-wave candidate lists in LDS;
-//   4. wave 0 ranks the candidates (order codes with -0.0 == +0.0, then the
-//      lower id) in registers.
-// Rows full of ties overflow a list; the block then falls back to exact
-// per-lane insertion of every element at or above T.
+// read once into registers) selects with select_block (select.h), which
+// reports the greedy token (rank 0) as soon as the block's largest element
+// is known, before the other ranks.
 #include "select.h"
 #include "tail.h"
 
@@ -77,20 +63,6 @@ StepPlan plan_step(int32_t B, const TreeDev& tree, int64_t V, int32_t k, int32_t
 
 namespace {
 
-// Flip codes of two bfloat16 halves (16-bit arithmetic per half) or of one
-// float: unsigned order = value order, -0.0 one below +0.0.
-__device__ __forceinline__ uint32_t flip16x2(uint32_t w) {
-  const uint32_t s = __builtin_bit_cast(uint32_t, __builtin_bit_cast(i16x2, w) >> (int16_t)15);
-  return w ^ (s | 0x80008000u);
-}
-__device__ __forceinline__ uint32_t flip32(uint32_t w) {
-  return w ^ (uint32_t(int32_t(w) >> 31) | 0x80000000u);
-}
-// The order code (ord32 of dev_common.h, which merges -0.0 and +0.0) of a
-// flip code: equal for non-negative values, one more for negative ones.
-__device__ __forceinline__ uint32_t ord_of_flip16(uint32_t u) { return (u < 0x8000u ? u + 1u : u) << 16; }
-__device__ __forceinline__ uint32_t ord_of_flip32(uint32_t u) { return u < 0x80000000u ? u + 1u : u; }
-
 __device__ __forceinline__ void mail_put(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -104,286 +76,34 @@ __device__ __forceinline__ uint64_t verdict_get(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// x[i] for a per-lane i, by a binary tree of selects on the bits of i
-// (indexing the register array itself would move it to scratch memory).
-template <int N>
-__device__ __forceinline__ u32x4 pick(const u32x4 (&x)[N], int i) {
-  u32x4 a[N];
-#pragma unroll
-  for (int q = 0; q < N; ++q) a[q] = x[q];
-#pragma unroll
-  for (int s = 0, w = N; w > 1; ++s, w >>= 1) {
-    const bool up = ((i >> s) & 1) != 0;
-#pragma unroll
-    for (int q = 0; q < w / 2; ++q) a[q] = up ? a[2 * q + 1] : a[2 * q];
-  }
-  return a[0];
-}
-
 // ---------------------------------------------------------------- rows
+// A row block: the row's top-k (select_block), its greedy token published
+// first, the other ranks after; each written to the output and to the
+// mailbox word the tail block polls.
+struct StepRowOut {
+  int32_t* orow;
+  uint32_t* mrow;
+  int32_t k;
+  __device__ __forceinline__ void first(uint32_t id) const {
+    orow[0] = int32_t(id);
+    mail_put(mrow, id | 0x80000000u);
+  }
+  __device__ __forceinline__ void put(int r, uint64_t key) const {
+    if (r < 1 || r >= k) return;
+    const uint32_t id = key_id(key);
+    orow[r] = int32_t(id);
+    mail_put(mrow + r, id | 0x80000000u);
+  }
+};
+
 template <bool BF16, int KM>
 __device__ __forceinline__ void step_row(const void* __restrict__ logits, int64_t V, int32_t k,
                                          int row, int32_t* __restrict__ ids_out, uint32_t* mail) {
-  constexpr int NT = kStepNT, NW = NT / 64;
-  constexpr int ESZ = BF16 ? 2 : 4;
-  constexpr int VE = 16 / ESZ;
   constexpr int NV = BF16 ? kStepVecs : 2 * kStepVecs;   // both: kStepMaxV elements
-  static_assert(int64_t(NV) * NT * VE == kStepMaxV, "row length");
-  constexpr uint32_t kZeroPos = BF16 ? 0x8000u : 0x80000000u;   // flip code of +0.0
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint8_t* rowp = reinterpret_cast<const uint8_t*>(logits) + int64_t(row) * V * ESZ;
-
-  __shared__ uint64_t s_cand[NW * kCandW];
-  __shared__ uint64_t s_keys[NW][KM];
-  __shared__ uint64_t s_best[KM];
-  __shared__ uint32_t s_top[NW * KM];
-  __shared__ uint32_t s_mx[NW];
-  __shared__ uint32_t s_am[NW];
-  __shared__ uint32_t s_wcnt[NW];
-
-  // aligned vectors [a0, a1); fewer than VE loose elements on either side
-  const uintptr_t addr0 = reinterpret_cast<uintptr_t>(rowp);
-  int64_t a0 = int64_t(((16 - (addr0 & 15)) & 15) / ESZ);
-  if (a0 > V) a0 = V;
-  const int nv = int((V - a0) / VE);
-  const int64_t a1 = a0 + int64_t(nv) * VE;
-  // loose elements first, from clamped (always valid) indices: their use
-  // comes after the vectors', so no wait lands between the loads
-  const int64_t hid = tid, tl = a1 + tid;
-  const bool hvalid = hid < a0, tvalid = tl < V;
-  uint32_t hraw, traw;
-  if (BF16) {
-    hraw = reinterpret_cast<const uint16_t*>(rowp)[min(hid, V - 1)];
-    traw = reinterpret_cast<const uint16_t*>(rowp)[min(tl, V - 1)];
-  } else {
-    hraw = reinterpret_cast<const uint32_t*>(rowp)[min(hid, V - 1)];
-    traw = reinterpret_cast<const uint32_t*>(rowp)[min(tl, V - 1)];
-  }
-  const u32x4* vp = reinterpret_cast<const u32x4*>(rowp + a0 * ESZ);
-  u32x4 x[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int idx = i * NT + tid;
-    x[i] = idx < nv ? __builtin_nontemporal_load(vp + idx) : u32x4{0, 0, 0, 0};
-  }
-
-  // ---- 1. flip codes in place (0: no element), vector and lane maxima
-  uint32_t vm[NV];
-  uint32_t lm = 0;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const uint32_t keep = (i * NT + tid < nv) ? ~0u : 0u;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) x[i][j] = (BF16 ? flip16x2(x[i][j]) : flip32(x[i][j])) & keep;
-    if (BF16) {
-      vm[i] = max16x2(max16x2(x[i][0], x[i][1]), max16x2(x[i][2], x[i][3]));
-      lm = max16x2(lm, vm[i]);
-    } else {
-      vm[i] = max(max(x[i][0], x[i][1]), max(x[i][2], x[i][3]));
-      lm = max(lm, vm[i]);
-    }
-  }
-  const uint32_t hu = hvalid ? (BF16 ? (flip16x2(hraw) & 0xFFFFu) : flip32(hraw)) : 0u;
-  const uint32_t tu = tvalid ? (BF16 ? (flip16x2(traw) & 0xFFFFu) : flip32(traw)) : 0u;
-  if (BF16) lm = max(lm & 0xFFFFu, lm >> 16);
-  lm = max(lm, max(hu, tu));
-
-  // ---- 2. the wave's k-th largest lane maximum
-  constexpr int kBits = BF16 ? 16 : 32;
-  uint32_t lo = 0;
-#pragma unroll
-  for (int bit = kBits - 1; bit >= 0; --bit) {
-    const uint32_t c = lo | (1u << bit);
-    if (__popcll(__ballot(lm >= c)) >= k) lo = c;
-  }
-  // the wave's k largest lane maxima (those above lo, then copies of lo)
-  {
-    const uint64_t gt = __ballot(lm > lo);               // fewer than k lanes
-    const int ngt = __popcll(gt);
-    const uint32_t below =
-        __builtin_amdgcn_mbcnt_hi(uint32_t(gt >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(gt), 0u));
-    if (lm > lo) s_top[wave * KM + below] = lm;
-    if (lane >= ngt && lane < k) s_top[wave * KM + lane] = lo;
-  }
-  const uint32_t wmx = wave_max_u32(lm);
-  if (lane == 0) s_mx[wave] = wmx;
-  __syncthreads();
-  uint32_t* mrow = mail + int64_t(row) * k;
-  int32_t* orow = ids_out + int64_t(row) * k;
-
-  // ---- the greedy token (rank 0) goes out first: the tail verifies on it
-  // while the other ranks are selected.  Ma admits the block's largest code
-  // (and -0.0 with +0.0); each lane that holds such an element finds its
-  // lowest id (head, then its vectors in order, then tail), the block the
-  // lowest of those.
-  uint32_t Mx = s_mx[0];
-#pragma unroll
-  for (int w = 1; w < NW; ++w) Mx = max(Mx, s_mx[w]);
-  const uint32_t Ma = Mx == kZeroPos ? kZeroPos - 1 : Mx;
-  uint32_t inv = 0;                                    // ~id of the lane's first element >= Ma
-  if (lm >= Ma) {
-    if (hu >= Ma) {
-      inv = ~uint32_t(hid);
-    } else {
-      const uint32_t bm = BF16 ? (Ma - 1) * 0x10001u : Ma - 1;
-      uint32_t am = 0;
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const bool hit = BF16 ? (max16x2(vm[i], bm) ^ bm) != 0u : vm[i] > bm;
-        am |= hit ? (1u << i) : 0u;
-      }
-      if (am) {
-        const int i0 = __builtin_ctz(am);
-        const u32x4 v = pick<NV>(x, i0);
-        int e = 0;
-#pragma unroll
-        for (int j = 3; j >= 0; --j) {
-          if (BF16) {
-            if ((v[j] >> 16) >= Ma) e = 2 * j + 1;
-            if ((v[j] & 0xFFFFu) >= Ma) e = 2 * j;
-          } else if (v[j] >= Ma) {
-            e = j;
-          }
-        }
-        inv = ~uint32_t(a0 + int64_t(i0 * NT + tid) * VE + e);
-      } else {
-        inv = ~uint32_t(tl);
-      }
-    }
-  }
-  inv = wave_max_u32(inv);
-  if (lane == 0) s_am[wave] = inv;
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t best = s_am[0];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) best = max(best, s_am[w]);
-    orow[0] = int32_t(~best);
-    mail_put(mrow, ~best | 0x80000000u);
-  }
-
-  // ---- 3. T = the block's k-th largest lane maximum (the k-th largest of
-  // the waves' k largest): k elements reach it, so every one of the k best
-  // does.  Candidates: elements at or above T, by ballot into the lists.
-  constexpr int NTOP = NW * KM;                        // 32 or 64: one per lane
-  const uint32_t tv = (lane < NTOP && (lane % KM) < k) ? s_top[min(lane, NTOP - 1)] : 0u;
-  uint32_t T = 0;
-#pragma unroll
-  for (int bit = kBits - 1; bit >= 0; --bit) {
-    const uint32_t c = T | (1u << bit);
-    if (__popcll(__ballot(tv >= c)) >= k) T = c;
-  }
-  if (T == kZeroPos) T = kZeroPos - 1;                 // -0.0 ties with +0.0
-  if (T == 0) T = 1;                                   // 0 marks "no element"
-  uint64_t* wc = s_cand + wave * kCandW;
-  uint32_t wpos = 0;                                   // wave-uniform
-  auto put = [&](bool pred, uint32_t code, int64_t id) {
-    const uint64_t m = __ballot(pred);
-    if (m) {
-      const uint32_t off =
-          wpos + __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
-      if (pred && off < uint32_t(kCandW)) wc[off] = key_of(code, uint32_t(id));
-      wpos += uint32_t(__popcll(m));
-    }
-  };
-  // per lane, the vectors whose maximum reaches T; then one such vector
-  // per lane and pass, taken out of the registers by a select tree.  The
-  // pass is a loop, not unrolled code: a block runs it once, from a cold
-  // instruction cache, so its length is what it costs.
-  const uint32_t below2 = BF16 ? (T - 1) * 0x10001u : T - 1;
-  uint32_t hm = 0;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const bool hit = BF16 ? (max16x2(vm[i], below2) ^ below2) != 0u : vm[i] > below2;
-    hm |= hit ? (1u << i) : 0u;
-  }
-  while (__ballot(hm != 0u) != 0) {
-    const bool act = hm != 0u;
-    const int i = act ? __builtin_ctz(hm) : 0;
-    hm &= hm - 1u;
-    const u32x4 v = pick<NV>(x, i);
-    const int64_t id = a0 + int64_t(i * NT + tid) * VE;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (BF16) {
-        const uint32_t u0 = v[j] & 0xFFFFu, u1 = v[j] >> 16;
-        put(act && u0 >= T, ord_of_flip16(u0), id + 2 * j);
-        put(act && u1 >= T, ord_of_flip16(u1), id + 2 * j + 1);
-      } else {
-        put(act && v[j] >= T, ord_of_flip32(v[j]), id + j);
-      }
-    }
-  }
-  put(hu >= T, BF16 ? ord_of_flip16(hu) : ord_of_flip32(hu), hid);
-  put(tu >= T, BF16 ? ord_of_flip16(tu) : ord_of_flip32(tu), tl);
-  if (lane == 0) s_wcnt[wave] = wpos;
-  __syncthreads();
-  uint32_t n = 0, most = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    n += s_wcnt[w];
-    most = max(most, s_wcnt[w]);
-  }
-  const bool overflow = most > uint32_t(kCandW);
-
-  // ---- 4. rank
-  if (!overflow && n <= 64u) {
-    if (wave == 0) {
-      uint32_t c[NW];
-#pragma unroll
-      for (int w = 0; w < NW; ++w) c[w] = s_wcnt[w];
-      int src = -1, before = 0;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        if (src < 0 && lane < before + int(c[w])) src = w * kCandW + (lane - before);
-        before += int(c[w]);
-      }
-      const uint64_t key = src >= 0 ? s_cand[src] : 0ull;
-      int rank = 0;
-      for (int j = 0; j < int(n); ++j) rank += readlane_u64(key, j) > key ? 1 : 0;
-      if (lane < int(n) && rank < k && rank > 0) {         // rank 0 is out already
-        const uint32_t id = key_id(key);
-        orow[rank] = int32_t(id);
-        mail_put(mrow + rank, id | 0x80000000u);
-      }
-    }
-    return;
-  }
-  if (!overflow && n <= uint32_t(NT)) {
-    rank_select_lists<KM, NW>(s_cand, s_wcnt, int(n), s_best);
-  } else {
-    TopList<KM> L;
-    L.clear();
-    if (!overflow) {
-      for (int c = tid; c < NW * kCandW; c += NT)
-        if (uint32_t(c % kCandW) < s_wcnt[c / kCandW]) L.insert(s_cand[c]);
-    } else {
-      // too many ties at the threshold: exact insertion from the registers
-#pragma unroll 1
-      for (int i = 0; i < NV; ++i) {
-        const u32x4 v = pick<NV>(x, i);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t id = a0 + int64_t(i * NT + tid) * VE + (BF16 ? 2 * j : j);
-          if (BF16) {
-            const uint32_t u0 = v[j] & 0xFFFFu, u1 = v[j] >> 16;
-            if (u0 >= T) L.insert(key_of(ord_of_flip16(u0), uint32_t(id)));
-            if (u1 >= T) L.insert(key_of(ord_of_flip16(u1), uint32_t(id + 1)));
-          } else if (v[j] >= T) {
-            L.insert(key_of(ord_of_flip32(v[j]), uint32_t(id)));
-          }
-        }
-      }
-      if (hu >= T) L.insert(key_of(BF16 ? ord_of_flip16(hu) : ord_of_flip32(hu), uint32_t(hid)));
-      if (tu >= T) L.insert(key_of(BF16 ? ord_of_flip16(tu) : ord_of_flip32(tu), uint32_t(tl)));
-    }
-    block_merge<KM, NW>(L, s_keys, s_best);
-  }
-  if (tid > 0 && tid < k) {
-    const uint32_t id = key_id(s_best[tid]);
-    orow[tid] = int32_t(id);
-    mail_put(mrow + tid, id | 0x80000000u);
-  }
+  static_assert(int64_t(NV) * kStepNT * (BF16 ? 8 : 4) == kStepMaxV, "row length");
+  const uint8_t* rowp = reinterpret_cast<const uint8_t*>(logits) + int64_t(row) * V * (BF16 ? 2 : 4);
+  StepRowOut out{ids_out + int64_t(row) * k, mail + int64_t(row) * k, k};
+  select_block<BF16, KM, kStepNT, NV, true>(rowp, 0, V, k, out);
 }
 
 // ---------------------------------------------------------------- tail

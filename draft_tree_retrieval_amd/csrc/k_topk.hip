@@ -152,6 +152,24 @@ __device__ __forceinline__ void seq_tail(TailShared& S, const TreeDev& tree, int
 // The sampling instantiations are held to three waves per SIMD (at most
 // 168 VGPRs), as many as the greedy ones reach by themselves: with many
 // rows the blocks of a launch run in rounds, so occupancy is throughput.
+// Where a top-k block's results go: with several segments per row, its KM
+// best keys (key 0 past the segment's elements) to the row's partial lists,
+// else the k ids to the output; written with device-scope atomics by wave 0
+// for the last-arriving block (dev_common.h).
+template <int KM>
+struct TopkOut {
+  uint64_t* part;
+  int32_t* ids;
+  int64_t row;
+  int seg, segs;
+  int32_t k;
+  __device__ __forceinline__ void first(uint32_t) const {}
+  __device__ __forceinline__ void put(int r, uint64_t key) const {
+    if (segs > 1) put_dev(&part[(row * segs + seg) * KM + r], key);
+    else if (r < k) put_dev(&ids[row * k + r], int32_t(key_id(key)));
+  }
+};
+
 template <bool BF16, int KM, int NT, int NV, bool SAMPLE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SAMPLE ? 3 : 1))) void topk_kernel(const void* __restrict__ logits, int64_t V,
                                                    int32_t k, int32_t segs, int64_t seg_len,
@@ -176,237 +194,244 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SAMPLE ? 3 :
   __shared__ uint32_t s_top[NW * KM];
   __shared__ float s_wsum[NW];
 
-  // aligned vector range [a0, a1) inside [s0, s1); at most VE-1 loose
-  // elements on each side
-  const uintptr_t addr0 = reinterpret_cast<uintptr_t>(rowp + s0 * ESZ);
-  int64_t a0 = s0 + int64_t(((16 - (addr0 & 15)) & 15) / ESZ);
-  if (a0 > s1) a0 = s1;
-  const int nv = int((s1 - a0) / VE);
-  const int64_t a1 = a0 + int64_t(nv) * VE;
-  auto code_at = [&](int64_t i) -> uint32_t {
-    return BF16 ? ord32(uint32_t(reinterpret_cast<const uint16_t*>(rowp)[i]) << 16)
-                : ord32(reinterpret_cast<const uint32_t*>(rowp)[i]);
-  };
+  if constexpr (!SAMPLE) {
+    // greedy steps and top-k alone: the compact selection of select.h
+    TopkOut<KM> out{part, ids_out, row, seg, segs, k};
+    select_block<BF16, KM, NT, NV, false>(rowp, s0, s1, k, out);
+  } else {
+    // sampling: the same selection, with each segment's softmax statistics
+    // aligned vector range [a0, a1) inside [s0, s1); at most VE-1 loose
+    // elements on each side
+    const uintptr_t addr0 = reinterpret_cast<uintptr_t>(rowp + s0 * ESZ);
+    int64_t a0 = s0 + int64_t(((16 - (addr0 & 15)) & 15) / ESZ);
+    if (a0 > s1) a0 = s1;
+    const int nv = int((s1 - a0) / VE);
+    const int64_t a1 = a0 + int64_t(nv) * VE;
+    auto code_at = [&](int64_t i) -> uint32_t {
+      return BF16 ? ord32(uint32_t(reinterpret_cast<const uint16_t*>(rowp)[i]) << 16)
+                  : ord32(reinterpret_cast<const uint32_t*>(rowp)[i]);
+    };
 
-  // ---- 1. load, order codes in place (0 marks "no element"), lane maximum
-  const u32x4* vp = reinterpret_cast<const u32x4*>(rowp + a0 * ESZ);
-  u32x4 x[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int idx = i * NT + tid;
-    x[i] = idx < nv ? __builtin_nontemporal_load(vp + idx) : u32x4{0, 0, 0, 0};
-  }
-  uint32_t loose_code[2] = {0, 0};       // head and tail elements
-  const int64_t loose_id[2] = {s0 + tid, a1 + tid};
-  if (loose_id[0] < a0) loose_code[0] = code_at(loose_id[0]);
-  if (loose_id[1] < s1) loose_code[1] = code_at(loose_id[1]);
-  uint32_t mt = max(loose_code[0], loose_code[1]);
-  uint32_t m2 = 0;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const uint32_t keep = (i * NT + tid < nv) ? ~0u : 0u;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (BF16) {
-        x[i][j] = ord16x2(x[i][j]) & keep;
-        m2 = max16x2(m2, x[i][j]);
-      } else {
-        x[i][j] = ord32(x[i][j]) & keep;
-        mt = max(mt, x[i][j]);
-      }
+    // ---- 1. load, order codes in place (0 marks "no element"), lane maximum
+    const u32x4* vp = reinterpret_cast<const u32x4*>(rowp + a0 * ESZ);
+    u32x4 x[NV];
+  #pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int idx = i * NT + tid;
+      x[i] = idx < nv ? __builtin_nontemporal_load(vp + idx) : u32x4{0, 0, 0, 0};
     }
-  }
-  if (BF16) mt = max(mt, max(m2 & 0xFFFFu, m2 >> 16) << 16);
-
-  // ---- 2. threshold: the largest code reached by at least k lane maxima
-  // of the block, i.e. the k-th largest lane maximum.  Each wave bisects
-  // over its own 64 lanes for its k-th largest and puts its k largest lane
-  // maxima into LDS (those above it, then copies of it); the block's k-th
-  // largest is the k-th largest of these NW * k values (the block's k
-  // largest are among them), found by every wave with a second bisection.
-  constexpr int kLowBit = BF16 ? 16 : 0;
-  uint32_t lo = 0;
-#pragma unroll
-  for (int bit = 31; bit >= kLowBit; --bit) {
-    const uint32_t c = lo | (1u << bit);
-    if (__popcll(__ballot(mt >= c)) >= k) lo = c;
-  }
-  {
-    const uint64_t gt = __ballot(mt > lo);            // fewer than k lanes
-    const int ngt = __popcll(gt);
-    const uint32_t below = __builtin_amdgcn_mbcnt_hi(uint32_t(gt >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(gt), 0u));
-    if (mt > lo) s_top[wave * KM + below] = mt;
-    if (lane >= ngt && lane < k) s_top[wave * KM + lane] = lo;
-  }
-  __syncthreads();
-  constexpr int NTOP = NW * KM;                       // 32 .. 256
-  constexpr int NTV = (NTOP + 63) / 64;
-  uint32_t tv[NTV];
-#pragma unroll
-  for (int h = 0; h < NTV; ++h) {
-    const int i = lane + 64 * h;
-    tv[h] = (i < NTOP && (i % KM) < k) ? s_top[min(i, NTOP - 1)] : 0u;
-  }
-
-  // sampling: softmax statistics of the segment, (max, sum of
-  // exp2((z - max) * scale)), handed over with the ids
-  float seg_max = 0.f;
-  if constexpr (SAMPLE) {
-    uint32_t bm = tv[0];
-#pragma unroll
-    for (int h = 1; h < NTV; ++h) bm = max(bm, tv[h]);
-    bm = wave_max_u32(bm);
-    seg_max = ord_to_f32(bm);
-    const float s2 = tail.temp_scale, off = -seg_max * s2;
-    float acc = 0.f;
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-#pragma unroll
+    uint32_t loose_code[2] = {0, 0};       // head and tail elements
+    const int64_t loose_id[2] = {s0 + tid, a1 + tid};
+    if (loose_id[0] < a0) loose_code[0] = code_at(loose_id[0]);
+    if (loose_id[1] < s1) loose_code[1] = code_at(loose_id[1]);
+    uint32_t mt = max(loose_code[0], loose_code[1]);
+    uint32_t m2 = 0;
+  #pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const uint32_t keep = (i * NT + tid < nv) ? ~0u : 0u;
+  #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        // an opaque copy: were the halves extracted here shared with the
-        // candidate scan below, all of them would stay live across the
-        // threshold search (twice the registers of x)
-        uint32_t word = x[i][j];
-        asm volatile("" : "+v"(word));
         if (BF16) {
-          const uint32_t c0 = (word & 0xFFFFu) << 16, c1 = word & 0xFFFF0000u;
-          acc += c0 ? soft_weight(ord_to_f32(c0), s2, off) : 0.f;
-          acc += c1 ? soft_weight(ord_to_f32(c1), s2, off) : 0.f;
+          x[i][j] = ord16x2(x[i][j]) & keep;
+          m2 = max16x2(m2, x[i][j]);
         } else {
-          acc += word ? soft_weight(ord_to_f32(word), s2, off) : 0.f;
+          x[i][j] = ord32(x[i][j]) & keep;
+          mt = max(mt, x[i][j]);
         }
       }
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      acc += loose_code[h] ? soft_weight(ord_to_f32(loose_code[h]), s2, off) : 0.f;
-    acc = wave_sum_f32(acc);
-    if (lane == 0) s_wsum[wave] = acc;
-  }
-  lo = 0;
-#pragma unroll
-  for (int bit = 31; bit >= kLowBit; --bit) {
-    const uint32_t c = lo | (1u << bit);
-    int reach = 0;
-#pragma unroll
-    for (int h = 0; h < NTV; ++h) reach += __popcll(__ballot(tv[h] >= c));
-    if (reach >= k) lo = c;
-  }
+    }
+    if (BF16) mt = max(mt, max(m2 & 0xFFFFu, m2 >> 16) << 16);
 
-  // ---- 3. candidates: each element at or above lo gets the next slot of
-  // its wave's list, in lane order (ballot + lane-masked bit count)
-  uint64_t* wc = s_cand + wave * kCandW;
-  uint32_t wpos = 0;                        // wave-uniform
-  auto put = [&](bool pred, uint32_t code, int64_t id) {
-    const uint64_t m = __ballot(pred);
-    if (m) {
-      const uint32_t off =
-          wpos + __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
-      if (pred && off < uint32_t(kCandW)) wc[off] = key_of(code, uint32_t(id));
-      wpos += uint32_t(__popcll(m));
+    // ---- 2. threshold: the largest code reached by at least k lane maxima
+    // of the block, i.e. the k-th largest lane maximum.  Each wave bisects
+    // over its own 64 lanes for its k-th largest and puts its k largest lane
+    // maxima into LDS (those above it, then copies of it); the block's k-th
+    // largest is the k-th largest of these NW * k values (the block's k
+    // largest are among them), found by every wave with a second bisection.
+    constexpr int kLowBit = BF16 ? 16 : 0;
+    uint32_t lo = 0;
+  #pragma unroll
+    for (int bit = 31; bit >= kLowBit; --bit) {
+      const uint32_t c = lo | (1u << bit);
+      if (__popcll(__ballot(mt >= c)) >= k) lo = c;
     }
-  };
-  const uint32_t lo16 = lo >> 16;
-  const uint32_t below2 = lo16 ? (lo16 - 1) * 0x10001u : 0u;     // bf16: lo16-1 in both halves
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    uint32_t hv[4];                          // nonzero where an element reaches lo
-    bool hit = false;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      hv[j] = BF16 ? (max16x2(x[i][j], below2) ^ below2) : ((x[i][j] && x[i][j] >= lo) ? 1u : 0u);
-      hit = hit || hv[j] != 0u;
+    {
+      const uint64_t gt = __ballot(mt > lo);            // fewer than k lanes
+      const int ngt = __popcll(gt);
+      const uint32_t below = __builtin_amdgcn_mbcnt_hi(uint32_t(gt >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(gt), 0u));
+      if (mt > lo) s_top[wave * KM + below] = mt;
+      if (lane >= ngt && lane < k) s_top[wave * KM + lane] = lo;
     }
-    if (__ballot(hit) == 0) continue;
-    const int64_t id = a0 + int64_t(i * NT + tid) * VE;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (BF16) {
-        put((hv[j] & 0xFFFFu) != 0u, (x[i][j] & 0xFFFFu) << 16, id + 2 * j);
-        put(hv[j] > 0xFFFFu, x[i][j] & 0xFFFF0000u, id + 2 * j + 1);
-      } else {
-        put(hv[j] != 0u, x[i][j], id + j);
-      }
+    __syncthreads();
+    constexpr int NTOP = NW * KM;                       // 32 .. 256
+    constexpr int NTV = (NTOP + 63) / 64;
+    uint32_t tv[NTV];
+  #pragma unroll
+    for (int h = 0; h < NTV; ++h) {
+      const int i = lane + 64 * h;
+      tv[h] = (i < NTOP && (i % KM) < k) ? s_top[min(i, NTOP - 1)] : 0u;
     }
-  }
-#pragma unroll
-  for (int h = 0; h < 2; ++h) put(loose_code[h] && loose_code[h] >= lo, loose_code[h], loose_id[h]);
-  if (lane == 0) s_wcnt[wave] = wpos;
-  __syncthreads();
-  uint32_t n = 0, most = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    n += s_wcnt[w];
-    most = max(most, s_wcnt[w]);
-  }
-  const bool overflow = most > uint32_t(kCandW);
-  if constexpr (SAMPLE) {
-    if (tid == 0) {
-      float tot = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) tot += s_wsum[w];
-      put_dev(&stat[row * segs + seg], (uint64_t(__float_as_uint(tot)) << 32) | __float_as_uint(seg_max));
-    }
-  }
 
-  // ---- the block's KM best
-  if (!overflow && n <= 64u) {
-    // one wave: lane i ranks candidate i against the others in registers
-    if (wave == 0) {
-      // lane i takes candidate i: its list and place from the list sizes,
-      // read at once (not one dependent LDS read per list)
-      uint32_t c[NW];
-#pragma unroll
-      for (int w = 0; w < NW; ++w) c[w] = s_wcnt[w];
-      int src = -1, before = 0;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        if (src < 0 && lane < before + int(c[w])) src = w * kCandW + (lane - before);
-        before += int(c[w]);
-      }
-      const uint64_t key = src >= 0 ? s_cand[src] : 0ull;
-      int rank = 0;
-      for (int j = 0; j < int(n); ++j) rank += readlane_u64(key, j) > key ? 1 : 0;
-      if (lane >= int(n)) rank = lane;           // empty places n.. hold key 0
-      if (rank < KM) {
-        if (segs > 1) put_dev(&part[(row * segs + seg) * KM + rank], key);
-        else if (rank < k) put_dev(&ids_out[row * k + rank], int32_t(key_id(key)));
-      }
-    }
-  } else {
-    if (!overflow && n <= uint32_t(NT)) {
-      rank_select_lists<KM, NW>(s_cand, s_wcnt, int(n), s_best);
-    } else {
-      TopList<KM> L;
-      L.clear();
-      if (!overflow) {
-        for (int c = tid; c < kCand; c += NT)
-          if (uint32_t(c % kCandW) < s_wcnt[c / kCandW]) L.insert(s_cand[c]);
-      } else {
-        // too many ties at the threshold: exact insertion from the registers
-#pragma unroll
-        for (int i = 0; i < NV; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int64_t id = a0 + int64_t(i * NT + tid) * VE + (BF16 ? 2 * j : j);
-            if (BF16) {
-              const uint32_t c0 = (x[i][j] & 0xFFFFu) << 16, c1 = x[i][j] & 0xFFFF0000u;
-              if (c0 && c0 >= lo) L.insert(key_of(c0, uint32_t(id)));
-              if (c1 && c1 >= lo) L.insert(key_of(c1, uint32_t(id + 1)));
-            } else if (x[i][j] && x[i][j] >= lo) {
-              L.insert(key_of(x[i][j], uint32_t(id)));
-            }
+    // sampling: softmax statistics of the segment, (max, sum of
+    // exp2((z - max) * scale)), handed over with the ids
+    float seg_max = 0.f;
+    if constexpr (SAMPLE) {
+      uint32_t bm = tv[0];
+  #pragma unroll
+      for (int h = 1; h < NTV; ++h) bm = max(bm, tv[h]);
+      bm = wave_max_u32(bm);
+      seg_max = ord_to_f32(bm);
+      const float s2 = tail.temp_scale, off = -seg_max * s2;
+      float acc = 0.f;
+  #pragma unroll
+      for (int i = 0; i < NV; ++i)
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // an opaque copy: were the halves extracted here shared with the
+          // candidate scan below, all of them would stay live across the
+          // threshold search (twice the registers of x)
+          uint32_t word = x[i][j];
+          asm volatile("" : "+v"(word));
+          if (BF16) {
+            const uint32_t c0 = (word & 0xFFFFu) << 16, c1 = word & 0xFFFF0000u;
+            acc += c0 ? soft_weight(ord_to_f32(c0), s2, off) : 0.f;
+            acc += c1 ? soft_weight(ord_to_f32(c1), s2, off) : 0.f;
+          } else {
+            acc += word ? soft_weight(ord_to_f32(word), s2, off) : 0.f;
           }
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          if (loose_code[h] && loose_code[h] >= lo) L.insert(key_of(loose_code[h], uint32_t(loose_id[h])));
-      }
-      block_merge<KM, NW>(L, s_keys, s_best);
+        }
+  #pragma unroll
+      for (int h = 0; h < 2; ++h)
+        acc += loose_code[h] ? soft_weight(ord_to_f32(loose_code[h]), s2, off) : 0.f;
+      acc = wave_sum_f32(acc);
+      if (lane == 0) s_wsum[wave] = acc;
     }
-    if (tid == 0) {
-#pragma unroll
-      for (int r = 0; r < KM; ++r) {
-        if (segs > 1) put_dev(&part[(row * segs + seg) * KM + r], s_best[r]);
-        else if (r < k) put_dev(&ids_out[row * k + r], int32_t(key_id(s_best[r])));
+    lo = 0;
+  #pragma unroll
+    for (int bit = 31; bit >= kLowBit; --bit) {
+      const uint32_t c = lo | (1u << bit);
+      int reach = 0;
+  #pragma unroll
+      for (int h = 0; h < NTV; ++h) reach += __popcll(__ballot(tv[h] >= c));
+      if (reach >= k) lo = c;
+    }
+
+    // ---- 3. candidates: each element at or above lo gets the next slot of
+    // its wave's list, in lane order (ballot + lane-masked bit count)
+    uint64_t* wc = s_cand + wave * kCandW;
+    uint32_t wpos = 0;                        // wave-uniform
+    auto put = [&](bool pred, uint32_t code, int64_t id) {
+      const uint64_t m = __ballot(pred);
+      if (m) {
+        const uint32_t off =
+            wpos + __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
+        if (pred && off < uint32_t(kCandW)) wc[off] = key_of(code, uint32_t(id));
+        wpos += uint32_t(__popcll(m));
+      }
+    };
+    const uint32_t lo16 = lo >> 16;
+    const uint32_t below2 = lo16 ? (lo16 - 1) * 0x10001u : 0u;     // bf16: lo16-1 in both halves
+  #pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      uint32_t hv[4];                          // nonzero where an element reaches lo
+      bool hit = false;
+  #pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        hv[j] = BF16 ? (max16x2(x[i][j], below2) ^ below2) : ((x[i][j] && x[i][j] >= lo) ? 1u : 0u);
+        hit = hit || hv[j] != 0u;
+      }
+      if (__ballot(hit) == 0) continue;
+      const int64_t id = a0 + int64_t(i * NT + tid) * VE;
+  #pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (BF16) {
+          put((hv[j] & 0xFFFFu) != 0u, (x[i][j] & 0xFFFFu) << 16, id + 2 * j);
+          put(hv[j] > 0xFFFFu, x[i][j] & 0xFFFF0000u, id + 2 * j + 1);
+        } else {
+          put(hv[j] != 0u, x[i][j], id + j);
+        }
+      }
+    }
+  #pragma unroll
+    for (int h = 0; h < 2; ++h) put(loose_code[h] && loose_code[h] >= lo, loose_code[h], loose_id[h]);
+    if (lane == 0) s_wcnt[wave] = wpos;
+    __syncthreads();
+    uint32_t n = 0, most = 0;
+  #pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      n += s_wcnt[w];
+      most = max(most, s_wcnt[w]);
+    }
+    const bool overflow = most > uint32_t(kCandW);
+    if constexpr (SAMPLE) {
+      if (tid == 0) {
+        float tot = 0.f;
+  #pragma unroll
+        for (int w = 0; w < NW; ++w) tot += s_wsum[w];
+        put_dev(&stat[row * segs + seg], (uint64_t(__float_as_uint(tot)) << 32) | __float_as_uint(seg_max));
+      }
+    }
+
+    // ---- the block's KM best
+    if (!overflow && n <= 64u) {
+      // one wave: lane i ranks candidate i against the others in registers
+      if (wave == 0) {
+        // lane i takes candidate i: its list and place from the list sizes,
+        // read at once (not one dependent LDS read per list)
+        uint32_t c[NW];
+  #pragma unroll
+        for (int w = 0; w < NW; ++w) c[w] = s_wcnt[w];
+        int src = -1, before = 0;
+  #pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          if (src < 0 && lane < before + int(c[w])) src = w * kCandW + (lane - before);
+          before += int(c[w]);
+        }
+        const uint64_t key = src >= 0 ? s_cand[src] : 0ull;
+        int rank = 0;
+        for (int j = 0; j < int(n); ++j) rank += readlane_u64(key, j) > key ? 1 : 0;
+        if (lane >= int(n)) rank = lane;           // empty places n.. hold key 0
+        if (rank < KM) {
+          if (segs > 1) put_dev(&part[(row * segs + seg) * KM + rank], key);
+          else if (rank < k) put_dev(&ids_out[row * k + rank], int32_t(key_id(key)));
+        }
+      }
+    } else {
+      if (!overflow && n <= uint32_t(NT)) {
+        rank_select_lists<KM, NW>(s_cand, s_wcnt, int(n), s_best);
+      } else {
+        TopList<KM> L;
+        L.clear();
+        if (!overflow) {
+          for (int c = tid; c < kCand; c += NT)
+            if (uint32_t(c % kCandW) < s_wcnt[c / kCandW]) L.insert(s_cand[c]);
+        } else {
+          // too many ties at the threshold: exact insertion from the registers
+  #pragma unroll
+          for (int i = 0; i < NV; ++i)
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int64_t id = a0 + int64_t(i * NT + tid) * VE + (BF16 ? 2 * j : j);
+              if (BF16) {
+                const uint32_t c0 = (x[i][j] & 0xFFFFu) << 16, c1 = x[i][j] & 0xFFFF0000u;
+                if (c0 && c0 >= lo) L.insert(key_of(c0, uint32_t(id)));
+                if (c1 && c1 >= lo) L.insert(key_of(c1, uint32_t(id + 1)));
+              } else if (x[i][j] && x[i][j] >= lo) {
+                L.insert(key_of(x[i][j], uint32_t(id)));
+              }
+            }
+  #pragma unroll
+          for (int h = 0; h < 2; ++h)
+            if (loose_code[h] && loose_code[h] >= lo) L.insert(key_of(loose_code[h], uint32_t(loose_id[h])));
+        }
+        block_merge<KM, NW>(L, s_keys, s_best);
+      }
+      if (tid == 0) {
+  #pragma unroll
+        for (int r = 0; r < KM; ++r) {
+          if (segs > 1) put_dev(&part[(row * segs + seg) * KM + r], s_best[r]);
+          else if (r < k) put_dev(&ids_out[row * k + r], int32_t(key_id(s_best[r])));
+        }
       }
     }
   }
