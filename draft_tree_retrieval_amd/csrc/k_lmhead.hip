@@ -7,27 +7,31 @@
 // softmax is increasing, so selecting on z is selecting on p.
 //
 // Decode-sized R makes this a skinny product bound by streaming W once:
-// each block owns 128 vocabulary rows and 96 query rows with 12 waves.
-// Eight consumer waves own one 16-row vocabulary tile each; a consumer
-// loads its W tile straight from HBM into registers, 64 contiguous bytes
-// per lane per 128-k super-step, four super-steps in flight, and uses it as
-// the A operand of v_mfma_f32_16x16x32_bf16.  Four producer waves copy the
+// each block owns 128 vocabulary rows and 96 query rows with 8 waves.
+// Four consumer waves own two 16-row vocabulary tiles each.  A consumer
+// loads its W tiles straight from HBM into registers: per 128-k
+// super-step, 256 contiguous bytes of each row, from four loads issued
+// back to back that each read 64 contiguous bytes of the tile's 16 rows
+// (the A operand of one v_mfma_f32_16x16x32_bf16 step), with four
+// super-steps in flight.  Four producer waves copy the
 // h chunk of each super-step HBM/L2 -> LDS with the LDS DMA
 // (global_load_lds_dwordx4), three chunks ahead, in an XOR-swizzled layout
 // that keeps the B operand reads (16 rows, one 16-byte column chunk)
-// conflict-free.  A wave's load counter completes in issue order, so
-// keeping the h copies in waves of their own means no consumer ever waits
-// for an h chunk behind its W loads.  The contraction index is permuted
-// consistently on both operands: MFMA step s of a super-step, lane group
-// g, element e stands for k = 32 g + 8 s + e, so a lane's 64 loaded bytes
-// feed its four steps.
+// conflict-free; each B operand read serves both of a consumer's tiles.  A
+// wave's load counter completes in issue order, so keeping the h copies in
+// waves of their own means no consumer ever waits for an h chunk behind its
+// W loads.
 //
-// Epilogue: a consumer lane holds 4 vocabulary ids x 1 query row per row
-// tile.  The 16 keys of a query row in a wave are sorted and merged across
-// the four lane groups down to the wave's 8 best; the eight lists of a row
-// are merged pairwise in three rounds by all threads, and the block writes
-// its 8 best keys per row.  A second kernel (one block per row) merges the
-// slices.
+// Epilogue, per query row: a consumer lane holds 8 of the block's 128
+// logits (a holder; 16 holders per row).  The threshold T is the 8th
+// largest of the 16 holder maxima: at least eight holders reach it, so
+// nothing below it is among the row's 8 best.  The values reaching T (10
+// on average for random logits, at most 128) go to a per-row LDS list as
+// 64-bit keys (order code, then the complemented id); a thread per
+// candidate counts the row's larger keys and writes ranks 0..7, so the
+// block's 8 best per row land descending.  The block's super-steps start at
+// a chunk that differs between the blocks an XCD runs at once.  A second
+// kernel (one block per row) merges the slices.
 #include "dev_common.h"
 
 namespace tr {
@@ -36,10 +40,12 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kLhRows = 96;     // query rows per block (6 tiles of 16)
 constexpr int kLhTiles = kLhRows / 16;
-constexpr int kLhCons = 8;      // consumer waves: one 16-row vocabulary tile each
+constexpr int kLhCons = 4;      // consumer waves: two 16-row vocabulary tiles each
+constexpr int kLhVtW = 2;
 constexpr int kLhProd = 4;      // producer waves: the h chunk DMA
 constexpr int kLhDmaPerProd = kLhRows * 16 / 64 / kLhProd;    // 6 DMA loads per chunk each
 constexpr int kLhKc = 128;      // k per super-step (one staged h chunk)
@@ -47,51 +53,45 @@ constexpr int kLhRing = 4;      // W super-steps in flight per consumer wave
 constexpr int kLhUnroll = 4;    // steps per loop round
 constexpr int kLhHBuf = 4;      // staged h chunks (three in flight ahead of the one in use)
 constexpr int kLhChunkBytes = kLhRows * kLhKc * 2;      // 24 KB
-
-__device__ __forceinline__ void ce(uint64_t& a, uint64_t& b) {   // a >= b afterwards
-  const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
-  a = hi;
-  b = lo;
-}
-
-// The 8 best of two descending lists of 8, descending.
-__device__ __forceinline__ void merge8(uint64_t (&a)[8], const uint64_t (&b)[8]) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) a[i] = a[i] > b[7 - i] ? a[i] : b[7 - i];   // bitonic
-#pragma unroll
-  for (int j = 4; j > 0; j >>= 1)
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if ((i & j) == 0) ce(a[i], a[i + j]);
-}
-
-__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) { return shfl_xor_u64(v, m); }
+constexpr int kLhCand = 128;    // candidate slots per row (every logit of the block)
+constexpr int kLhRowsPerBuf = kLhChunkBytes / (kLhCand * 8);   // candidate lists per h buffer
+static_assert(kLhRowsPerBuf * kLhHBuf >= kLhRows, "the candidate lists fit the h buffers");
 
 }  // namespace
 
-__global__ __launch_bounds__(768) void lmhead_topk_kernel(const uint16_t* __restrict__ h,
+__global__ __launch_bounds__(512) void lmhead_topk_kernel(const uint16_t* __restrict__ h,
                                                            const uint16_t* W, int R, int H,
                                                            int64_t V, int nvs,
                                                            uint64_t* __restrict__ part) {
-  // Four separate h buffers (the unrolled loops name each one statically)
-  // and a separate key table: with one array the compiler could not tell
-  // an LDS read from DMA writes still in flight elsewhere in it.
+  // Four separate h buffers (the unrolled loops name each one statically):
+  // with one array the compiler could not tell an LDS read from DMA writes
+  // still in flight elsewhere in it.  After the loop they hold the
+  // candidate lists.
   __shared__ __attribute__((aligned(16))) uint8_t hbuf0[kLhChunkBytes];
   __shared__ __attribute__((aligned(16))) uint8_t hbuf1[kLhChunkBytes];
   __shared__ __attribute__((aligned(16))) uint8_t hbuf2[kLhChunkBytes];
   __shared__ __attribute__((aligned(16))) uint8_t hbuf3[kLhChunkBytes];
-  __shared__ uint64_t s_top[kLhRows * 64];                              // 48 KB
+  __shared__ __attribute__((aligned(16))) uint32_t s_hm[kLhRows][16];   // holder maxima
+  __shared__ uint32_t s_thr[kLhRows];
+  __shared__ __attribute__((aligned(16))) uint32_t s_cnt[kLhRows];
   static_assert(kLhHBuf == 4 && kLhUnroll % kLhHBuf == 0 && kLhUnroll % kLhRing == 0,
                 "a static buffer and ring slot per unrolled step");
   auto hbuf = [&](int i) -> uint8_t* {
     return i == 0 ? hbuf0 : i == 1 ? hbuf1 : i == 2 ? hbuf2 : hbuf3;
   };
+  constexpr int kThreads = 64 * (kLhCons + kLhProd);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, g = lane >> 4;
   const int vs = blockIdx.x;
   const int row0 = blockIdx.y * kLhRows;
   const int nsteps = H / kLhKc;
+  // Super-step c of this block covers chunk (c + rot) mod nsteps: the 32
+  // blocks an XCD runs at once read different h chunks (its L2 serves them
+  // from different channels) instead of all reading the same one.
+  const int rot = (vs / 8) % nsteps;
+  auto chunk = [&](int c) { const int cc = c + rot; return cc >= nsteps ? cc - nsteps : cc; };
   // every wave passes the same number of barriers: whole loop rounds
   const int nround = (nsteps + kLhUnroll - 1) / kLhUnroll * kLhUnroll;
+  if (tid < kLhRows) s_cnt[tid] = 0;
 
   // Waves kLhCons.. are producers: they alone DMA the h chunks, so the
   // consumers' in-order load counters hold W loads only and their W ring
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(768) void lmhead_topk_kernel(const uint16_t* __rest
         const int p = base + lane;
         const int r = p >> 4, pos = p & 15, cc = pos ^ (r & 15);
         const int hr = min(row0 + r, R - 1);
-        const uint16_t* src = h + int64_t(hr) * H + c * kLhKc + cc * 8;
+        const uint16_t* src = h + int64_t(hr) * H + chunk(c) * kLhKc + cc * 8;
         __builtin_amdgcn_global_load_lds(src, hbuf(b) + base * 16, 16, 0, 0);
       }
       asm volatile("" ::: "memory");
@@ -132,22 +132,31 @@ __global__ __launch_bounds__(768) void lmhead_topk_kernel(const uint16_t* __rest
     }
   }
 
-  floatx4 acc[kLhTiles];
+  floatx4 acc[kLhVtW][kLhTiles];
 #pragma unroll
-  for (int t = 0; t < kLhTiles; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-  const int64_t v0 = int64_t(vs) * (kLhCons * 16) + w * 16;     // this wave's vocabulary tile
+  for (int j = 0; j < kLhVtW; ++j)
+#pragma unroll
+    for (int t = 0; t < kLhTiles; ++t) acc[j][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int64_t v0 = int64_t(vs) * (kLhCons * kLhVtW * 16) + w * (kLhVtW * 16);   // this wave's tiles
   if (w < kLhCons) {
     // W rows past V repeat the last row (their keys are dropped below)
-    const int64_t vrow = v0 + li < V ? v0 + li : V - 1;
-    const uint16_t* wp = W + vrow * H + 32 * g;
-    auto load_w = [&](u32x4 (&r)[4], int c) {
-      const u32x4* p = reinterpret_cast<const u32x4*>(wp + c * kLhKc);
+    const uint16_t* wp[kLhVtW];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) r[s] = p[s];
+    for (int j = 0; j < kLhVtW; ++j) {
+      const int64_t vrow = v0 + 16 * j + li < V ? v0 + 16 * j + li : V - 1;
+      wp[j] = W + vrow * H + 8 * g;
+    }
+    // load s of a super-step: 64 contiguous bytes of each of the tile's 16
+    // rows (lane group g the g-th 16 bytes), the A operand of MFMA step s
+    auto load_w = [&](u32x4 (&r)[kLhVtW][4], int c) {
+#pragma unroll
+      for (int j = 0; j < kLhVtW; ++j)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) r[j][s] = *reinterpret_cast<const u32x4*>(wp[j] + chunk(c) * kLhKc + 32 * s);
     };
     // (compiler memory barriers keep the ring in issue order, so the wait
     // before a slot's first use leaves the younger slots in flight)
-    u32x4 wr[kLhRing][4];
+    u32x4 wr[kLhRing][kLhVtW][4];
 #pragma unroll
     for (int j = 0; j < kLhRing; ++j) {
       load_w(wr[j], min(j, nsteps - 1));
@@ -157,27 +166,36 @@ __global__ __launch_bounds__(768) void lmhead_topk_kernel(const uint16_t* __rest
 #pragma unroll
       for (int j = 0; j < kLhUnroll; ++j) {
         const int c = c0 + j;                       // steps past the end only wait
-        // W(c): the younger ring slots (3 x 4 loads) may stay in flight.
+        // W(c): the younger ring slots (3 x 8 loads) may stay in flight.
         // Written out: the compiler's own count is lost across the loop's
         // back edge and would drain every load at the first step of a round.
-        static_assert((kLhRing - 1) * 4 == 12, "vmcnt below");
-        __builtin_amdgcn_s_waitcnt(0x0F7C);        // vmcnt(12), lgkm/exp not waited
+        static_assert((kLhRing - 1) * 4 * kLhVtW == 24, "vmcnt below");
+        __builtin_amdgcn_s_waitcnt(0x4F78);        // vmcnt(24), lgkm/exp not waited
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         if (c < nsteps) {
           const uint8_t* hb = hbuf(j % kLhHBuf);
+          // row 16 t + li sits at byte (16 t + li) * 256, its column chunk
+          // 4 s + g at position (4 s + g) ^ li (row & 15 == li).  The B
+          // operands of MFMA step s + 1 are read while step s multiplies.
+          bf16x8 bv[2][kLhTiles];
+          auto read_b = [&](bf16x8 (&b)[kLhTiles], int s) __attribute__((always_inline)) {
+            const uint8_t* hs = hb + li * 256 + (((4 * s + g) ^ li) << 4);
+#pragma unroll
+            for (int t = 0; t < kLhTiles; ++t) b[t] = *reinterpret_cast<const bf16x8*>(hs + t * 4096);
+          };
+          read_b(bv[0], 0);
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            const bf16x8 a = __builtin_bit_cast(bf16x8, wr[j % kLhRing][s]);
-            // row 16 t + li sits at byte (16 t + li) * 256, its column chunk
-            // 4 g + s at position (4 g + s) ^ li (row & 15 == li)
-            const uint8_t* hs = hb + li * 256 + (((4 * g + s) ^ li) << 4);
+            if (s < 3) read_b(bv[(s + 1) & 1], s + 1);
+            __builtin_amdgcn_sched_barrier(0);      // keep the reads ahead of the products
 #pragma unroll
-            for (int t = 0; t < kLhTiles; ++t) {
-              const bf16x8 bv = *reinterpret_cast<const bf16x8*>(hs + t * 4096);
-              acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bv, acc[t], 0, 0, 0);
-            }
+            for (int t = 0; t < kLhTiles; ++t)
+#pragma unroll
+              for (int vj = 0; vj < kLhVtW; ++vj)
+                acc[vj][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, wr[j % kLhRing][vj][s]), bv[s & 1][t], acc[vj][t], 0, 0, 0);
           }
         }
         // the LDS reads of this step are done before the next barrier
@@ -189,71 +207,111 @@ __global__ __launch_bounds__(768) void lmhead_topk_kernel(const uint16_t* __rest
     }
   }
 
-  // ---- epilogue: per query row 16 t + li, a consumer lane's keys are
-  // vocabulary ids v0 + 4 g + e
-  __syncthreads();
+  // ---- epilogue.  Lane (li, g) of consumer w holds z for vocabulary id
+  // v0 + 16 j + 4 g + e (tile j of the wave) and query row 16 t + li.
+  uint32_t code[kLhVtW][kLhTiles][4];
   if (w < kLhCons) {
 #pragma unroll
+    for (int j = 0; j < kLhVtW; ++j)
+#pragma unroll
+      for (int t = 0; t < kLhTiles; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t vid = v0 + 16 * j + 4 * g + e;
+          code[j][t][e] = vid < V ? ord32(__float_as_uint(acc[j][t][e])) : 0u;   // 0: no id
+        }
+#pragma unroll
     for (int t = 0; t < kLhTiles; ++t) {
-      uint64_t kk[8];
+      uint32_t m = code[0][t][0];
+#pragma unroll
+      for (int j = 0; j < kLhVtW; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m = max(m, code[j][t][e]);
+      s_hm[16 * t + li][4 * w + g] = m;
+    }
+  }
+  __syncthreads();                                // the h buffers are free from here
+
+  // ---- the row's threshold: the 8th largest of its 16 holder maxima (at
+  // least eight holders reach it, so nothing below it is among the 8 best).
+  // Thread (row, i) writes it when maximum i is that value.
+  for (int idx = tid; idx < kLhRows * 16; idx += kThreads) {
+    const int row = idx >> 4, i = idx & 15;
+    const uint32_t mi = s_hm[row][i];
+    int gt = 0, ge = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 mq = *reinterpret_cast<const u32x4*>(&s_hm[row][4 * q]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int64_t vid = v0 + 4 * g + e;
-        kk[e] = vid < V ? make_key(__float_as_uint(acc[t][e]), uint32_t(vid)) : 0ull;
+        gt += mq[e] > mi;
+        ge += mq[e] >= mi;
       }
-      ce(kk[0], kk[1]);
-      ce(kk[2], kk[3]);
-      ce(kk[0], kk[2]);
-      ce(kk[1], kk[3]);
-      ce(kk[1], kk[2]);
-      // with lane group g ^ 1: the 8 keys of both, descending
+    }
+    if (gt < 8 && ge >= 8) s_thr[row] = mi;
+  }
+  __syncthreads();
+
+  // ---- candidates: the values reaching the row's threshold
+  // slot s of row r sits at position s ^ (r & 15) of the row's list, so the
+  // same slot of 16 consecutive rows lies in 16 different banks
+  auto cand = [&](int row) -> uint64_t* {
+    return reinterpret_cast<uint64_t*>(hbuf(row / kLhRowsPerBuf)) + (row % kLhRowsPerBuf) * kLhCand;
+  };
+  if (w < kLhCons) {
+    // one slot reservation per lane and row (all six in flight at once),
+    // then plain stores
+    uint32_t T[kLhTiles], n[kLhTiles], slot[kLhTiles];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) kk[4 + e] = shfl_xor64(kk[3 - e], 16);   // partner's, ascending
+    for (int t = 0; t < kLhTiles; ++t) T[t] = s_thr[16 * t + li];
 #pragma unroll
-      for (int j = 4; j > 0; j >>= 1)
+    for (int t = 0; t < kLhTiles; ++t) {
+      n[t] = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if ((i & j) == 0) ce(kk[i], kk[i + j]);
-      // with lane group g ^ 2: the 8 best of the 16
-      uint64_t other[8];
+      for (int j = 0; j < kLhVtW; ++j)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) other[e] = shfl_xor64(kk[e], 32);
-      merge8(kk, other);
-      // lanes of group g write keys 2 g, 2 g + 1 of the wave's 8
-      const int row = t * 16 + li;
+        for (int e = 0; e < 4; ++e) n[t] += code[j][t][e] >= T[t];
+    }
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if ((e >> 1) == g) s_top[row * 64 + w * 8 + e] = kk[e];
+    for (int t = 0; t < kLhTiles; ++t) slot[t] = n[t] ? atomicAdd(&s_cnt[16 * t + li], n[t]) : 0u;
+#pragma unroll
+    for (int t = 0; t < kLhTiles; ++t) {
+      uint64_t* list = cand(16 * t + li);
+#pragma unroll
+      for (int j = 0; j < kLhVtW; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t c = code[j][t][e];
+          if (c >= T[t]) list[(slot[t]++) ^ li] = key_of(c, uint32_t(v0 + 16 * j + 4 * g + e));
+        }
     }
   }
   __syncthreads();
-  // The block's 8 best of each row: the 8 descending lists of a row (one
-  // per consumer wave) merged pairwise in three rounds, one thread per
-  // pair; list i of row r sits at s_top[r * 64 + 8 i].
-  constexpr int kThreads = 64 * (kLhCons + kLhProd);
+
+  // ---- lane (row, slot): the candidate's rank among the row's (all keys
+  // differ: distinct ids), ranks 0..7 written (code 0, ids past V, as key 0),
+  // so the block's 8 best per row land descending (a row has at least 8
+  // candidates).  A wave takes 4 rows at a time, 16 lanes per row; the keys
+  // are read 4 at a time over the aligned 16-position blocks that hold
+  // slots 0 .. n-1, the positions of slots past n skipped.
+  for (int rg = w; rg < kLhRows / 4; rg += kThreads / 64) {
+    const int row = 4 * rg + g;
+    const int n = int(s_cnt[row]);
+    const uint64_t* list = cand(row);
+    const int sw = row & 15;
+    for (int slot = li; slot < n; slot += 16) {
+      const uint64_t x = list[slot ^ sw];
+      int rank = 0;
+      for (int p0 = 0; p0 < ((n + 15) & ~15); p0 += 4) {   // the swizzle stays within 16
+        const u64x2 a = *reinterpret_cast<const u64x2*>(list + p0);
+        const u64x2 b = *reinterpret_cast<const u64x2*>(list + p0 + 2);
+        const uint64_t y[4] = {a[0], a[1], b[0], b[1]};
 #pragma unroll
-  for (int span = 1; span < kLhCons; span <<= 1) {
-    const int pairs = kLhCons / (2 * span);
-    for (int task = tid; task < kLhRows * pairs; task += kThreads) {
-      const int row = task / pairs, pr = task - row * pairs;
-      uint64_t* a = s_top + row * 64 + 8 * (2 * pr * span);
-      const uint64_t* b = a + 8 * span;
-      uint64_t x[8], y[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        x[e] = a[e];
-        y[e] = b[e];
+        for (int q = 0; q < 4; ++q) rank += (((p0 + q) ^ sw) < n) & (y[q] > x);
       }
-      merge8(x, y);
-      if (span * 2 < kLhCons) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] = x[e];
-      } else if (row0 + row < R) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) part[(int64_t(row0 + row) * nvs + vs) * 8 + e] = x[e];
-      }
+      if (rank < 8 && row0 + row < R)
+        part[(int64_t(row0 + row) * nvs + vs) * 8 + rank] = (x >> 32) ? x : 0ull;
     }
-    __syncthreads();
   }
 }
 
