@@ -512,7 +512,14 @@ tr_status step_impl(const tr_tree* t, int32_t B, int64_t V, int32_t k, const voi
     uint64_t* part = reinterpret_cast<uint64_t*>(w + lplan.part_off);
     hipError_t e = tr::launch_lmhead(lm->h, lm->W, int32_t(rows), lm->H, V, part, lplan.nvs,
                                      hipStream_t(stream));
-    if (e == hipSuccess)
+    // few rows: the few-row step kernel merges the slice lists in its row
+    // blocks; else one merge block per row, the tail in the last of each
+    // sequence
+    const tr::StepPlan sp = few_row_step_enabled() ? tr::plan_step(B, t->dev, V, k, 2, false, tail)
+                                                   : tr::StepPlan{};
+    if (e == hipSuccess && sp.use)
+      e = tr::launch_step_lmhead(t->dev, part, V, k, ids, tail, w, sp, hipStream_t(stream));
+    else if (e == hipSuccess)
       e = tr::launch_lmhead_merge(t->dev, rows, part, lplan.nvs, V, k, ids, tail, w,
                                   hipStream_t(stream));
     return hip_status(e, "tr_step_lmhead");

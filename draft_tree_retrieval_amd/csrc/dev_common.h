@@ -11,6 +11,7 @@ namespace tr {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- numbers
 // Order code of an IEEE float bit pattern: a larger value gets a larger

@@ -40,7 +40,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kLhRows = 96;     // query rows per block (6 tiles of 16)
 constexpr int kLhTiles = kLhRows / 16;
@@ -49,7 +48,7 @@ constexpr int kLhVtW = 2;
 constexpr int kLhProd = 4;      // producer waves: the h chunk DMA
 constexpr int kLhDmaPerProd = kLhRows * 16 / 64 / kLhProd;    // 6 DMA loads per chunk each
 constexpr int kLhKc = 128;      // k per super-step (one staged h chunk)
-constexpr int kLhRing = 4;      // W super-steps in flight per consumer wave
+constexpr int kLhWRing = 8;     // W k-steps (32 k) held per consumer wave, seven in flight
 constexpr int kLhUnroll = 4;    // steps per loop round
 constexpr int kLhHBuf = 4;      // staged h chunks (three in flight ahead of the one in use)
 constexpr int kLhChunkBytes = kLhRows * kLhKc * 2;      // 24 KB
@@ -74,7 +73,7 @@ __global__ __launch_bounds__(512) void lmhead_topk_kernel(const uint16_t* __rest
   __shared__ __attribute__((aligned(16))) uint32_t s_hm[kLhRows][16];   // holder maxima
   __shared__ uint32_t s_thr[kLhRows];
   __shared__ __attribute__((aligned(16))) uint32_t s_cnt[kLhRows];
-  static_assert(kLhHBuf == 4 && kLhUnroll % kLhHBuf == 0 && kLhUnroll % kLhRing == 0,
+  static_assert(kLhHBuf == 4 && kLhUnroll % kLhHBuf == 0 && (4 * kLhUnroll) % kLhWRing == 0,
                 "a static buffer and ring slot per unrolled step");
   auto hbuf = [&](int i) -> uint8_t* {
     return i == 0 ? hbuf0 : i == 1 ? hbuf1 : i == 2 ? hbuf2 : hbuf3;
@@ -146,63 +145,68 @@ __global__ __launch_bounds__(512) void lmhead_topk_kernel(const uint16_t* __rest
       const int64_t vrow = v0 + 16 * j + li < V ? v0 + 16 * j + li : V - 1;
       wp[j] = W + vrow * H + 8 * g;
     }
-    // load s of a super-step: 64 contiguous bytes of each of the tile's 16
-    // rows (lane group g the g-th 16 bytes), the A operand of MFMA step s
-    auto load_w = [&](u32x4 (&r)[kLhVtW][4], int c) {
+    // k-step q (32 k, the A operand of one MFMA step): 64 contiguous bytes of
+    // each of the tile's 16 rows (lane group g the g-th 16 bytes); k-steps
+    // past the end repeat the last one
+    const int nq = 4 * nsteps;
+    auto load_w = [&](u32x4 (&r)[kLhVtW], int q) __attribute__((always_inline)) {
+      q = min(q, nq - 1);
 #pragma unroll
       for (int j = 0; j < kLhVtW; ++j)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) r[j][s] = *reinterpret_cast<const u32x4*>(wp[j] + chunk(c) * kLhKc + 32 * s);
-    };
-    // (compiler memory barriers keep the ring in issue order, so the wait
-    // before a slot's first use leaves the younger slots in flight)
-    u32x4 wr[kLhRing][kLhVtW][4];
-#pragma unroll
-    for (int j = 0; j < kLhRing; ++j) {
-      load_w(wr[j], min(j, nsteps - 1));
+        r[j] = *reinterpret_cast<const u32x4*>(wp[j] + chunk(q >> 2) * kLhKc + 32 * (q & 3));
+      // (keeps the ring in issue order, so each wait below leaves exactly
+      // the younger k-steps in flight)
       asm volatile("" ::: "memory");
-    }
+    };
+    u32x4 wr[kLhWRing][kLhVtW];
+#pragma unroll
+    for (int q = 0; q < kLhWRing; ++q) load_w(wr[q], q);
     for (int c0 = 0; c0 < nround; c0 += kLhUnroll) {
 #pragma unroll
       for (int j = 0; j < kLhUnroll; ++j) {
         const int c = c0 + j;                       // steps past the end only wait
-        // W(c): the younger ring slots (3 x 8 loads) may stay in flight.
-        // Written out: the compiler's own count is lost across the loop's
-        // back edge and would drain every load at the first step of a round.
-        static_assert((kLhRing - 1) * 4 * kLhVtW == 24, "vmcnt below");
-        __builtin_amdgcn_s_waitcnt(0x4F78);        // vmcnt(24), lgkm/exp not waited
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        if (c < nsteps) {
-          const uint8_t* hb = hbuf(j % kLhHBuf);
-          // row 16 t + li sits at byte (16 t + li) * 256, its column chunk
-          // 4 s + g at position (4 s + g) ^ li (row & 15 == li).  The B
-          // operands of MFMA step s + 1 are read while step s multiplies.
-          bf16x8 bv[2][kLhTiles];
-          auto read_b = [&](bf16x8 (&b)[kLhTiles], int s) __attribute__((always_inline)) {
-            const uint8_t* hs = hb + li * 256 + (((4 * s + g) ^ li) << 4);
+        const uint8_t* hb = hbuf(j % kLhHBuf);
+        // row 16 t + li sits at byte (16 t + li) * 256, its column chunk
+        // 4 s + g at position (4 s + g) ^ li (row & 15 == li).  The B
+        // operands of MFMA step s + 1 are read while step s multiplies.
+        bf16x8 bv[2][kLhTiles];
+        auto read_b = [&](bf16x8 (&b)[kLhTiles], int s) __attribute__((always_inline)) {
+          const uint8_t* hs = hb + li * 256 + (((4 * s + g) ^ li) << 4);
 #pragma unroll
-            for (int t = 0; t < kLhTiles; ++t) b[t] = *reinterpret_cast<const bf16x8*>(hs + t * 4096);
-          };
-          read_b(bv[0], 0);
+          for (int t = 0; t < kLhTiles; ++t) b[t] = *reinterpret_cast<const bf16x8*>(hs + t * 4096);
+        };
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < 4; ++s) {
+          constexpr int kYoung = (kLhWRing - 1) * kLhVtW;   // loads of the younger k-steps
+          static_assert(kYoung == 14, "vmcnt below");
+          // k-step 4c + s landed; only the younger ones' loads may still fly.
+          // Written out: the compiler's own count is lost across the loop's
+          // back edge and would drain every load at the first step of a round.
+          __builtin_amdgcn_s_waitcnt(0x0F7E);      // vmcnt(14), lgkm/exp not waited
+          asm volatile("" ::: "memory");
+          if (s == 0) {                             // h chunk c is in and its buffer free
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            if (c < nsteps) read_b(bv[0], 0);
+          }
+          if (c < nsteps) {
             if (s < 3) read_b(bv[(s + 1) & 1], s + 1);
             __builtin_amdgcn_sched_barrier(0);      // keep the reads ahead of the products
+            const int slot = (4 * j + s) % kLhWRing;
 #pragma unroll
             for (int t = 0; t < kLhTiles; ++t)
 #pragma unroll
               for (int vj = 0; vj < kLhVtW; ++vj)
                 acc[vj][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, wr[j % kLhRing][vj][s]), bv[s & 1][t], acc[vj][t], 0, 0, 0);
+                    __builtin_bit_cast(bf16x8, wr[slot][vj]), bv[s & 1][t], acc[vj][t], 0, 0, 0);
           }
+          if (s == 3) {
+            // the LDS reads of this chunk are done before the next barrier
+            __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0), vm/exp not waited
+            asm volatile("" ::: "memory");
+          }
+          load_w(wr[(4 * j + s) % kLhWRing], 4 * c + s + kLhWRing);
         }
-        // the LDS reads of this step are done before the next barrier
-        __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0), vm/exp not waited
-        asm volatile("" ::: "memory");
-        load_w(wr[j % kLhRing], min(c + kLhRing, nsteps - 1));
-        asm volatile("" ::: "memory");
       }
     }
   }

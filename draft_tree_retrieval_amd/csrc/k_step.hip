@@ -106,6 +106,77 @@ __device__ __forceinline__ void step_row(const void* __restrict__ logits, int64_
   select_block<BF16, KM, kStepNT, NV, true>(rowp, 0, V, k, out);
 }
 
+// Largest 64-bit key over the wave, in every lane: the codes' maximum,
+// then the largest low word among the lanes holding that code (two DPP and
+// permlane reductions instead of six 64-bit shuffles).
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
+  const uint32_t hi = uint32_t(v >> 32);
+  const uint32_t mh = wave_max_u32(hi);
+  const uint32_t ml = wave_max_u32(hi == mh ? uint32_t(v) : 0u);
+  return (uint64_t(mh) << 32) | ml;
+}
+
+// A row block of the LM head's step: the row's candidates are the 8 best
+// keys of every 128-id vocabulary slice, descending per slice
+// (lmhead_topk_kernel), and thread t holds slice t's list (V <= 32768: at
+// most 256 slices).  Each wave takes its lists' 8 best in 8 rounds (the
+// largest head, popped from its list); wave 0 merges the four waves' lists
+// the same way and publishes rank 0 (the greedy token) at its first round.
+template <int KM>
+__device__ __forceinline__ void step_row_cand(const uint64_t* __restrict__ part, int64_t V,
+                                              int32_t k, int row, int32_t* __restrict__ ids_out,
+                                              uint32_t* mail) {
+  constexpr int NW = kStepNT / 64, NL = 8;             // lists of 8 keys per slice
+  static_assert(KM <= NL, "ranks within one slice list");
+  __shared__ uint64_t s_lists[NW][NL];
+  const int nvs = int((V + 127) / 128);
+  StepRowOut out{ids_out + int64_t(row) * k, mail + int64_t(row) * k, k};
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint64_t v[NL];
+  if (tid < nvs) {
+    const u64x2* p = reinterpret_cast<const u64x2*>(part + (int64_t(row) * nvs + tid) * NL);
+#pragma unroll
+    for (int q = 0; q < NL / 2; ++q) {
+      const u64x2 x = p[q];
+      v[2 * q] = x[0];
+      v[2 * q + 1] = x[1];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) v[i] = 0;
+  }
+  auto pop = [&](uint64_t (&l)[NL]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NL - 1; ++i) l[i] = l[i + 1];
+    l[NL - 1] = 0;
+  };
+  uint64_t best[NL];
+#pragma unroll
+  for (int r = 0; r < NL; ++r) {
+    const uint64_t m = wave_max_key(v[0]);
+    best[r] = m;
+    if (m != 0 && v[0] == m) pop(v);                   // keys are distinct: one lane pops
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < NL; ++r) s_lists[wave][r] = best[r];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int r = 0; r < NL; ++r) v[r] = lane < NW ? s_lists[lane][r] : 0;
+#pragma unroll
+    for (int r = 0; r < KM; ++r) {
+      const uint64_t m = wave_max_key(v[0]);
+      if (lane == 0) {
+        if (r == 0) out.first(key_id(m));
+        else out.put(r, m);
+      }
+      if (m != 0 && v[0] == m) pop(v);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- tail
 // Per-launch LDS of the tail block beyond the shared tail state: the
 // update map as a direct table (token -> node whose top-k row M now holds
@@ -581,7 +652,8 @@ __device__ __forceinline__ void step_helper(int b, int h, int H, int64_t V, int3
 
 }  // namespace
 
-template <bool BF16, int KM, typename MT>
+// CAND: the rows are the LM head's slice lists (step_row_cand), not logits.
+template <bool BF16, int KM, typename MT, bool CAND>
 __global__ __launch_bounds__(kStepNT) void step_kernel(const void* __restrict__ logits, int64_t V,
                                                        int32_t k, int32_t* ids_out, uint8_t* ws,
                                                        TreeDev tree, TailArgs tail, int32_t rows,
@@ -591,7 +663,10 @@ __global__ __launch_bounds__(kStepNT) void step_kernel(const void* __restrict__ 
   uint64_t* verdict = reinterpret_cast<uint64_t*>(ws + kVerdictOff);
   int bid = int(blockIdx.x);
   if (bid < rows) {
-    step_row<BF16, KM>(logits, V, k, bid, ids_out, mail);
+    if constexpr (CAND)
+      step_row_cand<KM>(static_cast<const uint64_t*>(logits), V, k, bid, ids_out, mail);
+    else
+      step_row<BF16, KM>(logits, V, k, bid, ids_out, mail);
     return;
   }
   bid -= rows;
@@ -619,8 +694,8 @@ hipError_t launch_step(const TreeDev& tree, const void* logits, int l_is_bf16, i
                        int32_t k, int32_t* topk_ids, const TailArgs& tail, uint8_t* ws,
                        const StepPlan& plan, hipStream_t s) {
 #define TR_STEP(BF, KMV, MTV)                                                                    \
-  hipLaunchKernelGGL((step_kernel<BF, KMV, MTV>), dim3(unsigned(plan.grid)), dim3(kStepNT), 0, s, \
-                     logits, V, k, topk_ids, ws, tree, tail, plan.rows, plan.B, plan.commit,     \
+  hipLaunchKernelGGL((step_kernel<BF, KMV, MTV, false>), dim3(unsigned(plan.grid)), dim3(kStepNT), \
+                     0, s, logits, V, k, topk_ids, ws, tree, tail, plan.rows, plan.B, plan.commit, \
                      plan.help_base, plan.helpers)
 #define TR_STEP_M(BF, KMV)                            \
   do {                                                \
@@ -636,6 +711,22 @@ hipError_t launch_step(const TreeDev& tree, const void* logits, int l_is_bf16, i
   prof_end(s);
 #undef TR_STEP_M
 #undef TR_STEP
+  return hipGetLastError();
+}
+
+hipError_t launch_step_lmhead(const TreeDev& tree, const uint64_t* part, int64_t V, int32_t k,
+                              int32_t* topk_ids, const TailArgs& tail, uint8_t* ws,
+                              const StepPlan& plan, hipStream_t s) {
+  prof_begin(s, TR_KERNEL_LMHEAD_MERGE);
+  if (tail.m_is64)
+    hipLaunchKernelGGL((step_kernel<true, 8, int64_t, true>), dim3(unsigned(plan.grid)),
+                       dim3(kStepNT), 0, s, part, V, k, topk_ids, ws, tree, tail, plan.rows,
+                       plan.B, plan.commit, plan.help_base, plan.helpers);
+  else
+    hipLaunchKernelGGL((step_kernel<true, 8, int32_t, true>), dim3(unsigned(plan.grid)),
+                       dim3(kStepNT), 0, s, part, V, k, topk_ids, ws, tree, tail, plan.rows,
+                       plan.B, plan.commit, plan.help_base, plan.helpers);
+  prof_end(s);
   return hipGetLastError();
 }
 

@@ -174,6 +174,10 @@ StepPlan plan_step(int32_t B, const TreeDev& tree, int64_t V, int32_t k, int32_t
 hipError_t launch_step(const TreeDev& tree, const void* logits, int l_is_bf16, int64_t V,
                        int32_t k, int32_t* topk_ids, const TailArgs& tail, uint8_t* ws,
                        const StepPlan& plan, hipStream_t s);
+// The few-row step on the LM head's slice lists (k <= 8) instead of logits.
+hipError_t launch_step_lmhead(const TreeDev& tree, const uint64_t* part, int64_t V, int32_t k,
+                              int32_t* topk_ids, const TailArgs& tail, uint8_t* ws,
+                              const StepPlan& plan, hipStream_t s);
 // Fused LM head + top-k: slices of 128 vocabulary rows, 8 keys per (row,
 // slice), then one merge block per row.
 struct LmheadPlan {

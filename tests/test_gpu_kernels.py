@@ -673,7 +673,12 @@ def test_lmhead_topk_large_vocab_sampled_rows(tr):
     check_lmhead_rows(z, out[pick].cpu().numpy(), k, lmhead_tol(H))
 
 
-def test_step_lmhead_parity(tr):
+@pytest.mark.parametrize("path", ["few_row", "merge"])
+def test_step_lmhead_parity(tr, path, monkeypatch):
+    # few rows go through the few-row step kernel's slice-list row blocks;
+    # with that kernel switched off, through one merge block per row
+    if path == "merge":
+        monkeypatch.setenv("TR_FEW_ROW_STEP", "0")
     levels = RAND_LEVELS[4]
     t = otree(levels)
     T, D = t.n_nodes, t.max_depth

@@ -207,3 +207,50 @@ def test_workspace_reused_across_shapes(tr, monkeypatch):
             assert bool(got["flags"] & tr.TR_FLAG_CACHE_FULL) == (not fits)
             if not fits:
                 assert int(got["P"][0]) == 44 and torch.equal(got["kc"], kc)
+
+
+@pytest.mark.parametrize("B,Hkv", [(1, 32), (3, 8)])
+def test_step_lmhead_paths_commit(tr, monkeypatch, B, Hkv):
+    # the fused LM head's step through the few-row step kernel (the slice
+    # lists merged in its row blocks) and through the merge kernel (one block
+    # per row, the tail in the last one of a sequence): the same bits, cache
+    # commits included
+    g = torch.Generator().manual_seed(300 + B)
+    rng = np.random.default_rng(300 + B)
+    V, k, cap, H = 32000, 8, 64, 256
+    P = [int(x) for x in rng.integers(0, cap - 7, size=B)]
+    t, tree, M, root, tok_h, _, kc, vc, kt, vt, Pt = planted_step_inputs(tr, g, rng, TREE_81, B, V,
+                                                                         k, Hkv, cap, P)
+    T = t.n_nodes
+    W = (torch.randn((V, H), generator=g) / H ** 0.5).to(torch.bfloat16)
+    # hidden states leaning towards the W row of a child's token, so that
+    # drafts are accepted along random edges
+    h = torch.randn((B, T, H), generator=g) * 0.3
+    for b in range(B):
+        for n in range(T):
+            ch = t.children(n)
+            if ch and rng.random() < 0.7:
+                h[b, n] += W[tok_h[b, ch[int(rng.integers(len(ch)))]]].float() * 4.0
+    h = h.to(torch.bfloat16)
+
+    def run(few):
+        set_kernel(monkeypatch, few)
+        ws = tr.new_lmhead_workspace(B * T, V, k)
+        dM, droot, dkc, dvc, dP = (x.to(DEV) for x in (M, root, kc, vc, Pt))
+        tok = torch.from_numpy(tok_h.astype(np.int32)).to(DEV)
+        L = torch.empty((B,), dtype=torch.int32, device=DEV)
+        path = torch.empty((B, t.max_depth + 1), dtype=torch.int32, device=DEV)
+        em = torch.empty((B, t.max_depth + 1), dtype=torch.int32, device=DEV)
+        topk = torch.empty((B, T, k), dtype=torch.int32, device=DEV)
+        tr.tr_step_lmhead(tree, h.to(DEV), W.to(DEV), dM, tok, droot, L, path, em, ws, kt.to(DEV),
+                          vt.to(DEV), dkc, dvc, dP, topk_out=topk)
+        return dict(M=dM.cpu(), root=droot.cpu(), kc=dkc.cpu(), vc=dvc.cpu(), P=dP.cpu(),
+                    tok=tok.cpu(), L=L.cpu(), path=path.cpu(), em=em.cpu(), topk=topk.cpu(),
+                    flags=tr.tr_read_device_status(ws))
+
+    few, merged = run(True), run(False)
+    assert few["flags"] == 0 and merged["flags"] == 0
+    assert int(few["L"].max()) >= 2                        # drafts were accepted
+    for key in few:
+        if key != "flags":
+            assert torch.equal(few[key], merged[key]), key
