@@ -581,8 +581,9 @@ __device__ __forceinline__ void step_tail(const TreeDev& tree, int b, int32_t k,
 
 // ---------------------------------------------------------------- commit
 // Commit block c of C for sequence b: waits for the tail's verdict, copies
-// its share of the accepted rows; the last of the C blocks clears the
-// verdict for the next call.
+// its share of the accepted rows; the last of the C blocks to read the
+// verdict clears it for the next call (before the copies, so nothing waits
+// for the copies' stores before the kernel ends).
 __device__ __forceinline__ void step_commit(const TreeDev& tree, int b, int c, int C,
                                             const TailArgs& a, uint8_t* ws, uint64_t* verdict,
                                             uint32_t* done) {
@@ -601,6 +602,15 @@ __device__ __forceinline__ void step_commit(const TreeDev& tree, int b, int c, i
       }
     }
     s_hdr = h;
+    // counted in once the verdict is read: the last of the C blocks clears
+    // it for the next call while the rows are still being copied
+    if (h >> 63) {
+      const uint32_t prev = __hip_atomic_fetch_add(done + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (prev == uint32_t(C - 1)) {
+        __hip_atomic_store(done + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        verdict_put(verdict + b, 0);
+      }
+    }
   }
   __syncthreads();
   const uint64_t h = s_hdr;
@@ -612,9 +622,6 @@ __device__ __forceinline__ void step_commit(const TreeDev& tree, int b, int c, i
       if (((t < 64 ? a0 >> t : a1 >> (t - 64)) & 1u) != 0u) s_path[tree.depth[t]] = t;
     __syncthreads();
     commit_rows(s_path, int(tree.depth[best]), P, tree, b, a, ws, c * kStepNT + tid, C * kStepNT);
-  }
-  if (h >> 63) {
-    if (last_block_arrives(done + b, uint32_t(C)) && tid == 0) verdict_put(verdict + b, 0);
   }
 }
 
