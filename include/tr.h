@@ -377,7 +377,10 @@ tr_status tr_lmhead_topk(int32_t rows, int32_t H, int64_t V, int32_t k, const vo
 /* tr_step_ex with the LM head in front: the top-k of every node comes from
  * h [B][T][H] and W instead of a logits tensor; everything after it
  * (verification, update, commit, next retrieval) and every other argument
- * as tr_step_ex.  Greedy verification only. */
+ * as tr_step_ex.  Greedy verification only.  With fewer than 256 rows (B*T)
+ * and V <= 32768 the slices' candidates are merged by the few-row step
+ * launch of tr_step (TR_FEW_ROW_STEP=0 selects one merge block per row
+ * instead; same results). */
 tr_status tr_step_lmhead(const tr_tree* t, int32_t B, int32_t H, int64_t V, int32_t k,
                          const void* h, const void* W, tr_dtype dtype, void* M, tr_dtype m_dtype,
                          int32_t* tree_tok, int32_t* root_tok, int32_t* accept_len,
