@@ -956,9 +956,12 @@ __global__ __launch_bounds__(256) void attn_merge_bf16(
   float2 ml[kBatch];
   u32x4 po[kBatch];
   for (int c0 = 0; c0 < nc; c0 += kBatch) {
+    // (nc is the record's: a branch the whole block takes alike, so a
+    // record of few partials issues only their loads)
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
-      const int c = min(c0 + i, nc - 1);
+      if (c0 + i >= nc) break;
+      const int c = c0 + i;
       const int slot = 2 * (first + c) + (c == 0 ? s0 : 0);
       const int64_t unit = (int64_t(t) * 2 * gl + slot) * rows_t + rt;
       ml[i] = part_ml[unit];
