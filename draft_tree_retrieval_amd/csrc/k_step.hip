@@ -106,16 +106,6 @@ __device__ __forceinline__ void step_row(const void* __restrict__ logits, int64_
   select_block<BF16, KM, kStepNT, NV, true>(rowp, 0, V, k, out);
 }
 
-// Largest 64-bit key over the wave, in every lane: the codes' maximum,
-// then the largest low word among the lanes holding that code (two DPP and
-// permlane reductions instead of six 64-bit shuffles).
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
-  const uint32_t hi = uint32_t(v >> 32);
-  const uint32_t mh = wave_max_u32(hi);
-  const uint32_t ml = wave_max_u32(hi == mh ? uint32_t(v) : 0u);
-  return (uint64_t(mh) << 32) | ml;
-}
-
 // A row block of the LM head's step: the row's candidates are the 8 best
 // keys of every 128-id vocabulary slice, descending per slice
 // (lmhead_topk_kernel), and thread t holds slice t's list (V <= 32768: at

@@ -175,7 +175,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SAMPLE ? 3 :
                                                    int32_t k, int32_t segs, int64_t seg_len,
                                                    int32_t* __restrict__ ids_out,
                                                    uint64_t* __restrict__ part, uint64_t* stat,
-                                                   uint8_t* ws, TreeDev tree, TailArgs tail) {
+                                                   uint8_t* ws, TreeDev tree, TailArgs tail,
+                                                   int32_t defer) {
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int VE = 16 / ESZ;             // elements per 16-byte vector
   constexpr int NW = NT / 64;              // waves
@@ -436,8 +437,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SAMPLE ? 3 :
     }
   }
 
-  // ---- segments of a row meet in the last one
+  // ---- segments of a row meet in the last one (defer: in topk_seq_kernel,
+  // launched next, so no block holds its slot through a hand-over)
   if (segs > 1) {
+    if (defer) return;
     uint32_t* row_cnt = reinterpret_cast<uint32_t*>(ws + kRowCntOff);
     if (!last_block_arrives(row_cnt + row, uint32_t(segs))) return;
     const int nk = segs * KM;                   // <= 256 by the plan
@@ -518,15 +521,86 @@ hipError_t launch_lmhead_merge(const TreeDev& tree, int64_t rows, const uint64_t
   return hipGetLastError();
 }
 
+// The segment lists of every row of sequence b meet here, one block per
+// sequence, which then runs the step's tail (greedy steps and updates after
+// topk_kernel with defer set).  The sequence's T x segs x KM keys (at most
+// kSeqKeys, segs <= kSeqSegs) come into LDS in one pass; then one thread
+// per row merges the row's segs descending lists: the largest of the lists'
+// heads is the next rank, and that list's next key (one LDS read) replaces
+// its head.
+constexpr int kSeqKeys = 4096;
+constexpr int kSeqSegs = 8;
+template <int KM, typename MT>
+__global__ __launch_bounds__(512) void topk_seq_kernel(const uint64_t* __restrict__ part,
+                                                       int32_t segs, int64_t V, int32_t k,
+                                                       int32_t* __restrict__ ids_out, uint8_t* ws,
+                                                       TreeDev tree, TailArgs tail) {
+  constexpr int NT = 512, NL = kSeqKeys / (2 * NT);  // pair loads per thread
+  __shared__ __attribute__((aligned(16))) uint64_t s_keys[kSeqKeys];
+  const int b = int(blockIdx.x);
+  const int tid = threadIdx.x;
+  const int nk = segs * KM;                          // keys per row
+  const int total = tree.T * nk;                     // <= kSeqKeys (the launch checks)
+  const uint64_t* ps = part + int64_t(b) * total;
+  u64x2 x[NL];
+#pragma unroll
+  for (int q = 0; q < NL; ++q) {                     // nk is even: pairs stay in range
+    const int i = 2 * (tid + q * NT);
+    if (i < total) x[q] = *reinterpret_cast<const u64x2*>(ps + i);
+  }
+#pragma unroll
+  for (int q = 0; q < NL; ++q) {
+    const int i = 2 * (tid + q * NT);
+    if (i < total) *reinterpret_cast<u64x2*>(s_keys + i) = x[q];
+  }
+  __syncthreads();
+  for (int n = tid; n < tree.T; n += NT) {
+    const uint64_t* pr = s_keys + n * nk;
+    uint64_t hd[kSeqSegs];
+#pragma unroll
+    for (int l = 0; l < kSeqSegs; ++l) hd[l] = l < segs ? pr[l * KM] : 0ull;
+    uint32_t pos = 0;                                // 4 bits per list: its head's index
+    const int64_t row = int64_t(b) * tree.T + n;
+#pragma unroll
+    for (int r = 0; r < KM; ++r) {
+      uint64_t m = hd[0];
+      int ml = 0;
+#pragma unroll
+      for (int l = 1; l < kSeqSegs; ++l)
+        if (hd[l] > m) {
+          m = hd[l];
+          ml = l;
+        }
+      if (r < k) put_dev(&ids_out[row * k + r], int32_t(key_id(m)));
+      const uint32_t nx = ((pos >> (4 * ml)) & 15u) + 1u;
+      pos += 1u << (4 * ml);
+      const uint64_t nh = nx < uint32_t(KM) ? pr[ml * KM + int(nx)] : 0ull;
+#pragma unroll
+      for (int l = 0; l < kSeqSegs; ++l) hd[l] = l == ml ? nh : hd[l];
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);                     // the ids' device-scope stores completed
+  __syncthreads();
+  __shared__ TailShared S;
+  const int32_t* topk_b = ids_out + int64_t(b) * tree.T * k;
+  int32_t* tok_b = tail.tree_tok + int64_t(b) * tree.T;
+  seq_tail<MT, KM, NT, true, false>(S, tree, b, k, V, topk_b, tok_b, tail, ws, nullptr, nullptr, segs);
+}
+
 hipError_t launch_topk(const TreeDev& tree, int32_t B, const void* logits, int l_is_bf16, int64_t V,
                        int32_t k, int32_t* topk_ids, const TailArgs& tail, uint8_t* ws,
                        const TopkPlan& plan, hipStream_t s) {
   dim3 grid(plan.segs, unsigned(plan.rows));
   uint64_t* part = reinterpret_cast<uint64_t*>(ws + plan.part_off);
   uint64_t* stat = reinterpret_cast<uint64_t*>(ws + plan.stat_off);
+  // greedy steps and updates with several segments per row: the rows'
+  // segments meet in a second launch, one block per sequence
+  const int defer = !tail.sample && plan.segs > 1 && tail.mode != TAIL_NONE &&
+                    int64_t(B) * tree.T == plan.rows &&
+                    int64_t(tree.T) * plan.segs * plan.kmax <= kSeqKeys && plan.segs <= kSeqSegs ? 1 : 0;
 #define TR_TOPK(BF, KMV, NTV, NVV, SMP)                                                         \
   hipLaunchKernelGGL((topk_kernel<BF, KMV, NTV, NVV, SMP>), grid, dim3(NTV), 0, s, logits, V,   \
-                     k, plan.segs, plan.seg_len, topk_ids, part, stat, ws, tree, tail)
+                     k, plan.segs, plan.seg_len, topk_ids, part, stat, ws, tree, tail, defer)
 #define TR_TOPK_NT(BF, KMV)                                                 \
   do {                                                                      \
     if (tail.sample) {                                                      \
@@ -542,6 +616,17 @@ hipError_t launch_topk(const TreeDev& tree, int32_t B, const void* logits, int l
     if (plan.kmax == 8) TR_TOPK_NT(true, 8); else TR_TOPK_NT(true, 16);
   } else {
     if (plan.kmax == 8) TR_TOPK_NT(false, 8); else TR_TOPK_NT(false, 16);
+  }
+  if (defer) {
+#define TR_SEQ(KMV, MTV)                                                                        \
+  hipLaunchKernelGGL((topk_seq_kernel<KMV, MTV>), dim3(unsigned(B)), dim3(512), 0, s, part,     \
+                     plan.segs, V, k, topk_ids, ws, tree, tail)
+    if (plan.kmax == 8) {
+      if (tail.m_is64) TR_SEQ(8, int64_t); else TR_SEQ(8, int32_t);
+    } else {
+      if (tail.m_is64) TR_SEQ(16, int64_t); else TR_SEQ(16, int32_t);
+    }
+#undef TR_SEQ
   }
   prof_end(s);
 #undef TR_TOPK_NT

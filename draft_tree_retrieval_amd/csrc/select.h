@@ -77,6 +77,16 @@ __device__ __forceinline__ void block_merge(TopList<KM>& L, uint64_t (*s_keys)[K
 }
 
 
+// Largest 64-bit key over the wave, in every lane: the codes' maximum,
+// then the largest low word among the lanes holding that code (two DPP and
+// permlane reductions instead of six 64-bit shuffles).
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
+  const uint32_t hi = uint32_t(v >> 32);
+  const uint32_t mh = wave_max_u32(hi);
+  const uint32_t ml = wave_max_u32(hi == mh ? uint32_t(v) : 0u);
+  return (uint64_t(mh) << 32) | ml;
+}
+
 // Flip codes of two bfloat16 halves (16-bit arithmetic per half) or of one
 // float: unsigned order = value order, -0.0 one below +0.0.
 __device__ __forceinline__ uint32_t flip16x2(uint32_t w) {
