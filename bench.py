@@ -533,6 +533,25 @@ def main():
         torch.cuda.synchronize()
         unfused = {"steps_per_s": round(steps / (time.perf_counter() - t0), 2),
                    "what": "attention + bf16 GEMM writing the logits (torch.matmul) + tr_step"}
+        if args.launch == "graph":
+            # the same steps captured once and replayed, as the fused value is
+            # (its trajectory differs from the fused one where the bf16
+            # logits round a ranking differently, so only the time is kept)
+            dec = fresh_decoder()
+            for i in range(args.warmup):
+                unfused_step(i)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for i in range(steps):
+                    unfused_step(args.warmup + i)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            graph.replay()
+            torch.cuda.synchronize()
+            unfused["graph_steps_per_s"] = round(steps / (time.perf_counter() - t0), 2)
+            assert dec.device_flags() == 0
+            del graph
         log("unfused:", json.dumps(unfused))
 
     cpu = None
