@@ -235,6 +235,75 @@ def test_update_parity_duplicate_rows(tr, m_dtype):
         assert (Md[b].cpu().numpy() == Mo).all()
 
 
+@pytest.mark.parametrize("k,m_dtype", [(3, torch.int32), (16, torch.int64)])
+def test_update_long_rows_segments(tr, k, m_dtype):
+    # rows longer than one block holds: each row's segments meet in the
+    # per-sequence merge launch, which then runs the update (tie-prone bf16
+    # rows, tokens that repeat, k = 3 and the 16-key lists)
+    rng = np.random.default_rng(40 + k)
+    levels = RAND_LEVELS[4] if k >= 8 else [[1]] * 80      # 81 nodes either way
+    t = otree(levels)
+    tree = tr.Tree.from_levels(levels, k)
+    B, V = 2, 128256
+    g = torch.Generator().manual_seed(41 + k)
+    z = (torch.randn((B, t.n_nodes, V), generator=g) * 3).to(torch.bfloat16)
+    tok = rng.integers(0, 40, size=(B, t.n_nodes)).astype(np.int32)
+    M0 = torch.from_numpy(rng.integers(0, V, size=(B, V, k))).to(m_dtype)
+    Md = M0.to(DEV)
+    out = torch.empty((B, t.n_nodes, k), dtype=torch.int32, device=DEV)
+    ws = ws_for(tr, tree, B, V, k)
+    tr.tr_update_topk(tree, z.to(DEV), torch.from_numpy(tok).to(DEV), Md, out, ws)
+    assert tr.tr_read_device_status(ws) == 0
+    for b in range(B):
+        want = O.topk_rows(z[b].float().numpy(), k)
+        assert (out[b].cpu().numpy() == want).all(), b
+        Mo = M0[b].numpy().astype(np.int64).copy()
+        O.update(Mo, tok[b], want)
+        assert (Md[b].cpu().numpy().astype(np.int64) == Mo).all(), b
+
+
+def test_step_long_rows_k16(tr):
+    # the greedy step with 16-key segment lists at a long vocabulary: top-k,
+    # verdict, M and the next tree against the oracle
+    rng = np.random.default_rng(77)
+    levels = RAND_LEVELS[4]
+    t = otree(levels)
+    k, B, V = 16, 2, 128256
+    tree = tr.Tree.from_levels(levels, k)
+    M = torch.from_numpy(rng.integers(0, V, size=(B, V, k))).to(torch.int32)
+    root = torch.from_numpy(rng.integers(0, V, size=(B,))).to(torch.int32)
+    ws = ws_for(tr, tree, B, V, k)
+    dM, droot = M.to(DEV), root.to(DEV)
+    tok = torch.empty((B, t.n_nodes), dtype=torch.int32, device=DEV)
+    tr.tr_retrieve(tree, dM, droot, tok, ws)
+    tok_h = tok.cpu().numpy().astype(np.int64)
+    g = torch.Generator().manual_seed(78)
+    z = torch.randn((B, t.n_nodes, V), generator=g) * 3
+    for b in range(B):                                  # accept along random edges
+        for n in range(1, t.n_nodes):
+            if rng.random() < 0.6:
+                z[b, t.parent[n], tok_h[b, n]] = 40.0 + float(rng.random())
+    z = z.to(torch.bfloat16)
+    L = torch.empty((B,), dtype=torch.int32, device=DEV)
+    path = torch.empty((B, t.max_depth + 1), dtype=torch.int32, device=DEV)
+    em = torch.empty((B, t.max_depth + 1), dtype=torch.int32, device=DEV)
+    topk = torch.empty((B, t.n_nodes, k), dtype=torch.int32, device=DEV)
+    tr.tr_step(tree, z.to(DEV), dM, tok, droot, L, path, em, ws, topk_out=topk)
+    assert tr.tr_read_device_status(ws) == 0
+    lengths = []
+    for b in range(B):
+        Mo = M[b].numpy().astype(np.int64).copy()
+        res, _ = O.step_after_forward(t, Mo, tok_h[b], z[b].float().numpy(), k)
+        v = res.verdict
+        assert (topk[b].cpu().numpy() == res.topk).all(), b
+        assert int(L[b]) == v.accept_len and int(droot[b]) == v.bonus
+        assert path[b, :v.accept_len + 1].cpu().tolist() == v.path.tolist()
+        assert (dM[b].cpu().numpy().astype(np.int64) == Mo).all(), b
+        assert tok[b].cpu().numpy().tolist() == res.next_tok.tolist()
+        lengths.append(v.accept_len)
+    assert max(lengths) >= 2                            # the plants were accepted
+
+
 # ------------------------------------------------------------------ attention
 def attn_inputs(g, B, T, Hq, Hkv, P, cap, dtype):
     q = torch.randn((B, T, Hq, 128), generator=g).to(dtype)
