@@ -124,10 +124,11 @@ __device__ __forceinline__ u32x4 pick(const u32x4 (&x)[N], int i) {
 // logits).  One block of NT threads, every element read once into registers
 // (NV 16-byte vectors per lane, so s1 - s0 <= NT * NV * 16 / element size):
 //   1. every element becomes a flip code and every vector keeps its largest;
-//   2. each wave bisects its lane maxima for the k-th largest and keeps its
-//      k largest; with FIRST, the block's largest code gives the best
-//      element (the lowest id among those with that code), reported at once
-//      through out.first(id) by thread 0;
+//   2. with FIRST, the block's largest code gives the best element (the
+//      lowest id among those with that code), reported at once through
+//      out.first(id) by thread 0 before the rest of the selection; then
+//      each wave bisects its lane maxima for the k-th largest and keeps its
+//      k largest;
 //   3. T = the k-th largest of the waves' kept maxima is reached by k
 //      elements, so every one of the k best reaches it (lowered by one when
 //      it is +0.0's flip code, so -0.0 passes too): only vectors whose
@@ -203,29 +204,11 @@ __device__ __forceinline__ void select_block(const uint8_t* __restrict__ rowp, i
   if (BF16) lm = max(lm & 0xFFFFu, lm >> 16);
   lm = max(lm, max(hu, tu));
 
-  // ---- 2. the wave's k-th largest lane maximum and its k largest
-  constexpr int kBits = BF16 ? 16 : 32;
-  uint32_t lo = 0;
-#pragma unroll
-  for (int bit = kBits - 1; bit >= 0; --bit) {
-    const uint32_t c = lo | (1u << bit);
-    if (__popcll(__ballot(lm >= c)) >= k) lo = c;
-  }
-  {
-    const uint64_t gt = __ballot(lm > lo);               // fewer than k lanes
-    const int ngt = __popcll(gt);
-    const uint32_t below =
-        __builtin_amdgcn_mbcnt_hi(uint32_t(gt >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(gt), 0u));
-    if (lm > lo) s_top[wave * KM + below] = lm;
-    if (lane >= ngt && lane < k) s_top[wave * KM + lane] = lo;
-  }
+  // ---- 2. with FIRST, the best element before the rest of the selection
   if (FIRST) {
     const uint32_t wmx = wave_max_u32(lm);
     if (lane == 0) s_mx[wave] = wmx;
-  }
-  __syncthreads();
-
-  if (FIRST) {
+    __syncthreads();
     // the best element: Ma admits the block's largest code (and -0.0 with
     // +0.0); each lane holding such an element finds its lowest id (head,
     // then its vectors in order, then tail), the block the lowest of those
@@ -274,6 +257,24 @@ __device__ __forceinline__ void select_block(const uint8_t* __restrict__ rowp, i
       out.first(~best);
     }
   }
+
+  // ---- 2b. the wave's k-th largest lane maximum and its k largest
+  constexpr int kBits = BF16 ? 16 : 32;
+  uint32_t lo = 0;
+#pragma unroll
+  for (int bit = kBits - 1; bit >= 0; --bit) {
+    const uint32_t c = lo | (1u << bit);
+    if (__popcll(__ballot(lm >= c)) >= k) lo = c;
+  }
+  {
+    const uint64_t gt = __ballot(lm > lo);               // fewer than k lanes
+    const int ngt = __popcll(gt);
+    const uint32_t below =
+        __builtin_amdgcn_mbcnt_hi(uint32_t(gt >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(gt), 0u));
+    if (lm > lo) s_top[wave * KM + below] = lm;
+    if (lane >= ngt && lane < k) s_top[wave * KM + lane] = lo;
+  }
+  __syncthreads();
 
   // ---- 3. T = the block's k-th largest lane maximum (the k-th largest of
   // the waves' k largest).  Candidates: elements at or above T.
