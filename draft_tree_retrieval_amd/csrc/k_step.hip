@@ -498,6 +498,11 @@ __device__ __forceinline__ void step_tail(const TreeDev& tree, int b, int32_t k,
   Verdict vd{};
   if (wave == 0) {
     vd = tail_verify_wave(S, tree, k);
+    if (tid == 0 && tail.k_cache) {                    // the verdict, before the prefetched rows land
+      const bool fits = tail_commit_fits(S, tail, vd.L);
+      if (commit) verdict_put(verdict + b, verdict_word(fits, vd.best, S.P));
+      if (!fits) set_flag(ws, TR_FLAG_CACHE_FULL);
+    }
     if (path_only) {
       wave_lds_sync();
       tail_update_claim(S, tree, V, ws, true);
@@ -526,11 +531,6 @@ __device__ __forceinline__ void step_tail(const TreeDev& tree, int b, int32_t k,
       if (fits) tail.prefix_len[b] = int32_t(S.P + vd.L + 1);
     }
   } else {
-    if (tid == 64 && tail.k_cache) {
-      const bool fits = tail_commit_fits(S, tail, S.L);
-      if (commit) verdict_put(verdict + b, verdict_word(fits, S.best, S.P));
-      if (!fits) set_flag(ws, TR_FLAG_CACHE_FULL);
-    }
     tail_write_verdict(S, tree, b, tail.accept_len, tail.accept_path, nullptr, tail.emitted, 64);
     // thread 64 + n: the rest of row n, then M[tok n] = row n if n wins its token
     const int n = tid - 64;

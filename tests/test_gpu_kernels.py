@@ -724,7 +724,9 @@ def test_lmhead_topk_parity(tr, rows, H, V, k):
     tr.tr_lmhead_topk(h.to(DEV), W.to(DEV), k, out, ws)
     z = O.lmhead_logits(h.float().numpy(), W.float().numpy())
     exact = check_lmhead_rows(z, out.cpu().numpy(), k, lmhead_tol(H))
-    assert exact >= rows * 0.6                       # the rest: valid within the bound
+    # the bound leaves every row of the short products separated (so each
+    # must match exactly) and 72 of 81 at H = 4096; the rest: valid within it
+    assert exact == rows if H <= 512 else exact >= int(rows * 0.85)
 
 
 def test_lmhead_topk_large_vocab_sampled_rows(tr):
