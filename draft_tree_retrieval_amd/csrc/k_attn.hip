@@ -23,7 +23,7 @@
 //    written out.  A unit cut by range boundaries leaves one (m, l, O) partial
 //    per block; the merge kernel combines them in block order.
 //  * Inside a block the keys and values stream HBM -> LDS by LDS DMA through a
-//    four-slot ring; each wave holds one or two 16-row query strips and
+//    four-slot ring, with one barrier per two slots; each wave holds one or two 16-row query strips and
 //    computes S^T = K Q^T and O^T = V^T P^T with v_mfma_f32_16x16x32_bf16, so
 //    a lane's output column is its query row and the softmax statistics stay
 //    in the lane.  K sits in LDS as [key][d] (16-byte chunks XOR-swizzled by
@@ -177,10 +177,12 @@ __device__ __forceinline__ void mark_empty(float2* part_ml, int64_t unit0, int r
 // first 16-key tile of the 32-key block for m < 4, of the second for
 // m >= 4) so that the probabilities need no cross-lane moves.
 // Waits are explicit: a workgroup fence would wait for every DMA in flight,
-// so the loop synchronises with a bare barrier after a vmcnt wait that
-// leaves the younger sub-blocks' DMA (4 loads each per wave) in flight, and
+// so the loop synchronises with a bare barrier after its own vmcnt wait, and
 // each ring slot is its own LDS array named statically (one array would make
-// the compiler wait for DMAs into the other slots before every read).
+// the compiler wait for DMAs into the other slots before every read).  One
+// barrier serves two 64-key steps: at an even step both of the pair's
+// sub-blocks have landed, and the two slots the previous pair read are
+// refilled with the next pair, which has two to three steps to land.
 constexpr int kSB = 64;                   // keys per sub-block
 constexpr float kLazy = 8.f;              // lazy rescaling threshold (log2 units)
 constexpr int kRingSlots = 4;
@@ -838,21 +840,17 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
     int slot = 0;                                   // the block's first unit: slot 0
     bool fresh = true;
     reset();
-    // three sub-blocks in flight (the pages of the first four looked up at once)
+    // two sub-blocks in flight before the loop (the pages of the first three looked up at once)
     {
-      Walk w1 = wd, w2, w3;
+      Walk w1 = wd, w2;
       advance(w1);
       w2 = w1;
       advance(w2);
-      w3 = w2;
-      advance(w3);
       const int p0 = page(wd), p1 = nj > 1 ? page(w1) : 0, p2 = nj > 2 ? page(w2) : 0;
-      const int p3 = nj > 3 ? page(w3) : 0;
       dma(wd, p0, 0);
       if (nj > 1) dma(w1, p1, 1);
-      if (nj > 2) dma(w2, p2, 2);
-      wd = w3;
-      pnext = p3;
+      wd = w2;
+      pnext = p2;
     }
     // the first unit's queries, then everything landed before the loop (an
     // explicit wait: otherwise the compiler waits for all loads in flight,
@@ -866,26 +864,29 @@ __global__ __launch_bounds__(512) void attn_prefix_bf16(
 #pragma unroll
       for (int jj = 0; jj < kRingSlots; ++jj) {
         const int j = j0 + jj;
-        // sub-block j landed: only the younger ones' loads may still fly
-        if (j + 2 < nj) {
-          __builtin_amdgcn_s_waitcnt(0x0F78);      // vmcnt(8)
-        } else if (j + 1 < nj) {
-          __builtin_amdgcn_s_waitcnt(0x0F74);      // vmcnt(4)
-        } else {
+        // even steps: sub-blocks j and j + 1 landed (nothing younger is in
+        // flight yet), then one barrier for both steps
+        if ((jj & 1) == 0) {
           __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0)
+          asm volatile("" ::: "memory");
+          __builtin_amdgcn_s_barrier();
+          asm volatile("" ::: "memory");
         }
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
         // this step's DMA is issued after the scores and probabilities, so
         // its issue overlaps the matrix cores instead of holding every wave
         // back right after the barrier
         if (j < nj && active) probs(kslot(jj), vslot(jj), wc.s, wc.P, fresh);
-        if (j + 3 < nj) {
-          const int pid = pnext;
-          dma(wd, pid, (jj + 3) % kRingSlots);
-          advance(wd);
-          if (j + 4 < nj) pnext = page(wd);
+        if ((jj & 1) == 0) {                       // the slots of steps j - 2 and j - 1
+          if (j + 2 < nj) {
+            dma(wd, pnext, (jj + 2) % kRingSlots);
+            advance(wd);
+            if (j + 3 < nj) pnext = page(wd);
+          }
+          if (j + 3 < nj) {
+            dma(wd, pnext, (jj + 3) % kRingSlots);
+            advance(wd);
+            if (j + 4 < nj) pnext = page(wd);
+          }
         }
         if (j < nj) {
           if (active) weigh(vslot(jj));
